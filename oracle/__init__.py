@@ -1,0 +1,28 @@
+"""Oracle: a plain, slow, fp64 CPU definition of the speculative-decoding
+verify step, used only to check the GPU path.
+
+TEST INFRASTRUCTURE.  Only the tests, ``__graft_entry__.smoke()`` and the
+CPU-baseline leg of ``bench.py`` may import or call anything here; the
+product path (the C-ABI library and its Python binding) never does, and
+shares no code, table or constant with it.
+
+Modules:
+  philox  -- Philox4x32-10 from its published definition (Salmon et al.,
+             SC'11), and the two verify uniforms per (seed, sequence, position).
+  verify  -- LM-head logits, greedy acceptance, speculative sampling with
+             residual / bonus draw, decision margins, and the closed-form
+             expected tokens per verify pass.
+
+Every function is pinned by the CPU tests (tests/test_oracle_*.py) to
+something other than itself: published Philox known-answer blocks and an
+independent library implementation, exact rational arithmetic for the
+logits, brute force over every draft sequence for greedy decoding,
+chi-square tests of the sampled output against the target distribution, the
+closed form for the expected tokens per pass, and the residual identity.
+"""
+from .philox import philox4x32_10, uniform24, verify_uniforms  # noqa: F401
+from .verify import (  # noqa: F401
+    GreedyResult, SampleResult, accept_greedy, accept_ratio, accept_sample,
+    expected_tokens, expected_tokens_positional, inverse_cdf, lm_head_logits,
+    softmax, widen_bf16,
+)

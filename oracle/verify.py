@@ -1,0 +1,309 @@
+"""fp64 CPU definition of the speculative-decoding verify step.
+
+Notation: q = target distribution, p = draft distribution ("Inference-4"
+names them the other way round; the other pages, and this code, call the
+target's distribution the one in the numerator of the accept ratio).  Every
+function below is written from the pages' description, in their order:
+
+  1. LM-head logits of the K+1 verify positions (the target runs one pass over
+     the last accepted token and the K drafts and yields K+1 distributions:
+     "Inference-4", Draft-model speculative decoding, step 2).
+  2. Greedy acceptance: accept drafts while they equal the target's most
+     likely token; at the first mismatch emit the target's token; if all K
+     match, emit the bonus token from the position after the last draft
+     (same page, greedy bullet, and its generate_speculative listing).
+  3. Speculative sampling: accept draft x with probability min(1, q(x)/p(x)),
+     left to right, stop at the first rejection and draw the replacement from
+     norm(max(0, q - p)); if every draft is accepted, draw the bonus token from
+     the target's distribution after the last draft ("Inference-4", sampling
+     bullet; "speculative-decoding" blog, Rejection sampling section;
+     "Speculative decoding" course page, Why this is not approximate; "What is
+     speculative decoding" guide, How speculative decoding works).
+
+Readings where the pages are silent (each is listed in the design notes):
+ties in argmax go to the lowest index; temperature T divides target and
+draft logits alike; the accept test is u < r with u on a 24-bit grid from
+Philox word 0 and the terminal draw uses Philox word 1; the terminal draw is
+an inverse CDF over the in-order cumulative sum of the weights; if the
+residual mass is zero the draw falls back to q.
+
+Rows with bad data (a draft token outside [0, V), a NaN or +inf logit, or a
+row whose maximum is -inf) are marked: accepted_len = -1, out_tokens all -1.
+
+Part of the oracle (test infrastructure); see oracle/__init__.py.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass
+
+import numpy as np
+
+from .philox import verify_uniforms
+
+
+# ---------------------------------------------------------------- inputs ----
+
+def widen_bf16(bits) -> np.ndarray:
+    """bf16 bit patterns (uint16) -> exact float64 values."""
+    b = np.asarray(bits, dtype=np.uint16).astype(np.uint32) << np.uint32(16)
+    return b.view(np.float32).astype(np.float64)
+
+
+# ---------------------------------------------------------- step 1: logits --
+
+def lm_head_logits(hidden, W, chunk: int = 4096) -> np.ndarray:
+    """logits[m, v] = sum_h hidden[m, h] * W[v, h], accumulated in fp64.
+
+    hidden: [M, H]; W: [V, H] (any float dtype; bf16 inputs are widened with
+    ``widen_bf16`` first).  The products of bf16 or fp32 inputs are exact in
+    fp64; only the summation rounds.  Chunked over V to bound memory.
+    """
+    x = np.asarray(hidden, dtype=np.float64)
+    M, H = x.shape
+    V = W.shape[0]
+    out = np.empty((M, V), dtype=np.float64)
+    for v0 in range(0, V, chunk):
+        v1 = min(V, v0 + chunk)
+        out[:, v0:v1] = x @ np.asarray(W[v0:v1], dtype=np.float64).T
+    return out
+
+
+# ------------------------------------------------------------ helpers ------
+
+def softmax(z, T: float) -> np.ndarray:
+    """softmax(z / T) along the last axis, shifted by the row maximum."""
+    z = np.asarray(z, dtype=np.float64)
+    m = np.max(z, axis=-1, keepdims=True)
+    e = np.exp((z - m) / T)
+    return e / np.sum(e, axis=-1, keepdims=True)
+
+
+def _bad_rows(z) -> np.ndarray:
+    """True for rows (last axis) holding NaN or +inf, or whose max is -inf."""
+    z = np.asarray(z)
+    if z.shape[-1] == 0:
+        return np.ones(z.shape[:-1], bool)
+    nan_or_pinf = np.any(np.isnan(z) | (z == np.inf), axis=-1)
+    all_ninf = np.all(z == -np.inf, axis=-1)
+    return nan_or_pinf | all_ninf
+
+
+def _top2_margin(z) -> np.ndarray:
+    """top1 - top2 of each row (inf when the row has one entry)."""
+    z = np.asarray(z, dtype=np.float64)
+    if z.shape[-1] < 2:
+        return np.full(z.shape[:-1], np.inf)
+    part = -np.partition(-z, 1, axis=-1)[..., :2]
+    return part[..., 0] - part[..., 1]
+
+
+def _rows_arg(rows, B):
+    if rows is None:
+        return np.arange(B)
+    return np.asarray(rows, dtype=np.int64)
+
+
+# ------------------------------------------------ step 2: greedy accept ----
+
+@dataclass
+class GreedyResult:
+    accepted_len: np.ndarray      # [B] int32: n (0..K), -1 bad row, -2 row not selected
+    out_tokens: np.ndarray        # [B, K+1] int32, -1 past the emitted token
+    argmax: np.ndarray            # [B, K+1] target argmax per position
+    margin: np.ndarray            # [B, K+1] top1 - top2 of the target logits
+
+
+def accept_greedy(logits, draft_tokens, rows=None) -> GreedyResult:
+    """Greedy verification of each selected row b.
+
+    a_i = argmax_v logits[b, i, v] (lowest index on ties), i = 0..K.
+    n = number of leading drafts with d_i == a_i.  Emitted: d_0..d_{n-1}, a_n.
+    """
+    z = np.asarray(logits, dtype=np.float64)
+    d = np.asarray(draft_tokens, dtype=np.int64)
+    B, P, V = z.shape
+    K = P - 1
+    rows = _rows_arg(rows, B)
+    acc = np.full(B, -2, np.int32)
+    out = np.full((B, K + 1), -1, np.int32)
+    amax = np.full((B, K + 1), -1, np.int64)
+    marg = np.full((B, K + 1), np.inf)
+    for b in rows:
+        bad = bool(np.any(_bad_rows(z[b])))
+        if K and np.any((d[b] < 0) | (d[b] >= V)):
+            bad = True
+        if bad:
+            acc[b] = -1
+            continue
+        a = np.argmax(z[b], axis=-1)          # numpy: first maximal index
+        amax[b] = a
+        marg[b] = _top2_margin(z[b])
+        n = 0
+        while n < K and d[b, n] == a[n]:
+            n += 1
+        out[b, :n] = d[b, :n]
+        out[b, n] = a[n]
+        acc[b] = n
+    return GreedyResult(acc, out, amax, marg)
+
+
+# ------------------------------------------- step 3: speculative sampling ----
+
+@dataclass
+class SampleResult:
+    accepted_len: np.ndarray      # [B] int32 (-1 bad row, -2 not selected)
+    out_tokens: np.ndarray        # [B, K+1] int32
+    probs_at_draft: np.ndarray    # [B, K, 2]: q_i(d_i), p_i(d_i)
+    ratio: np.ndarray             # [B, K]: r_i = min(1, q_i(d_i)/p_i(d_i))
+    u_accept: np.ndarray          # [B, K+1]: Philox word 0 uniforms
+    u_terminal: np.ndarray        # [B, K+1]: Philox word 1 uniforms
+    accept_margin: np.ndarray     # [B, K]: |u_i - r_i|
+    terminal_margin: np.ndarray   # [B]: distance of u'Z to the nearest CDF step, / Z
+    residual_mass: np.ndarray     # [B]: Z (sum of the terminal weights)
+    alpha: np.ndarray             # [B, K]: sum_v min(q_i, p_i), exact accept prob.
+
+
+def accept_ratio(q_d, p_d):
+    """r = min(1, q/p), with r = 0 where q = 0 and r = 1 where p = 0 < q."""
+    q_d = np.asarray(q_d, dtype=np.float64)
+    p_d = np.asarray(p_d, dtype=np.float64)
+    with np.errstate(divide="ignore", invalid="ignore"):
+        r = np.where(q_d >= p_d, 1.0, q_d / np.where(p_d > 0, p_d, 1.0))
+    return np.where(q_d > 0, np.minimum(r, 1.0), 0.0)
+
+
+def inverse_cdf(w, u):
+    """Inverse-CDF draw over the last axis of w with uniform(s) u.
+
+    t = min{v : C_v > u * Z}, C the in-order cumulative sum of w and
+    Z = C_{V-1}.  Returns (t, Z, margin) with margin = min(uZ - C_{t-1},
+    C_t - uZ) / Z, the relative distance of the draw point to the nearest
+    step of the CDF.  Works on w [..., V] and u [...].
+    """
+    C = np.cumsum(np.asarray(w, dtype=np.float64), axis=-1)
+    V = C.shape[-1]
+    Z = C[..., -1]
+    x = np.asarray(u, dtype=np.float64) * Z
+    t = np.minimum(np.sum(C <= x[..., None], axis=-1), V - 1)   # first C_v > x
+    hi = np.take_along_axis(C, t[..., None], axis=-1)[..., 0]
+    lo = np.take_along_axis(C, np.maximum(t - 1, 0)[..., None], axis=-1)[..., 0]
+    lo = np.where(t > 0, lo, 0.0)
+    with np.errstate(divide="ignore", invalid="ignore"):
+        margin = np.where(Z > 0, np.minimum(x - lo, hi - x) / Z, 0.0)
+    return t, Z, margin
+
+
+def terminal_weights(q_n, p_n=None):
+    """Weights of the terminal draw: max(0, q_n - p_n) after a rejection at n
+    (falling back to q_n when that residual has no mass), or q_n itself for
+    the bonus position (p_n is None).  Works on [..., V] arrays."""
+    q_n = np.asarray(q_n, dtype=np.float64)
+    if p_n is None:
+        return q_n
+    w = np.maximum(0.0, q_n - np.asarray(p_n, dtype=np.float64))
+    empty = ~(np.sum(w, axis=-1, keepdims=True) > 0)
+    return np.where(empty, q_n, w)
+
+
+def accept_sample(logits, draft_logits, draft_tokens, temperature, seeds, rows=None) -> SampleResult:
+    """Speculative sampling of each selected row b (B rows, K drafts, V tokens).
+
+    q_i = softmax(logits[b, i] / T), i = 0..K;  p_i = softmax(draft_logits[b, i] / T), i < K.
+    (u_i, u'_i) = Philox uniforms at (seed_b, b, i).
+    Accept d_i iff u_i < r_i = min(1, q_i(d_i)/p_i(d_i)); n = first rejected i, else K.
+    Terminal weights: w = max(0, q_n - p_n) if n < K, else q_K (bonus).
+    Terminal token: inverse CDF of w at u'_n.  Emitted: d_0..d_{n-1}, t.
+    Vectorised over the selected rows.
+    """
+    z = np.asarray(logits, dtype=np.float64)
+    B, P, V = z.shape
+    K = P - 1
+    zd = np.asarray(draft_logits, dtype=np.float64) if K else np.zeros((B, 0, V))
+    d = np.asarray(draft_tokens, dtype=np.int64).reshape(B, K)
+    seeds = np.asarray(seeds, dtype=np.uint64)
+    T = float(temperature)
+    rows = _rows_arg(rows, B)
+
+    acc = np.full(B, -2, np.int32)
+    out = np.full((B, K + 1), -1, np.int32)
+    pad = np.full((B, K, 2), np.nan)
+    ratio = np.full((B, K), np.nan)
+    ua = np.full((B, K + 1), np.nan)
+    ut = np.full((B, K + 1), np.nan)
+    am = np.full((B, K), np.inf)
+    tm = np.full(B, np.inf)
+    zz = np.full(B, np.nan)
+    alpha = np.full((B, K), np.nan)
+    if len(rows) == 0:
+        return SampleResult(acc, out, pad, ratio, ua, ut, am, tm, zz, alpha)
+
+    zr, zdr, dr = z[rows], zd[rows], d[rows]
+    bad = np.any(_bad_rows(zr), axis=-1)
+    if K:
+        bad |= np.any(_bad_rows(zdr), axis=-1)
+        bad |= np.any((dr < 0) | (dr >= V), axis=-1)
+    acc[rows[bad]] = -1
+    good = rows[~bad]
+    if len(good) == 0:
+        return SampleResult(acc, out, pad, ratio, ua, ut, am, tm, zz, alpha)
+    R = len(good)
+    zr, zdr, dr = z[good], zd[good], d[good]
+
+    q = softmax(zr, T)                                   # [R, K+1, V]
+    p = softmax(zdr, T) if K else np.zeros((R, 0, V))    # [R, K, V]
+    u, u2 = verify_uniforms(seeds[good][:, None], good[:, None], np.arange(K + 1)[None, :])
+    ua[good], ut[good] = u, u2
+
+    ri = np.arange(R)[:, None]
+    ki = np.arange(K)[None, :]
+    q_d = q[ri, ki, dr]                                  # q_i(d_i)   [R, K]
+    p_d = p[ri, ki, dr]                                  # p_i(d_i)
+    r = accept_ratio(q_d, p_d)
+    pad[good] = np.stack([q_d, p_d], axis=-1)
+    ratio[good] = r
+    alpha[good] = np.sum(np.minimum(q[:, :K], p), axis=-1)
+    am[good] = np.abs(u[:, :K] - r)
+
+    # n = index of the first rejection (u_i >= r_i), scanning left to right; K if none
+    rejected = ~(u[:, :K] < r)
+    n = np.where(rejected.any(axis=-1), np.argmax(rejected, axis=-1), K) if K else np.zeros(R, np.int64)
+
+    q_n = q[np.arange(R), n]                             # [R, V]
+    w = q_n.copy()
+    rej = n < K
+    if np.any(rej):
+        w[rej] = terminal_weights(q_n[rej], p[np.arange(R)[rej], n[rej]])
+
+    # terminal token: inverse CDF of w at u'_n
+    t, Z, margin = inverse_cdf(w, u2[np.arange(R), n])
+
+    for j, b in enumerate(good):
+        out[b, :n[j]] = dr[j, :n[j]]
+    out[good, n] = t
+    acc[good] = n
+    tm[good] = margin
+    zz[good] = Z
+    return SampleResult(acc, out, pad, ratio, ua, ut, am, tm, zz, alpha)
+
+
+# ------------------------------------------------ expected tokens per pass --
+
+def expected_tokens(alpha: float, K: int) -> float:
+    """(1 - alpha^(K+1)) / (1 - alpha): expected tokens per verify pass when
+    every draft is accepted independently with probability alpha
+    ("Inference-4", The idea; "speculative-decoding" blog, Why speculative
+    decoding is fast).  Limits: alpha = 1 gives K + 1, alpha = 0 gives 1."""
+    if alpha == 1.0:
+        return float(K + 1)
+    return (1.0 - alpha ** (K + 1)) / (1.0 - alpha)
+
+
+def expected_tokens_positional(alphas) -> float:
+    """sum_{i=0}^{K} prod_{j<i} alpha_j: the same expectation when the accept
+    probability differs per position (each term is the probability of
+    reaching position i)."""
+    total, reach = 1.0, 1.0
+    for a in alphas:
+        reach *= a
+        total += reach
+    return total
