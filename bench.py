@@ -1,0 +1,232 @@
+"""Benchmark of the speculative-decoding verify step on one MI355X.
+
+One step = one pass of the whole verify path over one batch: the LM-head
+contraction of the K+1 verify positions (spec_verify_logits) and the
+acceptance of every sequence (spec_accept_sample / spec_accept_greedy, by the
+workload's per-row mode), including the residual or bonus draw.  Inputs
+(weights, hidden states, draft logits, per-round draft tokens and seeds) are
+resident in HBM before the timed region; each timed step uses the next
+pre-drawn draft set and seed.
+
+Prints one JSON line: verified positions per second (B*(K+1) / step time) and
+the step time, with the roofline of the dominant kernel (the LM-head
+contraction, timed with HIP events on the stream it runs on) and the CPU
+oracle timed on a bounded sample of the same workload.
+
+    python bench.py [--gpus 1] [--steps 50] [--warmup 5] [--workload b1_k5_h4096_v128256]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak, published
+METRIC = "verified positions/sec + verify-step µs (B=1,K=5); % HBM / MFMA peak"
+GEMM_SRC = os.path.join(ROOT, "speculative_decoding_verification_02_amd", "csrc", "lmhead_gemm.hip")
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="b1_k5_h4096_v128256")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle sample")
+    return ap.parse_args()
+
+
+def gemm_source_sha() -> str:
+    return hashlib.sha256(open(GEMM_SRC, "rb").read()).hexdigest()[:16]
+
+
+def load_traffic(workload: str):
+    """HBM bytes per launch of the LM-head kernel from the committed counter
+    summary, or None if absent or taken on a different kernel source."""
+    path = os.path.join(ROOT, "profiles", "lmhead_traffic_%s.json" % workload)
+    if not os.path.exists(path):
+        return None
+    rec = json.load(open(path))
+    if rec.get("source_sha") != gemm_source_sha():
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path (run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import speculative_decoding_verification_02_amd as sv
+    import synth
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    sv.load_library()
+
+    wl = synth.WORKLOADS[args.workload]
+    B, K, H, V, T = wl.B, wl.K, wl.H, wl.V, wl.temperature
+    M = wl.M
+    print("bench: %s, generating inputs" % wl.name, file=sys.stderr, flush=True)
+    W = synth.weights(wl, dev)
+    hidden = synth.hidden_states(wl, dev)
+    zd = synth.draft_logits(wl, synth.base_logits(hidden, W))
+    smask = synth.sampled_mask(wl)
+    n_sets = 16
+    drafts = [synth.draft_tokens(zd, smask, T, seed=wl.data_seed * 104729 + r) for r in range(n_sets)]
+    n_seed_sets = args.warmup + args.steps
+    seeds = [torch.from_numpy(synth.seeds(wl, r).view(np.int64).copy()).to(dev) for r in range(n_seed_sets)]
+    greedy_rows = torch.as_tensor(np.nonzero(~smask)[0].astype(np.int32), device=dev)
+    sampled_rows = torch.as_tensor(np.nonzero(smask)[0].astype(np.int32), device=dev)
+    all_sampled, all_greedy = bool(smask.all()), bool((~smask).all())
+
+    logits = torch.empty((B, K + 1, V), dtype=torch.float32, device=dev)
+    ws = torch.empty(sv.spec_workspace_bytes(B, K, V), dtype=torch.uint8, device=dev)
+    acc = torch.empty((B,), dtype=torch.int32, device=dev)
+    out = torch.empty((B, K + 1), dtype=torch.int32, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def step(r, ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        sv.spec_verify_logits(hidden, W, logits, stream=stream)
+        if ev is not None:
+            ev[1].record(stream)
+        d = drafts[r % n_sets]
+        if all_sampled:
+            sv.spec_accept_sample(logits, zd, d, T, seeds[r], acc, out, ws, stream=stream)
+        elif all_greedy:
+            sv.spec_accept_greedy(logits, d, acc, out, ws, stream=stream)
+        else:
+            sv.spec_accept_greedy(logits, d, acc, out, ws, rows=greedy_rows, stream=stream)
+            sv.spec_accept_sample(logits, zd, d, T, seeds[r], acc, out, ws, rows=sampled_rows, stream=stream)
+
+    print("bench: warmup %d" % args.warmup, file=sys.stderr, flush=True)
+    for r in range(args.warmup):
+        step(r)
+    torch.cuda.synchronize()
+
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    accepted = []
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(args.steps):
+        step(args.warmup + k, evs[k])
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    step_s = (t1 - t0) / args.steps
+    gemm_ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
+    accepted = acc.cpu().numpy()
+    print("bench: %d steps, %.1f us/step, LM-head kernel %.1f us" % (args.steps, step_s * 1e6, gemm_ms * 1e3),
+          file=sys.stderr, flush=True)
+
+    # algorithmic bytes / flops of one LM-head launch
+    wbytes = 2 if wl.dtype == "bf16" else 4
+    gemm_bytes = V * H * wbytes + M * H * wbytes + M * V * 4
+    gemm_flops = 2.0 * M * V * H
+    intensity = gemm_flops / gemm_bytes
+    ridge = MFMA_BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9)
+    t_gemm = gemm_ms * 1e-3
+    if intensity < ridge:
+        roof = {"bound": "hbm", "achieved": gemm_bytes / t_gemm / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s"}
+    else:
+        roof = {"bound": "mfma", "achieved": gemm_flops / t_gemm / 1e12, "peak": MFMA_BF16_PEAK_TFLOPS,
+                "unit": "TFLOP/s"}
+    roof["frac"] = roof["achieved"] / roof["peak"]
+    roof["traffic"] = load_traffic(wl.name)
+    roof["kernel"] = "lmhead_skinny_bf16" if (wl.dtype == "bf16" and M <= 16) else "lmhead_tiled_bf16"
+    roof["algorithmic_bytes"] = gemm_bytes
+    roof["algorithmic_flops"] = gemm_flops
+    roof["avg_kernel_us"] = gemm_ms * 1e3
+
+    positions = B * (K + 1)
+    res = {
+        "metric": METRIC,
+        "value": positions / step_s,
+        "unit": "verified positions/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": step_s * 1e3,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": wl.dtype,
+        "data": "synthetic",
+        "config": {"workload": wl.name, "B": B, "K": K, "H": H, "V": V, "temperature": T,
+                   "sampled_rows": int(smask.sum()), "greedy_rows": int((~smask).sum())},
+        "verify_step_us": step_s * 1e6,
+        "committed_tokens_per_step_last": float(np.mean(accepted + 1)),
+        "roofline": roof,
+    }
+
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline(wl, W, hidden, zd, drafts, smask, args.cpu_seconds)
+    print(json.dumps(res), flush=True)
+
+
+def cpu_baseline(wl, W, hidden, zd, drafts, smask, budget_s):
+    """The oracle, as it stands, timed on this host on the same inputs: whole
+    verify steps (fp64 logits of all K+1 positions + acceptance) until about
+    budget_s seconds have been spent (at least one step)."""
+    import torch
+    from threadpoolctl import threadpool_info, threadpool_limits
+
+    import oracle
+
+    cores = min(len(os.sched_getaffinity(0)), 16)
+    print("bench: cpu baseline (oracle) on %d threads" % cores, file=sys.stderr, flush=True)
+    w64 = oracle.widen_bf16(W.cpu().view(torch.int16).numpy().view(np.uint16)) if wl.dtype == "bf16" \
+        else W.cpu().double().numpy()
+    h = hidden.cpu()
+    h64 = (oracle.widen_bf16(h.view(torch.int16).numpy().view(np.uint16)) if wl.dtype == "bf16"
+           else h.double().numpy()).reshape(wl.M, wl.H)
+    zd64 = zd.cpu().numpy()
+    ds = [d.cpu().numpy() for d in drafts]
+    g_rows = np.nonzero(~smask)[0]
+    s_rows = np.nonzero(smask)[0]
+    times = []
+    with threadpool_limits(limits=cores):
+        used = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+        t_start = time.perf_counter()
+        r = 0
+        while True:
+            t0 = time.perf_counter()
+            z = oracle.lm_head_logits(h64, w64).reshape(wl.B, wl.K + 1, wl.V)
+            if len(g_rows):
+                oracle.accept_greedy(z, ds[r % len(ds)], rows=g_rows)
+            if len(s_rows):
+                oracle.accept_sample(z, zd64, ds[r % len(ds)], wl.temperature, synth_seeds(wl, r), rows=s_rows)
+            times.append(time.perf_counter() - t0)
+            r += 1
+            if time.perf_counter() - t_start > budget_s:
+                break
+    t = float(np.mean(times))
+    return {"value": wl.M / t, "unit": "verified positions/s", "cores": int(min(used, cores)), "kind": "oracle",
+            "sample": "%d whole verify steps of %s (fp64 logits of all %d positions over V=%d, then acceptance), "
+                      "same inputs as the GPU run; %.2f s per step" % (len(times), wl.name, wl.M, wl.V, t)}
+
+
+def synth_seeds(wl, r):
+    import synth
+    return synth.seeds(wl, r)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,191 @@
+/*
+ * spec_verify.h -- C ABI of the speculative-decoding verify step on MI355X
+ * (gfx950).
+ *
+ * The verify step takes the target model's hidden states at the K+1 verify
+ * positions of each sequence (the last accepted token and the K drafts), turns
+ * them into logits with the LM head, and decides how many drafts to keep:
+ *
+ *   spec_verify_logits  -- logits = hidden . W_lmheadᵀ (the target's single
+ *                          pass yields one distribution per draft position plus
+ *                          one after the last draft: "Inference-4",
+ *                          Draft-model speculative decoding, step 2; the
+ *                          weights are read once for all positions:
+ *                          "speculative-decoding" blog, Verification mechanism).
+ *   spec_accept_greedy  -- accept drafts while they equal the target's most
+ *                          likely token, then emit the target's token at the
+ *                          first mismatch or the bonus token after the last
+ *                          draft ("Inference-4", greedy bullet).
+ *   spec_accept_sample  -- speculative sampling: accept draft x with
+ *                          probability min(1, q(x)/p(x)) (q target, p draft),
+ *                          stop at the first rejection and redraw it from
+ *                          norm(max(0, q - p)); if all K are accepted draw a
+ *                          bonus token from q after the last draft
+ *                          ("Inference-4", sampling bullet; "speculative-
+ *                          decoding" blog, Rejection sampling; "What is
+ *                          speculative decoding" guide, How speculative
+ *                          decoding works).
+ *
+ * Conventions shared by every entry point
+ *   - Every pointer argument is DEVICE memory on the current HIP device, owned
+ *     by the caller.  The library allocates nothing and keeps no state between
+ *     calls other than a per-device cache of the compute-unit count.
+ *   - Every call is asynchronous: it validates its arguments on the host,
+ *     enqueues kernels on `stream` and returns.  It never synchronises.  The
+ *     caller synchronises (event or stream) before reading outputs.
+ *   - Sizes: B sequences, K drafts per sequence (0 <= K <= 63; the accept
+ *     kernel scans the K+1 positions of a sequence in one 64-lane wavefront),
+ *     vocabulary V >= 1, hidden size H (a positive multiple of 8, so rows are
+ *     16-byte aligned for 128-bit loads).  M = B*(K+1) verify rows.
+ *   - Layouts are row-major and contiguous:
+ *       hidden        [B, K+1, H]   bf16 or fp32
+ *       w_lmhead      [V, H]        bf16 or fp32 (same dtype as hidden)
+ *       logits        [B, K+1, V]   fp32  (target logits, row b*(K+1)+i)
+ *       draft_logits  [B, K, V]     fp32  (draft logits, row b*K+i)
+ *       draft_tokens  [B, K]        int32
+ *       seeds         [B]           uint64 (per-sequence Philox key)
+ *       accepted_len  [B]           int32
+ *       out_tokens    [B, K+1]      int32
+ *   - Errors the host can see (null pointers, bad sizes, misalignment, a
+ *     non-positive or non-finite temperature, a short workspace) return a
+ *     status before anything is enqueued.  A failed HIP launch returns
+ *     SPEC_ERR_HIP; spec_last_error_detail() then names the HIP error.
+ *   - Data faults found on the device mark the sequence instead of failing
+ *     the call: accepted_len[b] = -1 and out_tokens[b, :] = -1 when a draft
+ *     token lies outside [0, V), or any of the sequence's target (or, in
+ *     sampled mode, draft) rows holds a NaN or +inf, or has no finite entry.
+ *
+ * Random numbers (sampled mode): for sequence slot b and verify position i the
+ * step draws one Philox4x32-10 block (Salmon et al., SC'11) with counter
+ * (i, b, 0, 0) and key (low 32 bits of seeds[b], high 32 bits).  Word 0 gives
+ * the accept uniform u_i = (w0 >> 8) * 2^-24 and word 1 the terminal uniform
+ * u'_i = (w1 >> 8) * 2^-24.  A draft is accepted iff u_i < r_i; the terminal
+ * token is t = min{v : C_v > u'_n * Z}, C the in-order cumulative sum of the
+ * terminal weights and Z their total.  The result is a pure function of the
+ * inputs and seeds: a round replays exactly.
+ */
+#ifndef SPEC_VERIFY_H
+#define SPEC_VERIFY_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum spec_status {
+    SPEC_OK = 0,
+    SPEC_ERR_ARG = 1,        /* null pointer, size out of range, bad temperature */
+    SPEC_ERR_DTYPE = 2,      /* unsupported element type */
+    SPEC_ERR_ALIGN = 3,      /* a pointer is not 16-byte aligned */
+    SPEC_ERR_WORKSPACE = 4,  /* workspace NULL or smaller than spec_workspace_bytes() */
+    SPEC_ERR_HIP = 5         /* a HIP call or kernel launch failed */
+} spec_status_t;
+
+typedef enum spec_dtype {
+    SPEC_BF16 = 0,           /* bfloat16, storage as uint16 bit patterns */
+    SPEC_F32 = 1             /* IEEE binary32 */
+} spec_dtype_t;
+
+/* A hipStream_t.  NULL selects the null stream of the current device. */
+typedef void* spec_stream_t;
+
+/*
+ * spec_verify_logits -- LM-head contraction of the K+1 verify positions.
+ *
+ *   logits[m, v] = sum_h hidden[m, h] * w_lmhead[v, h],  m < B*(K+1), v < V
+ *
+ * Products and sums are in fp32 (bf16 x bf16 products are exact in fp32; the
+ * bf16 path runs on the matrix cores).  The order of the fp32 sum over h is
+ * the kernel's and is fixed for a given (B, K, V, H, dtype).
+ *
+ *   hidden     device, [B, K+1, H] of `dtype`, 16-byte aligned
+ *   w_lmhead   device, [V, H] of `dtype`, 16-byte aligned
+ *   dtype      SPEC_BF16 or SPEC_F32 (hidden and weights share it)
+ *   logits     device, [B, K+1, V] fp32, written, 16-byte aligned
+ *   B, K, V, H sizes as above
+ *   stream     HIP stream
+ *
+ * Returns SPEC_ERR_ARG for null pointers or sizes out of range,
+ * SPEC_ERR_DTYPE for an unknown dtype, SPEC_ERR_ALIGN for misaligned pointers,
+ * SPEC_ERR_HIP if a launch fails.
+ */
+spec_status_t spec_verify_logits(const void* hidden, const void* w_lmhead, spec_dtype_t dtype,
+                                 float* logits, int B, int K, int V, int H,
+                                 spec_stream_t stream);
+
+/*
+ * spec_accept_greedy -- greedy verification of the selected sequences.
+ *
+ * For each selected sequence b: a_i = argmax_v logits[b, i, v] for i = 0..K
+ * (the lowest index wins a tie); n = the number of leading drafts with
+ * draft_tokens[b, i] == a_i; then accepted_len[b] = n and out_tokens[b, :] =
+ * (d_0, ..., d_{n-1}, a_n, -1, ..., -1).  a_K is the bonus token.
+ *
+ *   logits        device, [B, K+1, V] fp32, 16-byte aligned
+ *   draft_tokens  device, [B, K] int32 (may be NULL when K == 0)
+ *   rows          device, [n_rows] int32: the sequences to verify, distinct,
+ *                 each in [0, B) (entries outside are skipped).  NULL means
+ *                 all B sequences (n_rows is then ignored).
+ *   n_rows        0 <= n_rows <= B
+ *   accepted_len  device, [B] int32, written for the selected rows only
+ *   out_tokens    device, [B, K+1] int32, written for the selected rows only
+ *   workspace     device scratch of at least spec_workspace_bytes(B, K, V)
+ *                 bytes, 16-byte aligned; its contents on entry do not matter.
+ *                 Calls that share a workspace must be ordered on one stream.
+ *   workspace_bytes  its size
+ *   stream        HIP stream
+ */
+spec_status_t spec_accept_greedy(const float* logits, const int32_t* draft_tokens,
+                                 const int32_t* rows, int n_rows, int B, int K, int V,
+                                 int32_t* accepted_len, int32_t* out_tokens,
+                                 void* workspace, size_t workspace_bytes,
+                                 spec_stream_t stream);
+
+/*
+ * spec_accept_sample -- speculative sampling of the selected sequences.
+ *
+ * q_i = softmax(logits[b, i, :] / T) for i = 0..K and p_i =
+ * softmax(draft_logits[b, i, :] / T) for i < K (the same temperature divides
+ * both).  With d_i = draft_tokens[b, i] and (u_i, u'_i) the Philox uniforms
+ * above:
+ *   r_i = min(1, q_i(d_i) / p_i(d_i))   (r_i = 0 if q_i(d_i) = 0; 1 if p_i(d_i) = 0 < q_i(d_i))
+ *   n   = the first i < K with u_i >= r_i, else K
+ *   w   = max(0, q_n - p_n) if n < K (q_n itself if that has no mass), else q_K
+ *   t   = min{v : C_v > u'_n * Z},  C_v = w_0 + ... + w_v,  Z = C_{V-1}
+ * accepted_len[b] = n;  out_tokens[b, :] = (d_0, ..., d_{n-1}, t, -1, ...).
+ *
+ *   logits, draft_tokens, rows, n_rows, accepted_len, out_tokens, workspace,
+ *   workspace_bytes, stream: as in spec_accept_greedy
+ *   draft_logits    device, [B, K, V] fp32, 16-byte aligned (NULL when K == 0)
+ *   temperature     T, finite and > 0
+ *   seeds           device, [B] uint64
+ *   probs_at_draft  device, [B, K, 2] fp32 or NULL: (q_i(d_i), p_i(d_i)) for
+ *                   every i < K of the selected rows
+ */
+spec_status_t spec_accept_sample(const float* logits, const float* draft_logits,
+                                 const int32_t* draft_tokens, float temperature,
+                                 const uint64_t* seeds, const int32_t* rows, int n_rows,
+                                 int B, int K, int V,
+                                 int32_t* accepted_len, int32_t* out_tokens,
+                                 float* probs_at_draft,
+                                 void* workspace, size_t workspace_bytes,
+                                 spec_stream_t stream);
+
+/* Bytes of workspace either accept call needs for these sizes (0 if the sizes
+ * are out of range). */
+size_t spec_workspace_bytes(int B, int K, int V);
+
+/* Static, human-readable name of a status code. */
+const char* spec_status_string(spec_status_t status);
+
+/* Detail of the last SPEC_ERR_HIP returned on the calling thread (a static
+ * string owned by the HIP runtime), or "" if none. */
+const char* spec_last_error_detail(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SPEC_VERIFY_H */

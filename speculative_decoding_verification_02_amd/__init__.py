@@ -1,0 +1,172 @@
+"""Speculative-decoding verify step on MI355X (gfx950): Python binding.
+
+Thin ctypes wrapper over ``libspecverify.so`` (C ABI in include/spec_verify.h).
+It only marshals arguments: device pointers of torch tensors, sizes read from
+their shapes, and the current HIP stream.  Every step of the verify path runs
+in the library's HIP kernels; if the library is missing, every call raises.
+
+    spec_verify_logits(hidden, w_lmhead, logits)
+    spec_accept_greedy(logits, draft_tokens, accepted_len, out_tokens, workspace, rows=None)
+    spec_accept_sample(logits, draft_logits, draft_tokens, temperature, seeds,
+                       accepted_len, out_tokens, workspace, rows=None, probs_at_draft=None)
+    spec_workspace_bytes(B, K, V)
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+__all__ = [
+    "SpecVerifyError", "SPEC_OK", "SPEC_ERR_ARG", "SPEC_ERR_DTYPE", "SPEC_ERR_ALIGN",
+    "SPEC_ERR_WORKSPACE", "SPEC_ERR_HIP", "SPEC_BF16", "SPEC_F32", "LIB_PATH", "HEADER_PATH",
+    "load_library", "declared_symbols", "spec_verify_logits", "spec_accept_greedy",
+    "spec_accept_sample", "spec_workspace_bytes", "spec_status_string", "spec_last_error_detail",
+]
+
+PKG_DIR = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG_DIR, "libspecverify.so")
+HEADER_PATH = os.path.join(os.path.dirname(PKG_DIR), "include", "spec_verify.h")
+
+SPEC_OK, SPEC_ERR_ARG, SPEC_ERR_DTYPE, SPEC_ERR_ALIGN, SPEC_ERR_WORKSPACE, SPEC_ERR_HIP = range(6)
+SPEC_BF16, SPEC_F32 = 0, 1
+
+_c_void_p, _c_int, _c_size_t, _c_float = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t, ctypes.c_float
+
+_SIGNATURES = {
+    "spec_verify_logits": (_c_int, [_c_void_p, _c_void_p, _c_int, _c_void_p, _c_int, _c_int, _c_int, _c_int,
+                                    _c_void_p]),
+    "spec_accept_greedy": (_c_int, [_c_void_p, _c_void_p, _c_void_p, _c_int, _c_int, _c_int, _c_int, _c_void_p,
+                                    _c_void_p, _c_void_p, _c_size_t, _c_void_p]),
+    "spec_accept_sample": (_c_int, [_c_void_p, _c_void_p, _c_void_p, _c_float, _c_void_p, _c_void_p, _c_int, _c_int,
+                                    _c_int, _c_int, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_size_t,
+                                    _c_void_p]),
+    "spec_workspace_bytes": (_c_size_t, [_c_int, _c_int, _c_int]),
+    "spec_status_string": (ctypes.c_char_p, [_c_int]),
+    "spec_last_error_detail": (ctypes.c_char_p, []),
+}
+
+_lib = None
+
+
+class SpecVerifyError(RuntimeError):
+    """A library call returned a status other than SPEC_OK."""
+
+    def __init__(self, fn: str, status: int):
+        self.status = status
+        detail = ""
+        if status == SPEC_ERR_HIP:
+            detail = " (" + load_library().spec_last_error_detail().decode() + ")"
+        super().__init__("%s: %s%s" % (fn, spec_status_string(status), detail))
+
+
+def load_library(path: str = LIB_PATH):
+    """Load libspecverify.so (once).  Raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError("%s is missing: build it with `python -m speculative_decoding_verification_02_amd.build` "
+                           "(or __graft_entry__.build())" % path)
+    lib = ctypes.CDLL(path)
+    for name, (res, args) in _SIGNATURES.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    _lib = lib
+    return lib
+
+
+def declared_symbols(header: str = HEADER_PATH) -> list[str]:
+    """Names of the functions include/spec_verify.h declares."""
+    text = open(header).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(spec_[a-z_]+)\s*\(", text)))
+
+
+# ------------------------------------------------------------ marshalling --
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream))
+
+
+def _check(fn: str, status: int):
+    if status != SPEC_OK:
+        raise SpecVerifyError(fn, status)
+
+
+def _dtype_code(t):
+    import torch
+    if t.dtype == torch.bfloat16:
+        return SPEC_BF16
+    if t.dtype == torch.float32:
+        return SPEC_F32
+    raise TypeError("hidden/w_lmhead must be bfloat16 or float32, got %s" % t.dtype)
+
+
+def _rows(rows):
+    if rows is None:
+        return None, 0
+    return rows, int(rows.numel())
+
+
+def spec_workspace_bytes(B: int, K: int, V: int) -> int:
+    return int(load_library().spec_workspace_bytes(B, K, V))
+
+
+def spec_status_string(status: int) -> str:
+    return load_library().spec_status_string(status).decode()
+
+
+def spec_last_error_detail() -> str:
+    return load_library().spec_last_error_detail().decode()
+
+
+def spec_verify_logits(hidden, w_lmhead, logits, stream=None) -> None:
+    """logits[B, K+1, V] (fp32) = hidden[B, K+1, H] . w_lmhead[V, H]ᵀ."""
+    B, P, H = hidden.shape
+    V = w_lmhead.shape[0]
+    if w_lmhead.dtype != hidden.dtype:
+        raise TypeError("hidden and w_lmhead must share a dtype")
+    if tuple(logits.shape) != (B, P, V) or w_lmhead.shape[1] != H:
+        raise ValueError("shape mismatch: hidden %s, w_lmhead %s, logits %s"
+                         % (tuple(hidden.shape), tuple(w_lmhead.shape), tuple(logits.shape)))
+    for t in (hidden, w_lmhead, logits):
+        if not t.is_contiguous():
+            raise ValueError("tensors must be contiguous")
+    lib = load_library()
+    _check("spec_verify_logits",
+           lib.spec_verify_logits(_ptr(hidden), _ptr(w_lmhead), _dtype_code(hidden), _ptr(logits),
+                                  B, P - 1, V, H, _stream(stream)))
+
+
+def spec_accept_greedy(logits, draft_tokens, accepted_len, out_tokens, workspace, rows=None, stream=None) -> None:
+    """Greedy acceptance of the selected rows (all rows if ``rows`` is None)."""
+    B, P, V = logits.shape
+    rows_t, n_rows = _rows(rows)
+    lib = load_library()
+    _check("spec_accept_greedy",
+           lib.spec_accept_greedy(_ptr(logits), _ptr(draft_tokens) if P > 1 else None, _ptr(rows_t), n_rows,
+                                  B, P - 1, V, _ptr(accepted_len), _ptr(out_tokens), _ptr(workspace),
+                                  workspace.numel() * workspace.element_size(), _stream(stream)))
+
+
+def spec_accept_sample(logits, draft_logits, draft_tokens, temperature, seeds, accepted_len, out_tokens, workspace,
+                       rows=None, probs_at_draft=None, stream=None) -> None:
+    """Speculative sampling of the selected rows (all rows if ``rows`` is None)."""
+    B, P, V = logits.shape
+    rows_t, n_rows = _rows(rows)
+    lib = load_library()
+    _check("spec_accept_sample",
+           lib.spec_accept_sample(_ptr(logits), _ptr(draft_logits) if P > 1 else None,
+                                  _ptr(draft_tokens) if P > 1 else None, float(temperature), _ptr(seeds),
+                                  _ptr(rows_t), n_rows, B, P - 1, V, _ptr(accepted_len), _ptr(out_tokens),
+                                  _ptr(probs_at_draft), _ptr(workspace),
+                                  workspace.numel() * workspace.element_size(), _stream(stream)))

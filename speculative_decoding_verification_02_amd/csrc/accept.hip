@@ -1,0 +1,160 @@
+// accept.hip -- greedy and sampled acceptance of the verify step.
+//
+// One wavefront per selected sequence; lane i handles verify position i
+// (i <= K <= 63).  Each lane merges the chunk statistics of its target row
+// (and draft row), decides whether draft i would be accepted on its own, and
+// the wavefront finds the first rejection with one ballot:
+//   greedy  ("Inference-4", greedy bullet): ok_i = [d_i == argmax_v z_t[i, v]]
+//   sampled (same page, sampling bullet; "speculative-decoding" blog,
+//            Rejection sampling): ok_i = [u_i < min(1, q_i(d_i) / p_i(d_i))]
+// n = index of the first lane i < K with !ok_i, else K.  Drafts before n are
+// committed; greedy rows commit argmax z_t[n] at n (the target's token at the
+// mismatch, or the bonus token when n = K), sampled rows leave position n to
+// the residual kernels, which draw it from norm(max(0, q_n - p_n)) or q_K.
+//
+// The ratio is evaluated in log2 space so tiny probabilities do not underflow:
+//   r = min(1, exp2(lq - lp) * S_d / S_t),  lq = (z_t[d] - M_t) * c, lp = (z_d[d] - M_d) * c
+// with r = 0 when z_t[d] = -inf (the target rules d out) and r = 1 when
+// z_d[d] = -inf < z_t[d].
+#include <limits.h>
+
+#include "sv_common.h"
+#include "sv_launch.h"
+
+namespace sv {
+
+constexpr int kAcceptThreads = 256;  // 4 sequences per workgroup
+
+struct Merged {
+    float m;
+    float s;
+    int idx;
+    int bad;
+};
+
+__device__ __forceinline__ Merged merge_row(const StatRec* __restrict__ rec, int nc, float c, bool need_sum) {
+    Merged r{-INFINITY, 0.f, INT_MAX, 0};
+    for (int k = 0; k < nc; ++k) {
+        const StatRec x = rec[k];
+        argmax_combine(r.m, r.idx, x.m, x.idx);
+        r.bad |= x.bad;
+    }
+    if (need_sum && r.m != -INFINITY) {
+        for (int k = 0; k < nc; ++k) {
+            const StatRec x = rec[k];
+            if (x.m != -INFINITY) r.s += x.s * exp2f((x.m - r.m) * c);
+        }
+    }
+    return r;
+}
+
+template <bool SAMPLED>
+__global__ __launch_bounds__(kAcceptThreads) void accept_kernel(
+    const float* __restrict__ logits, const float* __restrict__ draft_logits, const int32_t* __restrict__ draft_tokens,
+    const uint64_t* __restrict__ seeds, const int32_t* __restrict__ rows, int n_rows, int B, int K, int V, int nc,
+    float c, const StatRec* __restrict__ stats, int32_t* __restrict__ accepted_len, int32_t* __restrict__ out_tokens,
+    float* __restrict__ probs_at_draft, AcceptInfo* __restrict__ info) {
+    const int lane = threadIdx.x & 63;
+    const int j = blockIdx.x * (kAcceptThreads / kWave) + (threadIdx.x >> 6);
+    if (j >= n_rows) return;
+    const int b = rows ? rows[j] : j;
+    if (b < 0 || b >= B) {
+        if (SAMPLED && lane == 0) info[j] = AcceptInfo{-1, b, 0.f, 0.f, 0.f, 0.f, 0.f, 0};
+        return;
+    }
+    const int i = lane;
+    const bool active = i <= K;
+    const bool has_draft = i < K;
+
+    Merged t{-INFINITY, 0.f, INT_MAX, 0}, d{-INFINITY, 0.f, INT_MAX, 0};
+    int tok = 0;
+    int bad = 0;
+    if (active) {
+        t = merge_row(stats + ((size_t)j * (K + 1) + i) * nc, nc, c, SAMPLED);
+        bad = t.bad | (t.m == -INFINITY);
+    }
+    if (has_draft) {
+        tok = draft_tokens[(size_t)b * K + i];
+        bad |= (tok < 0 || tok >= V);
+        if (SAMPLED) {
+            d = merge_row(stats + ((size_t)n_rows * (K + 1) + (size_t)j * K + i) * nc, nc, c, true);
+            bad |= d.bad | (d.m == -INFINITY);
+        }
+    }
+    int32_t* orow = out_tokens + (size_t)b * (K + 1);
+    if (__ballot(active && bad) != 0ull) {  // data fault anywhere in the sequence
+        if (active) orow[i] = -1;
+        if (lane == 0) {
+            accepted_len[b] = -1;
+            if (SAMPLED) info[j] = AcceptInfo{-1, b, 0.f, 0.f, 0.f, 0.f, 0.f, 0};
+        }
+        return;
+    }
+
+    bool ok = false;
+    float u_term = 0.f;
+    if (SAMPLED) {
+        if (active) {
+            const uint64_t seed = seeds[b];
+            const uint4 w = philox4x32_10(make_uint4((uint32_t)i, (uint32_t)b, 0u, 0u), (uint32_t)seed,
+                                          (uint32_t)(seed >> 32));
+            u_term = uniform24(w.y);
+            if (has_draft) {
+                const float zt = logits[((size_t)b * (K + 1) + i) * V + tok];
+                const float zd = draft_logits[((size_t)b * K + i) * V + tok];
+                const float lq = (zt - t.m) * c;
+                const float lp = (zd - d.m) * c;
+                float r;
+                if (zt == -INFINITY)
+                    r = 0.f;
+                else if (zd == -INFINITY)
+                    r = 1.f;
+                else
+                    r = fminf(1.f, exp2f(lq - lp) * (d.s / t.s));
+                ok = uniform24(w.x) < r;
+                if (probs_at_draft) {
+                    float* pp = probs_at_draft + ((size_t)b * K + i) * 2;
+                    pp[0] = exp2f(lq) / t.s;
+                    pp[1] = exp2f(lp) / d.s;
+                }
+            }
+        }
+    } else {
+        ok = has_draft && tok == t.idx;
+    }
+
+    const unsigned long long rej = __ballot(has_draft && !ok);
+    const int n = rej ? (__ffsll((long long)rej) - 1) : K;
+    if (active) {
+        if (i < n)
+            orow[i] = tok;
+        else if (i > n)
+            orow[i] = -1;
+        else
+            orow[i] = SAMPLED ? -1 : t.idx;  // sampled: filled in by the residual draw
+    }
+    if (lane == 0) accepted_len[b] = n;
+    if (SAMPLED && i == n)
+        info[j] = AcceptInfo{n, b, u_term, t.m, t.s, has_draft ? d.m : 0.f, has_draft ? d.s : 0.f, 0};
+}
+
+hipError_t launch_accept(const float* logits, const float* draft_logits, const int32_t* draft_tokens,
+                         const uint64_t* seeds, const int32_t* rows, int n_rows, int B, int K, int V,
+                         float inv_t_log2e, bool sampled, const StatRec* stats, int32_t* accepted_len,
+                         int32_t* out_tokens, float* probs_at_draft, AcceptInfo* info, hipStream_t stream) {
+    if (n_rows == 0) return hipSuccess;
+    const int nc = n_chunks(V);
+    const int per = kAcceptThreads / kWave;
+    const int grid = (n_rows + per - 1) / per;
+    if (sampled)
+        hipLaunchKernelGGL(accept_kernel<true>, dim3(grid), dim3(kAcceptThreads), 0, stream, logits, draft_logits,
+                           draft_tokens, seeds, rows, n_rows, B, K, V, nc, inv_t_log2e, stats, accepted_len,
+                           out_tokens, probs_at_draft, info);
+    else
+        hipLaunchKernelGGL(accept_kernel<false>, dim3(grid), dim3(kAcceptThreads), 0, stream, logits, draft_logits,
+                           draft_tokens, seeds, rows, n_rows, B, K, V, nc, inv_t_log2e, stats, accepted_len,
+                           out_tokens, probs_at_draft, info);
+    return hipGetLastError();
+}
+
+}  // namespace sv

@@ -1,0 +1,264 @@
+// residual.hip -- terminal draw of sampled sequences.
+//
+// After the first rejection at position n < K the replacement token is drawn
+// from norm(max(0, q_n - p_n)); when all K drafts are accepted the bonus token
+// is drawn from q_K ("Inference-4", sampling bullet; "speculative-decoding"
+// blog, Rejection sampling; "What is speculative decoding" guide, How
+// speculative decoding works).  The draw is an inverse CDF:
+//     t = min{v : C_v > u' * Z},  C_v = w_0 + ... + w_v,  Z = C_{V-1}.
+//
+// Two kernels:
+//   residual_chunk_sums  -- one workgroup per (sequence, chunk): the sum of the
+//                           weights over the chunk (fixed-order reduction).
+//   residual_select      -- one workgroup per sequence: a sequential prefix over
+//                           the chunk sums finds the chunk c* holding u'Z, then a
+//                           workgroup scan over c*'s weights finds t.
+// Both evaluate a weight with the same function from the same inputs, so a
+// chunk's elements agree bitwise between the passes; only the order of the
+// within-chunk sum differs, and the selection falls back to the last (or first)
+// token of positive weight in c* if rounding leaves u'Z outside the scanned
+// range.  A token of zero weight is never drawn.  If the residual has no mass
+// (possible only through rounding when q_n ~ p_n) the draw uses q_n instead.
+#include <limits.h>
+
+#include "sv_common.h"
+#include "sv_launch.h"
+
+namespace sv {
+
+constexpr int kMaxChunks = 1024;  // V <= kMaxChunks * kChunk (checked on the host)
+
+// w_v for the terminal row: q_n(v) - p_n(v) clipped at 0, or q_n(v) itself.
+__device__ __forceinline__ float term_weight(float zt, float zd, const AcceptInfo& a, float c, bool use_q) {
+    const float q = exp2f((zt - a.mt) * c) / a.st;
+    if (use_q) return q;
+    const float p = exp2f((zd - a.md) * c) / a.sd;
+    return fmaxf(q - p, 0.f);
+}
+
+// The thread's weights of one chunk, in the coalesced order of the statistics
+// pass: element (q * kStatThreads + tid) * 4 + e of the chunk.
+__device__ __forceinline__ void chunk_weights(const float* __restrict__ zt_row, const float* __restrict__ zd_row,
+                                              int v_begin, int V, bool vec, int tid, const AcceptInfo& a, float c,
+                                              bool use_q, float w[kStatPerThread]) {
+#pragma unroll
+    for (int q = 0; q < kStatPerThread / 4; ++q) {
+        const int v = v_begin + (q * kStatThreads + tid) * 4;
+        float zt[4], zd[4] = {0.f, 0.f, 0.f, 0.f};
+        if (vec && v + 3 < V) {
+            const float4 f = *reinterpret_cast<const float4*>(zt_row + v);
+            zt[0] = f.x; zt[1] = f.y; zt[2] = f.z; zt[3] = f.w;
+            if (!use_q) {
+                const float4 g = *reinterpret_cast<const float4*>(zd_row + v);
+                zd[0] = g.x; zd[1] = g.y; zd[2] = g.z; zd[3] = g.w;
+            }
+        } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                zt[e] = (v + e < V) ? zt_row[v + e] : -INFINITY;
+                if (!use_q) zd[e] = (v + e < V) ? zd_row[v + e] : 0.f;
+            }
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) w[4 * q + e] = (v + e < V) ? term_weight(zt[e], zd[e], a, c, use_q) : 0.f;
+    }
+}
+
+__device__ __forceinline__ float block_sum(float s, float* red) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    s = wave_sum(s);
+    __syncthreads();
+    if (lane == 0) red[wave] = s;
+    __syncthreads();
+    float t = red[0];
+#pragma unroll
+    for (int k = 1; k < kStatThreads / kWave; ++k) t += red[k];
+    return t;
+}
+
+struct TermRows {
+    const float* zt;
+    const float* zd;
+    bool bonus;
+};
+
+__device__ __forceinline__ TermRows term_rows(const float* logits, const float* draft_logits, const AcceptInfo& a,
+                                              int K, int V) {
+    TermRows r;
+    r.bonus = a.n == K;
+    r.zt = logits + ((size_t)a.b * (K + 1) + a.n) * V;
+    r.zd = r.bonus ? r.zt : draft_logits + ((size_t)a.b * K + a.n) * V;
+    return r;
+}
+
+__global__ __launch_bounds__(kStatThreads) void residual_chunk_sums(
+    const float* __restrict__ logits, const float* __restrict__ draft_logits, int K, int V, int nc, float c,
+    const AcceptInfo* __restrict__ info, float* __restrict__ chunk_sums) {
+    __shared__ float red[kStatThreads / kWave];
+    const int j = blockIdx.x / nc;
+    const int chunk = blockIdx.x - j * nc;
+    const AcceptInfo a = info[j];
+    if (a.n < 0) {
+        if (threadIdx.x == 0) chunk_sums[blockIdx.x] = 0.f;
+        return;
+    }
+    const TermRows tr = term_rows(logits, draft_logits, a, K, V);
+    float w[kStatPerThread];
+    chunk_weights(tr.zt, tr.zd, chunk * kChunk, V, (V & 3) == 0, threadIdx.x, a, c, tr.bonus, w);
+    float s = 0.f;
+#pragma unroll
+    for (int k = 0; k < kStatPerThread; ++k) s += w[k];
+    s = block_sum(s, red);
+    if (threadIdx.x == 0) chunk_sums[blockIdx.x] = s;
+}
+
+__global__ __launch_bounds__(kStatThreads) void residual_select(
+    const float* __restrict__ logits, const float* __restrict__ draft_logits, int K, int V, int nc, float c,
+    const AcceptInfo* __restrict__ info, const float* __restrict__ chunk_sums, int32_t* __restrict__ out_tokens) {
+    __shared__ float pre[kMaxChunks + 1];   // prefix over chunk sums
+    __shared__ float wl[kChunk];            // weights of the selected chunk, token order
+    __shared__ float red[kStatThreads / kWave];
+    __shared__ float wtot[kStatThreads / kWave];
+    __shared__ int sel[2];                  // selected chunk, selected token
+
+    const int j = blockIdx.x;
+    const AcceptInfo a = info[j];
+    if (a.n < 0) return;
+    const TermRows tr = term_rows(logits, draft_logits, a, K, V);
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const bool vec = (V & 3) == 0;
+
+    bool use_q = tr.bonus;
+    for (int k = tid; k < nc; k += kStatThreads) pre[k + 1] = chunk_sums[(size_t)j * nc + k];
+    __syncthreads();
+    if (tid == 0) {
+        pre[0] = 0.f;
+        for (int k = 0; k < nc; ++k) pre[k + 1] = pre[k] + pre[k + 1];
+    }
+    __syncthreads();
+    if (!(pre[nc] > 0.f) && !use_q) {
+        // residual without mass: draw from q_n, recomputing the chunk sums
+        use_q = true;
+        for (int k = 0; k < nc; ++k) {
+            float w[kStatPerThread];
+            chunk_weights(tr.zt, tr.zd, k * kChunk, V, vec, tid, a, c, true, w);
+            float s = 0.f;
+#pragma unroll
+            for (int e = 0; e < kStatPerThread; ++e) s += w[e];
+            s = block_sum(s, red);
+            if (tid == 0) pre[k + 1] = s;
+        }
+        __syncthreads();
+        if (tid == 0) {
+            pre[0] = 0.f;
+            for (int k = 0; k < nc; ++k) pre[k + 1] = pre[k] + pre[k + 1];
+        }
+        __syncthreads();
+    }
+
+    const float Z = pre[nc];
+    const float x = a.u_term * Z;
+    if (tid == 0) {
+        int cs = -1, last_pos = 0;
+        for (int k = 0; k < nc; ++k) {
+            if (pre[k + 1] > pre[k]) last_pos = k;
+            if (cs < 0 && pre[k + 1] > x) cs = k;
+        }
+        sel[0] = cs < 0 ? last_pos : cs;
+        sel[1] = -1;
+    }
+    __syncthreads();
+    const int cs = sel[0];
+    const int v_begin = cs * kChunk;
+
+    // weights of chunk cs into LDS in token order
+    {
+        float w[kStatPerThread];
+        chunk_weights(tr.zt, tr.zd, v_begin, V, vec, tid, a, c, use_q, w);
+#pragma unroll
+        for (int q = 0; q < kStatPerThread / 4; ++q)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) wl[(q * kStatThreads + tid) * 4 + e] = w[4 * q + e];
+    }
+    __syncthreads();
+
+    // thread tid owns tokens [tid*16, tid*16+16) of the chunk
+    float mine[kStatPerThread];
+    float s = 0.f;
+#pragma unroll
+    for (int e = 0; e < kStatPerThread; ++e) {
+        mine[e] = wl[tid * kStatPerThread + e];
+        s += mine[e];
+    }
+    // inclusive scan of the thread sums: within the wave, then across waves
+    float incl = s;
+#pragma unroll
+    for (int o = 1; o < kWave; o <<= 1) {
+        const float y = __shfl_up(incl, o, kWave);
+        if (lane >= o) incl += y;
+    }
+    if (lane == kWave - 1) wtot[wave] = incl;
+    __syncthreads();
+    float base = 0.f;
+    for (int w2 = 0; w2 < wave; ++w2) base += wtot[w2];
+    incl += base;
+    float excl = __shfl_up(incl, 1, kWave);
+    if (lane == 0) excl = base;
+
+    const float xr = x - pre[cs];
+    if (excl <= xr && xr < incl) {  // exactly one thread's interval can hold xr
+        float run = excl;
+        int tok = -1, lastp = -1;
+#pragma unroll
+        for (int e = 0; e < kStatPerThread; ++e) {
+            if (mine[e] > 0.f) lastp = e;
+            run += mine[e];
+            if (tok < 0 && run > xr && mine[e] > 0.f) tok = e;
+        }
+        if (tok < 0) tok = lastp;
+        sel[1] = v_begin + tid * kStatPerThread + tok;
+    }
+    __syncthreads();
+    if (sel[1] < 0) {  // block-uniform: read after the barrier
+        // rounding put xr outside the scanned range: take the first token of
+        // positive weight in the chunk if xr < 0, else the last one
+        const bool low = xr < 0.f;
+        int cand = low ? INT_MAX : -1;
+#pragma unroll
+        for (int e = 0; e < kStatPerThread; ++e) {
+            const int idx = tid * kStatPerThread + e;
+            if (mine[e] > 0.f) cand = low ? min(cand, idx) : max(cand, idx);
+        }
+#pragma unroll
+        for (int o = 32; o > 0; o >>= 1) {
+            const int y = __shfl_xor(cand, o, kWave);
+            cand = low ? min(cand, y) : max(cand, y);
+        }
+        __shared__ int redi[kStatThreads / kWave];
+        if (lane == 0) redi[wave] = cand;
+        __syncthreads();
+        if (tid == 0) {
+            int best = redi[0];
+            for (int w2 = 1; w2 < kStatThreads / kWave; ++w2) best = low ? min(best, redi[w2]) : max(best, redi[w2]);
+            sel[1] = v_begin + best;
+        }
+        __syncthreads();
+    }
+    if (tid == 0) out_tokens[(size_t)a.b * (K + 1) + a.n] = sel[1];
+}
+
+hipError_t launch_residual(const float* logits, const float* draft_logits, int n_rows, int K, int V,
+                           float inv_t_log2e, const AcceptInfo* info, float* chunk_sums, int32_t* out_tokens,
+                           hipStream_t stream) {
+    if (n_rows == 0) return hipSuccess;
+    const int nc = n_chunks(V);
+    hipLaunchKernelGGL(residual_chunk_sums, dim3((unsigned)((long)n_rows * nc)), dim3(kStatThreads), 0, stream,
+                       logits, draft_logits, K, V, nc, inv_t_log2e, info, chunk_sums);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(residual_select, dim3(n_rows), dim3(kStatThreads), 0, stream, logits, draft_logits, K, V, nc,
+                       inv_t_log2e, info, chunk_sums, out_tokens);
+    return hipGetLastError();
+}
+
+}  // namespace sv

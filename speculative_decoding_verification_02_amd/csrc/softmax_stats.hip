@@ -1,0 +1,145 @@
+// softmax_stats.hip -- per-chunk softmax statistics of the verify rows.
+//
+// The accept rules need, per row z of logits: its maximum and the lowest
+// index attaining it (the greedy rule compares drafts against the target's
+// most likely token, "Inference-4", greedy bullet), and the normaliser
+// s = sum_v exp((z_v - max) / T) of softmax(z / T) (the sampled rule compares
+// target and draft probabilities of the draft token, same page, sampling
+// bullet).  A row of V logits is split into chunks of kChunk entries; one
+// workgroup reads one chunk once (128-bit coalesced loads into registers),
+// reduces max/argmax across the wavefronts, then sums exp2((z - max) * c),
+// c = log2(e) / T, from the same registers.  The accept kernel merges the
+// chunk records of a row in chunk order:
+//     M = max_c m_c,  S = sum_c s_c * exp2((m_c - M) * c),  idx = first chunk's idx with m_c = M.
+// Every reduction has a fixed order, so results are bitwise reproducible.
+#include <float.h>
+#include <limits.h>
+
+#include "sv_common.h"
+#include "sv_launch.h"
+
+namespace sv {
+
+// Thread tid of a chunk workgroup owns elements v_begin + (q * kStatThreads + tid) * 4 + e,
+// q < 4, e < 4: each load instruction of a wavefront covers 1 KB contiguous.
+__device__ __forceinline__ void load_chunk(const float* __restrict__ row, int v_begin, int V, bool vec, int tid,
+                                           float x[kStatPerThread]) {
+#pragma unroll
+    for (int q = 0; q < kStatPerThread / 4; ++q) {
+        const int v = v_begin + (q * kStatThreads + tid) * 4;
+        if (vec && v + 3 < V) {
+            const float4 f = *reinterpret_cast<const float4*>(row + v);
+            x[4 * q + 0] = f.x;
+            x[4 * q + 1] = f.y;
+            x[4 * q + 2] = f.z;
+            x[4 * q + 3] = f.w;
+        } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) x[4 * q + e] = (v + e < V) ? row[v + e] : -INFINITY;
+        }
+    }
+}
+
+__device__ __forceinline__ int chunk_index(int v_begin, int tid, int k) {
+    return v_begin + ((k >> 2) * kStatThreads + tid) * 4 + (k & 3);
+}
+
+template <bool NEED_SUM>
+__global__ __launch_bounds__(kStatThreads) void softmax_stats_kernel(
+    const float* __restrict__ logits, const float* __restrict__ draft_logits, const int32_t* __restrict__ rows,
+    int n_rows, int B, int K, int V, int nc, float c, StatRec* __restrict__ stats) {
+    __shared__ float sm[kStatThreads / kWave];
+    __shared__ int si[kStatThreads / kWave];
+    __shared__ int sb[kStatThreads / kWave];
+
+    const int job = blockIdx.x / nc;
+    const int chunk = blockIdx.x - job * nc;
+    const int tgt_jobs = n_rows * (K + 1);
+    const float* row;
+    int b;
+    if (job < tgt_jobs) {
+        const int j = job / (K + 1), i = job - j * (K + 1);
+        b = rows ? rows[j] : j;
+        row = logits + ((size_t)b * (K + 1) + i) * V;
+    } else {
+        const int jj = job - tgt_jobs;
+        const int j = jj / K, i = jj - j * K;
+        b = rows ? rows[j] : j;
+        row = draft_logits + ((size_t)b * K + i) * V;
+    }
+    const int tid = threadIdx.x;
+    if (b < 0 || b >= B) {  // skipped sequence: the accept kernel ignores it
+        if (tid == 0) stats[blockIdx.x] = StatRec{-INFINITY, 0.f, INT_MAX, 0};
+        return;
+    }
+
+    const int v_begin = chunk * kChunk;
+    float x[kStatPerThread];
+    load_chunk(row, v_begin, V, (V & 3) == 0, tid, x);
+
+    float m = -INFINITY;
+    int mi = INT_MAX;
+    int bad = 0;
+#pragma unroll
+    for (int k = 0; k < kStatPerThread; ++k) {
+        float z = x[k];
+        if (z != z || z == INFINITY) {  // NaN or +inf: the row is unusable
+            bad = 1;
+            z = -INFINITY;
+            x[k] = -INFINITY;
+        }
+        if (z > m) {  // ascending index within a thread: strict > keeps the first
+            m = z;
+            mi = chunk_index(v_begin, tid, k);
+        }
+    }
+    wave_argmax(m, mi);
+    const int lane = tid & 63, wave = tid >> 6;
+    const unsigned long long anybad = __ballot(bad);
+    if (lane == 0) {
+        sm[wave] = m;
+        si[wave] = mi;
+        sb[wave] = anybad != 0ull;
+    }
+    __syncthreads();
+    float bm = sm[0];
+    int bi = si[0];
+    int bbad = sb[0];
+#pragma unroll
+    for (int w = 1; w < kStatThreads / kWave; ++w) {
+        argmax_combine(bm, bi, sm[w], si[w]);
+        bbad |= sb[w];
+    }
+
+    float s = 0.f;
+    if (NEED_SUM && bm != -INFINITY) {
+#pragma unroll
+        for (int k = 0; k < kStatPerThread; ++k) s += exp2f((x[k] - bm) * c);
+        s = wave_sum(s);
+        __syncthreads();  // everyone has read sm before it is reused
+        if (lane == 0) sm[wave] = s;
+        __syncthreads();
+        s = sm[0];
+#pragma unroll
+        for (int w = 1; w < kStatThreads / kWave; ++w) s += sm[w];
+    }
+    if (tid == 0) stats[blockIdx.x] = StatRec{bm, s, bi, bbad};
+}
+
+hipError_t launch_softmax_stats(const float* logits, const float* draft_logits, const int32_t* rows, int n_rows,
+                                int B, int K, int V, float inv_t_log2e, bool need_sum, StatRec* stats,
+                                hipStream_t stream) {
+    const int nc = n_chunks(V);
+    const long jobs = (long)n_rows * (K + 1) + (draft_logits ? (long)n_rows * K : 0);
+    const long blocks = jobs * nc;
+    if (blocks == 0) return hipSuccess;
+    if (need_sum)
+        hipLaunchKernelGGL(softmax_stats_kernel<true>, dim3((unsigned)blocks), dim3(kStatThreads), 0, stream, logits,
+                           draft_logits, rows, n_rows, B, K, V, nc, inv_t_log2e, stats);
+    else
+        hipLaunchKernelGGL(softmax_stats_kernel<false>, dim3((unsigned)blocks), dim3(kStatThreads), 0, stream,
+                           logits, draft_logits, rows, n_rows, B, K, V, nc, inv_t_log2e, stats);
+    return hipGetLastError();
+}
+
+}  // namespace sv

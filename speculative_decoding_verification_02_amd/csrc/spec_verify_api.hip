@@ -1,0 +1,186 @@
+// spec_verify_api.hip -- the C ABI declared in include/spec_verify.h.
+//
+// Host side only: argument checks, workspace layout, kernel launches on the
+// caller's stream.  Nothing here allocates device memory or synchronises.
+#include <math.h>
+#include <stdint.h>
+
+#include <atomic>
+
+#include "../../include/spec_verify.h"
+#include "sv_common.h"
+#include "sv_launch.h"
+
+namespace {
+
+thread_local const char* g_detail = "";
+
+constexpr int kMaxK = 63;                          // K+1 positions scanned by one wave64
+constexpr int kMaxV = 1024 * sv::kChunk;           // the residual prefix lives in LDS
+constexpr int kMaxDevices = 64;
+
+std::atomic<int> g_cus[kMaxDevices];
+
+spec_status_t hip_fail(hipError_t e) {
+    g_detail = hipGetErrorString(e);
+    return SPEC_ERR_HIP;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// B >= 1, 0 <= K <= 63, 1 <= V <= kMaxV, and every grid the calls launch fits
+// in 31 bits.
+bool sizes_ok(int B, int K, int V) {
+    if (B < 1 || K < 0 || K > kMaxK || V < 1 || V > kMaxV) return false;
+    const long long jobs = (long long)B * (2 * K + 1);
+    return jobs * sv::n_chunks(V) <= 0x7fffffffLL && (long long)B * (K + 1) <= 0x7fffffffLL;
+}
+
+hipError_t num_cus(int* out) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev >= 0 && dev < kMaxDevices) {
+        const int cached = g_cus[dev].load(std::memory_order_relaxed);
+        if (cached > 0) {
+            *out = cached;
+            return hipSuccess;
+        }
+    }
+    int n = 0;
+    e = hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess) return e;
+    if (n < 1) n = 1;
+    if (dev >= 0 && dev < kMaxDevices) g_cus[dev].store(n, std::memory_order_relaxed);
+    *out = n;
+    return hipSuccess;
+}
+
+size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+struct Workspace {
+    sv::StatRec* stats;
+    sv::AcceptInfo* info;
+    float* sums;
+};
+
+// Layout for up to B selected rows: chunk statistics of B*(K+1) target rows and
+// B*K draft rows, one AcceptInfo per row, and the residual chunk sums.
+size_t workspace_layout(int B, int K, int V, void* base, Workspace* ws) {
+    const size_t nc = (size_t)sv::n_chunks(V);
+    const size_t stats = align256(((size_t)B * (K + 1) + (size_t)B * K) * nc * sizeof(sv::StatRec));
+    const size_t info = align256((size_t)B * sizeof(sv::AcceptInfo));
+    const size_t sums = align256((size_t)B * nc * sizeof(float));
+    if (ws) {
+        char* p = static_cast<char*>(base);
+        ws->stats = reinterpret_cast<sv::StatRec*>(p);
+        ws->info = reinterpret_cast<sv::AcceptInfo*>(p + stats);
+        ws->sums = reinterpret_cast<float*>(p + stats + info);
+    }
+    return stats + info + sums;
+}
+
+spec_status_t check_accept_common(const float* logits, const int32_t* draft_tokens, const int32_t* rows,
+                                  int n_rows, int B, int K, int V, const int32_t* accepted_len,
+                                  const int32_t* out_tokens, void* workspace, size_t workspace_bytes) {
+    if (!sizes_ok(B, K, V)) return SPEC_ERR_ARG;
+    if (!logits || !accepted_len || !out_tokens) return SPEC_ERR_ARG;
+    if (K > 0 && !draft_tokens) return SPEC_ERR_ARG;
+    if (rows && (n_rows < 0 || n_rows > B)) return SPEC_ERR_ARG;
+    if (!aligned16(logits)) return SPEC_ERR_ALIGN;
+    if (!workspace || workspace_bytes < workspace_layout(B, K, V, nullptr, nullptr)) return SPEC_ERR_WORKSPACE;
+    if (!aligned16(workspace)) return SPEC_ERR_ALIGN;
+    return SPEC_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+spec_status_t spec_verify_logits(const void* hidden, const void* w_lmhead, spec_dtype_t dtype, float* logits, int B,
+                                 int K, int V, int H, spec_stream_t stream) {
+    if (!hidden || !w_lmhead || !logits) return SPEC_ERR_ARG;
+    if (dtype != SPEC_BF16 && dtype != SPEC_F32) return SPEC_ERR_DTYPE;
+    if (B < 1 || K < 0 || K > kMaxK || V < 1 || H < 8 || (H & 7) != 0) return SPEC_ERR_ARG;
+    if ((long long)B * (K + 1) > 0x7fffffffLL) return SPEC_ERR_ARG;
+    if (!aligned16(hidden) || !aligned16(w_lmhead) || !aligned16(logits)) return SPEC_ERR_ALIGN;
+    const int M = B * (K + 1);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    hipError_t e;
+    if (dtype == SPEC_BF16) {
+        int cus = 0;
+        e = num_cus(&cus);
+        if (e != hipSuccess) return hip_fail(e);
+        e = sv::launch_lmhead_bf16(static_cast<const uint16_t*>(hidden), static_cast<const uint16_t*>(w_lmhead),
+                                   logits, M, V, H, cus, s, 0);
+    } else {
+        e = sv::launch_lmhead_f32(static_cast<const float*>(hidden), static_cast<const float*>(w_lmhead), logits, M,
+                                  V, H, s);
+    }
+    return e == hipSuccess ? SPEC_OK : hip_fail(e);
+}
+
+spec_status_t spec_accept_greedy(const float* logits, const int32_t* draft_tokens, const int32_t* rows, int n_rows,
+                                 int B, int K, int V, int32_t* accepted_len, int32_t* out_tokens, void* workspace,
+                                 size_t workspace_bytes, spec_stream_t stream) {
+    spec_status_t st = check_accept_common(logits, draft_tokens, rows, n_rows, B, K, V, accepted_len, out_tokens,
+                                           workspace, workspace_bytes);
+    if (st != SPEC_OK) return st;
+    const int nr = rows ? n_rows : B;
+    if (nr == 0) return SPEC_OK;
+    Workspace ws;
+    workspace_layout(B, K, V, workspace, &ws);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    hipError_t e = sv::launch_softmax_stats(logits, nullptr, rows, nr, B, K, V, sv::kLog2e, false, ws.stats, s);
+    if (e == hipSuccess)
+        e = sv::launch_accept(logits, nullptr, draft_tokens, nullptr, rows, nr, B, K, V, sv::kLog2e, false, ws.stats,
+                              accepted_len, out_tokens, nullptr, ws.info, s);
+    return e == hipSuccess ? SPEC_OK : hip_fail(e);
+}
+
+spec_status_t spec_accept_sample(const float* logits, const float* draft_logits, const int32_t* draft_tokens,
+                                 float temperature, const uint64_t* seeds, const int32_t* rows, int n_rows, int B,
+                                 int K, int V, int32_t* accepted_len, int32_t* out_tokens, float* probs_at_draft,
+                                 void* workspace, size_t workspace_bytes, spec_stream_t stream) {
+    spec_status_t st = check_accept_common(logits, draft_tokens, rows, n_rows, B, K, V, accepted_len, out_tokens,
+                                           workspace, workspace_bytes);
+    if (st != SPEC_OK) return st;
+    if (!seeds) return SPEC_ERR_ARG;
+    if (K > 0 && !draft_logits) return SPEC_ERR_ARG;
+    if (!(temperature > 0.f) || !isfinite(temperature)) return SPEC_ERR_ARG;
+    if (K > 0 && !aligned16(draft_logits)) return SPEC_ERR_ALIGN;
+    const int nr = rows ? n_rows : B;
+    if (nr == 0) return SPEC_OK;
+    Workspace ws;
+    workspace_layout(B, K, V, workspace, &ws);
+    const float c = sv::kLog2e / temperature;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const float* dl = K > 0 ? draft_logits : nullptr;
+    hipError_t e = sv::launch_softmax_stats(logits, dl, rows, nr, B, K, V, c, true, ws.stats, s);
+    if (e == hipSuccess)
+        e = sv::launch_accept(logits, dl, draft_tokens, seeds, rows, nr, B, K, V, c, true, ws.stats, accepted_len,
+                              out_tokens, probs_at_draft, ws.info, s);
+    if (e == hipSuccess) e = sv::launch_residual(logits, dl, nr, K, V, c, ws.info, ws.sums, out_tokens, s);
+    return e == hipSuccess ? SPEC_OK : hip_fail(e);
+}
+
+size_t spec_workspace_bytes(int B, int K, int V) {
+    if (!sizes_ok(B, K, V)) return 0;
+    return workspace_layout(B, K, V, nullptr, nullptr);
+}
+
+const char* spec_status_string(spec_status_t status) {
+    switch (status) {
+        case SPEC_OK: return "SPEC_OK";
+        case SPEC_ERR_ARG: return "SPEC_ERR_ARG: null pointer, size out of range or bad temperature";
+        case SPEC_ERR_DTYPE: return "SPEC_ERR_DTYPE: unsupported element type";
+        case SPEC_ERR_ALIGN: return "SPEC_ERR_ALIGN: pointer not 16-byte aligned";
+        case SPEC_ERR_WORKSPACE: return "SPEC_ERR_WORKSPACE: workspace missing or too small";
+        case SPEC_ERR_HIP: return "SPEC_ERR_HIP: HIP call or kernel launch failed";
+    }
+    return "unknown spec_status_t";
+}
+
+const char* spec_last_error_detail(void) { return g_detail; }
+
+}  // extern "C"

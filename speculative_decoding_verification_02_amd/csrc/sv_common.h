@@ -1,0 +1,108 @@
+// sv_common.h -- device-side helpers shared by the verify-step kernels
+// (gfx950, wave64).  Internal to the library: not part of the C ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace sv {
+
+// ---------------------------------------------------------------- sizes ----
+
+constexpr int kWave = 64;
+// Softmax statistics and residual sums split each vocabulary row into fixed
+// chunks; one workgroup of kStatThreads threads owns a chunk, each thread
+// kStatPerThread consecutive... elements (see the kernels for the order).
+constexpr int kStatThreads = 256;
+constexpr int kStatPerThread = 16;
+constexpr int kChunk = kStatThreads * kStatPerThread;  // 4096 logits per chunk
+
+inline int n_chunks(int V) { return (V + kChunk - 1) / kChunk; }
+
+// ------------------------------------------------------------- records ----
+
+// Partial softmax statistics of one chunk of one row: m = max of the raw
+// logits z over the chunk, s = sum exp((z - m) / T) over the chunk, idx = the
+// lowest index attaining m, bad = the chunk held a NaN or +inf.
+struct __align__(16) StatRec {
+    float m;
+    float s;
+    int idx;
+    int bad;
+};
+
+// What the accept kernel hands to the residual kernels for one sampled
+// sequence: terminal position n (-1 = sequence faulted or skipped), the
+// terminal uniform, and the merged statistics of the terminal target row and
+// (if n < K) draft row.
+struct __align__(16) AcceptInfo {
+    int n;
+    int b;
+    float u_term;
+    float mt;
+    float st;
+    float md;
+    float sd;
+    int pad;
+};
+
+// ---------------------------------------------------------- reductions ----
+
+__device__ __forceinline__ float wave_sum(float x) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o, kWave);
+    return x;
+}
+
+// max with lowest-index tie break; NaN never enters (callers mask it).
+__device__ __forceinline__ void argmax_combine(float& m, int& i, float m2, int i2) {
+    if (m2 > m || (m2 == m && i2 < i)) {
+        m = m2;
+        i = i2;
+    }
+}
+
+__device__ __forceinline__ void wave_argmax(float& m, int& i) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+        float m2 = __shfl_xor(m, o, kWave);
+        int i2 = __shfl_xor(i, o, kWave);
+        argmax_combine(m, i, m2, i2);
+    }
+}
+
+// ----------------------------------------------------------------- Philox --
+// Philox4x32-10 (Salmon, Moraes, Dror, Shaw, SC'11): ten rounds of
+//   (c0,c1,c2,c3) -> (hi(M1*c2) ^ c1 ^ k0, lo(M1*c2), hi(M0*c0) ^ c3 ^ k1, lo(M0*c0))
+// with the key bumped by the Weyl increments between rounds.
+constexpr uint32_t kPhiloxM0 = 0xD2511F53u;
+constexpr uint32_t kPhiloxM1 = 0xCD9E8D57u;
+constexpr uint32_t kPhiloxW0 = 0x9E3779B9u;
+constexpr uint32_t kPhiloxW1 = 0xBB67AE85u;
+
+__device__ __forceinline__ uint4 philox4x32_10(uint4 c, uint32_t k0, uint32_t k1) {
+#pragma unroll
+    for (int r = 0; r < 10; ++r) {
+        if (r) {
+            k0 += kPhiloxW0;
+            k1 += kPhiloxW1;
+        }
+        const uint32_t hi0 = __umulhi(kPhiloxM0, c.x);
+        const uint32_t lo0 = kPhiloxM0 * c.x;
+        const uint32_t hi1 = __umulhi(kPhiloxM1, c.z);
+        const uint32_t lo1 = kPhiloxM1 * c.z;
+        c = make_uint4(hi1 ^ c.y ^ k0, lo1, hi0 ^ c.w ^ k1, lo0);
+    }
+    return c;
+}
+
+// 32-bit word -> [0, 1) on the 24-bit grid (exact in fp32).
+__device__ __forceinline__ float uniform24(uint32_t w) {
+    return static_cast<float>(w >> 8) * (1.0f / 16777216.0f);
+}
+
+// log2(e): exp(x) = exp2(x * log2e).  Weights are computed as
+// exp2((z - m) * c) with c = log2(e) / T.
+constexpr float kLog2e = 1.4426950408889634f;
+
+}  // namespace sv

@@ -1,0 +1,142 @@
+"""C-ABI checks that need no GPU: the library loads, exports every function
+include/spec_verify.h declares, sizes its workspace, and rejects bad
+arguments on the host before anything is enqueued (these calls return before
+the first HIP runtime call, so they run on a machine without a GPU)."""
+import ctypes
+import math
+import os
+import re
+
+import pytest
+
+import speculative_decoding_verification_02_amd as sv
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+P = ctypes.c_void_p
+A = P(0x10000)          # a 16-byte-aligned stand-in address (never dereferenced)
+MIS = P(0x10004)        # misaligned stand-in
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(sv.LIB_PATH):
+        pytest.fail("libspecverify.so is not built: run __graft_entry__.build()")
+    return sv.load_library()
+
+
+def test_exports_every_declared_symbol(lib):
+    names = sv.declared_symbols()
+    assert set(names) == {"spec_verify_logits", "spec_accept_greedy", "spec_accept_sample",
+                          "spec_workspace_bytes", "spec_status_string", "spec_last_error_detail"}
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_status_strings(lib):
+    for code in range(6):
+        assert sv.spec_status_string(code).startswith("SPEC_")
+    assert "unknown" in sv.spec_status_string(99)
+    assert sv.spec_last_error_detail() == ""
+
+
+def test_workspace_bytes(lib):
+    assert sv.spec_workspace_bytes(0, 1, 10) == 0
+    assert sv.spec_workspace_bytes(1, 64, 10) == 0
+    assert sv.spec_workspace_bytes(1, -1, 10) == 0
+    assert sv.spec_workspace_bytes(1, 1, 0) == 0
+    assert sv.spec_workspace_bytes(1, 1, 4096 * 1024 + 1) == 0
+    a = sv.spec_workspace_bytes(1, 5, 128256)
+    b = sv.spec_workspace_bytes(64, 4, 128256)
+    c = sv.spec_workspace_bytes(256, 8, 152064)
+    assert 0 < a < b < c
+    assert a % 256 == 0 and c % 256 == 0
+    assert sv.spec_workspace_bytes(1, 0, 1) > 0
+    assert sv.spec_workspace_bytes(1, 63, 4096 * 1024) > 0
+
+
+def test_verify_logits_validation(lib):
+    f = lib.spec_verify_logits
+    assert f(None, A, 0, A, 1, 1, 16, 8, None) == sv.SPEC_ERR_ARG
+    assert f(A, None, 0, A, 1, 1, 16, 8, None) == sv.SPEC_ERR_ARG
+    assert f(A, A, 0, None, 1, 1, 16, 8, None) == sv.SPEC_ERR_ARG
+    assert f(A, A, 7, A, 1, 1, 16, 8, None) == sv.SPEC_ERR_DTYPE
+    assert f(A, A, 0, A, 0, 1, 16, 8, None) == sv.SPEC_ERR_ARG     # B = 0
+    assert f(A, A, 0, A, 1, 64, 16, 8, None) == sv.SPEC_ERR_ARG    # K > 63
+    assert f(A, A, 0, A, 1, -1, 16, 8, None) == sv.SPEC_ERR_ARG
+    assert f(A, A, 0, A, 1, 1, 0, 8, None) == sv.SPEC_ERR_ARG      # V = 0
+    assert f(A, A, 0, A, 1, 1, 16, 12, None) == sv.SPEC_ERR_ARG    # H % 8
+    assert f(A, A, 0, A, 1, 1, 16, 0, None) == sv.SPEC_ERR_ARG
+    assert f(MIS, A, 0, A, 1, 1, 16, 8, None) == sv.SPEC_ERR_ALIGN
+    assert f(A, MIS, 1, A, 1, 1, 16, 8, None) == sv.SPEC_ERR_ALIGN
+    assert f(A, A, 0, MIS, 1, 1, 16, 8, None) == sv.SPEC_ERR_ALIGN
+
+
+def _greedy(lib, logits=A, drafts=A, rows=None, n_rows=0, B=2, K=3, V=100, acc=A, out=A, ws=A, wsb=None):
+    if wsb is None:
+        wsb = sv.spec_workspace_bytes(B, K, V) if sv.spec_workspace_bytes(B, K, V) else 1 << 20
+    return lib.spec_accept_greedy(logits, drafts, rows, n_rows, B, K, V, acc, out, ws, wsb, None)
+
+
+def test_accept_greedy_validation(lib):
+    need = sv.spec_workspace_bytes(2, 3, 100)
+    assert _greedy(lib, logits=None) == sv.SPEC_ERR_ARG
+    assert _greedy(lib, drafts=None) == sv.SPEC_ERR_ARG             # K > 0 needs drafts
+    assert _greedy(lib, acc=None) == sv.SPEC_ERR_ARG
+    assert _greedy(lib, out=None) == sv.SPEC_ERR_ARG
+    assert _greedy(lib, B=0) == sv.SPEC_ERR_ARG
+    assert _greedy(lib, K=64) == sv.SPEC_ERR_ARG
+    assert _greedy(lib, V=0) == sv.SPEC_ERR_ARG
+    assert _greedy(lib, rows=A, n_rows=3) == sv.SPEC_ERR_ARG        # n_rows > B
+    assert _greedy(lib, rows=A, n_rows=-1) == sv.SPEC_ERR_ARG
+    assert _greedy(lib, logits=MIS) == sv.SPEC_ERR_ALIGN
+    assert _greedy(lib, ws=None) == sv.SPEC_ERR_WORKSPACE
+    assert _greedy(lib, wsb=need - 1) == sv.SPEC_ERR_WORKSPACE
+    assert _greedy(lib, ws=MIS) == sv.SPEC_ERR_ALIGN
+
+
+def _sample(lib, T=1.0, seeds=A, dl=A, drafts=A, logits=A, K=3, B=2, V=100, wsb=None, rows=None, n_rows=0):
+    if wsb is None:
+        wsb = sv.spec_workspace_bytes(B, K, V) or (1 << 20)
+    return lib.spec_accept_sample(logits, dl, drafts, T, seeds, rows, n_rows, B, K, V, A, A, None, A, wsb, None)
+
+
+def test_accept_sample_validation(lib):
+    assert _sample(lib, T=0.0) == sv.SPEC_ERR_ARG
+    assert _sample(lib, T=-1.0) == sv.SPEC_ERR_ARG
+    assert _sample(lib, T=math.nan) == sv.SPEC_ERR_ARG
+    assert _sample(lib, T=math.inf) == sv.SPEC_ERR_ARG
+    assert _sample(lib, seeds=None) == sv.SPEC_ERR_ARG
+    assert _sample(lib, dl=None) == sv.SPEC_ERR_ARG                 # K > 0 needs draft logits
+    assert _sample(lib, drafts=None) == sv.SPEC_ERR_ARG
+    assert _sample(lib, dl=MIS) == sv.SPEC_ERR_ALIGN
+    assert _sample(lib, logits=MIS) == sv.SPEC_ERR_ALIGN
+    assert _sample(lib, wsb=16) == sv.SPEC_ERR_WORKSPACE
+    assert _sample(lib, B=1, rows=A, n_rows=2) == sv.SPEC_ERR_ARG
+
+
+def test_zero_selected_rows_is_a_no_op(lib):
+    # n_rows == 0 with a row list: valid, nothing to enqueue, no HIP call
+    assert _greedy(lib, rows=A, n_rows=0) == sv.SPEC_OK
+    assert _sample(lib, rows=A, n_rows=0) == sv.SPEC_OK
+
+
+def test_binding_fails_loudly_without_library(tmp_path):
+    import importlib
+    mod = importlib.import_module("speculative_decoding_verification_02_amd")
+    saved = mod._lib
+    mod._lib = None
+    try:
+        with pytest.raises(RuntimeError, match="missing"):
+            mod.load_library(str(tmp_path / "nope.so"))
+    finally:
+        mod._lib = saved
+
+
+def test_product_never_touches_the_oracle():
+    """The package (binding and kernels) neither imports nor names the oracle."""
+    pkg = os.path.join(ROOT, "speculative_decoding_verification_02_amd")
+    for dirpath, _, files in os.walk(pkg):
+        for fn in files:
+            if fn.endswith((".py", ".hip", ".h", ".cpp")):
+                text = open(os.path.join(dirpath, fn)).read()
+                assert not re.search(r"\boracle\b", text), fn

@@ -1,0 +1,109 @@
+"""GPU parity of spec_verify_logits (LM-head contraction) against the oracle.
+
+Covers the small-M streaming kernel (M <= 16), the LDS-tiled kernel (larger
+M), and the fp32 kernel, on shapes that span several tiles with ragged tails
+in V, M and H; integer-valued inputs that must come out bit-exact whatever the
+summation order; the full-size workloads (all entries at B=1, sampled entries
+at the larger ones); and run-to-run determinism.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from gpu_support import check_logits, dev, f64, gpu_logits, say
+
+pytestmark = pytest.mark.gpu
+
+
+def _case(B, K, H, V, dtype, w_std=0.05, seed=0, device="cpu"):
+    wl = synth.Workload("t", B=B, K=K, H=H, V=V, dtype=dtype, w_std=w_std, temperature=1.0,
+                        draft="additive", data_seed=seed)
+    return synth.weights(wl, device), synth.hidden_states(wl, device)
+
+
+def _check(hidden, W):
+    B, P, H = hidden.shape
+    say("logits case B=%d K=%d H=%d V=%d %s" % (B, P - 1, H, W.shape[0], hidden.dtype))
+    g = gpu_logits(hidden.to(dev()), W.to(dev()))
+    torch.cuda.synchronize()
+    x, w = f64(hidden).reshape(B * P, H), f64(W)
+    o = oracle.lm_head_logits(x, w)
+    absdot = oracle.lm_head_logits(np.abs(x), np.abs(w))
+    ratio = check_logits(g.cpu().numpy().reshape(B * P, -1).astype(np.float64), o, absdot, H)
+    say("  max err / fp32 bound = %.3g" % ratio)
+
+
+def test_fp32_tiny_workload():
+    W, h = _case(1, 4, 256, 1000, "f32", 0.05, seed=1)
+    _check(h, W)
+
+
+@pytest.mark.parametrize("B,K", [(1, 0), (1, 5), (2, 2), (4, 3), (16, 0)])
+@pytest.mark.parametrize("H,V", [(264, 1000), (4096, 4099), (520, 33)])
+def test_bf16_small_m(B, K, H, V):
+    W, h = _case(B, K, H, V, "bf16", 0.02, seed=B * 100 + K + H + V)
+    _check(h, W)
+
+
+@pytest.mark.parametrize("B,K", [(6, 2), (130, 0), (64, 4), (3, 63)])
+@pytest.mark.parametrize("H,V", [(64, 1000), (520, 2053), (1032, 257)])
+def test_bf16_tiled(B, K, H, V):
+    W, h = _case(B, K, H, V, "bf16", 0.02, seed=B * 7 + K + H + V)
+    _check(h, W)
+
+
+@pytest.mark.parametrize("B,K,V,dtype", [(1, 5, 3001, "bf16"), (64, 4, 1031, "bf16"), (1, 4, 999, "f32")])
+def test_small_integers_bit_exact(B, K, V, dtype):
+    """Inputs in -4..4 (exact in bf16): every partial sum is an integer below
+    2^24, so the fp32 result is exact in any summation order."""
+    H = 4096
+    g = torch.Generator().manual_seed(V)
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    h = torch.randint(-4, 5, (B, K + 1, H), generator=g).to(tdt)
+    W = torch.randint(-4, 5, (V, H), generator=g).to(tdt)
+    say("integer logits B=%d K=%d V=%d %s" % (B, K, V, dtype))
+    out = gpu_logits(h.to(dev()), W.to(dev())).cpu().numpy().reshape(B * (K + 1), V)
+    ref = oracle.lm_head_logits(f64(h).reshape(-1, H), f64(W))
+    np.testing.assert_array_equal(out.astype(np.float64), ref)
+
+
+def test_full_size_b1_k5_all_entries():
+    wl = synth.WORKLOADS["b1_k5_h4096_v128256"]
+    W, h = synth.weights(wl, dev()), synth.hidden_states(wl, dev())
+    _check(h, W)
+
+
+@pytest.mark.parametrize("name", ["b64_k4_h4096_v128256", "b256_k8_h8192_v152064", "b512_k3_h5120_v262144"])
+def test_full_size_sampled_entries(name):
+    wl = synth.WORKLOADS[name]
+    say("full-size logits %s: generating inputs on the GPU" % name)
+    W, h = synth.weights(wl, dev()), synth.hidden_states(wl, dev())
+    g = gpu_logits(h, W)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(5)
+    ms = rng.integers(0, wl.M, 512)
+    vs = np.concatenate([rng.integers(0, wl.V, 500), [0, 1, wl.V - 2, wl.V - 1] * 3])
+    ms = ms[: len(vs)]
+    x = f64(h.reshape(wl.M, wl.H)[torch.as_tensor(ms, device=dev())])
+    w = f64(W[torch.as_tensor(vs, device=dev())])
+    o = np.sum(x * w, axis=1)
+    absdot = np.sum(np.abs(x * w), axis=1)
+    gv = g.reshape(wl.M, wl.V)[torch.as_tensor(ms, device=dev()), torch.as_tensor(vs, device=dev())]
+    gv = gv.cpu().numpy().astype(np.float64)
+    u = 2.0 ** -24
+    gam = (wl.H + 1) * u / (1 - (wl.H + 1) * u)
+    err = np.abs(gv - o)
+    assert np.all(err <= gam * absdot), np.max(err / (gam * absdot))
+    assert not torch.isnan(g).any().item()
+    say("  %d entries, max err / fp32 bound = %.3g" % (len(vs), np.max(err / (gam * absdot))))
+
+
+@pytest.mark.parametrize("B,K,H,V", [(1, 5, 4096, 128256), (40, 7, 512, 5003)])
+def test_deterministic(B, K, H, V):
+    W, h = _case(B, K, H, V, "bf16", 0.02, seed=3, device=dev())
+    a = gpu_logits(h, W)
+    b = gpu_logits(h, W)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
