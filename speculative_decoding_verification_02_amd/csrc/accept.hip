@@ -1,9 +1,10 @@
 // accept.hip -- greedy and sampled acceptance of the verify step.
 //
-// One wavefront per selected sequence; lane i handles verify position i
-// (i <= K <= 63).  Each lane merges the chunk statistics of its target row
-// (and draft row), decides whether draft i would be accepted on its own, and
-// the wavefront finds the first rejection with one ballot:
+// One workgroup per selected sequence.  The chunk statistics of the
+// sequence's rows are staged in LDS with every load in flight at once and
+// merged row by row, one wavefront per row; then wavefront 0, lane i = verify
+// position i (i <= K <= 63), decides whether draft i would be accepted on its
+// own, and one ballot finds the first rejection:
 //   greedy  ("Inference-4", greedy bullet): ok_i = [d_i == argmax_v z_t[i, v]]
 //   sampled (same page, sampling bullet; "speculative-decoding" blog,
 //            Rejection sampling): ok_i = [u_i < min(1, q_i(d_i) / p_i(d_i))]
@@ -23,7 +24,10 @@
 
 namespace sv {
 
-constexpr int kAcceptThreads = 256;  // 4 sequences per workgroup
+constexpr int kAcceptThreads = 256;          // one workgroup per sequence
+constexpr int kAcceptWaves = kAcceptThreads / kWave;
+constexpr int kRecBuf = 2048;                // chunk records staged in LDS per pass (32 KB)
+constexpr int kMaxRows = 2 * 63 + 1;         // target rows 0..K plus draft rows 0..K-1
 
 struct Merged {
     float m;
@@ -32,20 +36,28 @@ struct Merged {
     int bad;
 };
 
-__device__ __forceinline__ Merged merge_row(const StatRec* __restrict__ rec, int nc, float c, bool need_sum) {
-    Merged r{-INFINITY, 0.f, INT_MAX, 0};
-    for (int k = 0; k < nc; ++k) {
+// Merge the chunk records of one row across a wavefront (records in LDS):
+//   M = max m_c (lowest index on ties), S = sum s_c * exp2((m_c - M) * c).
+__device__ __forceinline__ Merged wave_merge(const StatRec* rec, int nc, float c, bool need_sum, int lane) {
+    float m = -INFINITY;
+    int idx = INT_MAX;
+    int bad = 0;
+    for (int k = lane; k < nc; k += kWave) {
         const StatRec x = rec[k];
-        argmax_combine(r.m, r.idx, x.m, x.idx);
-        r.bad |= x.bad;
+        argmax_combine(m, idx, x.m, x.idx);
+        bad |= x.bad;
     }
-    if (need_sum && r.m != -INFINITY) {
-        for (int k = 0; k < nc; ++k) {
+    wave_argmax(m, idx);
+    bad = __ballot(bad) != 0ull;
+    float s = 0.f;
+    if (need_sum && m != -INFINITY) {
+        for (int k = lane; k < nc; k += kWave) {
             const StatRec x = rec[k];
-            if (x.m != -INFINITY) r.s += x.s * exp2f((x.m - r.m) * c);
+            if (x.m != -INFINITY) s += x.s * exp2f((x.m - m) * c);
         }
+        s = wave_sum(s);
     }
-    return r;
+    return Merged{m, s, idx, bad};
 }
 
 template <bool SAMPLED>
@@ -53,31 +65,55 @@ __global__ __launch_bounds__(kAcceptThreads) void accept_kernel(
     const float* __restrict__ logits, const float* __restrict__ draft_logits, const int32_t* __restrict__ draft_tokens,
     const uint64_t* __restrict__ seeds, const int32_t* __restrict__ rows, int n_rows, int B, int K, int V, int nc,
     float c, const StatRec* __restrict__ stats, int32_t* __restrict__ accepted_len, int32_t* __restrict__ out_tokens,
-    float* __restrict__ probs_at_draft, AcceptInfo* __restrict__ info) {
-    const int lane = threadIdx.x & 63;
-    const int j = blockIdx.x * (kAcceptThreads / kWave) + (threadIdx.x >> 6);
-    if (j >= n_rows) return;
+    float* __restrict__ probs_at_draft, AcceptInfo* __restrict__ info, int* __restrict__ counters) {
+    __shared__ StatRec recs[kRecBuf];
+    __shared__ Merged merged[kMaxRows];
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int j = blockIdx.x;
     const int b = rows ? rows[j] : j;
+    if (SAMPLED && tid == 0) counters[j] = 0;   // the residual kernel counts its chunk blocks from zero
     if (b < 0 || b >= B) {
-        if (SAMPLED && lane == 0) info[j] = AcceptInfo{-1, b, 0.f, 0.f, 0.f, 0.f, 0.f, 0};
+        if (SAMPLED && tid == 0) info[j] = AcceptInfo{-1, b, 0.f, 0.f, 0.f, 0.f, 0.f, 0};
         return;
     }
+
+    // rows of this sequence: target 0..K, then (sampled) draft 0..K-1
+    const int n_rows_seq = (K + 1) + (SAMPLED ? K : 0);
+    const int rows_per_pass = max(1, min(n_rows_seq, kRecBuf / nc));
+    for (int r0 = 0; r0 < n_rows_seq; r0 += rows_per_pass) {
+        const int nr = min(rows_per_pass, n_rows_seq - r0);
+        // stage the records of rows r0 .. r0+nr-1: every load in flight at once
+        for (int e = tid; e < nr * nc; e += kAcceptThreads) {
+            const int rr = r0 + e / nc, k = e - (e / nc) * nc;
+            const size_t row_rec = rr <= K ? (size_t)j * (K + 1) + rr
+                                           : (size_t)n_rows * (K + 1) + (size_t)j * K + (rr - K - 1);
+            recs[e] = stats[row_rec * nc + k];
+        }
+        __syncthreads();
+        for (int rr = wave; rr < nr; rr += kAcceptWaves) {
+            const Merged x = wave_merge(recs + rr * nc, nc, c, SAMPLED, lane);
+            if (lane == 0) merged[r0 + rr] = x;
+        }
+        __syncthreads();
+    }
+    if (wave != 0) return;
+
     const int i = lane;
     const bool active = i <= K;
     const bool has_draft = i < K;
-
     Merged t{-INFINITY, 0.f, INT_MAX, 0}, d{-INFINITY, 0.f, INT_MAX, 0};
     int tok = 0;
     int bad = 0;
     if (active) {
-        t = merge_row(stats + ((size_t)j * (K + 1) + i) * nc, nc, c, SAMPLED);
+        t = merged[i];
         bad = t.bad | (t.m == -INFINITY);
     }
     if (has_draft) {
         tok = draft_tokens[(size_t)b * K + i];
         bad |= (tok < 0 || tok >= V);
         if (SAMPLED) {
-            d = merge_row(stats + ((size_t)n_rows * (K + 1) + (size_t)j * K + i) * nc, nc, c, true);
+            d = merged[K + 1 + i];
             bad |= d.bad | (d.m == -INFINITY);
         }
     }
@@ -141,19 +177,18 @@ __global__ __launch_bounds__(kAcceptThreads) void accept_kernel(
 hipError_t launch_accept(const float* logits, const float* draft_logits, const int32_t* draft_tokens,
                          const uint64_t* seeds, const int32_t* rows, int n_rows, int B, int K, int V,
                          float inv_t_log2e, bool sampled, const StatRec* stats, int32_t* accepted_len,
-                         int32_t* out_tokens, float* probs_at_draft, AcceptInfo* info, hipStream_t stream) {
+                         int32_t* out_tokens, float* probs_at_draft, AcceptInfo* info, int* counters,
+                         hipStream_t stream) {
     if (n_rows == 0) return hipSuccess;
     const int nc = n_chunks(V);
-    const int per = kAcceptThreads / kWave;
-    const int grid = (n_rows + per - 1) / per;
     if (sampled)
-        hipLaunchKernelGGL(accept_kernel<true>, dim3(grid), dim3(kAcceptThreads), 0, stream, logits, draft_logits,
+        hipLaunchKernelGGL(accept_kernel<true>, dim3(n_rows), dim3(kAcceptThreads), 0, stream, logits, draft_logits,
                            draft_tokens, seeds, rows, n_rows, B, K, V, nc, inv_t_log2e, stats, accepted_len,
-                           out_tokens, probs_at_draft, info);
+                           out_tokens, probs_at_draft, info, counters);
     else
-        hipLaunchKernelGGL(accept_kernel<false>, dim3(grid), dim3(kAcceptThreads), 0, stream, logits, draft_logits,
+        hipLaunchKernelGGL(accept_kernel<false>, dim3(n_rows), dim3(kAcceptThreads), 0, stream, logits, draft_logits,
                            draft_tokens, seeds, rows, n_rows, B, K, V, nc, inv_t_log2e, stats, accepted_len,
-                           out_tokens, probs_at_draft, info);
+                           out_tokens, probs_at_draft, info, counters);
     return hipGetLastError();
 }
 

@@ -49,74 +49,238 @@ __device__ __forceinline__ void store_row4(float* __restrict__ out, int v, int V
 }
 
 // ------------------------------------------------------------ small M ------
-// One wave owns a tile of 16 vocabulary rows over the whole hidden dimension
-// and walks the tiles of the vocabulary with a grid stride.  The hidden states
-// (M <= 16 rows) are staged once per workgroup in LDS; W streams from HBM with
-// one 128-bit load per lane per 32 columns, kU loads in flight per stage and
-// two stages in registers.
-constexpr int kSkinnyThreads = 512;
-constexpr int kSkinnyU = 8;   // 32-column steps per pipeline stage
+// Streaming kernel for M <= 16.  The MFMA operand layout puts 16 vocabulary
+// rows in one instruction with only 64 bytes per row; loaded that way, HBM
+// streams at ~5.5 TB/s on MI355X, while 256-byte (or longer) runs per row
+// stream at ~6.9-7.0 TB/s.  So W is loaded with RPL rows per instruction
+// (64/RPL lanes per row, 1024/RPL contiguous bytes per row), written to a
+// per-wave LDS buffer, and read back in MFMA layout.  In the buffer the
+// 16-byte chunk c of tile row R sits at R*CPR + (c ^ (R % CPR)) (CPR = chunks
+// per row per stage): the writes (a run of chunks of one row) and the reads
+// (one chunk of 16 rows) both touch distinct banks.
+//
+// One wave owns tiles of 16 vocabulary rows (grid stride) and runs one
+// continuous load pipeline over all of its (tile, stage) steps, P stages deep,
+// so loads stay in flight across tile boundaries.  The hidden states (M <= 16
+// rows) are staged once per workgroup in LDS.  Each wave's buffer is private:
+// LDS operations of one wave complete in order, so no workgroup barrier is
+// needed between its writes and reads.
+template <int RPL, int P, int THREADS>
+struct Skinny {
+    static constexpr int kLanesPerRow = 64 / RPL;          // lanes sharing a row in one load
+    static constexpr int kCPR = kLanesPerRow;              // 16-byte chunks per row per stage
+    static constexpr int kKS = kCPR * 8;                   // k (hidden) elements per stage
+    static constexpr int kLoads = 16 / RPL;                // load instructions per stage
+    static constexpr int kSteps = kKS / 32;                // MFMA steps per stage
+    static constexpr int kWaves = THREADS / 64;
+    static constexpr int kBufChunks = 16 * kCPR;           // per-wave LDS buffer, 16-byte chunks
+    static size_t lds_bytes(int M, int H) { return (size_t)M * (H + 8) * 2 + (size_t)kWaves * kBufChunks * 16; }
+};
 
-__global__ __launch_bounds__(kSkinnyThreads) void lmhead_skinny_bf16(
+template <int RPL, int P, int THREADS>
+__global__ __launch_bounds__(THREADS) void lmhead_skinny_bf16(
     const uint16_t* __restrict__ hidden, const uint16_t* __restrict__ W, float* __restrict__ logits,
     int M, int V, int H, int n_tiles) {
-    extern __shared__ __align__(16) uint16_t hs[];
-    const int ld = H + 8;  // LDS row stride in elements (16-byte pad)
-    const int cpr = H >> 3;  // 16-byte chunks per row
-    for (int i = threadIdx.x; i < M * cpr; i += blockDim.x) {
+    using S = Skinny<RPL, P, THREADS>;
+    extern __shared__ __align__(16) unsigned char smem[];
+    uint16_t* hs = reinterpret_cast<uint16_t*>(smem);
+    const int ld = H + 8;                 // LDS row stride of the hidden states, elements
+    const int cpr = H >> 3;
+    for (int i = threadIdx.x; i < M * cpr; i += THREADS) {
         const int m = i / cpr, c = i - m * cpr;
         *reinterpret_cast<uint4*>(hs + m * ld + c * 8) =
             *reinterpret_cast<const uint4*>(hidden + (size_t)m * H + c * 8);
     }
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    u32x4* buf = reinterpret_cast<u32x4*>(smem + (size_t)M * ld * 2) + wave * S::kBufChunks;
     __syncthreads();
 
-    const int lane = threadIdx.x & 63;
+    // load-side coordinates: lane -> (row within the load, chunk)
+    const int la = lane / S::kLanesPerRow, lc = lane % S::kLanesPerRow;
+    // MFMA-side coordinates: lane -> (row r, k group g)
     const int r = lane & 15, g = lane >> 4;
-    const int wpb = blockDim.x >> 6;
     const bool hrow_ok = r < M;
-    const uint16_t* hp = hs + (hrow_ok ? r : 0) * ld + g * 8;
+    const uint16_t* hp = hs + (hrow_ok ? r : 0) * ld;
     const bool vec_ok = (V & 3) == 0;
-    const int n_steps = (H + 31) >> 5;        // 32-column steps
-    const int n_stages = (n_steps + kSkinnyU - 1) / kSkinnyU;
+    const int n_stages = (H + S::kKS - 1) / S::kKS;
 
-    for (int t = blockIdx.x * wpb + (threadIdx.x >> 6); t < n_tiles; t += gridDim.x * wpb) {
-        const int v0 = t << 4;
-        const int vrow = min(v0 + r, V - 1);
-        const uint16_t* wp = W + (size_t)vrow * H + g * 8;
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    const int wstride = gridDim.x * S::kWaves;
+    const int t0 = blockIdx.x * S::kWaves + wave;
+    if (t0 >= n_tiles) return;
+    const int my_tiles = (n_tiles - t0 + wstride - 1) / wstride;
+    const int n_steps = my_tiles * n_stages;
+
+    // issue the loads of step i (tile t0 + (i / n_stages) * wstride, stage i % n_stages)
+    auto issue = [&](int i, u32x4 (&dst)[S::kLoads]) {
         const u32x4 zero = {0u, 0u, 0u, 0u};
-        u32x4 cur[kSkinnyU], nxt[kSkinnyU];
+        if (i >= n_steps) {
+#pragma unroll
+            for (int q = 0; q < S::kLoads; ++q) dst[q] = zero;
+            return;
+        }
+        const int ti = i / n_stages, st = i - ti * n_stages;
+        const int v0 = (t0 + ti * wstride) << 4;
+        const int k = st * S::kKS + lc * 8;
+#pragma unroll
+        for (int q = 0; q < S::kLoads; ++q) {
+            const int row = min(v0 + q * RPL + la, V - 1);
+            dst[q] = (k < H) ? load_stream(W + (size_t)row * H + k) : zero;
+        }
+    };
 
+    u32x4 pipe[P][S::kLoads];
 #pragma unroll
-        for (int u = 0; u < kSkinnyU; ++u) {
-            const int k = u * 32;
-            cur[u] = (k + g * 8 < H) ? load_stream(wp + k) : zero;
+    for (int p = 0; p < P - 1; ++p) issue(p, pipe[p]);
+
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    for (int base = 0; base < n_steps; base += P) {
+#pragma unroll
+        for (int p = 0; p < P; ++p) {
+            const int i = base + p;
+            if (i >= n_steps) break;
+            issue(i + P - 1, pipe[(p + P - 1) % P]);
+            // transpose step i through the wave's LDS buffer
+#pragma unroll
+            for (int q = 0; q < S::kLoads; ++q) {
+                const int R = q * RPL + la;
+                buf[R * S::kCPR + (lc ^ (R % S::kCPR))] = pipe[p][q];
+            }
+            __builtin_amdgcn_wave_barrier();
+            const int ti = i / n_stages, st = i - ti * n_stages;
+            const int kb = st * S::kKS;
+#pragma unroll
+            for (int j = 0; j < S::kSteps; ++j) {
+                const int c = j * 4 + g;
+                const u32x4 wv = buf[r * S::kCPR + (c ^ (r % S::kCPR))];
+                const int k = kb + c * 8;
+                u32x4 hv = {0u, 0u, 0u, 0u};
+                if (hrow_ok && k < H) hv = *reinterpret_cast<const u32x4*>(hp + k);
+                acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(wv), as_bf16x8(hv), acc, 0, 0, 0);
+            }
+            __builtin_amdgcn_wave_barrier();
+            if (st == n_stages - 1) {
+                const int v0 = (t0 + ti * wstride) << 4;
+                if (hrow_ok) store_row4(logits + (size_t)r * V, v0 + 4 * g, V, acc, vec_ok);
+                acc = f32x4{0.f, 0.f, 0.f, 0.f};
+            }
         }
-        for (int s = 0; s < n_stages; ++s) {
-            const int kn = (s + 1) * kSkinnyU * 32;
-            if (s + 1 < n_stages) {
-#pragma unroll
-                for (int u = 0; u < kSkinnyU; ++u) {
-                    const int k = kn + u * 32;
-                    nxt[u] = (k + g * 8 < H) ? load_stream(wp + k) : zero;
-                }
-            }
-            const int kc = s * kSkinnyU * 32;
-#pragma unroll
-            for (int u = 0; u < kSkinnyU; ++u) {
-                const int k = kc + u * 32;
-                u32x4 hv = zero;
-                if (hrow_ok && k + g * 8 < H) hv = *reinterpret_cast<const u32x4*>(hp + k);
-                acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(cur[u]), as_bf16x8(hv), acc, 0, 0, 0);
-            }
-            if (s + 1 < n_stages) {
-#pragma unroll
-                for (int u = 0; u < kSkinnyU; ++u) cur[u] = nxt[u];
-            }
-        }
-        if (hrow_ok) store_row4(logits + (size_t)r * V, v0 + 4 * g, V, acc, vec_ok);
     }
 }
+
+// ------------------------------------------------- small M, cooperative ----
+// A workgroup of NW waves streams one 16-row vocabulary tile at a time (one
+// contiguous 16 * H * 2-byte block of W), the hidden dimension split into NW
+// slices of SLICE columns, one per wave.  Each wave keeps the B-operand
+// fragments of its hidden slice (M <= 16 rows) in registers for the whole
+// kernel, transposes its W fragments through a private LDS buffer as above,
+// and the NW partial 16 x 16 accumulators of a tile are summed in LDS in wave
+// order (fixed order: bitwise reproducible).  Loads run one tile ahead: while
+// stage st of tile t is consumed, stage st of the next tile is issued.  Each
+// workgroup takes a contiguous, balanced range of tiles, so it streams one
+// contiguous region of W and its output rows fill whole cache lines.
+template <int RPL, int MAXST, int NW>
+struct Coop {
+    static constexpr int kLanesPerRow = 64 / RPL;
+    static constexpr int kCPR = kLanesPerRow;
+    static constexpr int kKS = kCPR * 8;          // k elements per stage
+    static constexpr int kLoads = 16 / RPL;
+    static constexpr int kSteps = kKS / 32;
+    static constexpr int kSlice = MAXST * kKS;    // k elements per wave
+    static constexpr int kBufChunks = 16 * kCPR;
+    static constexpr int kThreads = NW * 64;
+    static size_t lds_bytes() { return (size_t)NW * kBufChunks * 16 + 2 * (size_t)NW * 64 * 16; }
+    static bool fits(int M, int H) { return M <= 16 && H <= NW * kSlice; }
+};
+
+template <int RPL, int MAXST, int NW>
+__global__ __launch_bounds__(NW * 64) void lmhead_coop_bf16(
+    const uint16_t* __restrict__ hidden, const uint16_t* __restrict__ W, float* __restrict__ logits,
+    int M, int V, int H, int n_tiles) {
+    using S = Coop<RPL, MAXST, NW>;
+    extern __shared__ __align__(16) unsigned char smem[];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    u32x4* buf = reinterpret_cast<u32x4*>(smem) + wave * S::kBufChunks;
+    f32x4* red = reinterpret_cast<f32x4*>(smem + (size_t)NW * S::kBufChunks * 16);   // [2][NW][64]
+
+    const int la = lane / S::kLanesPerRow, lc = lane % S::kLanesPerRow;
+    const int r = lane & 15, g = lane >> 4;
+    const int k_lo = wave * S::kSlice;
+    const int n_st = max(0, min(MAXST, (H - k_lo + S::kKS - 1) / S::kKS));
+    const u32x4 zero = {0u, 0u, 0u, 0u};
+
+    // B operand (hidden rows) for this wave's slice, kept in registers
+    u32x4 hreg[MAXST * S::kSteps];
+#pragma unroll
+    for (int st = 0; st < MAXST; ++st)
+#pragma unroll
+        for (int j = 0; j < S::kSteps; ++j) {
+            const int k = k_lo + st * S::kKS + (j * 4 + g) * 8;
+            hreg[st * S::kSteps + j] =
+                (r < M && k < H) ? *reinterpret_cast<const u32x4*>(hidden + (size_t)r * H + k) : zero;
+        }
+
+    auto issue = [&](int t, int st, u32x4 (&dst)[S::kLoads]) {
+        const int k = k_lo + st * S::kKS + lc * 8;
+        const bool ok = t < n_tiles && st < n_st && k < H;
+        const int v0 = t << 4;
+#pragma unroll
+        for (int q = 0; q < S::kLoads; ++q) {
+            const int row = min(v0 + q * RPL + la, V - 1);
+            dst[q] = ok ? load_stream(W + (size_t)row * H + k) : zero;
+        }
+    };
+
+    // this workgroup's tiles: a contiguous, balanced range [t_begin, t_end)
+    const int t_begin = (int)(((long)n_tiles * blockIdx.x) / gridDim.x);
+    const int t_end = (int)(((long)n_tiles * (blockIdx.x + 1)) / gridDim.x);
+
+    u32x4 pipe[MAXST][S::kLoads];
+#pragma unroll
+    for (int st = 0; st < MAXST; ++st) issue(t_begin < t_end ? t_begin : n_tiles, st, pipe[st]);
+
+    const bool vec_ok = (V & 3) == 0;
+    for (int t = t_begin, it = 0; t < t_end; ++t, ++it) {
+        const int tn = t + 1 < t_end ? t + 1 : n_tiles;   // next tile (n_tiles: nothing to load)
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int st = 0; st < MAXST; ++st) {
+            if (st < n_st) {
+#pragma unroll
+                for (int q = 0; q < S::kLoads; ++q) {
+                    const int R = q * RPL + la;
+                    buf[R * S::kCPR + (lc ^ (R % S::kCPR))] = pipe[st][q];
+                }
+                __builtin_amdgcn_wave_barrier();
+                issue(tn, st, pipe[st]);
+#pragma unroll
+                for (int j = 0; j < S::kSteps; ++j) {
+                    const int c = j * 4 + g;
+                    const u32x4 wv = buf[r * S::kCPR + (c ^ (r % S::kCPR))];
+                    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(wv), as_bf16x8(hreg[st * S::kSteps + j]),
+                                                                  acc, 0, 0, 0);
+                }
+                __builtin_amdgcn_wave_barrier();
+            }
+        }
+        // cross-wave sum of the tile's partial accumulators, in wave order
+        f32x4* rb = red + (it & 1) * NW * 64;
+        rb[wave * 64 + lane] = acc;
+        __syncthreads();
+        if (wave == (it % NW)) {
+            f32x4 s = rb[lane];
+#pragma unroll
+            for (int w = 1; w < NW; ++w) s += rb[w * 64 + lane];
+            if (r < M) store_row4(logits + (size_t)r * V, (t << 4) + 4 * g, V, s, vec_ok);
+        }
+    }
+}
+
+// Fallback for M <= 16 with hidden sizes beyond the cooperative kernel's
+// register-resident slices (chosen by measurement on MI355X).
+constexpr int kSkRPL = 2;
+constexpr int kSkP = 3;
+constexpr int kSkThreads = 512;
+using SkinnyCfg = Skinny<kSkRPL, kSkP, kSkThreads>;
 
 // ------------------------------------------------------------ large M ------
 // Classic LDS-tiled contraction: a workgroup of 4 waves computes a 128 (vocab)
@@ -250,29 +414,61 @@ __global__ __launch_bounds__(kF32Threads) void lmhead_f32(
 
 // ------------------------------------------------------------ launchers ----
 
-size_t skinny_lds_bytes(int M, int H) { return (size_t)M * (H + 8) * 2; }
+bool skinny_fits(int M, int H) { return M <= 16 && SkinnyCfg::lds_bytes(M, H) <= 160 * 1024; }
 
-bool skinny_fits(int M, int H) { return M <= 16 && skinny_lds_bytes(M, H) <= 64 * 1024; }
+template <int RPL, int P, int THREADS>
+hipError_t launch_skinny(const uint16_t* hidden, const uint16_t* W, float* logits, int M, int V, int H, int num_cus,
+                         hipStream_t stream) {
+    using S = Skinny<RPL, P, THREADS>;
+    auto kern = lmhead_skinny_bf16<RPL, P, THREADS>;
+    const int n_tiles = (V + 15) / 16;
+    const size_t lds = S::lds_bytes(M, H);
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+    int occ = 0;
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, kern, THREADS, lds);
+    if (e != hipSuccess) return e;
+    if (occ < 1) occ = 1;
+    // fewest grid-stride iterations the resident waves allow, then just
+    // enough waves to cover the tiles in that many iterations
+    const long max_waves = (long)num_cus * occ * S::kWaves;
+    const long iters = (n_tiles + max_waves - 1) / max_waves;
+    const long waves = (n_tiles + iters - 1) / iters;
+    const int grid = (int)((waves + S::kWaves - 1) / S::kWaves);
+    hipLaunchKernelGGL(kern, dim3(grid), dim3(THREADS), lds, stream, hidden, W, logits, M, V, H, n_tiles);
+    return hipGetLastError();
+}
+
+template <int RPL, int MAXST, int NW>
+hipError_t launch_coop(const uint16_t* hidden, const uint16_t* W, float* logits, int M, int V, int H, int num_cus,
+                       hipStream_t stream, int blocks_per_cu) {
+    using S = Coop<RPL, MAXST, NW>;
+    auto kern = lmhead_coop_bf16<RPL, MAXST, NW>;
+    const int n_tiles = (V + 15) / 16;
+    const size_t lds = S::lds_bytes();
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+    int occ = 0;
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, kern, S::kThreads, lds);
+    if (e != hipSuccess) return e;
+    occ = max(1, min(occ, blocks_per_cu));
+    const int grid = (int)min((long)n_tiles, (long)num_cus * occ);
+    hipLaunchKernelGGL(kern, dim3(grid), dim3(S::kThreads), lds, stream, hidden, W, logits, M, V, H, n_tiles);
+    return hipGetLastError();
+}
+
+// Small-M configuration of the cooperative kernel (measured best on MI355X
+// for B = 1, K = 5, H = 4096: 2 rows per load, 2 stages, 8 waves).
+using CoopCfg = Coop<2, 2, 8>;
 
 hipError_t launch_lmhead_bf16(const uint16_t* hidden, const uint16_t* W, float* logits, int M, int V, int H,
                               int num_cus, hipStream_t stream, int force_kernel) {
+    if (force_kernel == 0 && CoopCfg::fits(M, H))
+        return launch_coop<2, 2, 8>(hidden, W, logits, M, V, H, num_cus, stream, 1);
     const bool skinny = force_kernel == 1 || (force_kernel == 0 && skinny_fits(M, H));
-    if (skinny) {
-        const int n_tiles = (V + 15) / 16;
-        const size_t lds = skinny_lds_bytes(M, H);
-        int occ = 0;
-        hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, lmhead_skinny_bf16, kSkinnyThreads, lds);
-        if (e != hipSuccess) return e;
-        if (occ < 1) occ = 1;
-        const int wpb = kSkinnyThreads / 64;
-        const long max_waves = (long)num_cus * occ * wpb;
-        const long iters = (n_tiles + max_waves - 1) / max_waves;
-        const long waves = (n_tiles + iters - 1) / iters;
-        const int grid = (int)((waves + wpb - 1) / wpb);
-        hipLaunchKernelGGL(lmhead_skinny_bf16, dim3(grid), dim3(kSkinnyThreads), lds, stream, hidden, W, logits, M,
-                           V, H, n_tiles);
-        return hipGetLastError();
-    }
+    if (skinny) return launch_skinny<kSkRPL, kSkP, kSkThreads>(hidden, W, logits, M, V, H, num_cus, stream);
     const int tiles_n = (V + kTileN - 1) / kTileN;
     const int tiles_m = (M + kTileM - 1) / kTileM;
     const int total = tiles_n * tiles_m;

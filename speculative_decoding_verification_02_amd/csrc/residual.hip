@@ -7,14 +7,12 @@
 // speculative decoding works).  The draw is an inverse CDF:
 //     t = min{v : C_v > u' * Z},  C_v = w_0 + ... + w_v,  Z = C_{V-1}.
 //
-// Two kernels:
-//   residual_chunk_sums  -- one workgroup per (sequence, chunk): the sum of the
-//                           weights over the chunk (fixed-order reduction).
-//   residual_select      -- one workgroup per sequence: a sequential prefix over
-//                           the chunk sums finds the chunk c* holding u'Z, then a
-//                           workgroup scan over c*'s weights finds t.
-// Both evaluate a weight with the same function from the same inputs, so a
-// chunk's elements agree bitwise between the passes; only the order of the
+// One kernel, one workgroup per (sequence, chunk): each sums the weights of
+// its chunk (fixed-order reduction); the workgroup that finishes last for a
+// sequence then runs a sequential prefix over the chunk sums to find the
+// chunk c* holding u'Z, and a workgroup scan over c*'s weights to find t.
+// Both phases evaluate a weight with the same function from the same inputs,
+// so a chunk's elements agree bitwise between them; only the order of the
 // within-chunk sum differs, and the selection falls back to the last (or first)
 // token of positive weight in c* if rounding leaves u'Z outside the scanned
 // range.  A token of zero weight is never drawn.  If the residual has no mass
@@ -91,45 +89,26 @@ __device__ __forceinline__ TermRows term_rows(const float* logits, const float* 
     return r;
 }
 
-__global__ __launch_bounds__(kStatThreads) void residual_chunk_sums(
-    const float* __restrict__ logits, const float* __restrict__ draft_logits, int K, int V, int nc, float c,
-    const AcceptInfo* __restrict__ info, float* __restrict__ chunk_sums) {
-    __shared__ float red[kStatThreads / kWave];
-    const int j = blockIdx.x / nc;
-    const int chunk = blockIdx.x - j * nc;
-    const AcceptInfo a = info[j];
-    if (a.n < 0) {
-        if (threadIdx.x == 0) chunk_sums[blockIdx.x] = 0.f;
-        return;
-    }
-    const TermRows tr = term_rows(logits, draft_logits, a, K, V);
-    float w[kStatPerThread];
-    chunk_weights(tr.zt, tr.zd, chunk * kChunk, V, (V & 3) == 0, threadIdx.x, a, c, tr.bonus, w);
-    float s = 0.f;
-#pragma unroll
-    for (int k = 0; k < kStatPerThread; ++k) s += w[k];
-    s = block_sum(s, red);
-    if (threadIdx.x == 0) chunk_sums[blockIdx.x] = s;
-}
-
-__global__ __launch_bounds__(kStatThreads) void residual_select(
-    const float* __restrict__ logits, const float* __restrict__ draft_logits, int K, int V, int nc, float c,
-    const AcceptInfo* __restrict__ info, const float* __restrict__ chunk_sums, int32_t* __restrict__ out_tokens) {
+// Inverse-CDF selection of the terminal token of one sequence, by the block
+// that finished last among the sequence's chunk blocks.  chunk_sums holds the
+// per-chunk weight sums written by all of them (read past the L1 cache).
+__device__ void select_terminal(const float* __restrict__ logits, const float* __restrict__ draft_logits, int K,
+                                int V, int nc, float c, const AcceptInfo& a, const float* chunk_sums,
+                                int32_t* __restrict__ out_tokens) {
     __shared__ float pre[kMaxChunks + 1];   // prefix over chunk sums
     __shared__ float wl[kChunk];            // weights of the selected chunk, token order
     __shared__ float red[kStatThreads / kWave];
     __shared__ float wtot[kStatThreads / kWave];
     __shared__ int sel[2];                  // selected chunk, selected token
+    __shared__ int redi[kStatThreads / kWave];
 
-    const int j = blockIdx.x;
-    const AcceptInfo a = info[j];
-    if (a.n < 0) return;
     const TermRows tr = term_rows(logits, draft_logits, a, K, V);
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const bool vec = (V & 3) == 0;
 
     bool use_q = tr.bonus;
-    for (int k = tid; k < nc; k += kStatThreads) pre[k + 1] = chunk_sums[(size_t)j * nc + k];
+    for (int k = tid; k < nc; k += kStatThreads)
+        pre[k + 1] = __hip_atomic_load(chunk_sums + k, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     __syncthreads();
     if (tid == 0) {
         pre[0] = 0.f;
@@ -155,7 +134,6 @@ __global__ __launch_bounds__(kStatThreads) void residual_select(
         }
         __syncthreads();
     }
-
     const float Z = pre[nc];
     const float x = a.u_term * Z;
     if (tid == 0) {
@@ -234,7 +212,6 @@ __global__ __launch_bounds__(kStatThreads) void residual_select(
             const int y = __shfl_xor(cand, o, kWave);
             cand = low ? min(cand, y) : max(cand, y);
         }
-        __shared__ int redi[kStatThreads / kWave];
         if (lane == 0) redi[wave] = cand;
         __syncthreads();
         if (tid == 0) {
@@ -247,17 +224,44 @@ __global__ __launch_bounds__(kStatThreads) void residual_select(
     if (tid == 0) out_tokens[(size_t)a.b * (K + 1) + a.n] = sel[1];
 }
 
+// One workgroup per (sampled sequence, chunk): the sum of the terminal weights
+// over the chunk; the last workgroup of a sequence to finish (counted with an
+// atomic; the accept kernel zeroed the counter) then selects the token.
+__global__ __launch_bounds__(kStatThreads) void residual_kernel(
+    const float* __restrict__ logits, const float* __restrict__ draft_logits, int K, int V, int nc, float c,
+    const AcceptInfo* __restrict__ info, float* __restrict__ chunk_sums, int* __restrict__ counters,
+    int32_t* __restrict__ out_tokens) {
+    __shared__ float red[kStatThreads / kWave];
+    __shared__ int last;
+    const int j = blockIdx.x / nc;
+    const int chunk = blockIdx.x - j * nc;
+    const AcceptInfo a = info[j];
+    if (a.n < 0) return;
+    const TermRows tr = term_rows(logits, draft_logits, a, K, V);
+    float w[kStatPerThread];
+    chunk_weights(tr.zt, tr.zd, chunk * kChunk, V, (V & 3) == 0, threadIdx.x, a, c, tr.bonus, w);
+    float s = 0.f;
+#pragma unroll
+    for (int k = 0; k < kStatPerThread; ++k) s += w[k];
+    s = block_sum(s, red);
+    if (threadIdx.x == 0) {
+        chunk_sums[blockIdx.x] = s;
+        __threadfence();
+        last = atomicAdd(counters + j, 1) == nc - 1;
+    }
+    __syncthreads();
+    if (!last) return;
+    __threadfence();
+    select_terminal(logits, draft_logits, K, V, nc, c, a, chunk_sums + (size_t)j * nc, out_tokens);
+}
+
 hipError_t launch_residual(const float* logits, const float* draft_logits, int n_rows, int K, int V,
-                           float inv_t_log2e, const AcceptInfo* info, float* chunk_sums, int32_t* out_tokens,
-                           hipStream_t stream) {
+                           float inv_t_log2e, const AcceptInfo* info, float* chunk_sums, int* counters,
+                           int32_t* out_tokens, hipStream_t stream) {
     if (n_rows == 0) return hipSuccess;
     const int nc = n_chunks(V);
-    hipLaunchKernelGGL(residual_chunk_sums, dim3((unsigned)((long)n_rows * nc)), dim3(kStatThreads), 0, stream,
-                       logits, draft_logits, K, V, nc, inv_t_log2e, info, chunk_sums);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(residual_select, dim3(n_rows), dim3(kStatThreads), 0, stream, logits, draft_logits, K, V, nc,
-                       inv_t_log2e, info, chunk_sums, out_tokens);
+    hipLaunchKernelGGL(residual_kernel, dim3((unsigned)((long)n_rows * nc)), dim3(kStatThreads), 0, stream, logits,
+                       draft_logits, K, V, nc, inv_t_log2e, info, chunk_sums, counters, out_tokens);
     return hipGetLastError();
 }
 

@@ -62,22 +62,26 @@ struct Workspace {
     sv::StatRec* stats;
     sv::AcceptInfo* info;
     float* sums;
+    int* counters;
 };
 
 // Layout for up to B selected rows: chunk statistics of B*(K+1) target rows and
-// B*K draft rows, one AcceptInfo per row, and the residual chunk sums.
+// B*K draft rows, one AcceptInfo per row, the residual chunk sums, and one
+// completion counter per row (zeroed by the accept kernel before use).
 size_t workspace_layout(int B, int K, int V, void* base, Workspace* ws) {
     const size_t nc = (size_t)sv::n_chunks(V);
     const size_t stats = align256(((size_t)B * (K + 1) + (size_t)B * K) * nc * sizeof(sv::StatRec));
     const size_t info = align256((size_t)B * sizeof(sv::AcceptInfo));
     const size_t sums = align256((size_t)B * nc * sizeof(float));
+    const size_t counters = align256((size_t)B * sizeof(int));
     if (ws) {
         char* p = static_cast<char*>(base);
         ws->stats = reinterpret_cast<sv::StatRec*>(p);
         ws->info = reinterpret_cast<sv::AcceptInfo*>(p + stats);
         ws->sums = reinterpret_cast<float*>(p + stats + info);
+        ws->counters = reinterpret_cast<int*>(p + stats + info + sums);
     }
-    return stats + info + sums;
+    return stats + info + sums + counters;
 }
 
 spec_status_t check_accept_common(const float* logits, const int32_t* draft_tokens, const int32_t* rows,
@@ -134,7 +138,7 @@ spec_status_t spec_accept_greedy(const float* logits, const int32_t* draft_token
     hipError_t e = sv::launch_softmax_stats(logits, nullptr, rows, nr, B, K, V, sv::kLog2e, false, ws.stats, s);
     if (e == hipSuccess)
         e = sv::launch_accept(logits, nullptr, draft_tokens, nullptr, rows, nr, B, K, V, sv::kLog2e, false, ws.stats,
-                              accepted_len, out_tokens, nullptr, ws.info, s);
+                              accepted_len, out_tokens, nullptr, ws.info, ws.counters, s);
     return e == hipSuccess ? SPEC_OK : hip_fail(e);
 }
 
@@ -159,8 +163,9 @@ spec_status_t spec_accept_sample(const float* logits, const float* draft_logits,
     hipError_t e = sv::launch_softmax_stats(logits, dl, rows, nr, B, K, V, c, true, ws.stats, s);
     if (e == hipSuccess)
         e = sv::launch_accept(logits, dl, draft_tokens, seeds, rows, nr, B, K, V, c, true, ws.stats, accepted_len,
-                              out_tokens, probs_at_draft, ws.info, s);
-    if (e == hipSuccess) e = sv::launch_residual(logits, dl, nr, K, V, c, ws.info, ws.sums, out_tokens, s);
+                              out_tokens, probs_at_draft, ws.info, ws.counters, s);
+    if (e == hipSuccess)
+        e = sv::launch_residual(logits, dl, nr, K, V, c, ws.info, ws.sums, ws.counters, out_tokens, s);
     return e == hipSuccess ? SPEC_OK : hip_fail(e);
 }
 

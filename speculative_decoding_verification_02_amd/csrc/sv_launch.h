@@ -23,16 +23,18 @@ hipError_t launch_softmax_stats(const float* logits, const float* draft_logits, 
                                 int B, int K, int V, float inv_t_log2e, bool need_sum, StatRec* stats,
                                 hipStream_t stream);
 
-// Greedy or sampled acceptance: one wavefront per selected sequence.
+// Greedy or sampled acceptance: one workgroup per selected sequence.  The
+// sampled variant also zeroes the sequence's residual counter.
 hipError_t launch_accept(const float* logits, const float* draft_logits, const int32_t* draft_tokens,
                          const uint64_t* seeds, const int32_t* rows, int n_rows, int B, int K, int V,
                          float inv_t_log2e, bool sampled, const StatRec* stats, int32_t* accepted_len,
-                         int32_t* out_tokens, float* probs_at_draft, AcceptInfo* info, hipStream_t stream);
+                         int32_t* out_tokens, float* probs_at_draft, AcceptInfo* info, int* counters,
+                         hipStream_t stream);
 
-// Residual / bonus draw of the sampled sequences: per-chunk weight sums, then
-// the inverse-CDF selection of the terminal token.
+// Residual / bonus draw of the sampled sequences: per-chunk weight sums, and
+// the inverse-CDF selection of the terminal token by the last chunk block.
 hipError_t launch_residual(const float* logits, const float* draft_logits, int n_rows, int K, int V,
-                           float inv_t_log2e, const AcceptInfo* info, float* chunk_sums, int32_t* out_tokens,
-                           hipStream_t stream);
+                           float inv_t_log2e, const AcceptInfo* info, float* chunk_sums, int* counters,
+                           int32_t* out_tokens, hipStream_t stream);
 
 }  // namespace sv

@@ -47,6 +47,14 @@ def test_bf16_small_m(B, K, H, V):
     _check(h, W)
 
 
+@pytest.mark.parametrize("B,K,H,V", [(1, 0, 8192, 3001), (2, 1, 6144, 4099), (1, 3, 4104, 130)])
+def test_bf16_small_m_wide_hidden(B, K, H, V):
+    """M <= 16 with a hidden size beyond the register-resident slices of the
+    cooperative kernel: the LDS-staged streaming kernel."""
+    W, h = _case(B, K, H, V, "bf16", 0.02, seed=H + V)
+    _check(h, W)
+
+
 @pytest.mark.parametrize("B,K", [(6, 2), (130, 0), (64, 4), (3, 63)])
 @pytest.mark.parametrize("H,V", [(64, 1000), (520, 2053), (1032, 257)])
 def test_bf16_tiled(B, K, H, V):
