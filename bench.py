@@ -43,27 +43,107 @@ def parse():
     ap.add_argument("--workload", default="b1_k5_h4096_v128256")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle sample")
+    ap.add_argument("--copy-calibration-mib", type=int, default=0,
+                    help="before the run, copy a buffer of this many MiB 3 times (untimed), so a counter "
+                         "profile of this command holds a plain copy kernel of known size")
+    ap.add_argument("--traffic-kernel", default="lmhead_coop_bf16", help="LM-head kernel the counters cover")
+    ap.add_argument("--ingest-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="turn two rocprofv3 --pmc counter_collection.csv files (FETCH_SIZE, then WRITE_SIZE, of a "
+                         "run with --copy-calibration-mib) into profiles/lmhead_traffic_<workload>.json and exit")
     return ap.parse_args()
 
 
-def gemm_source_sha() -> str:
-    return hashlib.sha256(open(GEMM_SRC, "rb").read()).hexdigest()[:16]
+# Source section of each LM-head kernel in lmhead_gemm.hip (text from its
+# banner comment to the next one), so that stored counter readings stay tied
+# to the kernel they were taken on.
+_SECTIONS = {"lmhead_coop_bf16": "small M, cooperative", "lmhead_big_bf16": "big M",
+             "lmhead_tiled_bf16": "large M", "lmhead_f32": "fp32"}
 
 
-def load_traffic(workload: str):
+def kernel_source_sha(kernel: str) -> str:
+    """sha256 of the kernel's source section plus the launcher section that
+    picks its configuration."""
+    lines = open(GEMM_SRC).read().splitlines(keepends=True)
+    banners = [i for i, ln in enumerate(lines) if ln.startswith("// ---")]
+
+    def section(label):
+        i = next(i for i in banners if lines[i].strip("/ -\n") == label)
+        j = next((k for k in banners if k > i), len(lines))
+        return "".join(lines[i:j])
+
+    return hashlib.sha256((section(_SECTIONS[kernel]) + section("launchers")).encode()).hexdigest()[:16]
+
+
+def load_traffic(workload: str, kernel: str):
     """HBM bytes per launch of the LM-head kernel from the committed counter
     summary, or None if absent or taken on a different kernel source."""
     path = os.path.join(ROOT, "profiles", "lmhead_traffic_%s.json" % workload)
     if not os.path.exists(path):
         return None
     rec = json.load(open(path))
-    if rec.get("source_sha") != gemm_source_sha():
+    if rec.get("kernel") != kernel or rec.get("source_sha") != kernel_source_sha(kernel):
         return None
     return rec.get("hbm_bytes_per_launch")
 
 
+def _counter_rows(path, counter):
+    import csv
+    out = []
+    for r in csv.DictReader(open(path)):
+        if r.get("Counter_Name") == counter:
+            out.append((r["Kernel_Name"], float(r["Counter_Value"])))
+    return out
+
+
+def ingest_traffic(args):
+    """HBM bytes per launch of the LM-head kernel from FETCH_SIZE / WRITE_SIZE
+    (KiB per dispatch), each scaled so that the calibration copy of known size
+    reads and writes exactly its size."""
+    fetch = _counter_rows(args.ingest_traffic[0], "FETCH_SIZE")
+    write = _counter_rows(args.ingest_traffic[1], "WRITE_SIZE")
+    size = args.copy_calibration_mib * (1 << 20)
+    if size <= 0:
+        sys.exit("--ingest-traffic needs --copy-calibration-mib of the profiled run")
+
+    def median_of(rows, pred):
+        vals = sorted(v for n, v in rows if pred(n))
+        if not vals:
+            sys.exit("no matching dispatch in the counter file")
+        return vals[len(vals) // 2]
+
+    # the calibration copy is a contiguous same-type copy: the runtime's blit
+    # kernel; take its largest dispatches (the calibration is the biggest copy)
+    is_copy = lambda n: "copyBuffer" in n
+    is_gemm = lambda n: "sv::lmhead" in n
+
+    def calib(rows):
+        vals = sorted((v for n, v in rows if is_copy(n)), reverse=True)[:3]
+        if not vals:
+            sys.exit("no calibration copy in the counter file")
+        return vals[len(vals) // 2]
+
+    f_copy = calib(fetch)
+    w_copy = calib(write)
+    f_scale = size / (f_copy * 1024.0)
+    w_scale = size / (w_copy * 1024.0)
+    f_gemm = median_of(fetch, is_gemm) * 1024.0 * f_scale
+    w_gemm = median_of(write, is_gemm) * 1024.0 * w_scale
+    kernel = args.traffic_kernel
+    rec = {"workload": args.workload, "kernel": kernel, "source_sha": kernel_source_sha(kernel),
+           "fetch_bytes_per_launch": f_gemm, "write_bytes_per_launch": w_gemm,
+           "hbm_bytes_per_launch": f_gemm + w_gemm, "fetch_scale": f_scale, "write_scale": w_scale,
+           "calibration": "torch copy of %d MiB: FETCH_SIZE %.0f KiB, WRITE_SIZE %.0f KiB"
+                          % (args.copy_calibration_mib, f_copy, w_copy)}
+    path = os.path.join(ROOT, "profiles", "lmhead_traffic_%s.json" % args.workload)
+    json.dump(rec, open(path, "w"), indent=1)
+    print(json.dumps(rec))
+
+
 def main():
     args = parse()
+    if args.ingest_traffic:
+        ingest_traffic(args)
+        return
     if args.gpus != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path (run with --gpus 1)", file=sys.stderr)
         sys.exit(2)
@@ -113,6 +193,14 @@ def main():
             sv.spec_accept_greedy(logits, d, acc, out, ws, rows=greedy_rows, stream=stream)
             sv.spec_accept_sample(logits, zd, d, T, seeds[r], acc, out, ws, rows=sampled_rows, stream=stream)
 
+    if args.copy_calibration_mib:
+        src = torch.empty(args.copy_calibration_mib << 20, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
     print("bench: warmup %d" % args.warmup, file=sys.stderr, flush=True)
     for r in range(args.warmup):
         step(r)
@@ -153,9 +241,15 @@ def main():
         roof = {"bound": "mfma", "achieved": gemm_flops / t_gemm / 1e12, "peak": MFMA_BF16_PEAK_TFLOPS,
                 "unit": "TFLOP/s"}
     roof["frac"] = roof["achieved"] / roof["peak"]
-    roof["traffic"] = load_traffic(wl.name)
-    roof["kernel"] = ("lmhead_coop_bf16" if (wl.dtype == "bf16" and M <= 16 and H <= 4096)
-                      else "lmhead_tiled_bf16" if wl.dtype == "bf16" else "lmhead_f32")
+    if wl.dtype != "bf16":
+        roof["kernel"] = "lmhead_f32"
+    elif M <= 16 and H <= 4096:
+        roof["kernel"] = "lmhead_coop_bf16"
+    elif M >= 512 and H % 64 == 0:
+        roof["kernel"] = "lmhead_big_bf16"
+    else:
+        roof["kernel"] = "lmhead_tiled_bf16"
+    roof["traffic"] = load_traffic(wl.name, roof["kernel"])
     roof["algorithmic_bytes"] = gemm_bytes
     roof["algorithmic_flops"] = gemm_flops
     roof["avg_kernel_us"] = gemm_ms * 1e3

@@ -78,6 +78,21 @@ __global__ __launch_bounds__(kAcceptThreads) void accept_kernel(
         return;
     }
 
+    // wavefront 0, lane i: the draft token and (sampled) its two logits, loaded
+    // up front so the loads overlap the statistics merge
+    const int i = lane;
+    const bool active = wave == 0 && i <= K;
+    const bool has_draft = wave == 0 && i < K;
+    int tok = 0;
+    float zt_tok = 0.f, zd_tok = 0.f;
+    if (has_draft) {
+        tok = draft_tokens[(size_t)b * K + i];
+        if (SAMPLED && tok >= 0 && tok < V) {
+            zt_tok = logits[((size_t)b * (K + 1) + i) * V + tok];
+            zd_tok = draft_logits[((size_t)b * K + i) * V + tok];
+        }
+    }
+
     // rows of this sequence: target 0..K, then (sampled) draft 0..K-1
     const int n_rows_seq = (K + 1) + (SAMPLED ? K : 0);
     const int rows_per_pass = max(1, min(n_rows_seq, kRecBuf / nc));
@@ -99,18 +114,13 @@ __global__ __launch_bounds__(kAcceptThreads) void accept_kernel(
     }
     if (wave != 0) return;
 
-    const int i = lane;
-    const bool active = i <= K;
-    const bool has_draft = i < K;
     Merged t{-INFINITY, 0.f, INT_MAX, 0}, d{-INFINITY, 0.f, INT_MAX, 0};
-    int tok = 0;
     int bad = 0;
     if (active) {
         t = merged[i];
         bad = t.bad | (t.m == -INFINITY);
     }
     if (has_draft) {
-        tok = draft_tokens[(size_t)b * K + i];
         bad |= (tok < 0 || tok >= V);
         if (SAMPLED) {
             d = merged[K + 1 + i];
@@ -136,8 +146,7 @@ __global__ __launch_bounds__(kAcceptThreads) void accept_kernel(
                                           (uint32_t)(seed >> 32));
             u_term = uniform24(w.y);
             if (has_draft) {
-                const float zt = logits[((size_t)b * (K + 1) + i) * V + tok];
-                const float zd = draft_logits[((size_t)b * K + i) * V + tok];
+                const float zt = zt_tok, zd = zd_tok;
                 const float lq = (zt - t.m) * c;
                 const float lp = (zd - d.m) * c;
                 float r;

@@ -383,6 +383,210 @@ __global__ __launch_bounds__(kTiledThreads) void lmhead_tiled_bf16(
     }
 }
 
+// ------------------------------------------------------------- big M -----
+// Dense contraction for M in the thousands (MFMA-bound).  A workgroup of 4
+// waves owns a 256 (vocab) x 256 (hidden rows) tile; each wave a 128 x 128
+// quarter as 4 x 4 blocks of v_mfma_f32_32x32x16_bf16 (256 fp32 accumulators
+// per lane, one wave per SIMD).  On MI355X the 32x32x16 form issues at about
+// twice the rate of 16x16x32 (measured ~2.0 vs ~0.8 PFLOP/s at one wave per
+// SIMD), so the dense path uses it.  Operand layout: lane l holds
+// A[l % 32][8*(l/32) .. +8) (W rows) and B[8*(l/32) .. +8)[l % 32] (hidden
+// rows) and receives D[8*(i/4) + 4*(l/32) + i%4][l % 32], i < 16: four runs of
+// four consecutive vocabulary entries of one hidden row.
+//
+// Operands reach LDS by direct global->LDS loads (global_load_lds_dwordx4,
+// no register staging) into a ring of kBigSlots k-slices of 32 columns (32 KB
+// each: 256 W rows + 256 hidden rows, 64 bytes per row).  Loads run
+// kBigSlots-1 slices ahead of the multiply, so their latency under full load
+// (~2.5 us measured) hides behind several slices of MFMA work.  A DMA
+// instruction writes 1 KB of LDS in lane order; each lane picks the global
+// chunk that belongs at its LDS position, so the slice lands swizzled: chunk c
+// of row r at r*4 + (c ^ ((r >> 2) & 3)), which spreads any 16 consecutive
+// rows read at one chunk over the 16 bank groups.  Synchronisation is
+// explicit: a wait on the wave's own outstanding loads (vmcnt), then one
+// barrier per slice.  Tiles are ordered XCD-aware like the tiled kernel.
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+constexpr int kBigBN = 256;
+constexpr int kBigBM = 256;
+constexpr int kBigThreads = 256;
+
+// Geometry of one k-slice of BK columns: 256 W rows then 256 hidden rows,
+// CPR 16-byte chunks per row; a DMA instruction fills RPI rows (1 KB).
+template <int BK, int SLOTS>
+struct Big {
+    static constexpr int kCPR = BK / 8;
+    static constexpr int kRPI = 64 / kCPR;
+    static constexpr int kSliceChunks = 2 * 256 * kCPR;
+    static constexpr int kLoads = kSliceChunks / 64 / (kBigThreads / 64);   // DMA per lane per slice
+    static constexpr int kSteps = BK / 16;                                  // MFMA k-steps per slice
+    static constexpr size_t kLds = (size_t)SLOTS * kSliceChunks * 16;
+    // chunk c of row r sits at r*CPR + (c ^ f(r)), f(r) = (r / (16/CPR)) % CPR:
+    // 16 consecutive rows read at one chunk fall in 16 distinct bank groups
+    static __device__ __forceinline__ int pos(int row, int chunk) {
+        return row * kCPR + (chunk ^ ((row / (16 / kCPR)) % kCPR));
+    }
+};
+
+// s_waitcnt vmcnt(n) leaving the other counters alone (gfx9 encoding).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
+// wait until at most `after` slices' loads (of L each) are outstanding
+template <int L, int MAXAFTER>
+__device__ __forceinline__ void wait_slices(int after) {
+    if constexpr (MAXAFTER >= 3) {
+        if (after >= 3) { wait_vmcnt<3 * L>(); return; }
+    }
+    if constexpr (MAXAFTER >= 2) {
+        if (after >= 2) { wait_vmcnt<2 * L>(); return; }
+    }
+    if constexpr (MAXAFTER >= 1) {
+        if (after >= 1) { wait_vmcnt<L>(); return; }
+    }
+    wait_vmcnt<0>();
+}
+
+template <int BK, int SLOTS>
+__global__ __launch_bounds__(kBigThreads, 1) void lmhead_big_bf16(
+    const uint16_t* __restrict__ hidden, const uint16_t* __restrict__ W, float* __restrict__ logits,
+    int M, int V, int H, int tiles_n, int tiles_m) {
+    using G = Big<BK, SLOTS>;
+    extern __shared__ __align__(16) unsigned char smem[];
+    u32x4* lds = reinterpret_cast<u32x4*>(smem);   // [slot][W rows 0..255 | hidden rows 0..255][CPR chunks]
+
+    const int total = tiles_n * tiles_m;
+    const int per_xcd = (total + 7) / 8;
+    const int seq = (blockIdx.x % 8) * per_xcd + blockIdx.x / 8;
+    if (seq >= total) return;
+    const int tn = seq / tiles_m, tm = seq - tn * tiles_m;
+    const int v0 = tn * kBigBN, m0 = tm * kBigBM;
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, wave = tid >> 6;
+    const int r = lane & 31, h = lane >> 5;
+    const int wn = (wave & 1) * 128, wm = (wave >> 1) * 128;
+
+    // DMA source of each of this lane's loads: instruction q of this wave fills
+    // 1 KB block bi = wave * kLoads + q of the slice (RPI rows; the first half
+    // of the blocks hold W rows, the second half hidden rows); the lane's
+    // position in the block fixes its row and, through the swizzle, its chunk.
+    constexpr int kHalf = 256 / G::kRPI;
+    const uint16_t* src[G::kLoads];
+#pragma unroll
+    for (int q = 0; q < G::kLoads; ++q) {
+        const int bi = wave * G::kLoads + q;
+        const int row = (bi % kHalf) * G::kRPI + lane / G::kCPR;
+        const int chunk = (lane % G::kCPR) ^ ((row / (16 / G::kCPR)) % G::kCPR);
+        if (bi < kHalf) {
+            const int vr = min(v0 + row, V - 1);          // rows past V: read a valid row, outputs dropped
+            src[q] = W + (size_t)vr * H + chunk * 8;
+        } else {
+            const int mr = min(m0 + row, M - 1);
+            src[q] = hidden + (size_t)mr * H + chunk * 8;
+        }
+    }
+    auto issue = [&](int kt) {
+        u32x4* slot = lds + (kt % SLOTS) * G::kSliceChunks;
+#pragma unroll
+        for (int q = 0; q < G::kLoads; ++q)
+            __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(src[q] + (size_t)kt * BK),
+                                             (__attribute__((address_space(3))) void*)(slot + (wave * G::kLoads + q) * 64),
+                                             16, 0, 0);
+    };
+
+    f32x16 acc[4][4];
+#pragma unroll
+    for (int a = 0; a < 4; ++a)
+#pragma unroll
+        for (int b = 0; b < 4; ++b)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) acc[a][b][e] = 0.f;
+
+    const int nk = H / BK;
+#pragma unroll
+    for (int p = 0; p < SLOTS - 1; ++p)
+        if (p < nk) issue(p);
+
+    for (int kt = 0; kt < nk; ++kt) {
+        // this lane's loads of slice kt have landed once at most the slices
+        // issued after it are outstanding
+        wait_slices<G::kLoads, SLOTS - 2>(min(SLOTS - 2, nk - 1 - kt));
+        // everyone's slice kt has landed and everyone has finished reading
+        // slice kt-1, whose slot the next loads reuse
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
+        if (kt + SLOTS - 1 < nk) issue(kt + SLOTS - 1);
+
+        const u32x4* lw = lds + (kt % SLOTS) * G::kSliceChunks;
+        const u32x4* lh = lw + 256 * G::kCPR;
+#pragma unroll
+        for (int ks = 0; ks < G::kSteps; ++ks) {
+            const int ch = ks * 2 + h;
+            bf16x8 fa[4], fb[4];
+#pragma unroll
+            for (int a = 0; a < 4; ++a) fa[a] = as_bf16x8(lw[G::pos(wn + a * 32 + r, ch)]);
+#pragma unroll
+            for (int b = 0; b < 4; ++b) fb[b] = as_bf16x8(lh[G::pos(wm + b * 32 + r, ch)]);
+#pragma unroll
+            for (int a = 0; a < 4; ++a)
+#pragma unroll
+                for (int b = 0; b < 4; ++b)
+                    acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[a], fb[b], acc[a][b], 0, 0, 0);
+        }
+        // the slot is refilled only after the next barrier; make sure this
+        // wave's reads of it have completed before arriving there
+        __builtin_amdgcn_s_waitcnt((0xF) | (0x3 << 14) | (0x7 << 4) | (0x0 << 8));   // lgkmcnt(0)
+    }
+
+    const bool vec_ok = (V & 3) == 0;
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+        const int m = m0 + wm + b * 32 + r;
+        if (m >= M) continue;
+        float* out = logits + (size_t)m * V;
+#pragma unroll
+        for (int a = 0; a < 4; ++a)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const f32x4 v4 = {acc[a][b][4 * q], acc[a][b][4 * q + 1], acc[a][b][4 * q + 2], acc[a][b][4 * q + 3]};
+                store_row4(out, v0 + wn + a * 32 + 8 * q + 4 * h, V, v4, vec_ok);
+            }
+    }
+}
+
+// Configuration the library launches (measured best on MI355X at the
+// 256x8x8192 and 512x4x5120 verify shapes: whole 128-byte rows per slice).
+constexpr int kBigBK = 64;
+constexpr int kBigSlots = 2;
+constexpr int kBigMinM = 512;   // below this the LDS-tiled kernel wastes less of its tile
+
+bool big_fits(int M, int H) { return M >= kBigMinM && H % kBigBK == 0; }
+
+template <int BK, int SLOTS>
+hipError_t launch_big_cfg(const uint16_t* hidden, const uint16_t* W, float* logits, int M, int V, int H,
+                          hipStream_t stream) {
+    auto kern = lmhead_big_bf16<BK, SLOTS>;
+    const size_t lds = Big<BK, SLOTS>::kLds;
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+    const int tiles_n = (V + kBigBN - 1) / kBigBN;
+    const int tiles_m = (M + kBigBM - 1) / kBigBM;
+    const int grid = ((tiles_n * tiles_m + 7) / 8) * 8;
+    hipLaunchKernelGGL(kern, dim3(grid), dim3(kBigThreads), lds, stream, hidden, W, logits, M, V, H, tiles_n,
+                       tiles_m);
+    return hipGetLastError();
+}
+
+hipError_t launch_big(const uint16_t* hidden, const uint16_t* W, float* logits, int M, int V, int H,
+                      hipStream_t stream) {
+    return launch_big_cfg<kBigBK, kBigSlots>(hidden, W, logits, M, V, H, stream);
+}
+
 // ------------------------------------------------------------------ fp32 ---
 // Plain fp32 FMA contraction for fp32 weights (small workloads): one wave per
 // vocabulary row, lanes split the hidden dimension in float4 steps, a wave
@@ -467,6 +671,7 @@ hipError_t launch_lmhead_bf16(const uint16_t* hidden, const uint16_t* W, float* 
                               int num_cus, hipStream_t stream, int force_kernel) {
     if (force_kernel == 0 && CoopCfg::fits(M, H))
         return launch_coop<2, 2, 8>(hidden, W, logits, M, V, H, num_cus, stream, 1);
+    if (force_kernel == 0 && big_fits(M, H)) return launch_big(hidden, W, logits, M, V, H, stream);
     const bool skinny = force_kernel == 1 || (force_kernel == 0 && skinny_fits(M, H));
     if (skinny) return launch_skinny<kSkRPL, kSkP, kSkThreads>(hidden, W, logits, M, V, H, num_cus, stream);
     const int tiles_n = (V + kTileN - 1) / kTileN;

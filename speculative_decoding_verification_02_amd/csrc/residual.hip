@@ -89,9 +89,33 @@ __device__ __forceinline__ TermRows term_rows(const float* logits, const float* 
     return r;
 }
 
+// pre[0] = 0, pre[k+1] = chunk_sums[0] + ... + chunk_sums[k] for k < nc, by
+// one wavefront: 64 chunks at a time, a shuffle scan plus the running carry.
+// (src may alias pre + 1: each element is read before it is overwritten.)
+__device__ __forceinline__ void chunk_prefix(const float* src, int nc, int lane, float* pre, bool from_global) {
+    float carry = 0.f;
+    for (int base = 0; base < nc; base += kWave) {
+        const int k = base + lane;
+        float v = 0.f;
+        if (k < nc)
+            v = from_global ? __hip_atomic_fetch_add(const_cast<float*>(src) + k, 0.f, __ATOMIC_RELAXED,
+                                                     __HIP_MEMORY_SCOPE_AGENT)
+                            : src[k];
+#pragma unroll
+        for (int o = 1; o < kWave; o <<= 1) {
+            const float y = __shfl_up(v, o, kWave);
+            if (lane >= o) v += y;
+        }
+        v += carry;
+        if (k < nc) pre[k + 1] = v;
+        carry = __shfl(v, kWave - 1, kWave);
+    }
+    if (lane == 0) pre[0] = 0.f;
+}
+
 // Inverse-CDF selection of the terminal token of one sequence, by the block
 // that finished last among the sequence's chunk blocks.  chunk_sums holds the
-// per-chunk weight sums written by all of them (read past the L1 cache).
+// per-chunk weight sums published by all of them (read back with atomics).
 __device__ void select_terminal(const float* __restrict__ logits, const float* __restrict__ draft_logits, int K,
                                 int V, int nc, float c, const AcceptInfo& a, const float* chunk_sums,
                                 int32_t* __restrict__ out_tokens) {
@@ -107,13 +131,7 @@ __device__ void select_terminal(const float* __restrict__ logits, const float* _
     const bool vec = (V & 3) == 0;
 
     bool use_q = tr.bonus;
-    for (int k = tid; k < nc; k += kStatThreads)
-        pre[k + 1] = __hip_atomic_load(chunk_sums + k, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    __syncthreads();
-    if (tid == 0) {
-        pre[0] = 0.f;
-        for (int k = 0; k < nc; ++k) pre[k + 1] = pre[k] + pre[k + 1];
-    }
+    if (wave == 0) chunk_prefix(chunk_sums, nc, lane, pre, true);
     __syncthreads();
     if (!(pre[nc] > 0.f) && !use_q) {
         // residual without mass: draw from q_n, recomputing the chunk sums
@@ -128,22 +146,27 @@ __device__ void select_terminal(const float* __restrict__ logits, const float* _
             if (tid == 0) pre[k + 1] = s;
         }
         __syncthreads();
-        if (tid == 0) {
-            pre[0] = 0.f;
-            for (int k = 0; k < nc; ++k) pre[k + 1] = pre[k] + pre[k + 1];
-        }
+        if (wave == 0) chunk_prefix(pre + 1, nc, lane, pre, false);
         __syncthreads();
     }
     const float Z = pre[nc];
     const float x = a.u_term * Z;
-    if (tid == 0) {
+    if (wave == 0) {
+        // c* = first chunk whose inclusive prefix exceeds x; if rounding leaves
+        // none, the last chunk with positive mass
         int cs = -1, last_pos = 0;
-        for (int k = 0; k < nc; ++k) {
-            if (pre[k + 1] > pre[k]) last_pos = k;
-            if (cs < 0 && pre[k + 1] > x) cs = k;
+        for (int base = 0; base < nc && cs < 0; base += kWave) {
+            const int k = base + lane;
+            const bool in = k < nc;
+            const unsigned long long over = __ballot(in && pre[k + 1] > x);
+            const unsigned long long pos = __ballot(in && pre[k + 1] > pre[k]);
+            if (over) cs = base + __ffsll((long long)over) - 1;
+            if (pos) last_pos = base + 63 - __clzll((long long)pos);
         }
-        sel[0] = cs < 0 ? last_pos : cs;
-        sel[1] = -1;
+        if (lane == 0) {
+            sel[0] = cs < 0 ? last_pos : cs;
+            sel[1] = -1;
+        }
     }
     __syncthreads();
     const int cs = sel[0];
@@ -245,13 +268,19 @@ __global__ __launch_bounds__(kStatThreads) void residual_kernel(
     for (int k = 0; k < kStatPerThread; ++k) s += w[k];
     s = block_sum(s, red);
     if (threadIdx.x == 0) {
-        chunk_sums[blockIdx.x] = s;
-        __threadfence();
-        last = atomicAdd(counters + j, 1) == nc - 1;
+        // Publish the chunk sum with a device-scope atomic exchange and wait for
+        // its returned value, so the exchange has been performed, before
+        // counting this block in; the selecting block reads the sums back with
+        // atomic read-modify-writes, which are performed where the exchanges
+        // were.  (A device-scope release fence would publish it too, but by
+        // writing back and invalidating the XCD's whole L2.)
+        const float prev = __hip_atomic_exchange(chunk_sums + blockIdx.x, s, __ATOMIC_RELAXED,
+                                                 __HIP_MEMORY_SCOPE_AGENT);
+        asm volatile("" ::"v"(prev));
+        last = __hip_atomic_fetch_add(counters + j, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == nc - 1;
     }
     __syncthreads();
     if (!last) return;
-    __threadfence();
     select_terminal(logits, draft_logits, K, V, nc, c, a, chunk_sums + (size_t)j * nc, out_tokens);
 }
 

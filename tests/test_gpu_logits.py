@@ -62,7 +62,16 @@ def test_bf16_tiled(B, K, H, V):
     _check(h, W)
 
 
-@pytest.mark.parametrize("B,K,V,dtype", [(1, 5, 3001, "bf16"), (64, 4, 1031, "bf16"), (1, 4, 999, "f32")])
+@pytest.mark.parametrize("B,K,H,V", [(128, 3, 576, 1000), (300, 3, 1024, 2053), (171, 2, 64, 513)])
+def test_bf16_big_m(B, K, H, V):
+    """M >= 512 with H a multiple of 64: the direct-to-LDS 256 x 256 kernel,
+    including tiles cut by the ragged edges of M and V."""
+    W, h = _case(B, K, H, V, "bf16", 0.02, seed=B + K + H + V)
+    _check(h, W)
+
+
+@pytest.mark.parametrize("B,K,V,dtype", [(1, 5, 3001, "bf16"), (64, 4, 1031, "bf16"), (1, 4, 999, "f32"),
+                                         (160, 3, 777, "bf16")])
 def test_small_integers_bit_exact(B, K, V, dtype):
     """Inputs in -4..4 (exact in bf16): every partial sum is an integer below
     2^24, so the fp32 result is exact in any summation order."""
