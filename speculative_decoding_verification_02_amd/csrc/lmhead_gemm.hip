@@ -519,23 +519,40 @@ __global__ __launch_bounds__(kBigThreads, 1) void lmhead_big_bf16(
         // slice kt-1, whose slot the next loads reuse
         __builtin_amdgcn_s_barrier();
         asm volatile("" ::: "memory");
-        if (kt + SLOTS - 1 < nk) issue(kt + SLOTS - 1);
+        const bool refill = kt + SLOTS - 1 < nk;
+        const int kn = kt + SLOTS - 1;
+        u32x4* nslot = lds + (kn % SLOTS) * G::kSliceChunks;
 
         const u32x4* lw = lds + (kt % SLOTS) * G::kSliceChunks;
         const u32x4* lh = lw + 256 * G::kCPR;
+        // fragments of k-step ks+1 are read while the MFMAs of ks run, and
+        // the next slice's loads are issued one per MFMA of the first k-steps,
+        // so the wave never stalls on a full load queue before its MFMAs
+        bf16x8 fa[2][4], fb[2][4];
+        auto frag = [&](int ks, bf16x8 (&xa)[4], bf16x8 (&xb)[4]) {
+            const int ch = ks * 2 + h;
+#pragma unroll
+            for (int a = 0; a < 4; ++a) xa[a] = as_bf16x8(lw[G::pos(wn + a * 32 + r, ch)]);
+#pragma unroll
+            for (int b = 0; b < 4; ++b) xb[b] = as_bf16x8(lh[G::pos(wm + b * 32 + r, ch)]);
+        };
+        frag(0, fa[0], fb[0]);
 #pragma unroll
         for (int ks = 0; ks < G::kSteps; ++ks) {
-            const int ch = ks * 2 + h;
-            bf16x8 fa[4], fb[4];
-#pragma unroll
-            for (int a = 0; a < 4; ++a) fa[a] = as_bf16x8(lw[G::pos(wn + a * 32 + r, ch)]);
-#pragma unroll
-            for (int b = 0; b < 4; ++b) fb[b] = as_bf16x8(lh[G::pos(wm + b * 32 + r, ch)]);
+            if (ks + 1 < G::kSteps) frag(ks + 1, fa[(ks + 1) & 1], fb[(ks + 1) & 1]);
 #pragma unroll
             for (int a = 0; a < 4; ++a)
 #pragma unroll
-                for (int b = 0; b < 4; ++b)
-                    acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[a], fb[b], acc[a][b], 0, 0, 0);
+                for (int b = 0; b < 4; ++b) {
+                    acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[ks & 1][a], fb[ks & 1][b], acc[a][b], 0,
+                                                                        0, 0);
+                    const int q = ks * 16 + a * 4 + b;
+                    if (q < G::kLoads && refill)
+                        __builtin_amdgcn_global_load_lds(
+                            reinterpret_cast<const void*>(src[q] + (size_t)kn * BK),
+                            (__attribute__((address_space(3))) void*)(nslot + (wave * G::kLoads + q) * 64), 16, 0,
+                            0);
+                }
         }
         // the slot is refilled only after the next barrier; make sure this
         // wave's reads of it have completed before arriving there
