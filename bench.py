@@ -57,6 +57,7 @@ def parse():
 # banner comment to the next one), so that stored counter readings stay tied
 # to the kernel they were taken on.
 _SECTIONS = {"lmhead_coop_bf16": "small M, cooperative", "lmhead_big_bf16": "big M",
+             "lmhead_skinny_bf16": "small M",
              "lmhead_tiled_bf16": "large M", "lmhead_f32": "fp32"}
 
 
@@ -245,7 +246,9 @@ def main():
         roof["kernel"] = "lmhead_f32"
     elif M <= 16 and H <= 4096:
         roof["kernel"] = "lmhead_coop_bf16"
-    elif M >= 512 and H % 64 == 0:
+    elif M <= 16:
+        roof["kernel"] = "lmhead_skinny_bf16"
+    elif H % 64 == 0 and V * H < 2 ** 32 and M * H < 2 ** 32:
         roof["kernel"] = "lmhead_big_bf16"
     else:
         roof["kernel"] = "lmhead_tiled_bf16"

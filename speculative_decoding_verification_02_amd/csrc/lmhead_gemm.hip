@@ -384,49 +384,62 @@ __global__ __launch_bounds__(kTiledThreads) void lmhead_tiled_bf16(
 }
 
 // ------------------------------------------------------------- big M -----
-// Dense contraction for M in the thousands (MFMA-bound).  A workgroup of 4
-// waves owns a 256 (vocab) x 256 (hidden rows) tile; each wave a 128 x 128
-// quarter as 4 x 4 blocks of v_mfma_f32_32x32x16_bf16 (256 fp32 accumulators
-// per lane, one wave per SIMD).  On MI355X the 32x32x16 form issues at about
-// twice the rate of 16x16x32 (measured ~2.0 vs ~0.8 PFLOP/s at one wave per
-// SIMD), so the dense path uses it.  Operand layout: lane l holds
-// A[l % 32][8*(l/32) .. +8) (W rows) and B[8*(l/32) .. +8)[l % 32] (hidden
-// rows) and receives D[8*(i/4) + 4*(l/32) + i%4][l % 32], i < 16: four runs of
-// four consecutive vocabulary entries of one hidden row.
+// Dense contraction for M from a few dozen rows up (MFMA-bound at large M).
+// A workgroup of 4 waves owns a 256 (vocab) x BM (hidden rows) tile; each
+// wave a 32*NA x 32*NB part as NA x NB blocks of v_mfma_f32_32x32x16_bf16
+// (16*NA*NB fp32 accumulators per lane, one wave per SIMD), the waves laid out
+// 8/NA along the vocabulary and 4*NA/8 along the rows, so BM = 32*NB*4*NA/8.  On MI355X the 32x32x16 form issues at about twice the rate of
+// 16x16x32 (measured ~2.0 vs ~0.8 PFLOP/s at one wave per SIMD), so the dense
+// path uses it.  Operand layout: lane l holds A[l % 32][8*(l/32) .. +8) (W
+// rows) and B[8*(l/32) .. +8)[l % 32] (hidden rows) and receives
+// D[8*(i/4) + 4*(l/32) + i%4][l % 32], i < 16: four runs of four consecutive
+// vocabulary entries of one hidden row.
 //
-// Operands reach LDS by direct global->LDS loads (global_load_lds_dwordx4,
-// no register staging) into a ring of kBigSlots k-slices of 32 columns (32 KB
-// each: 256 W rows + 256 hidden rows, 64 bytes per row).  Loads run
-// kBigSlots-1 slices ahead of the multiply, so their latency under full load
-// (~2.5 us measured) hides behind several slices of MFMA work.  A DMA
-// instruction writes 1 KB of LDS in lane order; each lane picks the global
-// chunk that belongs at its LDS position, so the slice lands swizzled: chunk c
-// of row r at r*4 + (c ^ ((r >> 2) & 3)), which spreads any 16 consecutive
-// rows read at one chunk over the 16 bank groups.  Synchronisation is
-// explicit: a wait on the wave's own outstanding loads (vmcnt), then one
-// barrier per slice.  Tiles are ordered XCD-aware like the tiled kernel.
+// Operands reach LDS by direct global->LDS loads (global_load_lds_dwordx4, no
+// register staging) into a ring of SLOTS k-slices of BK columns (256 W rows
+// then BM hidden rows, BK*2 bytes per row).  A DMA instruction writes 1 KB of
+// LDS in lane order; each lane picks the global chunk that belongs at its LDS
+// position, so the slice lands swizzled (Big::pos), which spreads any 16
+// consecutive rows read at one chunk over the 16 bank groups.  The loads of
+// slice k+SLOTS-1 are issued one per MFMA while slice k is multiplied, and
+// each k-step's fragments are read from LDS during the previous k-step's
+// MFMAs, so neither a full load queue nor an LDS read stalls the matrix
+// pipe.  Synchronisation is explicit: a wait on the wave's own outstanding
+// loads (vmcnt), then one barrier per slice.  Tiles are ordered XCD-aware like
+// the tiled kernel, so the M-tiles of one vocabulary tile share an L2.
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 constexpr int kBigBN = 256;
-constexpr int kBigBM = 256;
 constexpr int kBigThreads = 256;
 
-// Geometry of one k-slice of BK columns: 256 W rows then 256 hidden rows,
-// CPR 16-byte chunks per row; a DMA instruction fills RPI rows (1 KB).
-template <int BK, int SLOTS>
+// Geometry of one k-slice of BK columns: 256 W rows then BM hidden rows, CPR
+// 16-byte chunks per row; a DMA instruction fills RPI rows (1 KB).
+template <int BK, int SLOTS, int NA, int NB>
 struct Big {
+    static constexpr int kWN = 8 / NA;                  // waves along the vocabulary
+    static constexpr int kWM = 4 / kWN;                 // waves along the hidden rows
+    static constexpr int kBM = kWM * NB * 32;
     static constexpr int kCPR = BK / 8;
     static constexpr int kRPI = 64 / kCPR;
-    static constexpr int kSliceChunks = 2 * 256 * kCPR;
+    static constexpr int kSliceChunks = (kBigBN + kBM) * kCPR;
     static constexpr int kLoads = kSliceChunks / 64 / (kBigThreads / 64);   // DMA per lane per slice
+    static constexpr int kWLoads = kBigBN * kCPR / 64;                      // DMA blocks holding W rows
     static constexpr int kSteps = BK / 16;                                  // MFMA k-steps per slice
     static constexpr size_t kLds = (size_t)SLOTS * kSliceChunks * 16;
+    static_assert(kSliceChunks % kBigThreads == 0, "slice must split evenly over the lanes");
+    static_assert(kWN * NA == 8 && kWN * kWM == 4, "wave layout must tile 256 x BM");
+    static_assert(kLoads <= kSteps * NA * NB, "every load must find an MFMA to ride on");
+    static_assert(kLds <= 160 * 1024, "LDS ring exceeds the 160 KB of a CU");
     // chunk c of row r sits at r*CPR + (c ^ f(r)), f(r) = (r / (16/CPR)) % CPR:
     // 16 consecutive rows read at one chunk fall in 16 distinct bank groups
     static __device__ __forceinline__ int pos(int row, int chunk) {
         return row * kCPR + (chunk ^ ((row / (16 / kCPR)) % kCPR));
     }
 };
+
+// the wave's index as a scalar (a non-template wrapper: inside a kernel
+// template the builtin would drop the host-side launch stub)
+__device__ __forceinline__ int wave_index_uniform(int tid) { return __builtin_amdgcn_readfirstlane(tid >> 6); }
 
 // s_waitcnt vmcnt(n) leaving the other counters alone (gfx9 encoding).
 template <int N>
@@ -450,66 +463,71 @@ __device__ __forceinline__ void wait_slices(int after) {
     wait_vmcnt<0>();
 }
 
-template <int BK, int SLOTS>
+template <int BK, int SLOTS, int NA, int NB>
 __global__ __launch_bounds__(kBigThreads, 1) void lmhead_big_bf16(
     const uint16_t* __restrict__ hidden, const uint16_t* __restrict__ W, float* __restrict__ logits,
     int M, int V, int H, int tiles_n, int tiles_m) {
-    using G = Big<BK, SLOTS>;
+    using G = Big<BK, SLOTS, NA, NB>;
     extern __shared__ __align__(16) unsigned char smem[];
-    u32x4* lds = reinterpret_cast<u32x4*>(smem);   // [slot][W rows 0..255 | hidden rows 0..255][CPR chunks]
+    u32x4* lds = reinterpret_cast<u32x4*>(smem);   // [slot][W rows 0..255 | hidden rows 0..BM-1][CPR chunks]
 
     const int total = tiles_n * tiles_m;
     const int per_xcd = (total + 7) / 8;
     const int seq = (blockIdx.x % 8) * per_xcd + blockIdx.x / 8;
     if (seq >= total) return;
     const int tn = seq / tiles_m, tm = seq - tn * tiles_m;
-    const int v0 = tn * kBigBN, m0 = tm * kBigBM;
+    const int v0 = tn * kBigBN, m0 = tm * G::kBM;
 
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
     const int r = lane & 31, h = lane >> 5;
-    const int wn = (wave & 1) * 128, wm = (wave >> 1) * 128;
+    const int wn = (wave % G::kWN) * (32 * NA), wm = (wave / G::kWN) * (32 * NB);
 
     // DMA source of each of this lane's loads: instruction q of this wave fills
-    // 1 KB block bi = wave * kLoads + q of the slice (RPI rows; the first half
-    // of the blocks hold W rows, the second half hidden rows); the lane's
-    // position in the block fixes its row and, through the swizzle, its chunk.
-    constexpr int kHalf = 256 / G::kRPI;
-    const uint16_t* src[G::kLoads];
+    // 1 KB block bi = wave * kLoads + q of the slice (RPI rows; the first
+    // kWLoads blocks hold W rows, the rest hidden rows); the lane's position in
+    // the block fixes its row and, through the swizzle, its chunk.  Sources are
+    // kept as 32-bit element offsets (the launcher checks V*H and M*H fit) to
+    // leave registers for the accumulators.
+    const int wave_u = wave_index_uniform(tid);
+    uint32_t off[G::kLoads];
 #pragma unroll
     for (int q = 0; q < G::kLoads; ++q) {
-        const int bi = wave * G::kLoads + q;
-        const int row = (bi % kHalf) * G::kRPI + lane / G::kCPR;
+        const int bi = wave_u * G::kLoads + q;
+        const int row = bi * G::kRPI + lane / G::kCPR;   // row of the slice, W rows first
         const int chunk = (lane % G::kCPR) ^ ((row / (16 / G::kCPR)) % G::kCPR);
-        if (bi < kHalf) {
+        if (bi < G::kWLoads) {
             const int vr = min(v0 + row, V - 1);          // rows past V: read a valid row, outputs dropped
-            src[q] = W + (size_t)vr * H + chunk * 8;
+            off[q] = (uint32_t)vr * (uint32_t)H + chunk * 8;
         } else {
-            const int mr = min(m0 + row, M - 1);
-            src[q] = hidden + (size_t)mr * H + chunk * 8;
+            const int mr = min(m0 + row - kBigBN, M - 1);
+            off[q] = (uint32_t)mr * (uint32_t)H + chunk * 8;
         }
     }
-    auto issue = [&](int kt) {
-        u32x4* slot = lds + (kt % SLOTS) * G::kSliceChunks;
-#pragma unroll
-        for (int q = 0; q < G::kLoads; ++q)
-            __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(src[q] + (size_t)kt * BK),
-                                             (__attribute__((address_space(3))) void*)(slot + (wave * G::kLoads + q) * 64),
-                                             16, 0, 0);
+    auto src = [&](int q, int kt) {
+        const uint16_t* base = wave_u * G::kLoads + q < G::kWLoads ? W : hidden;
+        return base + off[q] + (size_t)kt * BK;
     };
 
-    f32x16 acc[4][4];
+    f32x16 acc[NA][NB];
 #pragma unroll
-    for (int a = 0; a < 4; ++a)
+    for (int a = 0; a < NA; ++a)
 #pragma unroll
-        for (int b = 0; b < 4; ++b)
+        for (int b = 0; b < NB; ++b)
 #pragma unroll
             for (int e = 0; e < 16; ++e) acc[a][b][e] = 0.f;
 
     const int nk = H / BK;
 #pragma unroll
-    for (int p = 0; p < SLOTS - 1; ++p)
-        if (p < nk) issue(p);
+    for (int p = 0; p < SLOTS - 1; ++p) {
+        if (p >= nk) break;
+        u32x4* slot = lds + p * G::kSliceChunks;
+#pragma unroll
+        for (int q = 0; q < G::kLoads; ++q)
+            __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(src(q, p)),
+                                             (__attribute__((address_space(3))) void*)(slot + (wave * G::kLoads + q) * 64),
+                                             16, 0, 0);
+    }
 
     for (int kt = 0; kt < nk; ++kt) {
         // this lane's loads of slice kt have landed once at most the slices
@@ -524,32 +542,29 @@ __global__ __launch_bounds__(kBigThreads, 1) void lmhead_big_bf16(
         u32x4* nslot = lds + (kn % SLOTS) * G::kSliceChunks;
 
         const u32x4* lw = lds + (kt % SLOTS) * G::kSliceChunks;
-        const u32x4* lh = lw + 256 * G::kCPR;
-        // fragments of k-step ks+1 are read while the MFMAs of ks run, and
-        // the next slice's loads are issued one per MFMA of the first k-steps,
-        // so the wave never stalls on a full load queue before its MFMAs
-        bf16x8 fa[2][4], fb[2][4];
-        auto frag = [&](int ks, bf16x8 (&xa)[4], bf16x8 (&xb)[4]) {
+        const u32x4* lh = lw + kBigBN * G::kCPR;
+        bf16x8 fa[2][NA], fb[2][NB];
+        auto frag = [&](int ks, bf16x8 (&xa)[NA], bf16x8 (&xb)[NB]) {
             const int ch = ks * 2 + h;
 #pragma unroll
-            for (int a = 0; a < 4; ++a) xa[a] = as_bf16x8(lw[G::pos(wn + a * 32 + r, ch)]);
+            for (int a = 0; a < NA; ++a) xa[a] = as_bf16x8(lw[G::pos(wn + a * 32 + r, ch)]);
 #pragma unroll
-            for (int b = 0; b < 4; ++b) xb[b] = as_bf16x8(lh[G::pos(wm + b * 32 + r, ch)]);
+            for (int b = 0; b < NB; ++b) xb[b] = as_bf16x8(lh[G::pos(wm + b * 32 + r, ch)]);
         };
         frag(0, fa[0], fb[0]);
 #pragma unroll
         for (int ks = 0; ks < G::kSteps; ++ks) {
             if (ks + 1 < G::kSteps) frag(ks + 1, fa[(ks + 1) & 1], fb[(ks + 1) & 1]);
 #pragma unroll
-            for (int a = 0; a < 4; ++a)
+            for (int a = 0; a < NA; ++a)
 #pragma unroll
-                for (int b = 0; b < 4; ++b) {
+                for (int b = 0; b < NB; ++b) {
                     acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[ks & 1][a], fb[ks & 1][b], acc[a][b], 0,
                                                                         0, 0);
-                    const int q = ks * 16 + a * 4 + b;
+                    const int q = (ks * NA + a) * NB + b;
                     if (q < G::kLoads && refill)
                         __builtin_amdgcn_global_load_lds(
-                            reinterpret_cast<const void*>(src[q] + (size_t)kn * BK),
+                            reinterpret_cast<const void*>(src(q, kn)),
                             (__attribute__((address_space(3))) void*)(nslot + (wave * G::kLoads + q) * 64), 16, 0,
                             0);
                 }
@@ -561,12 +576,12 @@ __global__ __launch_bounds__(kBigThreads, 1) void lmhead_big_bf16(
 
     const bool vec_ok = (V & 3) == 0;
 #pragma unroll
-    for (int b = 0; b < 4; ++b) {
+    for (int b = 0; b < NB; ++b) {
         const int m = m0 + wm + b * 32 + r;
         if (m >= M) continue;
         float* out = logits + (size_t)m * V;
 #pragma unroll
-        for (int a = 0; a < 4; ++a)
+        for (int a = 0; a < NA; ++a)
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
                 const f32x4 v4 = {acc[a][b][4 * q], acc[a][b][4 * q + 1], acc[a][b][4 * q + 2], acc[a][b][4 * q + 3]};
@@ -575,33 +590,50 @@ __global__ __launch_bounds__(kBigThreads, 1) void lmhead_big_bf16(
     }
 }
 
-// Configuration the library launches (measured best on MI355X at the
-// 256x8x8192 and 512x4x5120 verify shapes: whole 128-byte rows per slice).
-constexpr int kBigBK = 64;
-constexpr int kBigSlots = 2;
-constexpr int kBigMinM = 512;   // below this the LDS-tiled kernel wastes less of its tile
-
-bool big_fits(int M, int H) { return M >= kBigMinM && H % kBigBK == 0; }
-
-template <int BK, int SLOTS>
+template <int BK, int SLOTS, int NA, int NB>
 hipError_t launch_big_cfg(const uint16_t* hidden, const uint16_t* W, float* logits, int M, int V, int H,
                           hipStream_t stream) {
-    auto kern = lmhead_big_bf16<BK, SLOTS>;
-    const size_t lds = Big<BK, SLOTS>::kLds;
+    using G = Big<BK, SLOTS, NA, NB>;
+    auto kern = lmhead_big_bf16<BK, SLOTS, NA, NB>;
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)G::kLds);
     if (e != hipSuccess) return e;
     const int tiles_n = (V + kBigBN - 1) / kBigBN;
-    const int tiles_m = (M + kBigBM - 1) / kBigBM;
+    const int tiles_m = (M + G::kBM - 1) / G::kBM;
     const int grid = ((tiles_n * tiles_m + 7) / 8) * 8;
-    hipLaunchKernelGGL(kern, dim3(grid), dim3(kBigThreads), lds, stream, hidden, W, logits, M, V, H, tiles_n,
+    hipLaunchKernelGGL(kern, dim3(grid), dim3(kBigThreads), G::kLds, stream, hidden, W, logits, M, V, H, tiles_n,
                        tiles_m);
     return hipGetLastError();
 }
 
+// Configurations the library launches, all with whole 128-byte rows per
+// slice.  The tile height follows M so that little of the tile is padding;
+// rows from 257 to 320 run as two 160-row tiles (4 waves side by side along
+// the vocabulary), whose smaller slices leave room for a third slot, i.e. two
+// slices in flight.  Measured on MI355X at H = 4096, V = 128256 (us per
+// GEMM): M = 40: 183 (64-row tile) vs 246 (128 x 128 tiled kernel); M = 96:
+// 214 vs 226; M = 130: 263 vs 362; M = 320: 395 (2 x 160) vs 535 (2 x 256)
+// vs 537 (tiled); M = 400: 546 (2 x 256) vs 679 (tiled).  256-row tiles use
+// waves of 64 x 256 (2 x 8 blocks): ~980 vs ~900 TFLOP/s for 128 x 128 waves
+// at M = 2048, H = 5120, V = 262144, and within 2% either way at M = 2304,
+// H = 8192, V = 152064.
+constexpr int kBigBK = 64;
+constexpr int kBigMinM = 17;
+
+// sources are 32-bit element offsets into W and hidden
+bool big_fits(int M, int V, int H) {
+    return M >= kBigMinM && H % kBigBK == 0 && (uint64_t)V * H < (1ull << 32) && (uint64_t)M * H < (1ull << 32);
+}
+
 hipError_t launch_big(const uint16_t* hidden, const uint16_t* W, float* logits, int M, int V, int H,
                       hipStream_t stream) {
-    return launch_big_cfg<kBigBK, kBigSlots>(hidden, W, logits, M, V, H, stream);
+    if (M <= 64) return launch_big_cfg<kBigBK, 3, 4, 1>(hidden, W, logits, M, V, H, stream);
+    if (M <= 128) return launch_big_cfg<kBigBK, 3, 4, 2>(hidden, W, logits, M, V, H, stream);
+    if (M <= 160) return launch_big_cfg<kBigBK, 3, 2, 5>(hidden, W, logits, M, V, H, stream);
+    if (M <= 192) return launch_big_cfg<kBigBK, 2, 4, 3>(hidden, W, logits, M, V, H, stream);
+    if (M <= 256) return launch_big_cfg<kBigBK, 2, 2, 8>(hidden, W, logits, M, V, H, stream);
+    if (M <= 320) return launch_big_cfg<kBigBK, 3, 2, 5>(hidden, W, logits, M, V, H, stream);
+    return launch_big_cfg<kBigBK, 2, 2, 8>(hidden, W, logits, M, V, H, stream);
 }
 
 // ------------------------------------------------------------------ fp32 ---
@@ -688,7 +720,7 @@ hipError_t launch_lmhead_bf16(const uint16_t* hidden, const uint16_t* W, float* 
                               int num_cus, hipStream_t stream, int force_kernel) {
     if (force_kernel == 0 && CoopCfg::fits(M, H))
         return launch_coop<2, 2, 8>(hidden, W, logits, M, V, H, num_cus, stream, 1);
-    if (force_kernel == 0 && big_fits(M, H)) return launch_big(hidden, W, logits, M, V, H, stream);
+    if (force_kernel == 0 && big_fits(M, V, H)) return launch_big(hidden, W, logits, M, V, H, stream);
     const bool skinny = force_kernel == 1 || (force_kernel == 0 && skinny_fits(M, H));
     if (skinny) return launch_skinny<kSkRPL, kSkP, kSkThreads>(hidden, W, logits, M, V, H, num_cus, stream);
     const int tiles_n = (V + kTileN - 1) / kTileN;

@@ -1,7 +1,8 @@
 """GPU parity of spec_verify_logits (LM-head contraction) against the oracle.
 
-Covers the small-M streaming kernel (M <= 16), the LDS-tiled kernel (larger
-M), and the fp32 kernel, on shapes that span several tiles with ragged tails
+Covers the small-M kernels (M <= 16), the direct-to-LDS MFMA kernel in each
+of its tile heights (M > 16, H a multiple of 64), the LDS-tiled kernel (other
+H), and the fp32 kernel, on shapes that span several tiles with ragged tails
 in V, M and H; integer-valued inputs that must come out bit-exact whatever the
 summation order; the full-size workloads (all entries at B=1, sampled entries
 at the larger ones); and run-to-run determinism.
@@ -58,6 +59,7 @@ def test_bf16_small_m_wide_hidden(B, K, H, V):
 @pytest.mark.parametrize("B,K", [(6, 2), (130, 0), (64, 4), (3, 63)])
 @pytest.mark.parametrize("H,V", [(64, 1000), (520, 2053), (1032, 257)])
 def test_bf16_tiled(B, K, H, V):
+    """H = 520 and 1032 are not multiples of 64: the 128 x 128 tiled kernel."""
     W, h = _case(B, K, H, V, "bf16", 0.02, seed=B * 7 + K + H + V)
     _check(h, W)
 
@@ -67,6 +69,17 @@ def test_bf16_big_m(B, K, H, V):
     """M >= 512 with H a multiple of 64: the direct-to-LDS 256 x 256 kernel,
     including tiles cut by the ragged edges of M and V."""
     W, h = _case(B, K, H, V, "bf16", 0.02, seed=B + K + H + V)
+    _check(h, W)
+
+
+# M = B*(K+1) in each tile-height band of the direct-to-LDS kernel (17-64,
+# 65-128, 129-160, 161-192, 193-256, 257-320 as two 160-row tiles, 321-511),
+# each at a band edge or with a ragged last tile, against a ragged V.
+@pytest.mark.parametrize("B,K", [(17, 0), (4, 4), (16, 3), (25, 3), (32, 3), (13, 9), (32, 4), (20, 7), (38, 4), (43, 5),
+                                 (64, 3), (51, 4), (64, 4), (107, 2), (90, 4), (511, 0)])
+@pytest.mark.parametrize("H,V", [(128, 1000), (448, 2053)])
+def test_bf16_tile_heights(B, K, H, V):
+    W, h = _case(B, K, H, V, "bf16", 0.02, seed=3 * B + K + H + V)
     _check(h, W)
 
 
