@@ -171,22 +171,39 @@ def main():
     smask = synth.sampled_mask(wl)
     n_sets = 16
     drafts = [synth.draft_tokens(zd, smask, T, seed=wl.data_seed * 104729 + r) for r in range(n_sets)]
+    row_start = None
+    if wl.ragged:
+        # per-sequence draft counts: pack every input, K is the bound K_max
+        counts = synth.draft_counts(B, K, wl.data_seed)
+        rs = synth.row_start(counts)
+        M = int(rs[-1])
+        hidden = synth.pack_rows(hidden, counts).contiguous().view(M, 1, H)
+        zd = synth.pack_rows(zd, counts, True).contiguous()
+        drafts = [synth.pack_rows(d, counts, True).contiguous() for d in drafts]
+        row_start = torch.as_tensor(rs, device=dev)
     n_seed_sets = args.warmup + args.steps
     seeds = [torch.from_numpy(synth.seeds(wl, r).view(np.int64).copy()).to(dev) for r in range(n_seed_sets)]
     greedy_rows = torch.as_tensor(np.nonzero(~smask)[0].astype(np.int32), device=dev)
     sampled_rows = torch.as_tensor(np.nonzero(smask)[0].astype(np.int32), device=dev)
     all_sampled, all_greedy = bool(smask.all()), bool((~smask).all())
 
-    logits = torch.empty((B, K + 1, V), dtype=torch.float32, device=dev)
+    logits = torch.empty(tuple(hidden.shape[:2]) + (V,), dtype=torch.float32, device=dev)
     ws = torch.empty(sv.spec_workspace_bytes(B, K, V), dtype=torch.uint8, device=dev)
     acc = torch.empty((B,), dtype=torch.int32, device=dev)
-    out = torch.empty((B, K + 1), dtype=torch.int32, device=dev)
+    out = torch.empty(tuple(hidden.shape[:2]), dtype=torch.int32, device=dev)
     stream = torch.cuda.current_stream()
 
     def step(r):
         sv.spec_verify_logits(hidden, W, logits, stream=stream)
         d = drafts[r % n_sets]
-        if all_sampled:
+        if row_start is not None:
+            lg, o = logits.view(M, V), out.view(M)
+            if len(greedy_rows):
+                sv.spec_accept_greedy_ragged(lg, d, row_start, K, acc, o, ws, rows=greedy_rows, stream=stream)
+            if len(sampled_rows):
+                sv.spec_accept_sample_ragged(lg, zd, d, row_start, K, T, seeds[r], acc, o, ws, rows=sampled_rows,
+                                             stream=stream)
+        elif all_sampled:
             sv.spec_accept_sample(logits, zd, d, T, seeds[r], acc, out, ws, stream=stream)
         elif all_greedy:
             sv.spec_accept_greedy(logits, d, acc, out, ws, stream=stream)
@@ -257,7 +274,7 @@ def main():
     roof["algorithmic_flops"] = gemm_flops
     roof["avg_kernel_us"] = gemm_ms * 1e3
 
-    positions = B * (K + 1)
+    positions = M
     res = {
         "metric": METRIC,
         "value": positions / step_s,
@@ -273,17 +290,19 @@ def main():
         "data": "synthetic",
         "config": {"workload": wl.name, "B": B, "K": K, "H": H, "V": V, "temperature": T,
                    "sampled_rows": int(smask.sum()), "greedy_rows": int((~smask).sum())},
+        **({"verify_rows": M, "draft_counts": "K_b ~ U{0..%d}, packed" % K} if row_start is not None else {}),
         "verify_step_us": step_s * 1e6,
         "committed_tokens_per_step_last": float(np.mean(accepted + 1)),
         "roofline": roof,
     }
 
     if not args.no_cpu_baseline:
-        res["cpu_baseline"] = cpu_baseline(wl, W, hidden, zd, drafts, smask, args.cpu_seconds)
+        rs_np = None if row_start is None else row_start.cpu().numpy()
+        res["cpu_baseline"] = cpu_baseline(wl, W, hidden, zd, drafts, smask, args.cpu_seconds, rs_np)
     print(json.dumps(res), flush=True)
 
 
-def cpu_baseline(wl, W, hidden, zd, drafts, smask, budget_s):
+def cpu_baseline(wl, W, hidden, zd, drafts, smask, budget_s, rs=None):
     """The oracle, as it stands, timed on this host on the same inputs: whole
     verify steps (fp64 logits of all K+1 positions + acceptance) until about
     budget_s seconds have been spent (at least one step)."""
@@ -297,8 +316,9 @@ def cpu_baseline(wl, W, hidden, zd, drafts, smask, budget_s):
     w64 = oracle.widen_bf16(W.cpu().view(torch.int16).numpy().view(np.uint16)) if wl.dtype == "bf16" \
         else W.cpu().double().numpy()
     h = hidden.cpu()
+    M = wl.M if rs is None else int(rs[-1])
     h64 = (oracle.widen_bf16(h.view(torch.int16).numpy().view(np.uint16)) if wl.dtype == "bf16"
-           else h.double().numpy()).reshape(wl.M, wl.H)
+           else h.double().numpy()).reshape(M, wl.H)
     zd64 = zd.cpu().numpy()
     ds = [d.cpu().numpy() for d in drafts]
     g_rows = np.nonzero(~smask)[0]
@@ -310,19 +330,28 @@ def cpu_baseline(wl, W, hidden, zd, drafts, smask, budget_s):
         r = 0
         while True:
             t0 = time.perf_counter()
-            z = oracle.lm_head_logits(h64, w64).reshape(wl.B, wl.K + 1, wl.V)
-            if len(g_rows):
-                oracle.accept_greedy(z, ds[r % len(ds)], rows=g_rows)
-            if len(s_rows):
-                oracle.accept_sample(z, zd64, ds[r % len(ds)], wl.temperature, synth_seeds(wl, r), rows=s_rows)
+            z = oracle.lm_head_logits(h64, w64)
+            d = ds[r % len(ds)]
+            if rs is not None:
+                if len(g_rows):
+                    oracle.accept_greedy_ragged(z, d, rs, wl.K, rows=g_rows)
+                if len(s_rows):
+                    oracle.accept_sample_ragged(z, zd64, d, rs, wl.K, wl.temperature, synth_seeds(wl, r),
+                                                rows=s_rows)
+            else:
+                z = z.reshape(wl.B, wl.K + 1, wl.V)
+                if len(g_rows):
+                    oracle.accept_greedy(z, d, rows=g_rows)
+                if len(s_rows):
+                    oracle.accept_sample(z, zd64, d, wl.temperature, synth_seeds(wl, r), rows=s_rows)
             times.append(time.perf_counter() - t0)
             r += 1
             if time.perf_counter() - t_start > budget_s:
                 break
     t = float(np.mean(times))
-    return {"value": wl.M / t, "unit": "verified positions/s", "cores": int(min(used, cores)), "kind": "oracle",
+    return {"value": M / t, "unit": "verified positions/s", "cores": int(min(used, cores)), "kind": "oracle",
             "sample": "%d whole verify steps of %s (fp64 logits of all %d positions over V=%d, then acceptance), "
-                      "same inputs as the GPU run; %.2f s per step" % (len(times), wl.name, wl.M, wl.V, t)}
+                      "same inputs as the GPU run; %.2f s per step" % (len(times), wl.name, M, wl.V, t)}
 
 
 def synth_seeds(wl, r):

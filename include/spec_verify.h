@@ -25,6 +25,18 @@
  *                          decoding" blog, Rejection sampling; "What is
  *                          speculative decoding" guide, How speculative
  *                          decoding works).
+ *   spec_accept_greedy_ragged, spec_accept_sample_ragged
+ *                       -- the same two rules on a batch whose sequences carry
+ *                          different draft counts K_b (0 <= K_b <= K_max),
+ *                          rows packed without padding.  A drafter may return
+ *                          fewer drafts than asked, or none ("Inference-4",
+ *                          Prompt lookup decoding, and the draft count capped
+ *                          by the context window in its verification loop);
+ *                          a scheduler may choose how many drafts to verify
+ *                          per request ("speculative-decoding" blog, DSpark,
+ *                          confidence-scheduled verification) or shorten them
+ *                          under load ("Speculative decoding" course page, Why
+ *                          engines disable speculation under load).
  *
  * Conventions shared by every entry point
  *   - Every pointer argument is DEVICE memory on the current HIP device, owned
@@ -173,8 +185,53 @@ spec_status_t spec_accept_sample(const float* logits, const float* draft_logits,
                                  void* workspace, size_t workspace_bytes,
                                  spec_stream_t stream);
 
-/* Bytes of workspace either accept call needs for these sizes (0 if the sizes
- * are out of range). */
+/*
+ * Ragged batches.  Sequence b has K_b drafts, 0 <= K_b <= K_max <= 63, and its
+ * rows are packed in sequence order with no padding:
+ *   row_start     device, [B+1] int32, 4-byte aligned: row_start[0] = 0 and
+ *                 row_start[b+1] = row_start[b] + K_b + 1, so row_start[B] =
+ *                 total_rows.  Sequence b owns target rows row_start[b] ..
+ *                 row_start[b] + K_b and draft rows / tokens row_start[b] - b
+ *                 .. row_start[b] - b + K_b - 1.
+ *   total_rows    R = sum_b (K_b + 1), with B <= R <= B*(K_max+1)
+ *   logits        device, [R, V] fp32 (spec_verify_logits with B = R, K = 0
+ *                 computes it from hidden states packed the same way)
+ *   draft_logits  device, [R-B, V] fp32 (sampled; may be NULL when R == B)
+ *   draft_tokens  device, [R-B] int32 (may be NULL when R == B)
+ *   accepted_len  device, [B] int32, n in 0..K_b
+ *   out_tokens    device, [R] int32: entries row_start[b] .. row_start[b]+K_b
+ *                 hold (d_0, ..., d_{n-1}, t, -1, ...) of sequence b
+ *   probs_at_draft  device, [R-B, 2] fp32 or NULL (sampled)
+ *   workspace     at least spec_workspace_bytes(B, K_max, V) bytes
+ *   rows, n_rows, seeds, temperature, stream: as in the dense calls.
+ * Each sequence is verified exactly as a dense sequence with K = K_b in batch
+ * slot b (so the Philox counter is (i, b, 0, 0)); a batch where every K_b = K
+ * gives the dense calls' results bit for bit.  Host checks: row_start non-NULL
+ * and aligned, B <= total_rows <= B*(K_max+1).  The device checks each
+ * selected sequence's own entries (0 <= K_b <= K_max, row_start[b] >= b, and
+ * row_start[b+1] leaving room for the later sequences' rows); a sequence that
+ * fails them gets accepted_len[b] = -1 and none of its rows is read or
+ * written.  Other data faults are marked as in the dense calls.
+ */
+spec_status_t spec_accept_greedy_ragged(const float* logits, const int32_t* draft_tokens,
+                                        const int32_t* row_start, int total_rows,
+                                        const int32_t* rows, int n_rows, int B, int K_max, int V,
+                                        int32_t* accepted_len, int32_t* out_tokens,
+                                        void* workspace, size_t workspace_bytes,
+                                        spec_stream_t stream);
+
+spec_status_t spec_accept_sample_ragged(const float* logits, const float* draft_logits,
+                                        const int32_t* draft_tokens,
+                                        const int32_t* row_start, int total_rows,
+                                        float temperature, const uint64_t* seeds,
+                                        const int32_t* rows, int n_rows, int B, int K_max, int V,
+                                        int32_t* accepted_len, int32_t* out_tokens,
+                                        float* probs_at_draft,
+                                        void* workspace, size_t workspace_bytes,
+                                        spec_stream_t stream);
+
+/* Bytes of workspace any accept call needs for these sizes (K = K_max for the
+ * ragged calls; 0 if the sizes are out of range). */
 size_t spec_workspace_bytes(int B, int K, int V);
 
 /* Static, human-readable name of a status code. */

@@ -10,19 +10,21 @@ Modules:
   philox  -- Philox4x32-10 from its published definition (Salmon et al.,
              SC'11), and the two verify uniforms per (seed, sequence, position).
   verify  -- LM-head logits, greedy acceptance, speculative sampling with
-             residual / bonus draw, decision margins, and the closed-form
-             expected tokens per verify pass.
+             residual / bonus draw, decision margins, the closed-form
+             expected tokens per verify pass, and both rules on packed
+             batches with per-sequence draft counts.
 
 Every function is pinned by the CPU tests (tests/test_oracle_*.py) to
 something other than itself: published Philox known-answer blocks and an
 independent library implementation, exact rational arithmetic for the
 logits, brute force over every draft sequence for greedy decoding,
 chi-square tests of the sampled output against the target distribution, the
-closed form for the expected tokens per pass, and the residual identity.
+closed form for the expected tokens per pass, the residual identity, and
+(for packed batches) reduction to the dense rule sequence by sequence.
 """
 from .philox import philox4x32_10, uniform24, verify_uniforms  # noqa: F401
 from .verify import (  # noqa: F401
-    GreedyResult, SampleResult, accept_greedy, accept_ratio, accept_sample,
-    expected_tokens, expected_tokens_positional, inverse_cdf, lm_head_logits,
-    softmax, widen_bf16,
+    GreedyResult, SampleResult, accept_greedy, accept_greedy_ragged, accept_ratio, accept_sample,
+    accept_sample_ragged, expected_tokens, expected_tokens_positional, inverse_cdf, lm_head_logits,
+    ragged_sequences, softmax, widen_bf16,
 )

@@ -205,11 +205,12 @@ def terminal_weights(q_n, p_n=None):
     return np.where(empty, q_n, w)
 
 
-def accept_sample(logits, draft_logits, draft_tokens, temperature, seeds, rows=None) -> SampleResult:
+def accept_sample(logits, draft_logits, draft_tokens, temperature, seeds, rows=None, slots=None) -> SampleResult:
     """Speculative sampling of each selected row b (B rows, K drafts, V tokens).
 
     q_i = softmax(logits[b, i] / T), i = 0..K;  p_i = softmax(draft_logits[b, i] / T), i < K.
-    (u_i, u'_i) = Philox uniforms at (seed_b, b, i).
+    (u_i, u'_i) = Philox uniforms at (seed_b, slot_b, i); slot_b = b unless
+    ``slots`` names each row's batch slot.
     Accept d_i iff u_i < r_i = min(1, q_i(d_i)/p_i(d_i)); n = first rejected i, else K.
     Terminal weights: w = max(0, q_n - p_n) if n < K, else q_K (bonus).
     Terminal token: inverse CDF of w at u'_n.  Emitted: d_0..d_{n-1}, t.
@@ -221,6 +222,7 @@ def accept_sample(logits, draft_logits, draft_tokens, temperature, seeds, rows=N
     zd = np.asarray(draft_logits, dtype=np.float64) if K else np.zeros((B, 0, V))
     d = np.asarray(draft_tokens, dtype=np.int64).reshape(B, K)
     seeds = np.asarray(seeds, dtype=np.uint64)
+    slot = np.arange(B) if slots is None else np.asarray(slots, dtype=np.int64).reshape(B)
     T = float(temperature)
     rows = _rows_arg(rows, B)
 
@@ -251,7 +253,7 @@ def accept_sample(logits, draft_logits, draft_tokens, temperature, seeds, rows=N
 
     q = softmax(zr, T)                                   # [R, K+1, V]
     p = softmax(zdr, T) if K else np.zeros((R, 0, V))    # [R, K, V]
-    u, u2 = verify_uniforms(seeds[good][:, None], good[:, None], np.arange(K + 1)[None, :])
+    u, u2 = verify_uniforms(seeds[good][:, None], slot[good][:, None], np.arange(K + 1)[None, :])
     ua[good], ut[good] = u, u2
 
     ri = np.arange(R)[:, None]
@@ -284,6 +286,91 @@ def accept_sample(logits, draft_logits, draft_tokens, temperature, seeds, rows=N
     tm[good] = margin
     zz[good] = Z
     return SampleResult(acc, out, pad, ratio, ua, ut, am, tm, zz, alpha)
+
+
+# ------------------------------------------- per-sequence draft counts ----
+# A drafter may hand back fewer drafts than asked, or none ("Inference-4",
+# Prompt lookup decoding, and the draft count its verification loop caps at
+# the context window), and a scheduler may pick the count per request
+# ("speculative-decoding" blog, DSpark).  Each sequence is then verified on its
+# own, exactly as above with K = K_b.  Rows are packed in sequence order:
+# sequence b owns target rows row_start[b] .. row_start[b] + K_b and draft
+# rows row_start[b] - b .. row_start[b] - b + K_b - 1.
+
+def ragged_sequences(row_start, total_rows: int, K_max: int):
+    """(t0, K_b, well_formed) per sequence.  A sequence is well formed when
+    0 <= K_b <= K_max, its draft rows start at or after row 0, and its last
+    row leaves one row for each later sequence (the entry points' rule)."""
+    rs = np.asarray(row_start, dtype=np.int64).reshape(-1)
+    B = len(rs) - 1
+    out = []
+    for b in range(B):
+        s0, s1 = int(rs[b]), int(rs[b + 1])
+        kb = s1 - s0 - 1
+        ok = 0 <= kb <= K_max and s0 >= b and s1 <= total_rows - (B - 1 - b)
+        out.append((s0, kb, ok))
+    return out
+
+
+def accept_greedy_ragged(logits, draft_tokens, row_start, K_max: int, rows=None) -> GreedyResult:
+    """Greedy verification of a packed batch.  logits [R, V]; draft_tokens
+    [R - B].  Result fields are packed: accepted_len [B] (-1 bad or malformed,
+    -2 not selected), out_tokens / argmax / margin [R]."""
+    z = np.asarray(logits, dtype=np.float64)
+    R, V = z.shape
+    d = np.asarray(draft_tokens if draft_tokens is not None else np.zeros(0), dtype=np.int64).reshape(-1)
+    seqs = ragged_sequences(row_start, R, K_max)
+    B = len(seqs)
+    acc = np.full(B, -2, np.int32)
+    out = np.full(R, -1, np.int32)
+    amax = np.full(R, -1, np.int64)
+    marg = np.full(R, np.inf)
+    for b in _rows_arg(rows, B):
+        t0, kb, ok = seqs[b]
+        if not ok:
+            acc[b] = -1
+            continue
+        g = accept_greedy(z[None, t0:t0 + kb + 1], d[None, t0 - b:t0 - b + kb])
+        acc[b] = g.accepted_len[0]
+        out[t0:t0 + kb + 1] = g.out_tokens[0]
+        amax[t0:t0 + kb + 1] = g.argmax[0]
+        marg[t0:t0 + kb + 1] = g.margin[0]
+    return GreedyResult(acc, out, amax, marg)
+
+
+def accept_sample_ragged(logits, draft_logits, draft_tokens, row_start, K_max: int, temperature, seeds,
+                         rows=None) -> SampleResult:
+    """Speculative sampling of a packed batch, each sequence in its own batch
+    slot b (Philox counter (i, b)).  logits [R, V]; draft_logits [R - B, V];
+    draft_tokens [R - B].  Result fields are packed: accepted_len,
+    terminal_margin, residual_mass [B]; out_tokens, u_accept, u_terminal [R];
+    probs_at_draft [R - B, 2]; ratio, accept_margin, alpha [R - B]."""
+    z = np.asarray(logits, dtype=np.float64)
+    R, V = z.shape
+    seqs = ragged_sequences(row_start, R, K_max)
+    B = len(seqs)
+    zd = np.asarray(draft_logits, dtype=np.float64) if R > B else np.zeros((0, V))
+    d = np.asarray(draft_tokens if draft_tokens is not None else np.zeros(0), dtype=np.int64).reshape(-1)
+    seeds = np.asarray(seeds, dtype=np.uint64).reshape(B)
+    D = R - B
+    res = SampleResult(np.full(B, -2, np.int32), np.full(R, -1, np.int32), np.full((D, 2), np.nan),
+                       np.full(D, np.nan), np.full(R, np.nan), np.full(R, np.nan), np.full(D, np.inf),
+                       np.full(B, np.inf), np.full(B, np.nan), np.full(D, np.nan))
+    for b in _rows_arg(rows, B):
+        t0, kb, ok = seqs[b]
+        if not ok:
+            res.accepted_len[b] = -1
+            continue
+        s = accept_sample(z[None, t0:t0 + kb + 1], zd[None, t0 - b:t0 - b + kb], d[None, t0 - b:t0 - b + kb],
+                          temperature, seeds[b:b + 1], slots=[b])
+        tr, dr = slice(t0, t0 + kb + 1), slice(t0 - b, t0 - b + kb)
+        res.accepted_len[b] = s.accepted_len[0]
+        res.out_tokens[tr] = s.out_tokens[0]
+        res.u_accept[tr], res.u_terminal[tr] = s.u_accept[0], s.u_terminal[0]
+        res.probs_at_draft[dr] = s.probs_at_draft[0]
+        res.ratio[dr], res.accept_margin[dr], res.alpha[dr] = s.ratio[0], s.accept_margin[0], s.alpha[0]
+        res.terminal_margin[b], res.residual_mass[b] = s.terminal_margin[0], s.residual_mass[0]
+    return res
 
 
 # ------------------------------------------------ expected tokens per pass --

@@ -9,6 +9,10 @@ in the library's HIP kernels; if the library is missing, every call raises.
     spec_accept_greedy(logits, draft_tokens, accepted_len, out_tokens, workspace, rows=None)
     spec_accept_sample(logits, draft_logits, draft_tokens, temperature, seeds,
                        accepted_len, out_tokens, workspace, rows=None, probs_at_draft=None)
+    spec_accept_greedy_ragged(logits, draft_tokens, row_start, K_max, accepted_len, out_tokens, workspace,
+                              rows=None)
+    spec_accept_sample_ragged(logits, draft_logits, draft_tokens, row_start, K_max, temperature, seeds,
+                              accepted_len, out_tokens, workspace, rows=None, probs_at_draft=None)
     spec_workspace_bytes(B, K, V)
 """
 from __future__ import annotations
@@ -21,7 +25,7 @@ __all__ = [
     "SpecVerifyError", "SPEC_OK", "SPEC_ERR_ARG", "SPEC_ERR_DTYPE", "SPEC_ERR_ALIGN",
     "SPEC_ERR_WORKSPACE", "SPEC_ERR_HIP", "SPEC_BF16", "SPEC_F32", "LIB_PATH", "HEADER_PATH",
     "load_library", "declared_symbols", "spec_verify_logits", "spec_accept_greedy",
-    "spec_accept_sample", "spec_workspace_bytes", "spec_status_string", "spec_last_error_detail",
+    "spec_accept_sample", "spec_accept_greedy_ragged", "spec_accept_sample_ragged", "spec_workspace_bytes", "spec_status_string", "spec_last_error_detail",
 ]
 
 PKG_DIR = os.path.dirname(os.path.abspath(__file__))
@@ -41,6 +45,11 @@ _SIGNATURES = {
     "spec_accept_sample": (_c_int, [_c_void_p, _c_void_p, _c_void_p, _c_float, _c_void_p, _c_void_p, _c_int, _c_int,
                                     _c_int, _c_int, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_size_t,
                                     _c_void_p]),
+    "spec_accept_greedy_ragged": (_c_int, [_c_void_p, _c_void_p, _c_void_p, _c_int, _c_void_p, _c_int, _c_int, _c_int,
+                                           _c_int, _c_void_p, _c_void_p, _c_void_p, _c_size_t, _c_void_p]),
+    "spec_accept_sample_ragged": (_c_int, [_c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_int, _c_float, _c_void_p,
+                                           _c_void_p, _c_int, _c_int, _c_int, _c_int, _c_void_p, _c_void_p,
+                                           _c_void_p, _c_void_p, _c_size_t, _c_void_p]),
     "spec_workspace_bytes": (_c_size_t, [_c_int, _c_int, _c_int]),
     "spec_status_string": (ctypes.c_char_p, [_c_int]),
     "spec_last_error_detail": (ctypes.c_char_p, []),
@@ -170,3 +179,34 @@ def spec_accept_sample(logits, draft_logits, draft_tokens, temperature, seeds, a
                                   _ptr(rows_t), n_rows, B, P - 1, V, _ptr(accepted_len), _ptr(out_tokens),
                                   _ptr(probs_at_draft), _ptr(workspace),
                                   workspace.numel() * workspace.element_size(), _stream(stream)))
+
+
+def spec_accept_greedy_ragged(logits, draft_tokens, row_start, K_max, accepted_len, out_tokens, workspace, rows=None,
+                              stream=None) -> None:
+    """Greedy acceptance of a ragged batch: logits [R, V] packed by row_start [B+1]."""
+    R, V = logits.shape
+    B = row_start.numel() - 1
+    rows_t, n_rows = _rows(rows)
+    lib = load_library()
+    _check("spec_accept_greedy_ragged",
+           lib.spec_accept_greedy_ragged(_ptr(logits), _ptr(draft_tokens) if R > B else None, _ptr(row_start), R,
+                                         _ptr(rows_t), n_rows, B, int(K_max), V, _ptr(accepted_len),
+                                         _ptr(out_tokens), _ptr(workspace),
+                                         workspace.numel() * workspace.element_size(), _stream(stream)))
+
+
+def spec_accept_sample_ragged(logits, draft_logits, draft_tokens, row_start, K_max, temperature, seeds, accepted_len,
+                              out_tokens, workspace, rows=None, probs_at_draft=None, stream=None) -> None:
+    """Speculative sampling of a ragged batch: logits [R, V], draft_logits [R-B, V]
+    packed by row_start [B+1]."""
+    R, V = logits.shape
+    B = row_start.numel() - 1
+    rows_t, n_rows = _rows(rows)
+    lib = load_library()
+    _check("spec_accept_sample_ragged",
+           lib.spec_accept_sample_ragged(_ptr(logits), _ptr(draft_logits) if R > B else None,
+                                         _ptr(draft_tokens) if R > B else None, _ptr(row_start), R,
+                                         float(temperature), _ptr(seeds), _ptr(rows_t), n_rows, B, int(K_max), V,
+                                         _ptr(accepted_len), _ptr(out_tokens), _ptr(probs_at_draft),
+                                         _ptr(workspace), workspace.numel() * workspace.element_size(),
+                                         _stream(stream)))

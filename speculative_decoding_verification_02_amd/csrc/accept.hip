@@ -3,15 +3,17 @@
 // One workgroup per selected sequence.  The chunk statistics of the
 // sequence's rows are staged in LDS with every load in flight at once and
 // merged row by row, one wavefront per row; then wavefront 0, lane i = verify
-// position i (i <= K <= 63), decides whether draft i would be accepted on its
-// own, and one ballot finds the first rejection:
+// position i (i <= kb <= 63, kb = the sequence's draft count: K in a dense
+// batch, its own K_b in a ragged one), decides whether draft i would be
+// accepted on its own, and one ballot finds the first rejection:
 //   greedy  ("Inference-4", greedy bullet): ok_i = [d_i == argmax_v z_t[i, v]]
 //   sampled (same page, sampling bullet; "speculative-decoding" blog,
 //            Rejection sampling): ok_i = [u_i < min(1, q_i(d_i) / p_i(d_i))]
-// n = index of the first lane i < K with !ok_i, else K.  Drafts before n are
-// committed; greedy rows commit argmax z_t[n] at n (the target's token at the
-// mismatch, or the bonus token when n = K), sampled rows leave position n to
-// the residual kernels, which draw it from norm(max(0, q_n - p_n)) or q_K.
+// n = index of the first lane i < kb with !ok_i, else kb.  Drafts before n
+// are committed; greedy rows commit argmax z_t[n] at n (the target's token at
+// the mismatch, or the bonus token when n = kb), sampled rows leave position
+// n to the residual kernels, which draw it from norm(max(0, q_n - p_n)) or
+// q_kb.
 //
 // The ratio is evaluated in log2 space so tiny probabilities do not underflow:
 //   r = min(1, exp2(lq - lp) * S_d / S_t),  lq = (z_t[d] - M_t) * c, lp = (z_d[d] - M_d) * c
@@ -63,46 +65,57 @@ __device__ __forceinline__ Merged wave_merge(const StatRec* rec, int nc, float c
 template <bool SAMPLED>
 __global__ __launch_bounds__(kAcceptThreads) void accept_kernel(
     const float* __restrict__ logits, const float* __restrict__ draft_logits, const int32_t* __restrict__ draft_tokens,
-    const uint64_t* __restrict__ seeds, const int32_t* __restrict__ rows, int n_rows, int B, int K, int V, int nc,
+    const uint64_t* __restrict__ seeds, const int32_t* __restrict__ rows, int n_rows, SeqRows seq, int V, int nc,
     float c, const StatRec* __restrict__ stats, int32_t* __restrict__ accepted_len, int32_t* __restrict__ out_tokens,
     float* __restrict__ probs_at_draft, AcceptInfo* __restrict__ info, int* __restrict__ counters) {
     __shared__ StatRec recs[kRecBuf];
     __shared__ Merged merged[kMaxRows];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int K = seq.K;
     const int j = blockIdx.x;
     const int b = rows ? rows[j] : j;
     if (SAMPLED && tid == 0) counters[j] = 0;   // the residual kernel counts its chunk blocks from zero
-    if (b < 0 || b >= B) {
-        if (SAMPLED && tid == 0) info[j] = AcceptInfo{-1, b, 0.f, 0.f, 0.f, 0.f, 0.f, 0};
+    if (b < 0 || b >= seq.B) {
+        if (SAMPLED && tid == 0) info[j] = AcceptInfo{-1, b, 0, 0, 0.f, 0.f, 0.f, 0.f, 0.f, {0, 0, 0}};
         return;
     }
+    int t0 = 0, kb = 0;
+    if (!seq.get(b, t0, kb)) {   // malformed row_start: no row of this sequence is touched
+        if (tid == 0) {
+            accepted_len[b] = -1;
+            if (SAMPLED) info[j] = AcceptInfo{-1, b, 0, 0, 0.f, 0.f, 0.f, 0.f, 0.f, {0, 0, 0}};
+        }
+        return;
+    }
+    const size_t d0 = (size_t)(t0 - b);   // first draft row / token of the sequence
 
     // wavefront 0, lane i: the draft token and (sampled) its two logits, loaded
     // up front so the loads overlap the statistics merge
     const int i = lane;
-    const bool active = wave == 0 && i <= K;
-    const bool has_draft = wave == 0 && i < K;
+    const bool active = wave == 0 && i <= kb;
+    const bool has_draft = wave == 0 && i < kb;
     int tok = 0;
     float zt_tok = 0.f, zd_tok = 0.f;
     if (has_draft) {
-        tok = draft_tokens[(size_t)b * K + i];
+        tok = draft_tokens[d0 + i];
         if (SAMPLED && tok >= 0 && tok < V) {
-            zt_tok = logits[((size_t)b * (K + 1) + i) * V + tok];
-            zd_tok = draft_logits[((size_t)b * K + i) * V + tok];
+            zt_tok = logits[((size_t)t0 + i) * V + tok];
+            zd_tok = draft_logits[(d0 + i) * V + tok];
         }
     }
 
-    // rows of this sequence: target 0..K, then (sampled) draft 0..K-1
-    const int n_rows_seq = (K + 1) + (SAMPLED ? K : 0);
+    // rows of this sequence: target 0..kb, then (sampled) draft 0..kb-1; their
+    // records sit at the slots of a K-draft sequence
+    const int n_rows_seq = (kb + 1) + (SAMPLED ? kb : 0);
     const int rows_per_pass = max(1, min(n_rows_seq, kRecBuf / nc));
     for (int r0 = 0; r0 < n_rows_seq; r0 += rows_per_pass) {
         const int nr = min(rows_per_pass, n_rows_seq - r0);
         // stage the records of rows r0 .. r0+nr-1: every load in flight at once
         for (int e = tid; e < nr * nc; e += kAcceptThreads) {
             const int rr = r0 + e / nc, k = e - (e / nc) * nc;
-            const size_t row_rec = rr <= K ? (size_t)j * (K + 1) + rr
-                                           : (size_t)n_rows * (K + 1) + (size_t)j * K + (rr - K - 1);
+            const size_t row_rec = rr <= kb ? (size_t)j * (K + 1) + rr
+                                            : (size_t)n_rows * (K + 1) + (size_t)j * K + (rr - kb - 1);
             recs[e] = stats[row_rec * nc + k];
         }
         __syncthreads();
@@ -123,16 +136,16 @@ __global__ __launch_bounds__(kAcceptThreads) void accept_kernel(
     if (has_draft) {
         bad |= (tok < 0 || tok >= V);
         if (SAMPLED) {
-            d = merged[K + 1 + i];
+            d = merged[kb + 1 + i];
             bad |= d.bad | (d.m == -INFINITY);
         }
     }
-    int32_t* orow = out_tokens + (size_t)b * (K + 1);
+    int32_t* orow = out_tokens + t0;
     if (__ballot(active && bad) != 0ull) {  // data fault anywhere in the sequence
         if (active) orow[i] = -1;
         if (lane == 0) {
             accepted_len[b] = -1;
-            if (SAMPLED) info[j] = AcceptInfo{-1, b, 0.f, 0.f, 0.f, 0.f, 0.f, 0};
+            if (SAMPLED) info[j] = AcceptInfo{-1, b, 0, 0, 0.f, 0.f, 0.f, 0.f, 0.f, {0, 0, 0}};
         }
         return;
     }
@@ -158,7 +171,7 @@ __global__ __launch_bounds__(kAcceptThreads) void accept_kernel(
                     r = fminf(1.f, exp2f(lq - lp) * (d.s / t.s));
                 ok = uniform24(w.x) < r;
                 if (probs_at_draft) {
-                    float* pp = probs_at_draft + ((size_t)b * K + i) * 2;
+                    float* pp = probs_at_draft + (d0 + i) * 2;
                     pp[0] = exp2f(lq) / t.s;
                     pp[1] = exp2f(lp) / d.s;
                 }
@@ -169,7 +182,7 @@ __global__ __launch_bounds__(kAcceptThreads) void accept_kernel(
     }
 
     const unsigned long long rej = __ballot(has_draft && !ok);
-    const int n = rej ? (__ffsll((long long)rej) - 1) : K;
+    const int n = rej ? (__ffsll((long long)rej) - 1) : kb;
     if (active) {
         if (i < n)
             orow[i] = tok;
@@ -180,11 +193,11 @@ __global__ __launch_bounds__(kAcceptThreads) void accept_kernel(
     }
     if (lane == 0) accepted_len[b] = n;
     if (SAMPLED && i == n)
-        info[j] = AcceptInfo{n, b, u_term, t.m, t.s, has_draft ? d.m : 0.f, has_draft ? d.s : 0.f, 0};
+        info[j] = AcceptInfo{n, b, t0, kb, u_term, t.m, t.s, has_draft ? d.m : 0.f, has_draft ? d.s : 0.f, {0, 0, 0}};
 }
 
 hipError_t launch_accept(const float* logits, const float* draft_logits, const int32_t* draft_tokens,
-                         const uint64_t* seeds, const int32_t* rows, int n_rows, int B, int K, int V,
+                         const uint64_t* seeds, const int32_t* rows, int n_rows, SeqRows seq, int V,
                          float inv_t_log2e, bool sampled, const StatRec* stats, int32_t* accepted_len,
                          int32_t* out_tokens, float* probs_at_draft, AcceptInfo* info, int* counters,
                          hipStream_t stream) {
@@ -192,11 +205,11 @@ hipError_t launch_accept(const float* logits, const float* draft_logits, const i
     const int nc = n_chunks(V);
     if (sampled)
         hipLaunchKernelGGL(accept_kernel<true>, dim3(n_rows), dim3(kAcceptThreads), 0, stream, logits, draft_logits,
-                           draft_tokens, seeds, rows, n_rows, B, K, V, nc, inv_t_log2e, stats, accepted_len,
+                           draft_tokens, seeds, rows, n_rows, seq, V, nc, inv_t_log2e, stats, accepted_len,
                            out_tokens, probs_at_draft, info, counters);
     else
         hipLaunchKernelGGL(accept_kernel<false>, dim3(n_rows), dim3(kAcceptThreads), 0, stream, logits, draft_logits,
-                           draft_tokens, seeds, rows, n_rows, B, K, V, nc, inv_t_log2e, stats, accepted_len,
+                           draft_tokens, seeds, rows, n_rows, seq, V, nc, inv_t_log2e, stats, accepted_len,
                            out_tokens, probs_at_draft, info, counters);
     return hipGetLastError();
 }

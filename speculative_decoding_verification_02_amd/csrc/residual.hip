@@ -1,8 +1,8 @@
 // residual.hip -- terminal draw of sampled sequences.
 //
-// After the first rejection at position n < K the replacement token is drawn
-// from norm(max(0, q_n - p_n)); when all K drafts are accepted the bonus token
-// is drawn from q_K ("Inference-4", sampling bullet; "speculative-decoding"
+// After the first rejection at position n < kb (the sequence's draft count)
+// the replacement token is drawn from norm(max(0, q_n - p_n)); when all kb
+// drafts are accepted the bonus token is drawn from q_kb ("Inference-4", sampling bullet; "speculative-decoding"
 // blog, Rejection sampling; "What is speculative decoding" guide, How
 // speculative decoding works).  The draw is an inverse CDF:
 //     t = min{v : C_v > u' * Z},  C_v = w_0 + ... + w_v,  Z = C_{V-1}.
@@ -81,11 +81,11 @@ struct TermRows {
 };
 
 __device__ __forceinline__ TermRows term_rows(const float* logits, const float* draft_logits, const AcceptInfo& a,
-                                              int K, int V) {
+                                              int V) {
     TermRows r;
-    r.bonus = a.n == K;
-    r.zt = logits + ((size_t)a.b * (K + 1) + a.n) * V;
-    r.zd = r.bonus ? r.zt : draft_logits + ((size_t)a.b * K + a.n) * V;
+    r.bonus = a.n == a.kb;
+    r.zt = logits + ((size_t)a.t0 + a.n) * V;
+    r.zd = r.bonus ? r.zt : draft_logits + ((size_t)(a.t0 - a.b) + a.n) * V;
     return r;
 }
 
@@ -116,7 +116,7 @@ __device__ __forceinline__ void chunk_prefix(const float* src, int nc, int lane,
 // Inverse-CDF selection of the terminal token of one sequence, by the block
 // that finished last among the sequence's chunk blocks.  chunk_sums holds the
 // per-chunk weight sums published by all of them (read back with atomics).
-__device__ void select_terminal(const float* __restrict__ logits, const float* __restrict__ draft_logits, int K,
+__device__ void select_terminal(const float* __restrict__ logits, const float* __restrict__ draft_logits,
                                 int V, int nc, float c, const AcceptInfo& a, const float* chunk_sums,
                                 int32_t* __restrict__ out_tokens) {
     __shared__ float pre[kMaxChunks + 1];   // prefix over chunk sums
@@ -126,7 +126,7 @@ __device__ void select_terminal(const float* __restrict__ logits, const float* _
     __shared__ int sel[2];                  // selected chunk, selected token
     __shared__ int redi[kStatThreads / kWave];
 
-    const TermRows tr = term_rows(logits, draft_logits, a, K, V);
+    const TermRows tr = term_rows(logits, draft_logits, a, V);
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const bool vec = (V & 3) == 0;
 
@@ -244,14 +244,14 @@ __device__ void select_terminal(const float* __restrict__ logits, const float* _
         }
         __syncthreads();
     }
-    if (tid == 0) out_tokens[(size_t)a.b * (K + 1) + a.n] = sel[1];
+    if (tid == 0) out_tokens[(size_t)a.t0 + a.n] = sel[1];
 }
 
 // One workgroup per (sampled sequence, chunk): the sum of the terminal weights
 // over the chunk; the last workgroup of a sequence to finish (counted with an
 // atomic; the accept kernel zeroed the counter) then selects the token.
 __global__ __launch_bounds__(kStatThreads) void residual_kernel(
-    const float* __restrict__ logits, const float* __restrict__ draft_logits, int K, int V, int nc, float c,
+    const float* __restrict__ logits, const float* __restrict__ draft_logits, int V, int nc, float c,
     const AcceptInfo* __restrict__ info, float* __restrict__ chunk_sums, int* __restrict__ counters,
     int32_t* __restrict__ out_tokens) {
     __shared__ float red[kStatThreads / kWave];
@@ -260,7 +260,7 @@ __global__ __launch_bounds__(kStatThreads) void residual_kernel(
     const int chunk = blockIdx.x - j * nc;
     const AcceptInfo a = info[j];
     if (a.n < 0) return;
-    const TermRows tr = term_rows(logits, draft_logits, a, K, V);
+    const TermRows tr = term_rows(logits, draft_logits, a, V);
     float w[kStatPerThread];
     chunk_weights(tr.zt, tr.zd, chunk * kChunk, V, (V & 3) == 0, threadIdx.x, a, c, tr.bonus, w);
     float s = 0.f;
@@ -281,16 +281,16 @@ __global__ __launch_bounds__(kStatThreads) void residual_kernel(
     }
     __syncthreads();
     if (!last) return;
-    select_terminal(logits, draft_logits, K, V, nc, c, a, chunk_sums + (size_t)j * nc, out_tokens);
+    select_terminal(logits, draft_logits, V, nc, c, a, chunk_sums + (size_t)j * nc, out_tokens);
 }
 
-hipError_t launch_residual(const float* logits, const float* draft_logits, int n_rows, int K, int V,
+hipError_t launch_residual(const float* logits, const float* draft_logits, int n_rows, int V,
                            float inv_t_log2e, const AcceptInfo* info, float* chunk_sums, int* counters,
                            int32_t* out_tokens, hipStream_t stream) {
     if (n_rows == 0) return hipSuccess;
     const int nc = n_chunks(V);
     hipLaunchKernelGGL(residual_kernel, dim3((unsigned)((long)n_rows * nc)), dim3(kStatThreads), 0, stream, logits,
-                       draft_logits, K, V, nc, inv_t_log2e, info, chunk_sums, counters, out_tokens);
+                       draft_logits, V, nc, inv_t_log2e, info, chunk_sums, counters, out_tokens);
     return hipGetLastError();
 }
 

@@ -47,31 +47,35 @@ __device__ __forceinline__ int chunk_index(int v_begin, int tid, int k) {
 template <bool NEED_SUM>
 __global__ __launch_bounds__(kStatThreads) void softmax_stats_kernel(
     const float* __restrict__ logits, const float* __restrict__ draft_logits, const int32_t* __restrict__ rows,
-    int n_rows, int B, int K, int V, int nc, float c, StatRec* __restrict__ stats) {
+    int n_rows, SeqRows seq, int V, int nc, float c, StatRec* __restrict__ stats) {
     __shared__ float sm[kStatThreads / kWave];
     __shared__ int si[kStatThreads / kWave];
     __shared__ int sb[kStatThreads / kWave];
 
+    const int K = seq.K;
     const int job = blockIdx.x / nc;
     const int chunk = blockIdx.x - job * nc;
     const int tgt_jobs = n_rows * (K + 1);
-    const float* row;
-    int b;
-    if (job < tgt_jobs) {
-        const int j = job / (K + 1), i = job - j * (K + 1);
-        b = rows ? rows[j] : j;
-        row = logits + ((size_t)b * (K + 1) + i) * V;
+    const bool target = job < tgt_jobs;
+    int j, i;
+    if (target) {
+        j = job / (K + 1);
+        i = job - j * (K + 1);
     } else {
         const int jj = job - tgt_jobs;
-        const int j = jj / K, i = jj - j * K;
-        b = rows ? rows[j] : j;
-        row = draft_logits + ((size_t)b * K + i) * V;
+        j = jj / K;
+        i = jj - j * K;
     }
+    const int b = rows ? rows[j] : j;
     const int tid = threadIdx.x;
-    if (b < 0 || b >= B) {  // skipped sequence: the accept kernel ignores it
+    int t0 = 0, kb = -1;
+    // skipped sequence, malformed row_start, or a position past this
+    // sequence's drafts: the accept kernel never reads the record
+    if (b < 0 || b >= seq.B || !seq.get(b, t0, kb) || (target ? i > kb : i >= kb)) {
         if (tid == 0) stats[blockIdx.x] = StatRec{-INFINITY, 0.f, INT_MAX, 0};
         return;
     }
+    const float* row = target ? logits + ((size_t)t0 + i) * V : draft_logits + ((size_t)(t0 - b) + i) * V;
 
     const int v_begin = chunk * kChunk;
     float x[kStatPerThread];
@@ -127,18 +131,18 @@ __global__ __launch_bounds__(kStatThreads) void softmax_stats_kernel(
 }
 
 hipError_t launch_softmax_stats(const float* logits, const float* draft_logits, const int32_t* rows, int n_rows,
-                                int B, int K, int V, float inv_t_log2e, bool need_sum, StatRec* stats,
+                                SeqRows seq, int V, float inv_t_log2e, bool need_sum, StatRec* stats,
                                 hipStream_t stream) {
     const int nc = n_chunks(V);
-    const long jobs = (long)n_rows * (K + 1) + (draft_logits ? (long)n_rows * K : 0);
+    const long jobs = (long)n_rows * (seq.K + 1) + (draft_logits ? (long)n_rows * seq.K : 0);
     const long blocks = jobs * nc;
     if (blocks == 0) return hipSuccess;
     if (need_sum)
         hipLaunchKernelGGL(softmax_stats_kernel<true>, dim3((unsigned)blocks), dim3(kStatThreads), 0, stream, logits,
-                           draft_logits, rows, n_rows, B, K, V, nc, inv_t_log2e, stats);
+                           draft_logits, rows, n_rows, seq, V, nc, inv_t_log2e, stats);
     else
         hipLaunchKernelGGL(softmax_stats_kernel<false>, dim3((unsigned)blocks), dim3(kStatThreads), 0, stream,
-                           logits, draft_logits, rows, n_rows, B, K, V, nc, inv_t_log2e, stats);
+                           logits, draft_logits, rows, n_rows, seq, V, nc, inv_t_log2e, stats);
     return hipGetLastError();
 }
 

@@ -85,17 +85,74 @@ size_t workspace_layout(int B, int K, int V, void* base, Workspace* ws) {
 }
 
 spec_status_t check_accept_common(const float* logits, const int32_t* draft_tokens, const int32_t* rows,
-                                  int n_rows, int B, int K, int V, const int32_t* accepted_len,
+                                  int n_rows, int B, int K, int V, bool has_drafts, const int32_t* accepted_len,
                                   const int32_t* out_tokens, void* workspace, size_t workspace_bytes) {
     if (!sizes_ok(B, K, V)) return SPEC_ERR_ARG;
     if (!logits || !accepted_len || !out_tokens) return SPEC_ERR_ARG;
-    if (K > 0 && !draft_tokens) return SPEC_ERR_ARG;
+    if (has_drafts && !draft_tokens) return SPEC_ERR_ARG;
     if (rows && (n_rows < 0 || n_rows > B)) return SPEC_ERR_ARG;
     if (!aligned16(logits)) return SPEC_ERR_ALIGN;
     if (!workspace || workspace_bytes < workspace_layout(B, K, V, nullptr, nullptr)) return SPEC_ERR_WORKSPACE;
     if (!aligned16(workspace)) return SPEC_ERR_ALIGN;
     return SPEC_OK;
 }
+
+// ragged batches: row_start[B+1] on the device, total target rows declared by
+// the caller (B <= total <= B*(K_max+1))
+spec_status_t check_ragged(const int32_t* row_start, int total_rows, int B, int K) {
+    if (!row_start) return SPEC_ERR_ARG;
+    if ((reinterpret_cast<uintptr_t>(row_start) & 3u) != 0) return SPEC_ERR_ALIGN;
+    if (B < 1 || total_rows < B || (long long)total_rows > (long long)B * (K + 1)) return SPEC_ERR_ARG;
+    return SPEC_OK;
+}
+
+spec_status_t greedy_impl(const float* logits, const int32_t* draft_tokens, const int32_t* rows, int n_rows,
+                          sv::SeqRows seq, int V, int32_t* accepted_len, int32_t* out_tokens, void* workspace,
+                          size_t workspace_bytes, hipStream_t s) {
+    const bool has_drafts = seq.total > seq.B;
+    spec_status_t st = check_accept_common(logits, draft_tokens, rows, n_rows, seq.B, seq.K, V, has_drafts,
+                                           accepted_len, out_tokens, workspace, workspace_bytes);
+    if (st != SPEC_OK) return st;
+    const int nr = rows ? n_rows : seq.B;
+    if (nr == 0) return SPEC_OK;
+    Workspace ws;
+    workspace_layout(seq.B, seq.K, V, workspace, &ws);
+    hipError_t e = sv::launch_softmax_stats(logits, nullptr, rows, nr, seq, V, sv::kLog2e, false, ws.stats, s);
+    if (e == hipSuccess)
+        e = sv::launch_accept(logits, nullptr, draft_tokens, nullptr, rows, nr, seq, V, sv::kLog2e, false, ws.stats,
+                              accepted_len, out_tokens, nullptr, ws.info, ws.counters, s);
+    return e == hipSuccess ? SPEC_OK : hip_fail(e);
+}
+
+spec_status_t sample_impl(const float* logits, const float* draft_logits, const int32_t* draft_tokens,
+                          float temperature, const uint64_t* seeds, const int32_t* rows, int n_rows, sv::SeqRows seq,
+                          int V, int32_t* accepted_len, int32_t* out_tokens, float* probs_at_draft, void* workspace,
+                          size_t workspace_bytes, hipStream_t s) {
+    const bool has_drafts = seq.total > seq.B;
+    spec_status_t st = check_accept_common(logits, draft_tokens, rows, n_rows, seq.B, seq.K, V, has_drafts,
+                                           accepted_len, out_tokens, workspace, workspace_bytes);
+    if (st != SPEC_OK) return st;
+    if (!seeds) return SPEC_ERR_ARG;
+    if (has_drafts && !draft_logits) return SPEC_ERR_ARG;
+    if (!(temperature > 0.f) || !isfinite(temperature)) return SPEC_ERR_ARG;
+    if (has_drafts && !aligned16(draft_logits)) return SPEC_ERR_ALIGN;
+    const int nr = rows ? n_rows : seq.B;
+    if (nr == 0) return SPEC_OK;
+    Workspace ws;
+    workspace_layout(seq.B, seq.K, V, workspace, &ws);
+    const float c = sv::kLog2e / temperature;
+    const float* dl = has_drafts ? draft_logits : nullptr;
+    hipError_t e = sv::launch_softmax_stats(logits, dl, rows, nr, seq, V, c, true, ws.stats, s);
+    if (e == hipSuccess)
+        e = sv::launch_accept(logits, dl, draft_tokens, seeds, rows, nr, seq, V, c, true, ws.stats, accepted_len,
+                              out_tokens, probs_at_draft, ws.info, ws.counters, s);
+    if (e == hipSuccess) e = sv::launch_residual(logits, dl, nr, V, c, ws.info, ws.sums, ws.counters, out_tokens, s);
+    return e == hipSuccess ? SPEC_OK : hip_fail(e);
+}
+
+// dense batch: sequence b owns target rows b*(K+1) .. b*(K+1)+K (sizes_ok has
+// bounded B*(K+1) to 31 bits)
+sv::SeqRows dense_rows(int B, int K) { return sv::SeqRows{nullptr, B, K, B * (K + 1)}; }
 
 }  // namespace
 
@@ -127,46 +184,43 @@ spec_status_t spec_verify_logits(const void* hidden, const void* w_lmhead, spec_
 spec_status_t spec_accept_greedy(const float* logits, const int32_t* draft_tokens, const int32_t* rows, int n_rows,
                                  int B, int K, int V, int32_t* accepted_len, int32_t* out_tokens, void* workspace,
                                  size_t workspace_bytes, spec_stream_t stream) {
-    spec_status_t st = check_accept_common(logits, draft_tokens, rows, n_rows, B, K, V, accepted_len, out_tokens,
-                                           workspace, workspace_bytes);
-    if (st != SPEC_OK) return st;
-    const int nr = rows ? n_rows : B;
-    if (nr == 0) return SPEC_OK;
-    Workspace ws;
-    workspace_layout(B, K, V, workspace, &ws);
-    hipStream_t s = static_cast<hipStream_t>(stream);
-    hipError_t e = sv::launch_softmax_stats(logits, nullptr, rows, nr, B, K, V, sv::kLog2e, false, ws.stats, s);
-    if (e == hipSuccess)
-        e = sv::launch_accept(logits, nullptr, draft_tokens, nullptr, rows, nr, B, K, V, sv::kLog2e, false, ws.stats,
-                              accepted_len, out_tokens, nullptr, ws.info, ws.counters, s);
-    return e == hipSuccess ? SPEC_OK : hip_fail(e);
+    if (!sizes_ok(B, K, V)) return SPEC_ERR_ARG;
+    return greedy_impl(logits, draft_tokens, rows, n_rows, dense_rows(B, K), V, accepted_len, out_tokens, workspace,
+                       workspace_bytes, static_cast<hipStream_t>(stream));
 }
 
 spec_status_t spec_accept_sample(const float* logits, const float* draft_logits, const int32_t* draft_tokens,
                                  float temperature, const uint64_t* seeds, const int32_t* rows, int n_rows, int B,
                                  int K, int V, int32_t* accepted_len, int32_t* out_tokens, float* probs_at_draft,
                                  void* workspace, size_t workspace_bytes, spec_stream_t stream) {
-    spec_status_t st = check_accept_common(logits, draft_tokens, rows, n_rows, B, K, V, accepted_len, out_tokens,
-                                           workspace, workspace_bytes);
+    if (!sizes_ok(B, K, V)) return SPEC_ERR_ARG;
+    return sample_impl(logits, draft_logits, draft_tokens, temperature, seeds, rows, n_rows, dense_rows(B, K), V,
+                       accepted_len, out_tokens, probs_at_draft, workspace, workspace_bytes,
+                       static_cast<hipStream_t>(stream));
+}
+
+spec_status_t spec_accept_greedy_ragged(const float* logits, const int32_t* draft_tokens, const int32_t* row_start,
+                                        int total_rows, const int32_t* rows, int n_rows, int B, int K_max, int V,
+                                        int32_t* accepted_len, int32_t* out_tokens, void* workspace,
+                                        size_t workspace_bytes, spec_stream_t stream) {
+    if (!sizes_ok(B, K_max, V)) return SPEC_ERR_ARG;
+    spec_status_t st = check_ragged(row_start, total_rows, B, K_max);
     if (st != SPEC_OK) return st;
-    if (!seeds) return SPEC_ERR_ARG;
-    if (K > 0 && !draft_logits) return SPEC_ERR_ARG;
-    if (!(temperature > 0.f) || !isfinite(temperature)) return SPEC_ERR_ARG;
-    if (K > 0 && !aligned16(draft_logits)) return SPEC_ERR_ALIGN;
-    const int nr = rows ? n_rows : B;
-    if (nr == 0) return SPEC_OK;
-    Workspace ws;
-    workspace_layout(B, K, V, workspace, &ws);
-    const float c = sv::kLog2e / temperature;
-    hipStream_t s = static_cast<hipStream_t>(stream);
-    const float* dl = K > 0 ? draft_logits : nullptr;
-    hipError_t e = sv::launch_softmax_stats(logits, dl, rows, nr, B, K, V, c, true, ws.stats, s);
-    if (e == hipSuccess)
-        e = sv::launch_accept(logits, dl, draft_tokens, seeds, rows, nr, B, K, V, c, true, ws.stats, accepted_len,
-                              out_tokens, probs_at_draft, ws.info, ws.counters, s);
-    if (e == hipSuccess)
-        e = sv::launch_residual(logits, dl, nr, K, V, c, ws.info, ws.sums, ws.counters, out_tokens, s);
-    return e == hipSuccess ? SPEC_OK : hip_fail(e);
+    return greedy_impl(logits, draft_tokens, rows, n_rows, sv::SeqRows{row_start, B, K_max, total_rows}, V,
+                       accepted_len, out_tokens, workspace, workspace_bytes, static_cast<hipStream_t>(stream));
+}
+
+spec_status_t spec_accept_sample_ragged(const float* logits, const float* draft_logits, const int32_t* draft_tokens,
+                                        const int32_t* row_start, int total_rows, float temperature,
+                                        const uint64_t* seeds, const int32_t* rows, int n_rows, int B, int K_max,
+                                        int V, int32_t* accepted_len, int32_t* out_tokens, float* probs_at_draft,
+                                        void* workspace, size_t workspace_bytes, spec_stream_t stream) {
+    if (!sizes_ok(B, K_max, V)) return SPEC_ERR_ARG;
+    spec_status_t st = check_ragged(row_start, total_rows, B, K_max);
+    if (st != SPEC_OK) return st;
+    return sample_impl(logits, draft_logits, draft_tokens, temperature, seeds, rows, n_rows,
+                       sv::SeqRows{row_start, B, K_max, total_rows}, V, accepted_len, out_tokens, probs_at_draft,
+                       workspace, workspace_bytes, static_cast<hipStream_t>(stream));
 }
 
 size_t spec_workspace_bytes(int B, int K, int V) {

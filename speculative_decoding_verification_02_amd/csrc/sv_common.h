@@ -12,7 +12,7 @@ namespace sv {
 constexpr int kWave = 64;
 // Softmax statistics and residual sums split each vocabulary row into fixed
 // chunks; one workgroup of kStatThreads threads owns a chunk, each thread
-// kStatPerThread consecutive... elements (see the kernels for the order).
+// kStatPerThread of its elements (see the kernels for the order).
 constexpr int kStatThreads = 256;
 constexpr int kStatPerThread = 16;
 constexpr int kChunk = kStatThreads * kStatPerThread;  // 4096 logits per chunk
@@ -32,18 +32,49 @@ struct __align__(16) StatRec {
 };
 
 // What the accept kernel hands to the residual kernels for one sampled
-// sequence: terminal position n (-1 = sequence faulted or skipped), the
-// terminal uniform, and the merged statistics of the terminal target row and
-// (if n < K) draft row.
+// sequence: terminal position n (-1 = sequence faulted or skipped), its batch
+// slot b, first target row t0 and draft count kb, the terminal uniform, and
+// the merged statistics of the terminal target row and (if n < kb) draft row.
 struct __align__(16) AcceptInfo {
     int n;
     int b;
+    int t0;
+    int kb;
     float u_term;
     float mt;
     float st;
     float md;
     float sd;
-    int pad;
+    int pad[3];
+};
+
+// Where the verify rows of sequence b sit.  Rows of all sequences are packed
+// in sequence order: target rows t0 .. t0+kb of sequence b, and its draft
+// rows / tokens t0-b .. t0-b+kb-1 (sequence b' < b contributes kb'+1 target
+// rows and kb' drafts).  Dense batches (row_start == nullptr) have
+// t0 = b*(K+1) and kb = K; ragged ones read row_start[b], row_start[b+1] and
+// K bounds every kb.  get() rejects a sequence whose entries would put any of
+// its rows outside the total / total-B rows the caller declared, so a
+// malformed row_start faults only the sequences it names.
+struct SeqRows {
+    const int32_t* row_start;
+    int B;
+    int K;
+    int total;
+
+    __device__ __forceinline__ bool get(int b, int& t0, int& kb) const {
+        if (!row_start) {
+            t0 = b * (K + 1);
+            kb = K;
+            return true;
+        }
+        const long long s0 = row_start[b], s1 = row_start[b + 1];
+        const long long k = s1 - s0 - 1;
+        if (k < 0 || k > K || s0 < b || s1 > (long long)total - (B - 1 - b)) return false;
+        t0 = (int)s0;
+        kb = (int)k;
+        return true;
+    }
 };
 
 // ---------------------------------------------------------- reductions ----

@@ -10,7 +10,7 @@
 namespace sv {
 
 // LM-head contraction.  force_kernel: 0 = pick by shape, 1 = small-M
-// streaming kernel, 2 = LDS-tiled kernel (used by tests to cover both).
+// streaming kernel, 2 = LDS-tiled kernel.
 hipError_t launch_lmhead_bf16(const uint16_t* hidden, const uint16_t* W, float* logits, int M, int V, int H,
                               int num_cus, hipStream_t stream, int force_kernel);
 hipError_t launch_lmhead_f32(const float* hidden, const float* W, float* logits, int M, int V, int H,
@@ -18,22 +18,23 @@ hipError_t launch_lmhead_f32(const float* hidden, const float* W, float* logits,
 bool skinny_fits(int M, int H);
 
 // Softmax statistics of the rows the accept step needs, per chunk.
-//   jobs = n_rows*(K+1) target rows, then (if draft_logits) n_rows*K draft rows.
+//   jobs = n_rows*(K+1) target slots, then (if draft_logits) n_rows*K draft
+//   slots, K = seq.K; slots past a ragged sequence's own rows are skipped.
 hipError_t launch_softmax_stats(const float* logits, const float* draft_logits, const int32_t* rows, int n_rows,
-                                int B, int K, int V, float inv_t_log2e, bool need_sum, StatRec* stats,
+                                SeqRows seq, int V, float inv_t_log2e, bool need_sum, StatRec* stats,
                                 hipStream_t stream);
 
 // Greedy or sampled acceptance: one workgroup per selected sequence.  The
 // sampled variant also zeroes the sequence's residual counter.
 hipError_t launch_accept(const float* logits, const float* draft_logits, const int32_t* draft_tokens,
-                         const uint64_t* seeds, const int32_t* rows, int n_rows, int B, int K, int V,
+                         const uint64_t* seeds, const int32_t* rows, int n_rows, SeqRows seq, int V,
                          float inv_t_log2e, bool sampled, const StatRec* stats, int32_t* accepted_len,
                          int32_t* out_tokens, float* probs_at_draft, AcceptInfo* info, int* counters,
                          hipStream_t stream);
 
 // Residual / bonus draw of the sampled sequences: per-chunk weight sums, and
 // the inverse-CDF selection of the terminal token by the last chunk block.
-hipError_t launch_residual(const float* logits, const float* draft_logits, int n_rows, int K, int V,
+hipError_t launch_residual(const float* logits, const float* draft_logits, int n_rows, int V,
                            float inv_t_log2e, const AcceptInfo* info, float* chunk_sums, int* counters,
                            int32_t* out_tokens, hipStream_t stream);
 

@@ -29,6 +29,7 @@ import torch
 __all__ = [
     "Workload", "WORKLOADS", "weights", "hidden_states", "base_logits",
     "draft_logits", "sampled_mask", "draft_tokens", "seeds", "round_inputs",
+    "draft_counts", "row_start", "pack_rows",
 ]
 
 
@@ -55,6 +56,7 @@ class Workload:
     zipf_s: float = 1.1               # "zipf": p_d ∝ q_t * rank^-s
     modes: str = "sample"      # "sample" | "greedy" | "both" | "half" | "bernoulli"
     data_seed: int = 1000
+    ragged: bool = False       # per-sequence draft counts K_b ~ U{0..K}, rows packed
     note: str = field(default="", compare=False)
 
     @property
@@ -90,6 +92,13 @@ WORKLOADS = {
         "b512_k3_h5120_v262144", B=512, K=3, H=5120, V=262144, dtype="bf16",
         w_std=0.02, temperature=1.0, draft="zipf", modes="bernoulli",
         data_seed=1004),
+    # per-sequence draft counts (not one of the five benchmark workloads): the
+    # 64-sequence mixed batch with K_b drawn uniformly from 0..7
+    "b64_k0to7_h4096_v128256": Workload(
+        "b64_k0to7_h4096_v128256", B=64, K=7, H=4096, V=128256, dtype="bf16",
+        w_std=0.02, temperature=0.8, draft="additive", draft_sigma=(0.0, 2.0),
+        modes="half", data_seed=1005, ragged=True,
+        note="K_b ~ U{0..7}, packed rows; rows 0..31 greedy, 32..63 sampled at T=0.8"),
 }
 
 
@@ -222,3 +231,27 @@ def round_inputs(wl: Workload, rnd: int = 0, device="cpu", W: torch.Tensor | Non
     return dict(W=W, hidden=hidden, draft_logits=zd, sampled=smask, drafts=d,
                 seeds=seeds(wl, rnd), temperature=wl.temperature)
 
+
+
+# ------------------------------------------------ per-sequence draft counts --
+
+def draft_counts(B: int, K_max: int, seed: int) -> np.ndarray:
+    """Per-sequence draft counts K_b ~ U{0..K_max}, int32 [B]."""
+    return np.random.default_rng(seed).integers(0, K_max + 1, B).astype(np.int32)
+
+
+def row_start(counts) -> np.ndarray:
+    """Packing offsets [B+1] int32: row_start[0] = 0, row_start[b+1] =
+    row_start[b] + K_b + 1 (target rows of sequence b)."""
+    c = np.asarray(counts, dtype=np.int64)
+    return np.concatenate([[0], np.cumsum(c + 1)]).astype(np.int32)
+
+
+def pack_rows(dense, counts, drafts: bool = False):
+    """Concatenate, in sequence order, the first K_b + 1 (target rows) or K_b
+    (``drafts``) entries along axis 1 of a dense [B, P, ...] array or tensor."""
+    keep = [int(k) + (0 if drafts else 1) for k in np.asarray(counts)]
+    parts = [dense[b, :keep[b]] for b in range(len(keep))]
+    if isinstance(dense, torch.Tensor):
+        return torch.cat(parts, dim=0) if parts else dense.reshape(0, *dense.shape[2:])
+    return np.concatenate(parts, axis=0)

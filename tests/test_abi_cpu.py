@@ -27,6 +27,7 @@ def lib():
 def test_exports_every_declared_symbol(lib):
     names = sv.declared_symbols()
     assert set(names) == {"spec_verify_logits", "spec_accept_greedy", "spec_accept_sample",
+                          "spec_accept_greedy_ragged", "spec_accept_sample_ragged",
                           "spec_workspace_bytes", "spec_status_string", "spec_last_error_detail"}
     for n in names:
         assert hasattr(lib, n), n
@@ -112,6 +113,34 @@ def test_accept_sample_validation(lib):
     assert _sample(lib, logits=MIS) == sv.SPEC_ERR_ALIGN
     assert _sample(lib, wsb=16) == sv.SPEC_ERR_WORKSPACE
     assert _sample(lib, B=1, rows=A, n_rows=2) == sv.SPEC_ERR_ARG
+
+
+def _greedy_ragged(lib, rs=A, total=5, B=2, K=3, V=100, drafts=A, rows=None, n_rows=0, wsb=None):
+    if wsb is None:
+        wsb = sv.spec_workspace_bytes(B, K, V) or (1 << 20)
+    return lib.spec_accept_greedy_ragged(A, drafts, rs, total, rows, n_rows, B, K, V, A, A, A, wsb, None)
+
+
+def _sample_ragged(lib, rs=A, total=5, B=2, K=3, V=100, dl=A, drafts=A, T=1.0, rows=None, n_rows=0):
+    wsb = sv.spec_workspace_bytes(B, K, V) or (1 << 20)
+    return lib.spec_accept_sample_ragged(A, dl, drafts, rs, total, T, A, rows, n_rows, B, K, V, A, A, None, A, wsb,
+                                         None)
+
+
+def test_ragged_validation(lib):
+    for f in (_greedy_ragged, _sample_ragged):
+        assert f(lib, rs=None) == sv.SPEC_ERR_ARG
+        assert f(lib, rs=P(0x10002)) == sv.SPEC_ERR_ALIGN             # int32 offsets: 4-byte aligned
+        assert f(lib, total=1) == sv.SPEC_ERR_ARG                     # fewer rows than sequences
+        assert f(lib, total=9) == sv.SPEC_ERR_ARG                     # more than B*(K_max+1)
+        assert f(lib, K=64, total=5) == sv.SPEC_ERR_ARG
+        assert f(lib, drafts=None) == sv.SPEC_ERR_ARG                 # total > B: there are drafts
+        assert f(lib, rows=A, n_rows=0) == sv.SPEC_OK                 # nothing selected: no-op
+        assert f(lib, total=2, drafts=None, rows=A, n_rows=0) == sv.SPEC_OK   # no drafts at all
+    assert _sample_ragged(lib, dl=None) == sv.SPEC_ERR_ARG
+    assert _sample_ragged(lib, dl=MIS) == sv.SPEC_ERR_ALIGN
+    assert _sample_ragged(lib, T=0.0) == sv.SPEC_ERR_ARG
+    assert _greedy_ragged(lib, wsb=16) == sv.SPEC_ERR_WORKSPACE
 
 
 def test_zero_selected_rows_is_a_no_op(lib):
