@@ -172,6 +172,17 @@ def main():
     n_sets = 16
     drafts = [synth.draft_tokens(zd, smask, T, seed=wl.data_seed * 104729 + r) for r in range(n_sets)]
     row_start = None
+    tree = None
+    if wl.tree:
+        # draft trees of K nodes: parents fixed, node tokens redrawn per set
+        par = synth.tree_parents(B, K, seed=wl.data_seed)
+        base = synth.base_logits(hidden, W)
+        tree = (torch.as_tensor(par, device=dev),
+                [synth.tree_tokens(base, par, seed=wl.data_seed + 1 + r, sigma=wl.draft_sigma[0]).to(dev)
+                 for r in range(n_sets)],
+                torch.empty((B, K + 1), dtype=torch.int32, device=dev))
+        drafts = [t.cpu() for t in tree[1]]
+        del base
     if wl.ragged:
         # per-sequence draft counts: pack every input, K is the bound K_max
         counts = synth.draft_counts(B, K, wl.data_seed)
@@ -196,7 +207,10 @@ def main():
     def step(r):
         sv.spec_verify_logits(hidden, W, logits, stream=stream)
         d = drafts[r % n_sets]
-        if row_start is not None:
+        if tree is not None:
+            sv.spec_tree_accept_greedy(logits, tree[0], tree[1][r % n_sets], acc, out, ws, out_nodes=tree[2],
+                                       stream=stream)
+        elif row_start is not None:
             lg, o = logits.view(M, V), out.view(M)
             if len(greedy_rows):
                 sv.spec_accept_greedy_ragged(lg, d, row_start, K, acc, o, ws, rows=greedy_rows, stream=stream)
@@ -291,6 +305,7 @@ def main():
         "config": {"workload": wl.name, "B": B, "K": K, "H": H, "V": V, "temperature": T,
                    "sampled_rows": int(smask.sum()), "greedy_rows": int((~smask).sum())},
         **({"verify_rows": M, "draft_counts": "K_b ~ U{0..%d}, packed" % K} if row_start is not None else {}),
+        **({"tree_nodes": K, "mean_kept_depth": float(np.mean(accepted))} if tree is not None else {}),
         "verify_step_us": step_s * 1e6,
         "committed_tokens_per_step_last": float(np.mean(accepted + 1)),
         "roofline": roof,
@@ -298,11 +313,12 @@ def main():
 
     if not args.no_cpu_baseline:
         rs_np = None if row_start is None else row_start.cpu().numpy()
-        res["cpu_baseline"] = cpu_baseline(wl, W, hidden, zd, drafts, smask, args.cpu_seconds, rs_np)
+        par_np = None if tree is None else tree[0].cpu().numpy()
+        res["cpu_baseline"] = cpu_baseline(wl, W, hidden, zd, drafts, smask, args.cpu_seconds, rs_np, par_np)
     print(json.dumps(res), flush=True)
 
 
-def cpu_baseline(wl, W, hidden, zd, drafts, smask, budget_s, rs=None):
+def cpu_baseline(wl, W, hidden, zd, drafts, smask, budget_s, rs=None, parents=None):
     """The oracle, as it stands, timed on this host on the same inputs: whole
     verify steps (fp64 logits of all K+1 positions + acceptance) until about
     budget_s seconds have been spent (at least one step)."""
@@ -332,7 +348,9 @@ def cpu_baseline(wl, W, hidden, zd, drafts, smask, budget_s, rs=None):
             t0 = time.perf_counter()
             z = oracle.lm_head_logits(h64, w64)
             d = ds[r % len(ds)]
-            if rs is not None:
+            if parents is not None:
+                oracle.tree_accept_greedy(z.reshape(wl.B, wl.K + 1, wl.V), parents, d)
+            elif rs is not None:
                 if len(g_rows):
                     oracle.accept_greedy_ragged(z, d, rs, wl.K, rows=g_rows)
                 if len(s_rows):

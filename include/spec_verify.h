@@ -37,6 +37,13 @@
  *                          confidence-scheduled verification) or shorten them
  *                          under load ("Speculative decoding" course page, Why
  *                          engines disable speculation under load).
+ *   spec_tree_accept_greedy
+ *                       -- greedy verification of a draft tree: keep the
+ *                          longest root-to-node path the target agrees with
+ *                          ("Inference-4", Medusa; "speculative-decoding"
+ *                          blog, Medusa and EAGLE-2; "Speculative decoding"
+ *                          course page, One pass, many candidate
+ *                          continuations).
  *
  * Conventions shared by every entry point
  *   - Every pointer argument is DEVICE memory on the current HIP device, owned
@@ -229,6 +236,44 @@ spec_status_t spec_accept_sample_ragged(const float* logits, const float* draft_
                                         float* probs_at_draft,
                                         void* workspace, size_t workspace_bytes,
                                         spec_stream_t stream);
+
+/*
+ * spec_tree_accept_greedy -- greedy verification of draft trees.
+ *
+ * Each sequence carries a tree of N draft nodes (0 <= N <= 63) in
+ * topological order: node 0 is the root (the last accepted token), node
+ * v >= 1 holds token d_v and has parent p_v with 0 <= p_v < v.  Row v of the
+ * sequence's logits is the target's prediction after the path root -> v (the
+ * verify pass runs every node under a mask that lets it see only its
+ * ancestors; spec_verify_logits with K = N computes the rows from the hidden
+ * states of such a pass).  With a_u = argmax_v logits[b, u, v] (lowest index
+ * on ties): node v is accepted iff its parent is and d_v == a_{p_v}; the root
+ * is.  The kept node k is the deepest accepted node, the lowest index among
+ * equally deep ones; n = its depth.  Then accepted_len[b] = n, out_tokens[b,
+ * :] = (the tokens on the path root -> k, a_k, -1, ...) and out_nodes[b, :] =
+ * (the node indices on that path, -1, ...): the caller keeps the cache
+ * entries of exactly those nodes.  A chain (p_v = v - 1) is the linear
+ * greedy rule of spec_accept_greedy.
+ *
+ *   logits        device, [B, N+1, V] fp32, 16-byte aligned
+ *   parents       device, [B, N+1] int32 (entry 0 ignored; NULL when N == 0)
+ *   tokens        device, [B, N+1] int32 (entry 0 ignored; NULL when N == 0)
+ *   rows, n_rows  as in spec_accept_greedy
+ *   accepted_len  device, [B] int32
+ *   out_tokens    device, [B, N+1] int32
+ *   out_nodes     device, [B, N+1] int32, or NULL
+ *   workspace     at least spec_workspace_bytes(B, N, V) bytes
+ * Data faults (a parent outside [0, v), a token outside [0, V), a NaN or
+ * +inf logit or a row with no finite entry anywhere in the tree) give
+ * accepted_len[b] = -1 and rows of -1.
+ */
+spec_status_t spec_tree_accept_greedy(const float* logits, const int32_t* parents,
+                                      const int32_t* tokens, const int32_t* rows, int n_rows,
+                                      int B, int N, int V,
+                                      int32_t* accepted_len, int32_t* out_tokens,
+                                      int32_t* out_nodes,
+                                      void* workspace, size_t workspace_bytes,
+                                      spec_stream_t stream);
 
 /* Bytes of workspace any accept call needs for these sizes (K = K_max for the
  * ragged calls; 0 if the sizes are out of range). */

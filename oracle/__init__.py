@@ -13,6 +13,7 @@ Modules:
              residual / bonus draw, decision margins, the closed-form
              expected tokens per verify pass, and both rules on packed
              batches with per-sequence draft counts.
+  tree    -- greedy verification of a draft tree (longest accepted path).
 
 Every function is pinned by the CPU tests (tests/test_oracle_*.py) to
 something other than itself: published Philox known-answer blocks and an
@@ -20,7 +21,9 @@ independent library implementation, exact rational arithmetic for the
 logits, brute force over every draft sequence for greedy decoding,
 chi-square tests of the sampled output against the target distribution, the
 closed form for the expected tokens per pass, the residual identity, and
-(for packed batches) reduction to the dense rule sequence by sequence.
+(for packed batches) reduction to the dense rule sequence by sequence, and
+(for trees) reduction to the linear rule on chains plus brute force against
+target-only greedy decoding.
 """
 from .philox import philox4x32_10, uniform24, verify_uniforms  # noqa: F401
 from .verify import (  # noqa: F401
@@ -28,3 +31,4 @@ from .verify import (  # noqa: F401
     accept_sample_ragged, expected_tokens, expected_tokens_positional, inverse_cdf, lm_head_logits,
     ragged_sequences, softmax, widen_bf16,
 )
+from .tree import TreeResult, tree_accept_greedy  # noqa: F401,E402

@@ -13,6 +13,8 @@ in the library's HIP kernels; if the library is missing, every call raises.
                               rows=None)
     spec_accept_sample_ragged(logits, draft_logits, draft_tokens, row_start, K_max, temperature, seeds,
                               accepted_len, out_tokens, workspace, rows=None, probs_at_draft=None)
+    spec_tree_accept_greedy(logits, parents, tokens, accepted_len, out_tokens, workspace, out_nodes=None,
+                            rows=None)
     spec_workspace_bytes(B, K, V)
 """
 from __future__ import annotations
@@ -25,7 +27,7 @@ __all__ = [
     "SpecVerifyError", "SPEC_OK", "SPEC_ERR_ARG", "SPEC_ERR_DTYPE", "SPEC_ERR_ALIGN",
     "SPEC_ERR_WORKSPACE", "SPEC_ERR_HIP", "SPEC_BF16", "SPEC_F32", "LIB_PATH", "HEADER_PATH",
     "load_library", "declared_symbols", "spec_verify_logits", "spec_accept_greedy",
-    "spec_accept_sample", "spec_accept_greedy_ragged", "spec_accept_sample_ragged", "spec_workspace_bytes", "spec_status_string", "spec_last_error_detail",
+    "spec_accept_sample", "spec_accept_greedy_ragged", "spec_accept_sample_ragged", "spec_tree_accept_greedy", "spec_workspace_bytes", "spec_status_string", "spec_last_error_detail",
 ]
 
 PKG_DIR = os.path.dirname(os.path.abspath(__file__))
@@ -50,6 +52,8 @@ _SIGNATURES = {
     "spec_accept_sample_ragged": (_c_int, [_c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_int, _c_float, _c_void_p,
                                            _c_void_p, _c_int, _c_int, _c_int, _c_int, _c_void_p, _c_void_p,
                                            _c_void_p, _c_void_p, _c_size_t, _c_void_p]),
+    "spec_tree_accept_greedy": (_c_int, [_c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_int, _c_int, _c_int, _c_int,
+                                         _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_size_t, _c_void_p]),
     "spec_workspace_bytes": (_c_size_t, [_c_int, _c_int, _c_int]),
     "spec_status_string": (ctypes.c_char_p, [_c_int]),
     "spec_last_error_detail": (ctypes.c_char_p, []),
@@ -210,3 +214,17 @@ def spec_accept_sample_ragged(logits, draft_logits, draft_tokens, row_start, K_m
                                          _ptr(accepted_len), _ptr(out_tokens), _ptr(probs_at_draft),
                                          _ptr(workspace), workspace.numel() * workspace.element_size(),
                                          _stream(stream)))
+
+
+def spec_tree_accept_greedy(logits, parents, tokens, accepted_len, out_tokens, workspace, out_nodes=None, rows=None,
+                            stream=None) -> None:
+    """Greedy verification of draft trees: logits [B, N+1, V], parents and
+    tokens [B, N+1] (entry 0 of each row is the root and is ignored)."""
+    B, P, V = logits.shape
+    rows_t, n_rows = _rows(rows)
+    lib = load_library()
+    _check("spec_tree_accept_greedy",
+           lib.spec_tree_accept_greedy(_ptr(logits), _ptr(parents) if P > 1 else None,
+                                       _ptr(tokens) if P > 1 else None, _ptr(rows_t), n_rows, B, P - 1, V,
+                                       _ptr(accepted_len), _ptr(out_tokens), _ptr(out_nodes), _ptr(workspace),
+                                       workspace.numel() * workspace.element_size(), _stream(stream)))

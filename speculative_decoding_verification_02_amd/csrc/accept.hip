@@ -196,6 +196,125 @@ __global__ __launch_bounds__(kAcceptThreads) void accept_kernel(
         info[j] = AcceptInfo{n, b, t0, kb, u_term, t.m, t.s, has_draft ? d.m : 0.f, has_draft ? d.s : 0.f, {0, 0, 0}};
 }
 
+// ----------------------------------------------------------- draft trees --
+// Greedy verification of a draft tree of N <= 63 nodes per sequence
+// ("Inference-4", Medusa; "speculative-decoding" blog, EAGLE-2's dynamic
+// draft trees; "Speculative decoding" course page, One pass, many candidate
+// continuations).  Row v of the sequence's logits is the target's prediction
+// after the path root -> v; node v >= 1 extends its parent p(v) < v by token
+// d_v.  Node v is accepted iff its parent is and d_v == argmax of row p(v);
+// the deepest accepted node (lowest index among equals) is kept: its path's
+// tokens are committed and the argmax of its own row is the bonus token.
+//
+// One workgroup per sequence merges the chunk statistics of its N+1 rows as
+// the linear kernel does; then wavefront 0 holds node v in lane v and finds,
+// by pointer jumping over the parent links (six rounds of shuffles reach any
+// depth below 64), each node's depth and whether its whole path is accepted.
+__global__ __launch_bounds__(kAcceptThreads) void tree_accept_kernel(
+    const int32_t* __restrict__ parents, const int32_t* __restrict__ tokens, const int32_t* __restrict__ rows,
+    int n_rows, int B, int N, int V, int nc, const StatRec* __restrict__ stats, int32_t* __restrict__ accepted_len,
+    int32_t* __restrict__ out_tokens, int32_t* __restrict__ out_nodes) {
+    __shared__ StatRec recs[kRecBuf];
+    __shared__ Merged merged[kWave];
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int j = blockIdx.x;
+    const int b = rows ? rows[j] : j;
+    if (b < 0 || b >= B) return;
+
+    const int v = lane;
+    const bool node = wave == 0 && v <= N;
+    const size_t base = (size_t)b * (N + 1);
+    int par = 0, tok = 0;
+    if (node && v > 0) {
+        par = parents[base + v];
+        tok = tokens[base + v];
+    }
+
+    const int rows_per_pass = max(1, min(N + 1, kRecBuf / nc));
+    for (int r0 = 0; r0 <= N; r0 += rows_per_pass) {
+        const int nr = min(rows_per_pass, N + 1 - r0);
+        for (int e = tid; e < nr * nc; e += kAcceptThreads) {
+            const int rr = r0 + e / nc, k = e - (e / nc) * nc;
+            recs[e] = stats[((size_t)j * (N + 1) + rr) * nc + k];
+        }
+        __syncthreads();
+        for (int rr = wave; rr < nr; rr += kAcceptWaves) {
+            const Merged x = wave_merge(recs + rr * nc, nc, 0.f, false, lane);
+            if (lane == 0) merged[r0 + rr] = x;
+        }
+        __syncthreads();
+    }
+    if (wave != 0) return;
+
+    Merged t{-INFINITY, 0.f, INT_MAX, 0};
+    int bad = 0;
+    if (node) {
+        t = merged[v];
+        bad = t.bad | (t.m == -INFINITY);
+        if (v > 0) bad |= par < 0 || par >= v || tok < 0 || tok >= V;
+    }
+    int32_t* orow = out_tokens + base;
+    int32_t* nrow = out_nodes ? out_nodes + base : nullptr;
+    if (__ballot(node && bad) != 0ull) {  // data fault anywhere in the tree
+        if (node) {
+            orow[v] = -1;
+            if (nrow) nrow[v] = -1;
+        }
+        if (lane == 0) accepted_len[b] = -1;
+        return;
+    }
+
+    // lanes past N stand for nothing: parked at the root, never accepted
+    const int p0 = (node && v > 0) ? par : 0;
+    const int arg_parent = __shfl(t.idx, p0, kWave);
+    int ok = node && (v == 0 || tok == arg_parent);
+    int anc = p0;
+    int dist = (node && v > 0) ? 1 : 0;
+#pragma unroll
+    for (int r = 0; r < 6; ++r) {
+        const int ok_a = __shfl(ok, anc, kWave);
+        const int dist_a = __shfl(dist, anc, kWave);
+        const int anc_a = __shfl(anc, anc, kWave);
+        ok &= ok_a;
+        dist += dist_a;
+        anc = anc_a;
+    }
+    // deepest accepted node, lowest index among equals (the root always qualifies)
+    int key = ok ? (dist << 6) | (63 - v) : -1;
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) key = max(key, __shfl_xor(key, o, kWave));
+    const int best = 63 - (key & 63);
+    const int depth = key >> 6;
+
+    // commit the path: walk from the kept node up to the root
+    int cur = best;
+    for (int s = depth - 1; s >= 0; --s) {
+        const int tv = __shfl(tok, cur, kWave);
+        if (lane == 0) {
+            orow[s] = tv;
+            if (nrow) nrow[s] = cur;
+        }
+        cur = __shfl(p0, cur, kWave);
+    }
+    const int bonus = __shfl(t.idx, best, kWave);
+    if (node) {
+        if (v == depth) orow[v] = bonus;
+        else if (v > depth) orow[v] = -1;
+        if (nrow && v >= depth) nrow[v] = -1;
+    }
+    if (lane == 0) accepted_len[b] = depth;
+}
+
+hipError_t launch_tree_accept(const int32_t* parents, const int32_t* tokens, const int32_t* rows, int n_rows, int B,
+                              int N, int V, const StatRec* stats, int32_t* accepted_len, int32_t* out_tokens,
+                              int32_t* out_nodes, hipStream_t stream) {
+    if (n_rows == 0) return hipSuccess;
+    hipLaunchKernelGGL(tree_accept_kernel, dim3(n_rows), dim3(kAcceptThreads), 0, stream, parents, tokens, rows,
+                       n_rows, B, N, V, n_chunks(V), stats, accepted_len, out_tokens, out_nodes);
+    return hipGetLastError();
+}
+
 hipError_t launch_accept(const float* logits, const float* draft_logits, const int32_t* draft_tokens,
                          const uint64_t* seeds, const int32_t* rows, int n_rows, SeqRows seq, int V,
                          float inv_t_log2e, bool sampled, const StatRec* stats, int32_t* accepted_len,

@@ -223,6 +223,27 @@ spec_status_t spec_accept_sample_ragged(const float* logits, const float* draft_
                        workspace, workspace_bytes, static_cast<hipStream_t>(stream));
 }
 
+spec_status_t spec_tree_accept_greedy(const float* logits, const int32_t* parents, const int32_t* tokens,
+                                      const int32_t* rows, int n_rows, int B, int N, int V, int32_t* accepted_len,
+                                      int32_t* out_tokens, int32_t* out_nodes, void* workspace,
+                                      size_t workspace_bytes, spec_stream_t stream) {
+    spec_status_t st = check_accept_common(logits, tokens, rows, n_rows, B, N, V, N > 0, accepted_len, out_tokens,
+                                           workspace, workspace_bytes);
+    if (st != SPEC_OK) return st;
+    if (N > 0 && !parents) return SPEC_ERR_ARG;
+    const int nr = rows ? n_rows : B;
+    if (nr == 0) return SPEC_OK;
+    Workspace ws;
+    workspace_layout(B, N, V, workspace, &ws);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    hipError_t e = sv::launch_softmax_stats(logits, nullptr, rows, nr, dense_rows(B, N), V, sv::kLog2e, false,
+                                            ws.stats, s);
+    if (e == hipSuccess)
+        e = sv::launch_tree_accept(parents, tokens, rows, nr, B, N, V, ws.stats, accepted_len, out_tokens, out_nodes,
+                                   s);
+    return e == hipSuccess ? SPEC_OK : hip_fail(e);
+}
+
 size_t spec_workspace_bytes(int B, int K, int V) {
     if (!sizes_ok(B, K, V)) return 0;
     return workspace_layout(B, K, V, nullptr, nullptr);

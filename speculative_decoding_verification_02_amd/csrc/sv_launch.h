@@ -32,6 +32,12 @@ hipError_t launch_accept(const float* logits, const float* draft_logits, const i
                          int32_t* out_tokens, float* probs_at_draft, AcceptInfo* info, int* counters,
                          hipStream_t stream);
 
+// Greedy verification of draft trees (N+1 rows per sequence, statistics from
+// launch_softmax_stats over the dense layout with K = N).
+hipError_t launch_tree_accept(const int32_t* parents, const int32_t* tokens, const int32_t* rows, int n_rows, int B,
+                              int N, int V, const StatRec* stats, int32_t* accepted_len, int32_t* out_tokens,
+                              int32_t* out_nodes, hipStream_t stream);
+
 // Residual / bonus draw of the sampled sequences: per-chunk weight sums, and
 // the inverse-CDF selection of the terminal token by the last chunk block.
 hipError_t launch_residual(const float* logits, const float* draft_logits, int n_rows, int V,

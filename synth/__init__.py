@@ -29,7 +29,7 @@ import torch
 __all__ = [
     "Workload", "WORKLOADS", "weights", "hidden_states", "base_logits",
     "draft_logits", "sampled_mask", "draft_tokens", "seeds", "round_inputs",
-    "draft_counts", "row_start", "pack_rows",
+    "draft_counts", "row_start", "pack_rows", "tree_parents", "tree_tokens",
 ]
 
 
@@ -57,6 +57,7 @@ class Workload:
     modes: str = "sample"      # "sample" | "greedy" | "both" | "half" | "bernoulli"
     data_seed: int = 1000
     ragged: bool = False       # per-sequence draft counts K_b ~ U{0..K}, rows packed
+    tree: bool = False         # K = N draft nodes per sequence in a random tree
     note: str = field(default="", compare=False)
 
     @property
@@ -99,6 +100,13 @@ WORKLOADS = {
         w_std=0.02, temperature=0.8, draft="additive", draft_sigma=(0.0, 2.0),
         modes="half", data_seed=1005, ragged=True,
         note="K_b ~ U{0..7}, packed rows; rows 0..31 greedy, 32..63 sampled at T=0.8"),
+    # draft trees (not one of the five benchmark workloads): 8 sequences with
+    # 63-node trees, greedy
+    "b8_tree63_h4096_v128256": Workload(
+        "b8_tree63_h4096_v128256", B=8, K=63, H=4096, V=128256, dtype="bf16",
+        w_std=0.02, temperature=1.0, draft="additive", draft_sigma=(0.05, 0.05),
+        modes="greedy", data_seed=1006, tree=True,
+        note="63-node random trees; children take the parent's top-k tokens under N(0, 0.05^2) noise"),
 }
 
 
@@ -255,3 +263,46 @@ def pack_rows(dense, counts, drafts: bool = False):
     if isinstance(dense, torch.Tensor):
         return torch.cat(parts, dim=0) if parts else dense.reshape(0, *dense.shape[2:])
     return np.concatenate(parts, axis=0)
+
+
+# ----------------------------------------------------------- draft trees --
+
+def tree_parents(B: int, N: int, seed: int) -> np.ndarray:
+    """Random tree shapes [B, N+1] int32 in topological order: node v >= 1
+    hangs under v - g, g >= 1 geometric(0.45) (clipped at the root), so trees
+    mix long chains with branches; entry 0 (the root) is 0."""
+    rng = np.random.default_rng(seed)
+    par = np.zeros((B, N + 1), np.int64)
+    for v in range(1, N + 1):
+        g = rng.geometric(0.45, B)
+        par[:, v] = np.maximum(v - g, 0)
+    return par.astype(np.int32)
+
+
+def tree_tokens(node_logits: torch.Tensor, parents, seed: int, p_random: float = 0.25,
+                sigma: float = 1.0) -> torch.Tensor:
+    """Draft tokens of tree nodes [B, N+1] int32 (entry 0 unused): the j-th
+    child of a node takes the j-th most likely token of a copy of the parent's
+    logits with N(0, sigma^2) noise added (a top-k expansion), or a uniform
+    random token with probability p_random."""
+    B, P, V = node_logits.shape
+    par = np.asarray(parents, np.int64)
+    rank = np.zeros((B, P), np.int64)
+    for b in range(B):
+        seen = {}
+        for v in range(1, P):
+            p = par[b, v]
+            rank[b, v] = seen.get(p, 0)
+            seen[p] = rank[b, v] + 1
+    kmax = int(rank.max()) + 1 if P > 1 else 1
+    g = _gen(seed, node_logits.device)
+    noisy = node_logits.float() + sigma * torch.randn(node_logits.shape, generator=g, device=node_logits.device)
+    top = torch.topk(noisy, min(kmax, V), dim=-1).indices.cpu().numpy()     # [B, P, kmax]
+    rs = np.random.default_rng(seed)
+    tok = np.zeros((B, P), np.int64)
+    for v in range(1, P):
+        tok[:, v] = top[np.arange(B), par[:, v], np.minimum(rank[:, v], top.shape[-1] - 1)]
+    rnd = rs.random((B, P)) < p_random
+    tok = np.where(rnd, rs.integers(0, V, (B, P)), tok)
+    tok[:, 0] = 0
+    return torch.from_numpy(tok.astype(np.int32))

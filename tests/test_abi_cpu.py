@@ -27,7 +27,7 @@ def lib():
 def test_exports_every_declared_symbol(lib):
     names = sv.declared_symbols()
     assert set(names) == {"spec_verify_logits", "spec_accept_greedy", "spec_accept_sample",
-                          "spec_accept_greedy_ragged", "spec_accept_sample_ragged",
+                          "spec_accept_greedy_ragged", "spec_accept_sample_ragged", "spec_tree_accept_greedy",
                           "spec_workspace_bytes", "spec_status_string", "spec_last_error_detail"}
     for n in names:
         assert hasattr(lib, n), n
@@ -141,6 +141,22 @@ def test_ragged_validation(lib):
     assert _sample_ragged(lib, dl=MIS) == sv.SPEC_ERR_ALIGN
     assert _sample_ragged(lib, T=0.0) == sv.SPEC_ERR_ARG
     assert _greedy_ragged(lib, wsb=16) == sv.SPEC_ERR_WORKSPACE
+
+
+def _tree(lib, par=A, tok=A, N=5, B=2, V=100, logits=A, rows=None, n_rows=0, wsb=None):
+    if wsb is None:
+        wsb = sv.spec_workspace_bytes(B, N, V) or (1 << 20)
+    return lib.spec_tree_accept_greedy(logits, par, tok, rows, n_rows, B, N, V, A, A, None, A, wsb, None)
+
+
+def test_tree_validation(lib):
+    assert _tree(lib, par=None) == sv.SPEC_ERR_ARG
+    assert _tree(lib, tok=None) == sv.SPEC_ERR_ARG
+    assert _tree(lib, N=64) == sv.SPEC_ERR_ARG
+    assert _tree(lib, logits=MIS) == sv.SPEC_ERR_ALIGN
+    assert _tree(lib, wsb=16) == sv.SPEC_ERR_WORKSPACE
+    assert _tree(lib, par=None, tok=None, N=0, rows=A, n_rows=0) == sv.SPEC_OK
+    assert _tree(lib, rows=A, n_rows=0) == sv.SPEC_OK
 
 
 def test_zero_selected_rows_is_a_no_op(lib):
