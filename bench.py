@@ -160,6 +160,9 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     sv.load_library()
+    if args.workload in synth.NGRAM_WORKLOADS:
+        bench_ngram(args, dev)
+        return
 
     wl = synth.WORKLOADS[args.workload]
     B, K, H, V, T = wl.B, wl.K, wl.H, wl.V, wl.temperature
@@ -370,6 +373,77 @@ def cpu_baseline(wl, W, hidden, zd, drafts, smask, budget_s, rs=None, parents=No
     return {"value": M / t, "unit": "verified positions/s", "cores": int(min(used, cores)), "kind": "oracle",
             "sample": "%d whole verify steps of %s (fp64 logits of all %d positions over V=%d, then acceptance), "
                       "same inputs as the GPU run; %.2f s per step" % (len(times), wl.name, M, wl.V, t)}
+
+
+def bench_ngram(args, dev):
+    """The prompt-lookup drafter on its own: one step = one
+    spec_ngram_propose call over every history of the workload."""
+    import torch
+
+    import speculative_decoding_verification_02_amd as sv
+    import synth
+
+    wl = synth.NGRAM_WORKLOADS[args.workload]
+    print("bench: %s, generating histories" % wl.name, file=sys.stderr, flush=True)
+    hist = synth.histories(wl.B, wl.L, wl.V, wl.data_seed, wl.copy_frac)
+    starts = np.concatenate([[0], np.cumsum([len(h) for h in hist])]).astype(np.int64)
+    n_tok = int(starts[-1])
+    flat = torch.from_numpy(np.concatenate(hist).astype(np.int32)).to(dev)
+    hs = torch.from_numpy(starts).to(dev)
+    max_len = max(len(h) for h in hist)
+    drafts = torch.empty((wl.B, wl.n_drafts), dtype=torch.int32, device=dev)
+    count = torch.empty((wl.B,), dtype=torch.int32, device=dev)
+    rs = torch.empty((wl.B + 1,), dtype=torch.int32, device=dev)
+    ws = torch.empty(sv.spec_ngram_workspace_bytes(wl.B, max_len), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def step():
+        sv.spec_ngram_propose(flat, hs, max_len, wl.max_ngram, wl.n_drafts, drafts, count, ws, row_start=rs,
+                              stream=stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    step_s = (time.perf_counter() - t0) / args.steps
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    for a, b in evs:
+        a.record(stream)
+        step()
+        b.record(stream)
+    torch.cuda.synchronize()
+    call_ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
+    # algorithmic bytes: every history token read once, the drafts, counts
+    # and offsets written once
+    alg = n_tok * 4 + wl.B * (wl.n_drafts + 2) * 4 + (wl.B + 1) * 8
+    roof = {"bound": "hbm", "achieved": alg / (call_ms * 1e-3) / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "kernel": "spec_ngram_propose (scan + finalize)", "traffic": None, "algorithmic_bytes": alg,
+            "avg_call_us": call_ms * 1e3}
+    roof["frac"] = roof["achieved"] / roof["peak"]
+    res = {"metric": "history tokens scanned/s (prompt-lookup drafter)", "value": n_tok / step_s,
+           "unit": "tokens/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+           "ms_per_step": step_s * 1e3, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+           "dtype": "int32", "data": "synthetic",
+           "config": {"workload": wl.name, "B": wl.B, "max_len": max_len, "tokens": n_tok, "V": wl.V,
+                      "max_ngram": wl.max_ngram, "n_drafts": wl.n_drafts},
+           "mean_drafts": float(count.float().mean().item()), "roofline": roof}
+    if not args.no_cpu_baseline:
+        import oracle
+        t0 = time.perf_counter()
+        n = 0
+        while n < wl.B:
+            oracle.ngram_propose_one(hist[n], wl.n_drafts, wl.max_ngram)
+            n += 1
+            if time.perf_counter() - t0 > args.cpu_seconds:
+                break
+        t = time.perf_counter() - t0
+        scanned = sum(len(h) for h in hist[:n])
+        res["cpu_baseline"] = {"value": scanned / t, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+                               "sample": "%d of the %d histories (%d tokens), one thread (numpy)" % (n, wl.B, scanned)}
+    print(json.dumps(res), flush=True)
 
 
 def synth_seeds(wl, r):

@@ -44,6 +44,10 @@
  *                          blog, Medusa and EAGLE-2; "Speculative decoding"
  *                          course page, One pass, many candidate
  *                          continuations).
+ *   spec_ngram_propose  -- the step before verification for prompt lookup:
+ *                          drafts copied from the most recent earlier
+ *                          occurrence of the sequence's last n tokens
+ *                          ("Inference-4", Prompt lookup decoding).
  *
  * Conventions shared by every entry point
  *   - Every pointer argument is DEVICE memory on the current HIP device, owned
@@ -274,6 +278,47 @@ spec_status_t spec_tree_accept_greedy(const float* logits, const int32_t* parent
                                       int32_t* out_nodes,
                                       void* workspace, size_t workspace_bytes,
                                       spec_stream_t stream);
+
+/*
+ * spec_ngram_propose -- prompt-lookup drafts for B token histories.
+ *
+ * For history s of length L: for n = max_ngram, ..., 1, look for the window
+ * s[j .. j+n-1] == s[L-n .. L-1] with the largest j <= L-1-n (a window ending
+ * before the last token); the first n that has one fixes start = j + n and
+ * the drafts s[start .. start + n_drafts - 1], cut at L.  No window for any n:
+ * no drafts.  Only token equality is used, so the result is exact.
+ *
+ *   history       device, int32 tokens of all histories, packed
+ *   hist_start    device, [B+1] int64, 8-byte aligned: history b is
+ *                 history[hist_start[b] .. hist_start[b+1]-1]
+ *   B             number of histories, >= 1
+ *   max_len       bound on every history's length (0 <= max_len < 2^31 - 1);
+ *                 it sizes the launch
+ *   max_ngram     longest n-gram tried, 1 ..16 (the page's listing uses 3)
+ *   n_drafts      drafts wanted per history, 0 .. 63
+ *   drafts        device, [B, n_drafts] int32: the drafts, then -1
+ *   draft_count   device, [B] int32: drafts proposed (0 .. n_drafts)
+ *   row_start     device, [B+1] int32, or NULL: row_start[0] = 0,
+ *                 row_start[b+1] = row_start[b] + draft_count[b] + 1 -- the
+ *                 packing the ragged verify calls take (a history with bad
+ *                 offsets counts as 0 drafts there)
+ *   workspace     device scratch of spec_ngram_workspace_bytes(B, max_len)
+ *                 bytes, 8-byte aligned; contents on entry do not matter
+ * The caller guarantees that every well-formed span lies inside history.
+ * A history whose offsets are malformed (negative start, negative length or
+ * a length above max_len) gets draft_count[b] = -1 and drafts of -1, and is
+ * not read.
+ */
+spec_status_t spec_ngram_propose(const int32_t* history, const int64_t* hist_start, int B,
+                                 int max_len, int max_ngram, int n_drafts,
+                                 int32_t* drafts, int32_t* draft_count, int32_t* row_start,
+                                 void* workspace, size_t workspace_bytes,
+                                 spec_stream_t stream);
+
+/* Bytes of workspace spec_ngram_propose needs for B histories of at most
+ * max_len tokens (one 8-byte slot per 8192-position segment; 0 if B < 1 or
+ * max_len is out of range). */
+size_t spec_ngram_workspace_bytes(int B, int max_len);
 
 /* Bytes of workspace any accept call needs for these sizes (K = K_max for the
  * ragged calls; 0 if the sizes are out of range). */

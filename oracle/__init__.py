@@ -14,6 +14,8 @@ Modules:
              expected tokens per verify pass, and both rules on packed
              batches with per-sequence draft counts.
   tree    -- greedy verification of a draft tree (longest accepted path).
+  ngram   -- the prompt-lookup drafter (most recent earlier occurrence of
+             the longest matching suffix n-gram).
 
 Every function is pinned by the CPU tests (tests/test_oracle_*.py) to
 something other than itself: published Philox known-answer blocks and an
@@ -23,7 +25,8 @@ chi-square tests of the sampled output against the target distribution, the
 closed form for the expected tokens per pass, the residual identity, and
 (for packed batches) reduction to the dense rule sequence by sequence, and
 (for trees) reduction to the linear rule on chains plus brute force against
-target-only greedy decoding.
+target-only greedy decoding; the n-gram drafter by an independent string
+search and hand-worked sequences.
 """
 from .philox import philox4x32_10, uniform24, verify_uniforms  # noqa: F401
 from .verify import (  # noqa: F401
@@ -32,3 +35,4 @@ from .verify import (  # noqa: F401
     ragged_sequences, softmax, widen_bf16,
 )
 from .tree import TreeResult, tree_accept_greedy  # noqa: F401,E402
+from .ngram import ngram_propose, ngram_propose_one  # noqa: F401,E402

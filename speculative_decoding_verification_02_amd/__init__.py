@@ -15,7 +15,9 @@ in the library's HIP kernels; if the library is missing, every call raises.
                               accepted_len, out_tokens, workspace, rows=None, probs_at_draft=None)
     spec_tree_accept_greedy(logits, parents, tokens, accepted_len, out_tokens, workspace, out_nodes=None,
                             rows=None)
-    spec_workspace_bytes(B, K, V)
+    spec_ngram_propose(history, hist_start, max_len, max_ngram, n_drafts, drafts, draft_count, workspace,
+                       row_start=None)
+    spec_workspace_bytes(B, K, V), spec_ngram_workspace_bytes(B, max_len)
 """
 from __future__ import annotations
 
@@ -27,7 +29,8 @@ __all__ = [
     "SpecVerifyError", "SPEC_OK", "SPEC_ERR_ARG", "SPEC_ERR_DTYPE", "SPEC_ERR_ALIGN",
     "SPEC_ERR_WORKSPACE", "SPEC_ERR_HIP", "SPEC_BF16", "SPEC_F32", "LIB_PATH", "HEADER_PATH",
     "load_library", "declared_symbols", "spec_verify_logits", "spec_accept_greedy",
-    "spec_accept_sample", "spec_accept_greedy_ragged", "spec_accept_sample_ragged", "spec_tree_accept_greedy", "spec_workspace_bytes", "spec_status_string", "spec_last_error_detail",
+    "spec_accept_sample", "spec_accept_greedy_ragged", "spec_accept_sample_ragged", "spec_tree_accept_greedy", "spec_ngram_propose", "spec_ngram_workspace_bytes",
+    "spec_workspace_bytes", "spec_status_string", "spec_last_error_detail",
 ]
 
 PKG_DIR = os.path.dirname(os.path.abspath(__file__))
@@ -54,6 +57,9 @@ _SIGNATURES = {
                                            _c_void_p, _c_void_p, _c_size_t, _c_void_p]),
     "spec_tree_accept_greedy": (_c_int, [_c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_int, _c_int, _c_int, _c_int,
                                          _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_size_t, _c_void_p]),
+    "spec_ngram_propose": (_c_int, [_c_void_p, _c_void_p, _c_int, _c_int, _c_int, _c_int, _c_void_p, _c_void_p,
+                                    _c_void_p, _c_void_p, _c_size_t, _c_void_p]),
+    "spec_ngram_workspace_bytes": (_c_size_t, [_c_int, _c_int]),
     "spec_workspace_bytes": (_c_size_t, [_c_int, _c_int, _c_int]),
     "spec_status_string": (ctypes.c_char_p, [_c_int]),
     "spec_last_error_detail": (ctypes.c_char_p, []),
@@ -228,3 +234,21 @@ def spec_tree_accept_greedy(logits, parents, tokens, accepted_len, out_tokens, w
                                        _ptr(tokens) if P > 1 else None, _ptr(rows_t), n_rows, B, P - 1, V,
                                        _ptr(accepted_len), _ptr(out_tokens), _ptr(out_nodes), _ptr(workspace),
                                        workspace.numel() * workspace.element_size(), _stream(stream)))
+
+
+def spec_ngram_workspace_bytes(B: int, max_len: int) -> int:
+    return int(load_library().spec_ngram_workspace_bytes(B, max_len))
+
+
+def spec_ngram_propose(history, hist_start, max_len, max_ngram, n_drafts, drafts, draft_count, workspace,
+                       row_start=None, stream=None) -> None:
+    """Prompt-lookup drafts: history int32 (packed), hist_start int64 [B+1];
+    drafts [B, n_drafts] and draft_count [B] int32 (row_start [B+1] int32
+    optional)."""
+    B = hist_start.numel() - 1
+    lib = load_library()
+    _check("spec_ngram_propose",
+           lib.spec_ngram_propose(_ptr(history) if history.numel() else None, _ptr(hist_start), B, int(max_len),
+                                  int(max_ngram), int(n_drafts), _ptr(drafts) if n_drafts else None,
+                                  _ptr(draft_count), _ptr(row_start), _ptr(workspace),
+                                  workspace.numel() * workspace.element_size(), _stream(stream)))

@@ -5,6 +5,7 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <algorithm>
 #include <atomic>
 
 #include "../../include/spec_verify.h"
@@ -242,6 +243,29 @@ spec_status_t spec_tree_accept_greedy(const float* logits, const int32_t* parent
         e = sv::launch_tree_accept(parents, tokens, rows, nr, B, N, V, ws.stats, accepted_len, out_tokens, out_nodes,
                                    s);
     return e == hipSuccess ? SPEC_OK : hip_fail(e);
+}
+
+spec_status_t spec_ngram_propose(const int32_t* history, const int64_t* hist_start, int B, int max_len,
+                                 int max_ngram, int n_drafts, int32_t* drafts, int32_t* draft_count,
+                                 int32_t* row_start, void* workspace, size_t workspace_bytes, spec_stream_t stream) {
+    if (B < 1 || max_len < 0 || max_len == 0x7fffffff || max_ngram < 1 || max_ngram > sv::kNgMaxGram ||
+        n_drafts < 0 || n_drafts > kMaxK)
+        return SPEC_ERR_ARG;
+    if (!hist_start || !draft_count || (n_drafts > 0 && !drafts) || (max_len > 0 && !history)) return SPEC_ERR_ARG;
+    if ((long long)B * sv::ngram_segments(max_len) > 0x7fffffffLL) return SPEC_ERR_ARG;
+    if ((reinterpret_cast<uintptr_t>(hist_start) & 7u) != 0) return SPEC_ERR_ALIGN;
+    if (!workspace || workspace_bytes < spec_ngram_workspace_bytes(B, max_len)) return SPEC_ERR_WORKSPACE;
+    if ((reinterpret_cast<uintptr_t>(workspace) & 7u) != 0) return SPEC_ERR_ALIGN;
+    hipError_t e = sv::launch_ngram(history, hist_start, B, max_len, max_ngram, n_drafts, drafts, draft_count,
+                                    row_start, static_cast<unsigned long long*>(workspace),
+                                    static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? SPEC_OK : hip_fail(e);
+}
+
+size_t spec_ngram_workspace_bytes(int B, int max_len) {
+    if (B < 1 || max_len < 0 || max_len == 0x7fffffff) return 0;
+    const size_t segs = (size_t)std::max(1, sv::ngram_segments(max_len));
+    return align256((size_t)B * segs * sizeof(unsigned long long));
 }
 
 size_t spec_workspace_bytes(int B, int K, int V) {

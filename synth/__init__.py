@@ -30,6 +30,7 @@ __all__ = [
     "Workload", "WORKLOADS", "weights", "hidden_states", "base_logits",
     "draft_logits", "sampled_mask", "draft_tokens", "seeds", "round_inputs",
     "draft_counts", "row_start", "pack_rows", "tree_parents", "tree_tokens",
+    "NgramWorkload", "NGRAM_WORKLOADS", "histories",
 ]
 
 
@@ -306,3 +307,55 @@ def tree_tokens(node_logits: torch.Tensor, parents, seed: int, p_random: float =
     tok = np.where(rnd, rs.integers(0, V, (B, P)), tok)
     tok[:, 0] = 0
     return torch.from_numpy(tok.astype(np.int32))
+
+
+# ------------------------------------------------ prompt-lookup histories --
+
+@dataclass(frozen=True)
+class NgramWorkload:
+    """Token histories for the prompt-lookup drafter: B sequences of length
+    U[L/2, L] over a vocabulary of V tokens, built from fresh random tokens
+    and copies of earlier spans (copy-heavy text such as summarisation or
+    retrieval answers, where the pages say prompt lookup pays)."""
+    name: str
+    B: int
+    L: int
+    V: int
+    max_ngram: int
+    n_drafts: int
+    copy_frac: float
+    data_seed: int
+
+
+NGRAM_WORKLOADS = {
+    "ngram_b256_l131072": NgramWorkload("ngram_b256_l131072", B=256, L=131072, V=128256, max_ngram=3, n_drafts=7,
+                                        copy_frac=0.5, data_seed=1007),
+}
+
+
+def histories(B: int, L: int, V: int, seed: int, copy_frac: float = 0.5, lengths=None) -> list:
+    """B int32 token histories.  Lengths U[L/2, L] unless given.  Start from
+    uniform random tokens, then copy spans of 8..64 tokens from earlier
+    positions over about copy_frac of the sequence; with probability
+    copy_frac the sequence ends inside a copied span."""
+    rng = np.random.default_rng(seed)
+    if lengths is None:
+        lengths = rng.integers(L // 2, L + 1, B)
+    out = []
+    for b in range(B):
+        n = int(lengths[b])
+        s = rng.integers(0, V, n).astype(np.int32)
+        if n > 16:
+            n_copies = int(copy_frac * n / 36)
+            dst = np.sort(rng.integers(8, n, n_copies))
+            ln = rng.integers(8, 65, n_copies)
+            for d, k in zip(dst, ln):
+                src = int(rng.integers(0, d - 4))
+                k = int(min(k, n - d, d - src))
+                s[d:d + k] = s[src:src + k]
+            if rng.random() < copy_frac:
+                k = int(min(rng.integers(8, 65), n // 2))
+                src = int(rng.integers(0, n - k - k // 2 + 1)) if n - k - k // 2 > 0 else 0
+                s[n - k:] = s[src:src + k]
+        out.append(s)
+    return out

@@ -28,6 +28,7 @@ def test_exports_every_declared_symbol(lib):
     names = sv.declared_symbols()
     assert set(names) == {"spec_verify_logits", "spec_accept_greedy", "spec_accept_sample",
                           "spec_accept_greedy_ragged", "spec_accept_sample_ragged", "spec_tree_accept_greedy",
+                          "spec_ngram_propose", "spec_ngram_workspace_bytes",
                           "spec_workspace_bytes", "spec_status_string", "spec_last_error_detail"}
     for n in names:
         assert hasattr(lib, n), n
@@ -157,6 +158,34 @@ def test_tree_validation(lib):
     assert _tree(lib, wsb=16) == sv.SPEC_ERR_WORKSPACE
     assert _tree(lib, par=None, tok=None, N=0, rows=A, n_rows=0) == sv.SPEC_OK
     assert _tree(lib, rows=A, n_rows=0) == sv.SPEC_OK
+
+
+def _ngram(lib, hist=A, hs=A, B=2, max_len=100, g=3, k=5, drafts=A, count=A, ws=A, wsb=None):
+    if wsb is None:
+        wsb = sv.spec_ngram_workspace_bytes(B, max_len) or 256
+    return lib.spec_ngram_propose(hist, hs, B, max_len, g, k, drafts, count, None, ws, wsb, None)
+
+
+def test_ngram_validation(lib):
+    assert sv.spec_ngram_workspace_bytes(0, 10) == 0 and sv.spec_ngram_workspace_bytes(3, 100) == 256
+    assert sv.spec_ngram_workspace_bytes(3, -1) == 0
+    assert sv.spec_ngram_workspace_bytes(64, 8193) == 64 * 8         # 8192 end positions: one segment
+    assert sv.spec_ngram_workspace_bytes(64, 8194) == 64 * 8 * 2
+    assert sv.spec_ngram_workspace_bytes(64, 16386) == 64 * 8 * 3
+    assert _ngram(lib, B=0) == sv.SPEC_ERR_ARG
+    assert _ngram(lib, max_len=-1) == sv.SPEC_ERR_ARG
+    assert _ngram(lib, g=0) == sv.SPEC_ERR_ARG
+    assert _ngram(lib, g=17) == sv.SPEC_ERR_ARG
+    assert _ngram(lib, k=64) == sv.SPEC_ERR_ARG
+    assert _ngram(lib, k=-1) == sv.SPEC_ERR_ARG
+    assert _ngram(lib, hist=None) == sv.SPEC_ERR_ARG
+    assert _ngram(lib, hs=None) == sv.SPEC_ERR_ARG
+    assert _ngram(lib, drafts=None) == sv.SPEC_ERR_ARG
+    assert _ngram(lib, count=None) == sv.SPEC_ERR_ARG
+    assert _ngram(lib, hs=P(0x10004)) == sv.SPEC_ERR_ALIGN
+    assert _ngram(lib, ws=None) == sv.SPEC_ERR_WORKSPACE
+    assert _ngram(lib, wsb=8) == sv.SPEC_ERR_WORKSPACE
+    assert _ngram(lib, ws=P(0x10004)) == sv.SPEC_ERR_ALIGN
 
 
 def test_zero_selected_rows_is_a_no_op(lib):

@@ -1,0 +1,127 @@
+"""GPU parity of spec_ngram_propose (prompt-lookup drafts) against the
+oracle, which follows the pages' search n = max_ngram .. 1 directly.  Token
+equality only, so drafts, counts and verify-row offsets must match exactly:
+histories from empty to several scan segments long (8192 end positions per
+workgroup) with matches on either side of segment borders, tiny and large
+vocabularies (every position matching, or almost none), the n-gram and
+draft-count limits, malformed offsets, the full 256 x 128K-token workload,
+and the drafter's row offsets feeding the ragged verify call.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+import speculative_decoding_verification_02_amd as sv
+from gpu_support import dev, say, workspace
+
+pytestmark = pytest.mark.gpu
+
+
+def _pack(hist):
+    starts = np.concatenate([[0], np.cumsum([len(h) for h in hist])]).astype(np.int64)
+    flat = np.concatenate(hist).astype(np.int32) if starts[-1] else np.zeros(1, np.int32)
+    return flat, starts
+
+
+def _run(hist, G, k, starts=None, max_len=None):
+    flat, st = _pack(hist)
+    starts = st if starts is None else starts
+    B = len(starts) - 1
+    max_len = max([len(h) for h in hist] + [0]) if max_len is None else max_len
+    drafts = torch.full((B, max(k, 1)), -9, dtype=torch.int32, device=dev())
+    count = torch.full((B,), -9, dtype=torch.int32, device=dev())
+    rs = torch.full((B + 1,), -9, dtype=torch.int32, device=dev())
+    ws = torch.empty(sv.spec_ngram_workspace_bytes(B, max_len), dtype=torch.uint8, device=dev())
+    sv.spec_ngram_propose(torch.from_numpy(flat).to(dev()), torch.from_numpy(starts).to(dev()), max_len, G, k,
+                          drafts, count, ws, row_start=rs)
+    return drafts.cpu().numpy()[:, :k], count.cpu().numpy(), rs.cpu().numpy()
+
+
+def _check(hist, G, k):
+    d, c, rs = _run(hist, G, k)
+    od, oc, om, ors = oracle.ngram_propose(hist, k, G)
+    np.testing.assert_array_equal(c, oc)
+    np.testing.assert_array_equal(d, od)
+    np.testing.assert_array_equal(rs, ors)
+    return oc, om
+
+
+@pytest.mark.parametrize("V", [3, 50, 128256])
+@pytest.mark.parametrize("G,k", [(1, 1), (3, 7), (8, 63), (16, 4)])
+def test_ngram_exact(V, G, k):
+    rng = np.random.default_rng(V + 10 * G + k)
+    lengths = np.concatenate([[0, 1, 2, 3, 8193, 8194, 16385], rng.integers(0, 30000, 33)])
+    hist = synth.histories(len(lengths), 0, V, seed=V + G, copy_frac=0.5, lengths=lengths)
+    say("ngram exact B=%d V=%d max_ngram=%d n_drafts=%d" % (len(hist), V, G, k))
+    oc, om = _check(hist, G, k)
+    say("  matched n-gram lengths %s, mean drafts %.2f" % (np.bincount(om, minlength=G + 1).tolist(), oc.mean()))
+
+
+def test_matches_at_segment_borders():
+    # the only earlier occurrence of the final trigram ends exactly at, just
+    # before, or just after a segment border (end positions 8191 | 8192)
+    V = 1 << 20
+    hist = []
+    for e in (8190, 8191, 8192, 8193, 16383, 16384):
+        s = np.arange(20000, dtype=np.int64) + 1000      # all distinct
+        s[e - 2:e + 1] = [7, 8, 9]
+        s[-3:] = [7, 8, 9]
+        hist.append(s.astype(np.int32) % V)
+    say("ngram segment borders")
+    _, om = _check(hist, 3, 5)
+    assert np.all(om == 3)
+
+
+def test_ngram_malformed_offsets():
+    hist = synth.histories(6, 0, 50, seed=3, lengths=[100, 200, 50, 300, 10, 80])
+    flat, starts = _pack(hist)
+    bad = starts.copy()
+    bad[2] = bad[1] - 5        # history 1 gets a negative length, history 2 is 255 long
+    bad[4] = bad[3] + 270      # history 3 longer than max_len = 260, history 4 is 40 long
+    say("ngram malformed offsets")
+    d, c, rs = _run(hist, 3, 4, starts=bad, max_len=260)
+    assert c[1] == -1 and c[3] == -1 and np.all(d[[1, 3]] == -1)
+    for b in (0, 2, 4, 5):
+        seq = flat[bad[b]:bad[b + 1]]
+        od, _ = oracle.ngram_propose_one(seq, 4, 3)
+        assert c[b] == len(od) and d[b, :len(od)].tolist() == od.tolist()
+    cnt = np.where(c < 0, 0, c)
+    np.testing.assert_array_equal(rs, np.concatenate([[0], np.cumsum(cnt + 1)]))
+
+
+def test_full_size_workload():
+    wl = synth.NGRAM_WORKLOADS["ngram_b256_l131072"]
+    hist = synth.histories(wl.B, wl.L, wl.V, wl.data_seed, wl.copy_frac)
+    say("full-size ngram workload %s: %d tokens" % (wl.name, sum(len(h) for h in hist)))
+    oc, om = _check(hist, wl.max_ngram, wl.n_drafts)
+    say("  matched n-gram lengths %s, mean drafts %.2f" % (np.bincount(om).tolist(), oc.mean()))
+
+
+def test_drafts_feed_ragged_verify():
+    """The drafter's row offsets and drafts drive spec_accept_greedy_ragged:
+    with target logits whose argmax equals each draft, every draft is
+    accepted and the bonus is the last row's argmax."""
+    B, V, k = 12, 500, 6
+    hist = synth.histories(B, 3000, V, seed=8, copy_frac=0.8)
+    d, c, rs = _run(hist, 3, k)
+    R = int(rs[-1])
+    logits = torch.randn((R, V), generator=torch.Generator().manual_seed(1))
+    packed = []
+    for b in range(B):
+        for i in range(int(c[b])):
+            logits[rs[b] + i, int(d[b, i])] = 100.0          # row i predicts draft i
+            packed.append(int(d[b, i]))
+    dp = torch.tensor(packed, dtype=torch.int32)
+    acc = torch.full((B,), -2, dtype=torch.int32, device=dev())
+    out = torch.full((R,), -9, dtype=torch.int32, device=dev())
+    sv.spec_accept_greedy_ragged(logits.to(dev()), dp.to(dev()) if R > B else None,
+                                 torch.as_tensor(rs, device=dev()), k, acc, out, workspace(B, k, V))
+    acc, out = acc.cpu().numpy(), out.cpu().numpy()
+    say("ngram -> ragged verify: drafts %s" % c.tolist())
+    np.testing.assert_array_equal(acc, c)
+    for b in range(B):
+        n = int(c[b])
+        assert out[rs[b]:rs[b] + n].tolist() == d[b, :n].tolist()
+        assert out[rs[b] + n] == int(torch.argmax(logits[rs[b] + n]))
