@@ -54,25 +54,22 @@ def parse():
 
 
 # Source section of each LM-head kernel in lmhead_gemm.hip (text from its
-# banner comment to the next one), so that stored counter readings stay tied
-# to the kernel they were taken on.
+# banner comment to the next one: the kernel, its configuration and its
+# launcher), so that stored counter readings stay tied to the kernel they
+# were taken on.
 _SECTIONS = {"lmhead_coop_bf16": "small M, cooperative", "lmhead_big_bf16": "big M",
              "lmhead_skinny_bf16": "small M",
              "lmhead_tiled_bf16": "large M", "lmhead_f32": "fp32"}
 
 
 def kernel_source_sha(kernel: str) -> str:
-    """sha256 of the kernel's source section plus the launcher section that
-    picks its configuration."""
+    """sha256 of the kernel's source section (kernel, configuration and its
+    launcher), so edits elsewhere in the file keep stored readings valid."""
     lines = open(GEMM_SRC).read().splitlines(keepends=True)
     banners = [i for i, ln in enumerate(lines) if ln.startswith("// ---")]
-
-    def section(label):
-        i = next(i for i in banners if lines[i].strip("/ -\n") == label)
-        j = next((k for k in banners if k > i), len(lines))
-        return "".join(lines[i:j])
-
-    return hashlib.sha256((section(_SECTIONS[kernel]) + section("launchers")).encode()).hexdigest()[:16]
+    i = next(i for i in banners if lines[i].strip("/ -\n") == _SECTIONS[kernel])
+    j = next((k for k in banners if k > i), len(lines))
+    return hashlib.sha256("".join(lines[i:j]).encode()).hexdigest()[:16]
 
 
 def load_traffic(workload: str, kernel: str):

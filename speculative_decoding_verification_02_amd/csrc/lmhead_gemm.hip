@@ -167,6 +167,39 @@ __global__ __launch_bounds__(THREADS) void lmhead_skinny_bf16(
     }
 }
 
+// Fallback for M <= 16 with hidden sizes beyond the cooperative kernel's
+// register-resident slices (chosen by measurement on MI355X).
+constexpr int kSkRPL = 2;
+constexpr int kSkP = 3;
+constexpr int kSkThreads = 512;
+using SkinnyCfg = Skinny<kSkRPL, kSkP, kSkThreads>;
+
+bool skinny_fits(int M, int H) { return M <= 16 && SkinnyCfg::lds_bytes(M, H) <= 160 * 1024; }
+
+template <int RPL, int P, int THREADS>
+hipError_t launch_skinny(const uint16_t* hidden, const uint16_t* W, float* logits, int M, int V, int H, int num_cus,
+                         hipStream_t stream) {
+    using S = Skinny<RPL, P, THREADS>;
+    auto kern = lmhead_skinny_bf16<RPL, P, THREADS>;
+    const int n_tiles = (V + 15) / 16;
+    const size_t lds = S::lds_bytes(M, H);
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+    int occ = 0;
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, kern, THREADS, lds);
+    if (e != hipSuccess) return e;
+    if (occ < 1) occ = 1;
+    // fewest grid-stride iterations the resident waves allow, then just
+    // enough waves to cover the tiles in that many iterations
+    const long max_waves = (long)num_cus * occ * S::kWaves;
+    const long iters = (n_tiles + max_waves - 1) / max_waves;
+    const long waves = (n_tiles + iters - 1) / iters;
+    const int grid = (int)((waves + S::kWaves - 1) / S::kWaves);
+    hipLaunchKernelGGL(kern, dim3(grid), dim3(THREADS), lds, stream, hidden, W, logits, M, V, H, n_tiles);
+    return hipGetLastError();
+}
+
 // ------------------------------------------------- small M, cooperative ----
 // A workgroup of NW waves streams one 16-row vocabulary tile at a time (one
 // contiguous 16 * H * 2-byte block of W), the hidden dimension split into NW
@@ -275,12 +308,28 @@ __global__ __launch_bounds__(NW * 64) void lmhead_coop_bf16(
     }
 }
 
-// Fallback for M <= 16 with hidden sizes beyond the cooperative kernel's
-// register-resident slices (chosen by measurement on MI355X).
-constexpr int kSkRPL = 2;
-constexpr int kSkP = 3;
-constexpr int kSkThreads = 512;
-using SkinnyCfg = Skinny<kSkRPL, kSkP, kSkThreads>;
+template <int RPL, int MAXST, int NW>
+hipError_t launch_coop(const uint16_t* hidden, const uint16_t* W, float* logits, int M, int V, int H, int num_cus,
+                       hipStream_t stream, int blocks_per_cu) {
+    using S = Coop<RPL, MAXST, NW>;
+    auto kern = lmhead_coop_bf16<RPL, MAXST, NW>;
+    const int n_tiles = (V + 15) / 16;
+    const size_t lds = S::lds_bytes();
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+    int occ = 0;
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, kern, S::kThreads, lds);
+    if (e != hipSuccess) return e;
+    occ = max(1, min(occ, blocks_per_cu));
+    const int grid = (int)min((long)n_tiles, (long)num_cus * occ);
+    hipLaunchKernelGGL(kern, dim3(grid), dim3(S::kThreads), lds, stream, hidden, W, logits, M, V, H, n_tiles);
+    return hipGetLastError();
+}
+
+// Small-M configuration of the cooperative kernel (measured best on MI355X
+// for B = 1, K = 5, H = 4096: 2 rows per load, 2 stages, 8 waves).
+using CoopCfg = Coop<2, 2, 8>;
 
 // ------------------------------------------------------------ large M ------
 // Classic LDS-tiled contraction: a workgroup of 4 waves computes a 128 (vocab)
@@ -666,55 +715,6 @@ __global__ __launch_bounds__(kF32Threads) void lmhead_f32(
 }
 
 // ------------------------------------------------------------ launchers ----
-
-bool skinny_fits(int M, int H) { return M <= 16 && SkinnyCfg::lds_bytes(M, H) <= 160 * 1024; }
-
-template <int RPL, int P, int THREADS>
-hipError_t launch_skinny(const uint16_t* hidden, const uint16_t* W, float* logits, int M, int V, int H, int num_cus,
-                         hipStream_t stream) {
-    using S = Skinny<RPL, P, THREADS>;
-    auto kern = lmhead_skinny_bf16<RPL, P, THREADS>;
-    const int n_tiles = (V + 15) / 16;
-    const size_t lds = S::lds_bytes(M, H);
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    if (e != hipSuccess) return e;
-    int occ = 0;
-    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, kern, THREADS, lds);
-    if (e != hipSuccess) return e;
-    if (occ < 1) occ = 1;
-    // fewest grid-stride iterations the resident waves allow, then just
-    // enough waves to cover the tiles in that many iterations
-    const long max_waves = (long)num_cus * occ * S::kWaves;
-    const long iters = (n_tiles + max_waves - 1) / max_waves;
-    const long waves = (n_tiles + iters - 1) / iters;
-    const int grid = (int)((waves + S::kWaves - 1) / S::kWaves);
-    hipLaunchKernelGGL(kern, dim3(grid), dim3(THREADS), lds, stream, hidden, W, logits, M, V, H, n_tiles);
-    return hipGetLastError();
-}
-
-template <int RPL, int MAXST, int NW>
-hipError_t launch_coop(const uint16_t* hidden, const uint16_t* W, float* logits, int M, int V, int H, int num_cus,
-                       hipStream_t stream, int blocks_per_cu) {
-    using S = Coop<RPL, MAXST, NW>;
-    auto kern = lmhead_coop_bf16<RPL, MAXST, NW>;
-    const int n_tiles = (V + 15) / 16;
-    const size_t lds = S::lds_bytes();
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    if (e != hipSuccess) return e;
-    int occ = 0;
-    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, kern, S::kThreads, lds);
-    if (e != hipSuccess) return e;
-    occ = max(1, min(occ, blocks_per_cu));
-    const int grid = (int)min((long)n_tiles, (long)num_cus * occ);
-    hipLaunchKernelGGL(kern, dim3(grid), dim3(S::kThreads), lds, stream, hidden, W, logits, M, V, H, n_tiles);
-    return hipGetLastError();
-}
-
-// Small-M configuration of the cooperative kernel (measured best on MI355X
-// for B = 1, K = 5, H = 4096: 2 rows per load, 2 stages, 8 waves).
-using CoopCfg = Coop<2, 2, 8>;
 
 hipError_t launch_lmhead_bf16(const uint16_t* hidden, const uint16_t* W, float* logits, int M, int V, int H,
                               int num_cus, hipStream_t stream, int force_kernel) {
