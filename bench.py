@@ -42,6 +42,9 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="b1_k5_h4096_v128256")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--path", choices=["fused", "separate"], default="separate",
+                    help="fused: spec_verify_step (statistics in the LM-head epilogue); separate: "
+                         "spec_verify_logits then the accept calls")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle sample")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="before the run, copy a buffer of this many MiB 3 times (untimed), so a counter "
@@ -204,9 +207,19 @@ def main():
     out = torch.empty(tuple(hidden.shape[:2]), dtype=torch.int32, device=dev)
     stream = torch.cuda.current_stream()
 
+    step_ws = None
+    if args.path == "fused" and tree is None and row_start is None:
+        step_ws = torch.empty(sv.spec_verify_step_workspace_bytes(B, K, V), dtype=torch.uint8, device=dev)
+        g_arg = None if not len(greedy_rows) else ("all" if all_greedy else greedy_rows)
+        s_arg = None if not len(sampled_rows) else ("all" if all_sampled else sampled_rows)
+
     def step(r):
-        sv.spec_verify_logits(hidden, W, logits, stream=stream)
         d = drafts[r % n_sets]
+        if step_ws is not None:
+            sv.spec_verify_step(hidden, W, logits, acc, out, step_ws, draft_logits=zd, draft_tokens=d, temperature=T,
+                                seeds=seeds[r], greedy_rows=g_arg, sampled_rows=s_arg, stream=stream)
+            return
+        sv.spec_verify_logits(hidden, W, logits, stream=stream)
         if tree is not None:
             sv.spec_tree_accept_greedy(logits, tree[0], tree[1][r % n_sets], acc, out, ws, out_nodes=tree[2],
                                        stream=stream)
@@ -307,6 +320,7 @@ def main():
         **({"verify_rows": M, "draft_counts": "K_b ~ U{0..%d}, packed" % K} if row_start is not None else {}),
         **({"tree_nodes": K, "mean_kept_depth": float(np.mean(accepted))} if tree is not None else {}),
         "verify_step_us": step_s * 1e6,
+        "path": "spec_verify_step (fused statistics)" if step_ws is not None else "separate calls",
         "committed_tokens_per_step_last": float(np.mean(accepted + 1)),
         "roofline": roof,
     }

@@ -44,6 +44,10 @@
  *                          blog, Medusa and EAGLE-2; "Speculative decoding"
  *                          course page, One pass, many candidate
  *                          continuations).
+ *   spec_verify_step    -- the whole step in one call: LM head, statistics
+ *                          (the target rows' folded into the LM head's
+ *                          epilogue, which saves a pass over the logits) and
+ *                          both accept rules.
  *   spec_ngram_propose  -- the step before verification for prompt lookup:
  *                          drafts copied from the most recent earlier
  *                          occurrence of the sequence's last n tokens
@@ -278,6 +282,47 @@ spec_status_t spec_tree_accept_greedy(const float* logits, const int32_t* parent
                                       int32_t* out_nodes,
                                       void* workspace, size_t workspace_bytes,
                                       spec_stream_t stream);
+
+/*
+ * spec_verify_step -- the whole verify step in one call.
+ *
+ * Same results as spec_verify_logits followed by spec_accept_greedy over
+ * greedy_rows and spec_accept_sample over sampled_rows, up to the rounding
+ * order of the softmax sums (so a sampled decision with a margin below about
+ * 1e-6 may differ; greedy decisions and the logits are identical).  The
+ * statistics of the target rows are computed in the LM-head kernel's epilogue
+ * while the logits are in registers (the cooperative and direct-to-LDS
+ * kernels; the other kernels fall back to the statistics pass), so the
+ * logits are written once and not read back for statistics; the draft rows'
+ * statistics are computed before the LM head.  Long verify blocks (K = 15 at
+ * B <= 32) make the LM head compute-bound ("Inference-4", DFlash), where this
+ * saves the most.
+ *
+ *   hidden, w_lmhead, dtype, logits, B, K, V, H: as in spec_verify_logits
+ *   draft_logits, draft_tokens, temperature, seeds, probs_at_draft,
+ *   accepted_len, out_tokens: as in spec_accept_sample (draft_logits, seeds and
+ *                 temperature are needed only when sampled rows exist)
+ *   greedy_rows, n_greedy / sampled_rows, n_sampled
+ *                 the sequences verified by each rule: a device list of
+ *                 distinct entries (as `rows` in the accept calls), or NULL
+ *                 with n = 0 (none) or n = B (all)
+ *   workspace     at least spec_verify_step_workspace_bytes(B, K, V) bytes,
+ *                 16-byte aligned; contents on entry do not matter
+ * Errors as in the three calls it replaces.
+ */
+spec_status_t spec_verify_step(const void* hidden, const void* w_lmhead, spec_dtype_t dtype,
+                               const float* draft_logits, const int32_t* draft_tokens,
+                               float temperature, const uint64_t* seeds,
+                               const int32_t* greedy_rows, int n_greedy,
+                               const int32_t* sampled_rows, int n_sampled,
+                               int B, int K, int V, int H,
+                               float* logits, int32_t* accepted_len, int32_t* out_tokens,
+                               float* probs_at_draft,
+                               void* workspace, size_t workspace_bytes,
+                               spec_stream_t stream);
+
+/* Bytes of workspace spec_verify_step needs (0 if the sizes are out of range). */
+size_t spec_verify_step_workspace_bytes(int B, int K, int V);
 
 /*
  * spec_ngram_propose -- prompt-lookup drafts for B token histories.

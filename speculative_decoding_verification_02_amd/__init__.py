@@ -17,7 +17,10 @@ in the library's HIP kernels; if the library is missing, every call raises.
                             rows=None)
     spec_ngram_propose(history, hist_start, max_len, max_ngram, n_drafts, drafts, draft_count, workspace,
                        row_start=None)
-    spec_workspace_bytes(B, K, V), spec_ngram_workspace_bytes(B, max_len)
+    spec_verify_step(hidden, w_lmhead, logits, accepted_len, out_tokens, workspace, draft_logits=None,
+                     draft_tokens=None, temperature=1.0, seeds=None, greedy_rows=None, sampled_rows=None,
+                     probs_at_draft=None)
+    spec_workspace_bytes(B, K, V), spec_ngram_workspace_bytes(B, max_len), spec_verify_step_workspace_bytes(B, K, V)
 """
 from __future__ import annotations
 
@@ -30,6 +33,7 @@ __all__ = [
     "SPEC_ERR_WORKSPACE", "SPEC_ERR_HIP", "SPEC_BF16", "SPEC_F32", "LIB_PATH", "HEADER_PATH",
     "load_library", "declared_symbols", "spec_verify_logits", "spec_accept_greedy",
     "spec_accept_sample", "spec_accept_greedy_ragged", "spec_accept_sample_ragged", "spec_tree_accept_greedy", "spec_ngram_propose", "spec_ngram_workspace_bytes",
+    "spec_verify_step", "spec_verify_step_workspace_bytes",
     "spec_workspace_bytes", "spec_status_string", "spec_last_error_detail",
 ]
 
@@ -60,6 +64,10 @@ _SIGNATURES = {
     "spec_ngram_propose": (_c_int, [_c_void_p, _c_void_p, _c_int, _c_int, _c_int, _c_int, _c_void_p, _c_void_p,
                                     _c_void_p, _c_void_p, _c_size_t, _c_void_p]),
     "spec_ngram_workspace_bytes": (_c_size_t, [_c_int, _c_int]),
+    "spec_verify_step": (_c_int, [_c_void_p, _c_void_p, _c_int, _c_void_p, _c_void_p, _c_float, _c_void_p, _c_void_p,
+                                  _c_int, _c_void_p, _c_int, _c_int, _c_int, _c_int, _c_int, _c_void_p, _c_void_p,
+                                  _c_void_p, _c_void_p, _c_void_p, _c_size_t, _c_void_p]),
+    "spec_verify_step_workspace_bytes": (_c_size_t, [_c_int, _c_int, _c_int]),
     "spec_workspace_bytes": (_c_size_t, [_c_int, _c_int, _c_int]),
     "spec_status_string": (ctypes.c_char_p, [_c_int]),
     "spec_last_error_detail": (ctypes.c_char_p, []),
@@ -252,3 +260,38 @@ def spec_ngram_propose(history, hist_start, max_len, max_ngram, n_drafts, drafts
                                   int(max_ngram), int(n_drafts), _ptr(drafts) if n_drafts else None,
                                   _ptr(draft_count), _ptr(row_start), _ptr(workspace),
                                   workspace.numel() * workspace.element_size(), _stream(stream)))
+
+
+def spec_verify_step_workspace_bytes(B: int, K: int, V: int) -> int:
+    return int(load_library().spec_verify_step_workspace_bytes(B, K, V))
+
+
+def _row_list(rows, B):
+    """(pointer, n) for the fused step: None = none, "all" = every sequence,
+    else an int32 device tensor."""
+    if rows is None:
+        return None, 0
+    if isinstance(rows, str) and rows == "all":
+        return None, B
+    return rows, int(rows.numel())
+
+
+def spec_verify_step(hidden, w_lmhead, logits, accepted_len, out_tokens, workspace, draft_logits=None,
+                     draft_tokens=None, temperature=1.0, seeds=None, greedy_rows=None, sampled_rows=None,
+                     probs_at_draft=None, stream=None) -> None:
+    """The whole verify step: logits[B, K+1, V] = hidden . w_lmheadᵀ, then greedy
+    acceptance of ``greedy_rows`` and speculative sampling of ``sampled_rows``
+    (each None, "all", or an int32 device tensor of sequence indices)."""
+    B, P, H = hidden.shape
+    V = w_lmhead.shape[0]
+    if w_lmhead.dtype != hidden.dtype or tuple(logits.shape) != (B, P, V) or w_lmhead.shape[1] != H:
+        raise ValueError("shape or dtype mismatch")
+    g, ng = _row_list(greedy_rows, B)
+    sm, ns = _row_list(sampled_rows, B)
+    lib = load_library()
+    _check("spec_verify_step",
+           lib.spec_verify_step(_ptr(hidden), _ptr(w_lmhead), _dtype_code(hidden),
+                                _ptr(draft_logits) if P > 1 else None, _ptr(draft_tokens) if P > 1 else None,
+                                float(temperature), _ptr(seeds), _ptr(g), ng, _ptr(sm), ns, B, P - 1, V, H,
+                                _ptr(logits), _ptr(accepted_len), _ptr(out_tokens), _ptr(probs_at_draft),
+                                _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream)))

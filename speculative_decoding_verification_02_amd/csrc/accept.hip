@@ -62,11 +62,41 @@ __device__ __forceinline__ Merged wave_merge(const StatRec* rec, int nc, float c
     return Merged{m, s, idx, bad};
 }
 
+// Merge the records of n consecutive rows (nc records each, row r at
+// base + r*nc) into merged[out0 + r], one wavefront per row.  Rows are staged
+// through LDS with every load in flight at once when they fit; rows longer
+// than the buffer are merged straight from global memory.  Called by the
+// whole workgroup.
+__device__ void merge_rows(const StatRec* __restrict__ base, int n, int nc, float c, bool need_sum, StatRec* recs,
+                           Merged* merged, int out0) {
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    if (nc > kRecBuf) {
+        for (int rr = wave; rr < n; rr += kAcceptWaves) {
+            const Merged x = wave_merge(base + (size_t)rr * nc, nc, c, need_sum, lane);
+            if (lane == 0) merged[out0 + rr] = x;
+        }
+        __syncthreads();
+        return;
+    }
+    const int rows_per_pass = max(1, min(n, kRecBuf / nc));
+    for (int r0 = 0; r0 < n; r0 += rows_per_pass) {
+        const int nr = min(rows_per_pass, n - r0);
+        const StatRec* src = base + (size_t)r0 * nc;
+        for (int e = tid; e < nr * nc; e += kAcceptThreads) recs[e] = src[e];
+        __syncthreads();
+        for (int rr = wave; rr < nr; rr += kAcceptWaves) {
+            const Merged x = wave_merge(recs + rr * nc, nc, c, need_sum, lane);
+            if (lane == 0) merged[out0 + r0 + rr] = x;
+        }
+        __syncthreads();
+    }
+}
+
 template <bool SAMPLED>
 __global__ __launch_bounds__(kAcceptThreads) void accept_kernel(
     const float* __restrict__ logits, const float* __restrict__ draft_logits, const int32_t* __restrict__ draft_tokens,
-    const uint64_t* __restrict__ seeds, const int32_t* __restrict__ rows, int n_rows, SeqRows seq, int V, int nc,
-    float c, const StatRec* __restrict__ stats, int32_t* __restrict__ accepted_len, int32_t* __restrict__ out_tokens,
+    const uint64_t* __restrict__ seeds, const int32_t* __restrict__ rows, int n_rows, SeqRows seq, int V,
+    float c, RecLayout rec, int32_t* __restrict__ accepted_len, int32_t* __restrict__ out_tokens,
     float* __restrict__ probs_at_draft, AcceptInfo* __restrict__ info, int* __restrict__ counters) {
     __shared__ StatRec recs[kRecBuf];
     __shared__ Merged merged[kMaxRows];
@@ -105,26 +135,11 @@ __global__ __launch_bounds__(kAcceptThreads) void accept_kernel(
         }
     }
 
-    // rows of this sequence: target 0..kb, then (sampled) draft 0..kb-1; their
-    // records sit at the slots of a K-draft sequence
-    const int n_rows_seq = (kb + 1) + (SAMPLED ? kb : 0);
-    const int rows_per_pass = max(1, min(n_rows_seq, kRecBuf / nc));
-    for (int r0 = 0; r0 < n_rows_seq; r0 += rows_per_pass) {
-        const int nr = min(rows_per_pass, n_rows_seq - r0);
-        // stage the records of rows r0 .. r0+nr-1: every load in flight at once
-        for (int e = tid; e < nr * nc; e += kAcceptThreads) {
-            const int rr = r0 + e / nc, k = e - (e / nc) * nc;
-            const size_t row_rec = rr <= kb ? (size_t)j * (K + 1) + rr
-                                            : (size_t)n_rows * (K + 1) + (size_t)j * K + (rr - kb - 1);
-            recs[e] = stats[row_rec * nc + k];
-        }
-        __syncthreads();
-        for (int rr = wave; rr < nr; rr += kAcceptWaves) {
-            const Merged x = wave_merge(recs + rr * nc, nc, c, SAMPLED, lane);
-            if (lane == 0) merged[r0 + rr] = x;
-        }
-        __syncthreads();
-    }
+    // merged statistics of the target rows 0..kb, then (sampled) the draft
+    // rows 0..kb-1 (merged[kb+1+i])
+    const StatRec* tgt0 = rec.tgt + (size_t)(rec.tgt_by_row ? t0 : j * (K + 1)) * rec.tgt_nc;
+    merge_rows(tgt0, kb + 1, rec.tgt_nc, c, SAMPLED, recs, merged, 0);
+    if (SAMPLED && kb > 0) merge_rows(rec.drf + (size_t)j * K * rec.drf_nc, kb, rec.drf_nc, c, true, recs, merged, kb + 1);
     if (wave != 0) return;
 
     Merged t{-INFINITY, 0.f, INT_MAX, 0}, d{-INFINITY, 0.f, INT_MAX, 0};
@@ -317,18 +332,17 @@ hipError_t launch_tree_accept(const int32_t* parents, const int32_t* tokens, con
 
 hipError_t launch_accept(const float* logits, const float* draft_logits, const int32_t* draft_tokens,
                          const uint64_t* seeds, const int32_t* rows, int n_rows, SeqRows seq, int V,
-                         float inv_t_log2e, bool sampled, const StatRec* stats, int32_t* accepted_len,
+                         float inv_t_log2e, bool sampled, RecLayout rec, int32_t* accepted_len,
                          int32_t* out_tokens, float* probs_at_draft, AcceptInfo* info, int* counters,
                          hipStream_t stream) {
     if (n_rows == 0) return hipSuccess;
-    const int nc = n_chunks(V);
     if (sampled)
         hipLaunchKernelGGL(accept_kernel<true>, dim3(n_rows), dim3(kAcceptThreads), 0, stream, logits, draft_logits,
-                           draft_tokens, seeds, rows, n_rows, seq, V, nc, inv_t_log2e, stats, accepted_len,
+                           draft_tokens, seeds, rows, n_rows, seq, V, inv_t_log2e, rec, accepted_len,
                            out_tokens, probs_at_draft, info, counters);
     else
         hipLaunchKernelGGL(accept_kernel<false>, dim3(n_rows), dim3(kAcceptThreads), 0, stream, logits, draft_logits,
-                           draft_tokens, seeds, rows, n_rows, seq, V, nc, inv_t_log2e, stats, accepted_len,
+                           draft_tokens, seeds, rows, n_rows, seq, V, inv_t_log2e, rec, accepted_len,
                            out_tokens, probs_at_draft, info, counters);
     return hipGetLastError();
 }

@@ -18,6 +18,8 @@
 // of one hidden row, stored as one float4.  The contraction does not depend on
 // the order of the hidden columns, only on A and B pairing the same column in
 // the same (lane group, element) slot, which both loads below guarantee.
+#include <limits.h>
+
 #include "sv_common.h"
 #include "sv_launch.h"
 
@@ -221,19 +223,26 @@ struct Coop {
     static constexpr int kSlice = MAXST * kKS;    // k elements per wave
     static constexpr int kBufChunks = 16 * kCPR;
     static constexpr int kThreads = NW * 64;
-    static size_t lds_bytes() { return (size_t)NW * kBufChunks * 16 + 2 * (size_t)NW * 64 * 16; }
+    static size_t lds_bytes() { return (size_t)NW * kBufChunks * 16 + 2 * (size_t)NW * 64 * 16 + (size_t)NW * 16 * 16; }
     static bool fits(int M, int H) { return M <= 16 && H <= NW * kSlice; }
 };
 
-template <int RPL, int MAXST, int NW>
+// With STATS, the workgroup also folds each stored tile into running softmax
+// statistics of its rows (max, lowest argmax, sum of 2^((z - max) c)) and
+// writes one record per row for its whole tile range: stats[r * gridDim.x +
+// blockIdx.x].  Workgroups own contiguous ranges in order, so the records of
+// a row are in vocabulary order.
+template <int RPL, int MAXST, int NW, bool STATS>
 __global__ __launch_bounds__(NW * 64) void lmhead_coop_bf16(
     const uint16_t* __restrict__ hidden, const uint16_t* __restrict__ W, float* __restrict__ logits,
-    int M, int V, int H, int n_tiles) {
+    int M, int V, int H, int n_tiles, StatRec* __restrict__ stats, float c) {
     using S = Coop<RPL, MAXST, NW>;
     extern __shared__ __align__(16) unsigned char smem[];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     u32x4* buf = reinterpret_cast<u32x4*>(smem) + wave * S::kBufChunks;
     f32x4* red = reinterpret_cast<f32x4*>(smem + (size_t)NW * S::kBufChunks * 16);   // [2][NW][64]
+    StatRec* run = reinterpret_cast<StatRec*>(smem + (size_t)NW * S::kBufChunks * 16 + 2 * (size_t)NW * 64 * 16);
+    StatRec own{-INFINITY, 0.f, INT_MAX, 0};   // this wave's running record of row lane % 16
 
     const int la = lane / S::kLanesPerRow, lc = lane % S::kLanesPerRow;
     const int r = lane & 15, g = lane >> 4;
@@ -304,15 +313,54 @@ __global__ __launch_bounds__(NW * 64) void lmhead_coop_bf16(
 #pragma unroll
             for (int w = 1; w < NW; ++w) s += rb[w * 64 + lane];
             if (r < M) store_row4(logits + (size_t)r * V, (t << 4) + 4 * g, V, s, vec_ok);
+            if constexpr (STATS) {
+                // row r of the tile: lanes r, r+16, r+32, r+48 hold entries
+                // 4g .. 4g+3 in ascending order; folded into this wave's
+                // running record (kept by the lanes with g == 0)
+                const int vb = (t << 4) + 4 * g;
+                float m = -INFINITY;
+                int mi = INT_MAX;
+                float ze[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    ze[e] = vb + e < V ? s[e] : -INFINITY;
+                    mi = ze[e] > m ? vb + e : mi;
+                    m = fmaxf(m, ze[e]);
+                }
+#pragma unroll
+                for (int o = 16; o < 64; o <<= 1) argmax_combine(m, mi, __shfl_xor(m, o, kWave), __shfl_xor(mi, o, kWave));
+                const float mc = (m == -INFINITY ? 0.f : m) * c;
+                float sum = 0.f;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) sum += __builtin_amdgcn_exp2f(fmaf(ze[e], c, -mc));
+                sum += __shfl_xor(sum, 16, kWave);
+                sum += __shfl_xor(sum, 32, kWave);
+                const int bad = m == INFINITY || sum != sum;
+                stat_fold(own, bad ? -INFINITY : m, sum, mi, bad, c);
+            }
+        }
+    }
+    if constexpr (STATS) {
+        // the waves' records of each row, folded in wave order
+        __syncthreads();
+        if (lane < 16) run[wave * 16 + lane] = own;
+        __syncthreads();
+        if (threadIdx.x < M) {
+            StatRec a{-INFINITY, 0.f, INT_MAX, 0};
+            for (int w = 0; w < NW; ++w) {
+                const StatRec x = run[w * 16 + threadIdx.x];
+                stat_fold(a, x.m, x.s, x.idx, x.bad, c);
+            }
+            stats[(size_t)threadIdx.x * gridDim.x + blockIdx.x] = a;
         }
     }
 }
 
-template <int RPL, int MAXST, int NW>
+template <int RPL, int MAXST, int NW, bool STATS>
 hipError_t launch_coop(const uint16_t* hidden, const uint16_t* W, float* logits, int M, int V, int H, int num_cus,
-                       hipStream_t stream, int blocks_per_cu) {
+                       hipStream_t stream, int blocks_per_cu, StatRec* stats, float c, int* n_rec) {
     using S = Coop<RPL, MAXST, NW>;
-    auto kern = lmhead_coop_bf16<RPL, MAXST, NW>;
+    auto kern = lmhead_coop_bf16<RPL, MAXST, NW, STATS>;
     const int n_tiles = (V + 15) / 16;
     const size_t lds = S::lds_bytes();
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
@@ -322,8 +370,10 @@ hipError_t launch_coop(const uint16_t* hidden, const uint16_t* W, float* logits,
     e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, kern, S::kThreads, lds);
     if (e != hipSuccess) return e;
     occ = max(1, min(occ, blocks_per_cu));
-    const int grid = (int)min((long)n_tiles, (long)num_cus * occ);
-    hipLaunchKernelGGL(kern, dim3(grid), dim3(S::kThreads), lds, stream, hidden, W, logits, M, V, H, n_tiles);
+    const int grid = (int)min(min((long)n_tiles, (long)num_cus * occ), (long)kMaxStatRecs);
+    hipLaunchKernelGGL(kern, dim3(grid), dim3(S::kThreads), lds, stream, hidden, W, logits, M, V, H, n_tiles, stats,
+                       c);
+    if (n_rec) *n_rec = grid;
     return hipGetLastError();
 }
 
@@ -512,10 +562,12 @@ __device__ __forceinline__ void wait_slices(int after) {
     wait_vmcnt<0>();
 }
 
-template <int BK, int SLOTS, int NA, int NB>
+// With STATS, the workgroup also writes the softmax statistics of each of its
+// hidden rows over its 256 vocabulary columns: stats[m * tiles_n + tn].
+template <int BK, int SLOTS, int NA, int NB, bool STATS>
 __global__ __launch_bounds__(kBigThreads, 1) void lmhead_big_bf16(
     const uint16_t* __restrict__ hidden, const uint16_t* __restrict__ W, float* __restrict__ logits,
-    int M, int V, int H, int tiles_n, int tiles_m) {
+    int M, int V, int H, int tiles_n, int tiles_m, StatRec* __restrict__ stats, float c) {
     using G = Big<BK, SLOTS, NA, NB>;
     extern __shared__ __align__(16) unsigned char smem[];
     u32x4* lds = reinterpret_cast<u32x4*>(smem);   // [slot][W rows 0..255 | hidden rows 0..BM-1][CPR chunks]
@@ -623,11 +675,11 @@ __global__ __launch_bounds__(kBigThreads, 1) void lmhead_big_bf16(
         __builtin_amdgcn_s_waitcnt((0xF) | (0x3 << 14) | (0x7 << 4) | (0x0 << 8));   // lgkmcnt(0)
     }
 
+    // logits of row block b: four runs of four consecutive vocabulary entries
     const bool vec_ok = (V & 3) == 0;
-#pragma unroll
-    for (int b = 0; b < NB; ++b) {
+    auto store_rows = [&](int b) {
         const int m = m0 + wm + b * 32 + r;
-        if (m >= M) continue;
+        if (m >= M) return;
         float* out = logits + (size_t)m * V;
 #pragma unroll
         for (int a = 0; a < NA; ++a)
@@ -636,14 +688,74 @@ __global__ __launch_bounds__(kBigThreads, 1) void lmhead_big_bf16(
                 const f32x4 v4 = {acc[a][b][4 * q], acc[a][b][4 * q + 1], acc[a][b][4 * q + 2], acc[a][b][4 * q + 3]};
                 store_row4(out, v0 + wn + a * 32 + 8 * q + 4 * h, V, v4, vec_ok);
             }
+    };
+
+    if constexpr (STATS) {
+        // per hidden row: this lane's 16*NA entries (ascending vocabulary
+        // index), then its partner lane^32 (the other half of the columns),
+        // then the kWN waves side by side along the vocabulary, in order,
+        // through the LDS ring (free once every wave is past its last slice);
+        // each row block's logits are stored right after its statistics.
+        // No per-entry checks: fmaxf skips NaN and a NaN or +inf shows in the
+        // maximum or the sum, which marks the row bad; entries past V are
+        // masked only in the last vocabulary tile.
+        __syncthreads();
+        StatRec* part = reinterpret_cast<StatRec*>(smem);   // [kWN][BM]
+        const bool full = v0 + wn + 32 * NA <= V;
+#pragma unroll
+        for (int b = 0; b < NB; ++b) {
+            float mx = -INFINITY;
+            int mi = INT_MAX;
+#pragma unroll
+            for (int a = 0; a < NA; ++a)
+#pragma unroll
+                for (int i = 0; i < 16; ++i) {
+                    const int v = v0 + wn + a * 32 + 8 * (i / 4) + 4 * h + (i % 4);
+                    const float z = (full || v < V) ? acc[a][b][i] : -INFINITY;
+                    mi = z > mx ? v : mi;
+                    mx = fmaxf(mx, z);
+                }
+            argmax_combine(mx, mi, __shfl_xor(mx, 32, kWave), __shfl_xor(mi, 32, kWave));
+            const float mc = (mx == -INFINITY ? 0.f : mx) * c;
+            float sum = 0.f;
+#pragma unroll
+            for (int a = 0; a < NA; ++a)
+#pragma unroll
+                for (int i = 0; i < 16; ++i) {
+                    const int v = v0 + wn + a * 32 + 8 * (i / 4) + 4 * h + (i % 4);
+                    const float z = (full || v < V) ? acc[a][b][i] : -INFINITY;
+                    sum += __builtin_amdgcn_exp2f(fmaf(z, c, -mc));
+                }
+            sum += __shfl_xor(sum, 32, kWave);
+            const int bad = mx == INFINITY || sum != sum;
+            if (h == 0) part[(wave % G::kWN) * G::kBM + wm + b * 32 + r] = StatRec{mx, sum, mi, bad};
+            store_rows(b);   // block b's registers are free after this
+        }
+        __syncthreads();
+        for (int row = threadIdx.x; row < G::kBM; row += kBigThreads) {
+            if (m0 + row >= M) continue;
+            StatRec t{-INFINITY, 0.f, INT_MAX, 0};
+#pragma unroll
+            for (int w = 0; w < G::kWN; ++w) {
+                const StatRec x = part[w * G::kBM + row];
+                stat_fold(t, x.bad ? -INFINITY : x.m, x.s, x.idx, x.bad, c);
+            }
+            stats[(size_t)(m0 + row) * tiles_n + tn] = t;
+        }
+    }
+
+    if constexpr (!STATS) {
+#pragma unroll
+        for (int b = 0; b < NB; ++b) store_rows(b);
     }
 }
 
-template <int BK, int SLOTS, int NA, int NB>
+template <int BK, int SLOTS, int NA, int NB, bool STATS>
 hipError_t launch_big_cfg(const uint16_t* hidden, const uint16_t* W, float* logits, int M, int V, int H,
-                          hipStream_t stream) {
+                          hipStream_t stream, StatRec* stats = nullptr, float c = 0.f) {
     using G = Big<BK, SLOTS, NA, NB>;
-    auto kern = lmhead_big_bf16<BK, SLOTS, NA, NB>;
+    static_assert(!STATS || (size_t)G::kWN * G::kBM * sizeof(StatRec) <= G::kLds, "statistics exchange fits the ring");
+    auto kern = lmhead_big_bf16<BK, SLOTS, NA, NB, STATS>;
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)G::kLds);
     if (e != hipSuccess) return e;
@@ -651,7 +763,7 @@ hipError_t launch_big_cfg(const uint16_t* hidden, const uint16_t* W, float* logi
     const int tiles_m = (M + G::kBM - 1) / G::kBM;
     const int grid = ((tiles_n * tiles_m + 7) / 8) * 8;
     hipLaunchKernelGGL(kern, dim3(grid), dim3(kBigThreads), G::kLds, stream, hidden, W, logits, M, V, H, tiles_n,
-                       tiles_m);
+                       tiles_m, stats, c);
     return hipGetLastError();
 }
 
@@ -674,15 +786,16 @@ bool big_fits(int M, int V, int H) {
     return M >= kBigMinM && H % kBigBK == 0 && (uint64_t)V * H < (1ull << 32) && (uint64_t)M * H < (1ull << 32);
 }
 
+template <bool STATS>
 hipError_t launch_big(const uint16_t* hidden, const uint16_t* W, float* logits, int M, int V, int H,
-                      hipStream_t stream) {
-    if (M <= 64) return launch_big_cfg<kBigBK, 3, 4, 1>(hidden, W, logits, M, V, H, stream);
-    if (M <= 128) return launch_big_cfg<kBigBK, 3, 4, 2>(hidden, W, logits, M, V, H, stream);
-    if (M <= 160) return launch_big_cfg<kBigBK, 3, 2, 5>(hidden, W, logits, M, V, H, stream);
-    if (M <= 192) return launch_big_cfg<kBigBK, 2, 4, 3>(hidden, W, logits, M, V, H, stream);
-    if (M <= 256) return launch_big_cfg<kBigBK, 2, 2, 8>(hidden, W, logits, M, V, H, stream);
-    if (M <= 320) return launch_big_cfg<kBigBK, 3, 2, 5>(hidden, W, logits, M, V, H, stream);
-    return launch_big_cfg<kBigBK, 2, 2, 8>(hidden, W, logits, M, V, H, stream);
+                      hipStream_t stream, StatRec* stats, float c) {
+    if (M <= 64) return launch_big_cfg<kBigBK, 3, 4, 1, STATS>(hidden, W, logits, M, V, H, stream, stats, c);
+    if (M <= 128) return launch_big_cfg<kBigBK, 3, 4, 2, STATS>(hidden, W, logits, M, V, H, stream, stats, c);
+    if (M <= 160) return launch_big_cfg<kBigBK, 3, 2, 5, STATS>(hidden, W, logits, M, V, H, stream, stats, c);
+    if (M <= 192) return launch_big_cfg<kBigBK, 2, 4, 3, STATS>(hidden, W, logits, M, V, H, stream, stats, c);
+    if (M <= 256) return launch_big_cfg<kBigBK, 2, 2, 8, STATS>(hidden, W, logits, M, V, H, stream, stats, c);
+    if (M <= 320) return launch_big_cfg<kBigBK, 3, 2, 5, STATS>(hidden, W, logits, M, V, H, stream, stats, c);
+    return launch_big_cfg<kBigBK, 2, 2, 8, STATS>(hidden, W, logits, M, V, H, stream, stats, c);
 }
 
 // ------------------------------------------------------------------ fp32 ---
@@ -717,10 +830,20 @@ __global__ __launch_bounds__(kF32Threads) void lmhead_f32(
 // ------------------------------------------------------------ launchers ----
 
 hipError_t launch_lmhead_bf16(const uint16_t* hidden, const uint16_t* W, float* logits, int M, int V, int H,
-                              int num_cus, hipStream_t stream, int force_kernel) {
-    if (force_kernel == 0 && CoopCfg::fits(M, H))
-        return launch_coop<2, 2, 8>(hidden, W, logits, M, V, H, num_cus, stream, 1);
-    if (force_kernel == 0 && big_fits(M, V, H)) return launch_big(hidden, W, logits, M, V, H, stream);
+                              int num_cus, hipStream_t stream, int force_kernel, StatRec* stats, float c,
+                              int* n_rec) {
+    if (n_rec) *n_rec = 0;
+    if (force_kernel == 0 && CoopCfg::fits(M, H)) {
+        if (stats) return launch_coop<2, 2, 8, true>(hidden, W, logits, M, V, H, num_cus, stream, 1, stats, c, n_rec);
+        return launch_coop<2, 2, 8, false>(hidden, W, logits, M, V, H, num_cus, stream, 1, nullptr, 0.f, nullptr);
+    }
+    if (force_kernel == 0 && big_fits(M, V, H)) {
+        if (stats) {
+            if (n_rec) *n_rec = (V + kBigBN - 1) / kBigBN;
+            return launch_big<true>(hidden, W, logits, M, V, H, stream, stats, c);
+        }
+        return launch_big<false>(hidden, W, logits, M, V, H, stream, nullptr, 0.f);
+    }
     const bool skinny = force_kernel == 1 || (force_kernel == 0 && skinny_fits(M, H));
     if (skinny) return launch_skinny<kSkRPL, kSkP, kSkThreads>(hidden, W, logits, M, V, H, num_cus, stream);
     const int tiles_n = (V + kTileN - 1) / kTileN;

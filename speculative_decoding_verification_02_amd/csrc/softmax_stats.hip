@@ -55,7 +55,7 @@ __global__ __launch_bounds__(kStatThreads) void softmax_stats_kernel(
     const int K = seq.K;
     const int job = blockIdx.x / nc;
     const int chunk = blockIdx.x - job * nc;
-    const int tgt_jobs = n_rows * (K + 1);
+    const int tgt_jobs = logits ? n_rows * (K + 1) : 0;   // no target rows: draft rows only
     const bool target = job < tgt_jobs;
     int j, i;
     if (target) {
@@ -134,7 +134,7 @@ hipError_t launch_softmax_stats(const float* logits, const float* draft_logits, 
                                 SeqRows seq, int V, float inv_t_log2e, bool need_sum, StatRec* stats,
                                 hipStream_t stream) {
     const int nc = n_chunks(V);
-    const long jobs = (long)n_rows * (seq.K + 1) + (draft_logits ? (long)n_rows * seq.K : 0);
+    const long jobs = (logits ? (long)n_rows * (seq.K + 1) : 0) + (draft_logits ? (long)n_rows * seq.K : 0);
     const long blocks = jobs * nc;
     if (blocks == 0) return hipSuccess;
     if (need_sum)

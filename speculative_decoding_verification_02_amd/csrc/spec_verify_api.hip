@@ -107,6 +107,12 @@ spec_status_t check_ragged(const int32_t* row_start, int total_rows, int B, int 
     return SPEC_OK;
 }
 
+// records written by the statistics pass: target slots, then draft slots
+sv::RecLayout pass_layout(const sv::StatRec* stats, int n_rows, int K, int V) {
+    const int nc = sv::n_chunks(V);
+    return sv::RecLayout{stats, nc, false, stats + (size_t)n_rows * (K + 1) * nc, nc};
+}
+
 spec_status_t greedy_impl(const float* logits, const int32_t* draft_tokens, const int32_t* rows, int n_rows,
                           sv::SeqRows seq, int V, int32_t* accepted_len, int32_t* out_tokens, void* workspace,
                           size_t workspace_bytes, hipStream_t s) {
@@ -120,8 +126,9 @@ spec_status_t greedy_impl(const float* logits, const int32_t* draft_tokens, cons
     workspace_layout(seq.B, seq.K, V, workspace, &ws);
     hipError_t e = sv::launch_softmax_stats(logits, nullptr, rows, nr, seq, V, sv::kLog2e, false, ws.stats, s);
     if (e == hipSuccess)
-        e = sv::launch_accept(logits, nullptr, draft_tokens, nullptr, rows, nr, seq, V, sv::kLog2e, false, ws.stats,
-                              accepted_len, out_tokens, nullptr, ws.info, ws.counters, s);
+        e = sv::launch_accept(logits, nullptr, draft_tokens, nullptr, rows, nr, seq, V, sv::kLog2e, false,
+                              pass_layout(ws.stats, nr, seq.K, V), accepted_len, out_tokens, nullptr, ws.info,
+                              ws.counters, s);
     return e == hipSuccess ? SPEC_OK : hip_fail(e);
 }
 
@@ -145,8 +152,9 @@ spec_status_t sample_impl(const float* logits, const float* draft_logits, const 
     const float* dl = has_drafts ? draft_logits : nullptr;
     hipError_t e = sv::launch_softmax_stats(logits, dl, rows, nr, seq, V, c, true, ws.stats, s);
     if (e == hipSuccess)
-        e = sv::launch_accept(logits, dl, draft_tokens, seeds, rows, nr, seq, V, c, true, ws.stats, accepted_len,
-                              out_tokens, probs_at_draft, ws.info, ws.counters, s);
+        e = sv::launch_accept(logits, dl, draft_tokens, seeds, rows, nr, seq, V, c, true,
+                              pass_layout(ws.stats, nr, seq.K, V), accepted_len, out_tokens, probs_at_draft, ws.info,
+                              ws.counters, s);
     if (e == hipSuccess) e = sv::launch_residual(logits, dl, nr, V, c, ws.info, ws.sums, ws.counters, out_tokens, s);
     return e == hipSuccess ? SPEC_OK : hip_fail(e);
 }
@@ -154,6 +162,19 @@ spec_status_t sample_impl(const float* logits, const float* draft_logits, const 
 // dense batch: sequence b owns target rows b*(K+1) .. b*(K+1)+K (sizes_ok has
 // bounded B*(K+1) to 31 bits)
 sv::SeqRows dense_rows(int B, int K) { return sv::SeqRows{nullptr, B, K, B * (K + 1)}; }
+
+// Records per target row the fused step may write: the cooperative kernel
+// writes one per workgroup (at most one per 16 vocabulary entries, at most
+// kMaxStatRecs), the direct-to-LDS kernel one per 256 entries, the
+// statistics pass one per 4096-entry chunk.
+size_t step_target_recs(int M, int V) {
+    const size_t by16 = ((size_t)V + 15) / 16, by256 = ((size_t)V + 255) / 256;
+    return M <= 16 ? std::min(by16, (size_t)sv::kMaxStatRecs) : by256;
+}
+
+// A row list as the fused step takes it: (NULL, 0) none, (NULL, B) all,
+// (list, 0..B) those.
+bool rows_ok(const int32_t* rows, int n, int B) { return rows ? (n >= 0 && n <= B) : (n == 0 || n == B); }
 
 }  // namespace
 
@@ -266,6 +287,80 @@ size_t spec_ngram_workspace_bytes(int B, int max_len) {
     if (B < 1 || max_len < 0 || max_len == 0x7fffffff) return 0;
     const size_t segs = (size_t)std::max(1, sv::ngram_segments(max_len));
     return align256((size_t)B * segs * sizeof(unsigned long long));
+}
+
+spec_status_t spec_verify_step(const void* hidden, const void* w_lmhead, spec_dtype_t dtype,
+                               const float* draft_logits, const int32_t* draft_tokens, float temperature,
+                               const uint64_t* seeds, const int32_t* greedy_rows, int n_greedy,
+                               const int32_t* sampled_rows, int n_sampled, int B, int K, int V, int H,
+                               float* logits, int32_t* accepted_len, int32_t* out_tokens, float* probs_at_draft,
+                               void* workspace, size_t workspace_bytes, spec_stream_t stream) {
+    if (!hidden || !w_lmhead || !logits || !accepted_len || !out_tokens) return SPEC_ERR_ARG;
+    if (dtype != SPEC_BF16 && dtype != SPEC_F32) return SPEC_ERR_DTYPE;
+    if (!sizes_ok(B, K, V) || H < 8 || (H & 7) != 0) return SPEC_ERR_ARG;
+    if (!rows_ok(greedy_rows, n_greedy, B) || !rows_ok(sampled_rows, n_sampled, B)) return SPEC_ERR_ARG;
+    const bool any = n_greedy > 0 || n_sampled > 0;
+    if (any && K > 0 && !draft_tokens) return SPEC_ERR_ARG;
+    if (n_sampled > 0) {
+        if (!seeds || (K > 0 && !draft_logits)) return SPEC_ERR_ARG;
+        if (!(temperature > 0.f) || !isfinite(temperature)) return SPEC_ERR_ARG;
+        if (K > 0 && !aligned16(draft_logits)) return SPEC_ERR_ALIGN;
+    }
+    if (!aligned16(hidden) || !aligned16(w_lmhead) || !aligned16(logits)) return SPEC_ERR_ALIGN;
+    if (!workspace || workspace_bytes < spec_verify_step_workspace_bytes(B, K, V)) return SPEC_ERR_WORKSPACE;
+    if (!aligned16(workspace)) return SPEC_ERR_ALIGN;
+
+    const int M = B * (K + 1);
+    Workspace ws;
+    const size_t base = workspace_layout(B, K, V, workspace, &ws);
+    sv::StatRec* tstats = reinterpret_cast<sv::StatRec*>(static_cast<char*>(workspace) + base);
+    const sv::SeqRows seq = dense_rows(B, K);
+    const float c = n_sampled > 0 ? sv::kLog2e / temperature : sv::kLog2e;
+    const int ns = sampled_rows ? n_sampled : (n_sampled ? B : 0);
+    const int ng = greedy_rows ? n_greedy : (n_greedy ? B : 0);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    hipError_t e = hipSuccess;
+
+    // draft-row statistics first: they do not depend on the LM head
+    const float* dl = (ns > 0 && K > 0) ? draft_logits : nullptr;
+    if (dl) e = sv::launch_softmax_stats(nullptr, dl, sampled_rows, ns, seq, V, c, true, ws.stats, s);
+    // LM head, with the target-row statistics in its epilogue where the
+    // chosen kernel has one; otherwise the statistics pass over all rows
+    int nrec = 0;
+    if (e == hipSuccess) {
+        if (dtype == SPEC_BF16) {
+            int cus = 0;
+            e = num_cus(&cus);
+            if (e == hipSuccess)
+                e = sv::launch_lmhead_bf16(static_cast<const uint16_t*>(hidden), static_cast<const uint16_t*>(w_lmhead),
+                                           logits, M, V, H, cus, s, 0, any ? tstats : nullptr, c, &nrec);
+        } else {
+            e = sv::launch_lmhead_f32(static_cast<const float*>(hidden), static_cast<const float*>(w_lmhead), logits,
+                                      M, V, H, s);
+        }
+    }
+    if (e == hipSuccess && any && nrec == 0) {
+        e = sv::launch_softmax_stats(logits, nullptr, nullptr, B, seq, V, c, true, tstats, s);
+        nrec = sv::n_chunks(V);
+    }
+    if (e == hipSuccess && ng > 0)
+        e = sv::launch_accept(logits, nullptr, draft_tokens, nullptr, greedy_rows, ng, seq, V, sv::kLog2e, false,
+                              sv::RecLayout{tstats, nrec, true, nullptr, 0}, accepted_len, out_tokens, nullptr,
+                              ws.info, ws.counters, s);
+    if (e == hipSuccess && ns > 0) {
+        e = sv::launch_accept(logits, dl, draft_tokens, seeds, sampled_rows, ns, seq, V, c, true,
+                              sv::RecLayout{tstats, nrec, true, ws.stats, sv::n_chunks(V)}, accepted_len, out_tokens,
+                              probs_at_draft, ws.info, ws.counters, s);
+        if (e == hipSuccess)
+            e = sv::launch_residual(logits, dl, ns, V, c, ws.info, ws.sums, ws.counters, out_tokens, s);
+    }
+    return e == hipSuccess ? SPEC_OK : hip_fail(e);
+}
+
+size_t spec_verify_step_workspace_bytes(int B, int K, int V) {
+    if (!sizes_ok(B, K, V)) return 0;
+    const size_t M = (size_t)B * (K + 1);
+    return workspace_layout(B, K, V, nullptr, nullptr) + align256(M * step_target_recs((int)M, V) * sizeof(sv::StatRec));
 }
 
 size_t spec_workspace_bytes(int B, int K, int V) {

@@ -102,6 +102,30 @@ __device__ __forceinline__ void wave_argmax(float& m, int& i) {
     }
 }
 
+// Fold the statistics (m, s, i, bad) of one span of a row into a running
+// record a, both relative to c = log2(e) / T:
+//   M = max(a.m, m),  S = a.s * 2^((a.m - M) c) + s * 2^((m - M) c),
+//   idx = the lower index among spans attaining M.
+// Spans with no finite entry (m = -inf) only contribute their bad flag.
+__device__ __forceinline__ void stat_fold(StatRec& a, float m, float s, int i, int bad, float c) {
+    a.bad |= bad;
+    if (m == -INFINITY) return;
+    if (a.m == -INFINITY) {
+        a.m = m;
+        a.s = s;
+        a.idx = i;
+        return;
+    }
+    const float M = fmaxf(a.m, m);
+    a.s = a.s * exp2f((a.m - M) * c) + s * exp2f((m - M) * c);
+    if (m > a.m || (m == a.m && i < a.idx)) a.idx = i;
+    a.m = M;
+}
+
+// A logit that makes its row unusable (NaN or +inf): the row is marked bad
+// and the value takes no part in the statistics.
+__device__ __forceinline__ bool stat_bad_value(float z) { return z != z || z == INFINITY; }
+
 // ----------------------------------------------------------------- Philox --
 // Philox4x32-10 (Salmon, Moraes, Dror, Shaw, SC'11): ten rounds of
 //   (c0,c1,c2,c3) -> (hi(M1*c2) ^ c1 ^ k0, lo(M1*c2), hi(M0*c0) ^ c3 ^ k1, lo(M0*c0))

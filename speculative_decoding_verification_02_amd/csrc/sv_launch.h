@@ -9,26 +9,47 @@
 
 namespace sv {
 
+// Most statistics records per row the LM-head epilogue writes.
+constexpr int kMaxStatRecs = 1024;
+
 // LM-head contraction.  force_kernel: 0 = pick by shape, 1 = small-M
-// streaming kernel, 2 = LDS-tiled kernel.
+// streaming kernel, 2 = LDS-tiled kernel.  With stats non-null the kernels
+// that have a statistics epilogue (cooperative and direct-to-LDS) also write
+// *n_rec records per row, stats[m * *n_rec + k], in vocabulary order, with
+// sums relative to c = log2(e) / T; *n_rec = 0 means the chosen kernel has no
+// epilogue and the caller runs the statistics pass.
 hipError_t launch_lmhead_bf16(const uint16_t* hidden, const uint16_t* W, float* logits, int M, int V, int H,
-                              int num_cus, hipStream_t stream, int force_kernel);
+                              int num_cus, hipStream_t stream, int force_kernel, StatRec* stats = nullptr,
+                              float c = 0.f, int* n_rec = nullptr);
 hipError_t launch_lmhead_f32(const float* hidden, const float* W, float* logits, int M, int V, int H,
                              hipStream_t stream);
 bool skinny_fits(int M, int H);
 
 // Softmax statistics of the rows the accept step needs, per chunk.
-//   jobs = n_rows*(K+1) target slots, then (if draft_logits) n_rows*K draft
-//   slots, K = seq.K; slots past a ragged sequence's own rows are skipped.
+//   jobs = (if logits) n_rows*(K+1) target slots, then (if draft_logits)
+//   n_rows*K draft slots, K = seq.K; slots past a ragged sequence's own rows
+//   are skipped.
 hipError_t launch_softmax_stats(const float* logits, const float* draft_logits, const int32_t* rows, int n_rows,
                                 SeqRows seq, int V, float inv_t_log2e, bool need_sum, StatRec* stats,
                                 hipStream_t stream);
+
+// Where the accept kernel finds the statistics records of a sequence's rows.
+// Target rows: tgt + (tgt_by_row ? t0 + i : j*(K+1) + i) * tgt_nc (by packed
+// row for the LM-head epilogue's records, by selection slot for the
+// statistics pass).  Draft rows: drf + (j*K + i) * drf_nc.
+struct RecLayout {
+    const StatRec* tgt;
+    int tgt_nc;
+    bool tgt_by_row;
+    const StatRec* drf;
+    int drf_nc;
+};
 
 // Greedy or sampled acceptance: one workgroup per selected sequence.  The
 // sampled variant also zeroes the sequence's residual counter.
 hipError_t launch_accept(const float* logits, const float* draft_logits, const int32_t* draft_tokens,
                          const uint64_t* seeds, const int32_t* rows, int n_rows, SeqRows seq, int V,
-                         float inv_t_log2e, bool sampled, const StatRec* stats, int32_t* accepted_len,
+                         float inv_t_log2e, bool sampled, RecLayout rec, int32_t* accepted_len,
                          int32_t* out_tokens, float* probs_at_draft, AcceptInfo* info, int* counters,
                          hipStream_t stream);
 

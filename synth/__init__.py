@@ -94,6 +94,14 @@ WORKLOADS = {
         "b512_k3_h5120_v262144", B=512, K=3, H=5120, V=262144, dtype="bf16",
         w_std=0.02, temperature=1.0, draft="zipf", modes="bernoulli",
         data_seed=1004),
+    # long verify blocks (not one of the five benchmark workloads): 16-token
+    # blocks (K = 15) at 32 concurrent sequences, the LM-head shape of the
+    # 8B-parameter target the pages measure block drafting on
+    "b32_k15_h4096_v151936": Workload(
+        "b32_k15_h4096_v151936", B=32, K=15, H=4096, V=151936, dtype="bf16",
+        w_std=0.02, temperature=1.0, draft="additive", draft_sigma=(0.5, 0.5),
+        modes="half", data_seed=1008,
+        note="K = 15 blocks at B = 32; rows 0..15 greedy, 16..31 sampled at T=1"),
     # per-sequence draft counts (not one of the five benchmark workloads): the
     # 64-sequence mixed batch with K_b drawn uniformly from 0..7
     "b64_k0to7_h4096_v128256": Workload(

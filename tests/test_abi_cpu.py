@@ -29,6 +29,7 @@ def test_exports_every_declared_symbol(lib):
     assert set(names) == {"spec_verify_logits", "spec_accept_greedy", "spec_accept_sample",
                           "spec_accept_greedy_ragged", "spec_accept_sample_ragged", "spec_tree_accept_greedy",
                           "spec_ngram_propose", "spec_ngram_workspace_bytes",
+                          "spec_verify_step", "spec_verify_step_workspace_bytes",
                           "spec_workspace_bytes", "spec_status_string", "spec_last_error_detail"}
     for n in names:
         assert hasattr(lib, n), n
@@ -186,6 +187,40 @@ def test_ngram_validation(lib):
     assert _ngram(lib, ws=None) == sv.SPEC_ERR_WORKSPACE
     assert _ngram(lib, wsb=8) == sv.SPEC_ERR_WORKSPACE
     assert _ngram(lib, ws=P(0x10004)) == sv.SPEC_ERR_ALIGN
+
+
+def _step(lib, hid=A, w=A, dt=0, dl=A, dtok=A, T=1.0, seeds=A, g=None, ng=0, sm=None, ns=2, B=2, K=3, V=100,
+          H=64, logits=A, acc=A, out=A, ws=A, wsb=None):
+    if wsb is None:
+        wsb = sv.spec_verify_step_workspace_bytes(B, K, V) or (1 << 20)
+    return lib.spec_verify_step(hid, w, dt, dl, dtok, T, seeds, g, ng, sm, ns, B, K, V, H, logits, acc, out, None,
+                                ws, wsb, None)
+
+
+def test_step_validation(lib):
+    a = sv.spec_verify_step_workspace_bytes(1, 5, 128256)
+    assert a > sv.spec_workspace_bytes(1, 5, 128256) and a % 256 == 0
+    assert sv.spec_verify_step_workspace_bytes(1, 64, 100) == 0
+    assert _step(lib, hid=None) == sv.SPEC_ERR_ARG
+    assert _step(lib, logits=None) == sv.SPEC_ERR_ARG
+    assert _step(lib, acc=None) == sv.SPEC_ERR_ARG
+    assert _step(lib, dt=5) == sv.SPEC_ERR_DTYPE
+    assert _step(lib, K=64) == sv.SPEC_ERR_ARG
+    assert _step(lib, H=12) == sv.SPEC_ERR_ARG
+    assert _step(lib, ns=1) == sv.SPEC_ERR_ARG             # NULL list: 0 or B only
+    assert _step(lib, sm=A, ns=3) == sv.SPEC_ERR_ARG       # more than B
+    assert _step(lib, g=A, ng=-1) == sv.SPEC_ERR_ARG
+    assert _step(lib, dtok=None) == sv.SPEC_ERR_ARG
+    assert _step(lib, dl=None) == sv.SPEC_ERR_ARG
+    assert _step(lib, seeds=None) == sv.SPEC_ERR_ARG
+    assert _step(lib, T=0.0) == sv.SPEC_ERR_ARG
+    assert _step(lib, T=math.nan) == sv.SPEC_ERR_ARG
+    assert _step(lib, dl=MIS) == sv.SPEC_ERR_ALIGN
+    assert _step(lib, hid=MIS) == sv.SPEC_ERR_ALIGN
+    assert _step(lib, wsb=16) == sv.SPEC_ERR_WORKSPACE
+    assert _step(lib, ws=MIS) == sv.SPEC_ERR_ALIGN
+    # greedy rows only: no seeds, draft logits or temperature needed
+    assert _step(lib, ns=0, seeds=None, dl=None, T=0.0, g=A, ng=0, ws=None) == sv.SPEC_ERR_WORKSPACE
 
 
 def test_zero_selected_rows_is_a_no_op(lib):

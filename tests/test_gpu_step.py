@@ -1,0 +1,122 @@
+"""GPU parity of spec_verify_step (LM head with the target rows' softmax
+statistics in its epilogue, then both accept rules) against the oracle and
+against the separate calls it replaces.
+
+Every LM-head kernel path is covered: the cooperative kernel (M <= 16) and
+the direct-to-LDS kernel in several tile heights, which both fold the
+statistics into their epilogue, and the paths that fall back to the
+statistics pass (the small-M kernel for wide hidden sizes, the tiled kernel
+for H not a multiple of 64, fp32 weights).  The logits must be bit-identical
+to spec_verify_logits, greedy outputs identical to spec_accept_greedy, and
+both sides must meet the oracle run on the same fp32 logits (sampled
+decisions by the margin rule, probabilities within 1e-5).  Full-size cases:
+the B=1 and B=64 workloads and the K = 15 long-block workload.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+import speculative_decoding_verification_02_amd as sv
+from gpu_support import (PROB_ATOL, ParityCounts, compare_greedy, compare_sample, dev, gpu_accept_greedy,
+                         gpu_accept_sample, gpu_logits, say, seeds_tensor)
+
+pytestmark = pytest.mark.gpu
+
+
+def _inputs(wl, device):
+    inp = synth.round_inputs(wl, 0, device=device)
+    return inp
+
+
+def _step(inp, T, greedy_rows, sampled_rows, K, V):
+    hid, W = inp["hidden"], inp["W"]
+    B = hid.shape[0]
+    logits = torch.full((B, K + 1, V), float("nan"), dtype=torch.float32, device=dev())
+    acc = torch.full((B,), -2, dtype=torch.int32, device=dev())
+    out = torch.full((B, K + 1), -9, dtype=torch.int32, device=dev())
+    pad = torch.full((B, K, 2), float("nan"), dtype=torch.float32, device=dev())
+    ws = torch.empty(sv.spec_verify_step_workspace_bytes(B, K, V), dtype=torch.uint8, device=dev())
+
+    def rl(r):
+        if r is None or isinstance(r, str):
+            return r
+        return torch.as_tensor(np.asarray(r, np.int32), device=dev())
+    sv.spec_verify_step(hid, W, logits, acc, out, ws, draft_logits=inp["draft_logits"], draft_tokens=inp["drafts"],
+                        temperature=T, seeds=seeds_tensor(inp["seeds"]), greedy_rows=rl(greedy_rows),
+                        sampled_rows=rl(sampled_rows), probs_at_draft=pad)
+    return logits, acc, out, pad
+
+
+def _check(wl, greedy_rows, sampled_rows):
+    B, K, V, T = wl.B, wl.K, wl.V, wl.temperature
+    inp = _inputs(wl, dev())
+    g_rows = np.arange(B) if isinstance(greedy_rows, str) else (np.asarray(greedy_rows) if greedy_rows is not None
+                                                                  else np.zeros(0, np.int64))
+    s_rows = np.arange(B) if isinstance(sampled_rows, str) else (np.asarray(sampled_rows) if sampled_rows is not None
+                                                                   else np.zeros(0, np.int64))
+    logits, acc, out, pad = _step(inp, T, greedy_rows, sampled_rows, K, V)
+    torch.cuda.synchronize()
+    # the separate calls on the same inputs
+    ref = gpu_logits(inp["hidden"], inp["W"])
+    assert torch.equal(logits, ref), "fused step changed the logits"
+    z = logits.double().cpu().numpy()
+    acc_c, out_c = acc.cpu().numpy(), out.cpu().numpy()
+    c = ParityCounts()
+    if len(g_rows):
+        acc_g, out_g = gpu_accept_greedy(ref, inp["drafts"], rows=g_rows)
+        acc_g, out_g = acc_g.cpu().numpy(), out_g.cpu().numpy()
+        np.testing.assert_array_equal(acc_c[g_rows], acc_g[g_rows])
+        np.testing.assert_array_equal(out_c[g_rows], out_g[g_rows])
+        c.merge(compare_greedy(oracle.accept_greedy(z, inp["drafts"].cpu().numpy(), rows=g_rows), acc_c, out_c,
+                               g_rows, exact=True))
+    if len(s_rows):
+        res = oracle.accept_sample(z, inp["draft_logits"].double().cpu().numpy(), inp["drafts"].cpu().numpy(), T,
+                                   inp["seeds"], rows=s_rows)
+        c.merge(compare_sample(res, acc_c, out_c, s_rows))
+        acc_s, out_s, _ = gpu_accept_sample(ref, inp["draft_logits"], inp["drafts"], T, inp["seeds"], rows=s_rows)
+        c.merge(compare_sample(res, acc_s.cpu().numpy(), out_s.cpu().numpy(), s_rows))
+        if K:
+            p = pad.cpu().numpy()[s_rows]
+            np.testing.assert_allclose(p, res.probs_at_draft[s_rows], atol=PROB_ATOL, rtol=0)
+    say("  " + str(c))
+
+
+def _wl(B, K, H, V, dtype="bf16", T=0.9, seed=7):
+    return synth.Workload("t", B=B, K=K, H=H, V=V, dtype=dtype, w_std=0.03 if dtype == "bf16" else 0.05,
+                          temperature=T, draft="additive", draft_sigma=(0.5, 0.5), data_seed=seed)
+
+
+@pytest.mark.parametrize("B,K,H,V,dtype,path", [
+    (1, 5, 512, 3001, "bf16", "cooperative, epilogue"),
+    (3, 4, 4096, 5003, "bf16", "cooperative, epilogue"),
+    (2, 3, 8192, 3001, "bf16", "small-M wide H, statistics pass"),
+    (8, 7, 576, 4099, "bf16", "direct-to-LDS 64-row tiles, epilogue"),
+    (30, 4, 128, 2053, "bf16", "direct-to-LDS 160-row tiles, epilogue"),
+    (64, 4, 576, 1000, "bf16", "direct-to-LDS 2 x 160-row tiles, epilogue"),
+    (100, 5, 256, 1031, "bf16", "direct-to-LDS 256-row tiles, epilogue"),
+    (40, 3, 520, 1000, "bf16", "tiled (H % 64 != 0), statistics pass"),
+    (1, 4, 256, 1000, "f32", "fp32, statistics pass"),
+])
+def test_step_paths(B, K, H, V, dtype, path):
+    wl = _wl(B, K, H, V, dtype, seed=B + K + H + V)
+    say("fused step B=%d K=%d H=%d V=%d %s: %s" % (B, K, H, V, dtype, path))
+    half = B // 2
+    _check(wl, list(range(half)), list(range(half, B)))
+
+
+def test_step_row_list_forms():
+    wl = _wl(6, 3, 256, 2000, seed=3)
+    say("fused step: all greedy, all sampled, sampled subset only")
+    _check(wl, "all", None)
+    _check(wl, None, "all")
+    _check(wl, None, [5, 0, 2])
+
+
+@pytest.mark.parametrize("name", ["b1_k5_h4096_v128256", "b64_k4_h4096_v128256", "b32_k15_h4096_v151936"])
+def test_step_full_size(name):
+    wl = synth.WORKLOADS[name]
+    say("fused step, full-size workload %s" % name)
+    sm = synth.sampled_mask(wl)
+    _check(wl, np.nonzero(~sm)[0], np.nonzero(sm)[0])
