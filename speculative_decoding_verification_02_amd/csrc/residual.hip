@@ -19,8 +19,7 @@
 // (possible only through rounding when q_n ~ p_n) the draw uses q_n instead.
 #include <limits.h>
 
-#include "sv_common.h"
-#include "sv_launch.h"
+#include "sv_accept.h"
 
 namespace sv {
 
@@ -282,6 +281,63 @@ __global__ __launch_bounds__(kStatThreads) void residual_kernel(
     __syncthreads();
     if (!last) return;
     select_terminal(logits, draft_logits, V, nc, c, a, chunk_sums + (size_t)j * nc, out_tokens);
+}
+
+// Acceptance and residual draw in one launch, for small batches where the
+// two kernels' latency dominates: one workgroup per (sampled sequence, chunk).
+// Every workgroup of a sequence takes the acceptance decision itself (a few
+// hundred statistics records and K token logits: cheap next to the chunk it
+// streams), the one of chunk 0 writes it out, each sums its chunk of the
+// terminal weights, and the last to finish selects the token as above.  The
+// completion counters are zeroed by the statistics pass that runs first.
+__global__ __launch_bounds__(kStatThreads) void accept_residual_kernel(
+    const float* __restrict__ logits, const float* __restrict__ draft_logits, const int32_t* __restrict__ draft_tokens,
+    const uint64_t* __restrict__ seeds, const int32_t* __restrict__ rows, SeqRows seq, int V, int nc, float c,
+    RecLayout rec, int32_t* __restrict__ accepted_len, int32_t* __restrict__ out_tokens,
+    float* __restrict__ probs_at_draft, float* __restrict__ chunk_sums, int* __restrict__ counters) {
+    static_assert(kStatThreads == kAcceptThreads, "one workgroup shape for both phases");
+    __shared__ StatRec recs[kRecBuf];
+    __shared__ Merged merged[kMaxRows];
+    __shared__ AcceptInfo sinfo;
+    __shared__ float red[kStatThreads / kWave];
+    __shared__ int last;
+    const int j = blockIdx.x / nc;
+    const int chunk = blockIdx.x - j * nc;
+    const int b = rows ? rows[j] : j;
+    const AcceptInfo a = accept_sequence<true>(logits, draft_logits, draft_tokens, seeds, j, b, seq, V, c, rec,
+                                               chunk == 0, accepted_len, out_tokens, probs_at_draft, recs, merged,
+                                               &sinfo);
+    if (a.n < 0) return;
+    const TermRows tr = term_rows(logits, draft_logits, a, V);
+    float w[kStatPerThread];
+    chunk_weights(tr.zt, tr.zd, chunk * kChunk, V, (V & 3) == 0, threadIdx.x, a, c, tr.bonus, w);
+    float s = 0.f;
+#pragma unroll
+    for (int k = 0; k < kStatPerThread; ++k) s += w[k];
+    s = block_sum(s, red);
+    if (threadIdx.x == 0) {
+        // published as in residual_kernel: an exchange whose result is waited
+        // for, then the count
+        const float prev = __hip_atomic_exchange(chunk_sums + blockIdx.x, s, __ATOMIC_RELAXED,
+                                                 __HIP_MEMORY_SCOPE_AGENT);
+        asm volatile("" ::"v"(prev));
+        last = __hip_atomic_fetch_add(counters + j, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == nc - 1;
+    }
+    __syncthreads();
+    if (!last) return;
+    select_terminal(logits, draft_logits, V, nc, c, a, chunk_sums + (size_t)j * nc, out_tokens);
+}
+
+hipError_t launch_accept_residual(const float* logits, const float* draft_logits, const int32_t* draft_tokens,
+                                  const uint64_t* seeds, const int32_t* rows, int n_rows, SeqRows seq, int V,
+                                  float inv_t_log2e, RecLayout rec, int32_t* accepted_len, int32_t* out_tokens,
+                                  float* probs_at_draft, float* chunk_sums, int* counters, hipStream_t stream) {
+    if (n_rows == 0) return hipSuccess;
+    const int nc = n_chunks(V);
+    hipLaunchKernelGGL(accept_residual_kernel, dim3((unsigned)((long)n_rows * nc)), dim3(kStatThreads), 0, stream,
+                       logits, draft_logits, draft_tokens, seeds, rows, seq, V, nc, inv_t_log2e, rec, accepted_len,
+                       out_tokens, probs_at_draft, chunk_sums, counters);
+    return hipGetLastError();
 }
 
 hipError_t launch_residual(const float* logits, const float* draft_logits, int n_rows, int V,

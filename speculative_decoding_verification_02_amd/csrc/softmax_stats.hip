@@ -47,12 +47,14 @@ __device__ __forceinline__ int chunk_index(int v_begin, int tid, int k) {
 template <bool NEED_SUM>
 __global__ __launch_bounds__(kStatThreads) void softmax_stats_kernel(
     const float* __restrict__ logits, const float* __restrict__ draft_logits, const int32_t* __restrict__ rows,
-    int n_rows, SeqRows seq, int V, int nc, float c, StatRec* __restrict__ stats) {
+    int n_rows, SeqRows seq, int V, int nc, float c, StatRec* __restrict__ stats, int* __restrict__ zero_counters) {
     __shared__ float sm[kStatThreads / kWave];
     __shared__ int si[kStatThreads / kWave];
     __shared__ int sb[kStatThreads / kWave];
 
     const int K = seq.K;
+    // completion counters of a fused accept + residual launch that follows
+    if (zero_counters && blockIdx.x < n_rows && threadIdx.x == 0) zero_counters[blockIdx.x] = 0;
     const int job = blockIdx.x / nc;
     const int chunk = blockIdx.x - job * nc;
     const int tgt_jobs = logits ? n_rows * (K + 1) : 0;   // no target rows: draft rows only
@@ -132,17 +134,17 @@ __global__ __launch_bounds__(kStatThreads) void softmax_stats_kernel(
 
 hipError_t launch_softmax_stats(const float* logits, const float* draft_logits, const int32_t* rows, int n_rows,
                                 SeqRows seq, int V, float inv_t_log2e, bool need_sum, StatRec* stats,
-                                hipStream_t stream) {
+                                hipStream_t stream, int* zero_counters) {
     const int nc = n_chunks(V);
     const long jobs = (logits ? (long)n_rows * (seq.K + 1) : 0) + (draft_logits ? (long)n_rows * seq.K : 0);
     const long blocks = jobs * nc;
     if (blocks == 0) return hipSuccess;
     if (need_sum)
         hipLaunchKernelGGL(softmax_stats_kernel<true>, dim3((unsigned)blocks), dim3(kStatThreads), 0, stream, logits,
-                           draft_logits, rows, n_rows, seq, V, nc, inv_t_log2e, stats);
+                           draft_logits, rows, n_rows, seq, V, nc, inv_t_log2e, stats, zero_counters);
     else
         hipLaunchKernelGGL(softmax_stats_kernel<false>, dim3((unsigned)blocks), dim3(kStatThreads), 0, stream,
-                           logits, draft_logits, rows, n_rows, seq, V, nc, inv_t_log2e, stats);
+                           logits, draft_logits, rows, n_rows, seq, V, nc, inv_t_log2e, stats, zero_counters);
     return hipGetLastError();
 }
 

@@ -150,12 +150,23 @@ spec_status_t sample_impl(const float* logits, const float* draft_logits, const 
     workspace_layout(seq.B, seq.K, V, workspace, &ws);
     const float c = sv::kLog2e / temperature;
     const float* dl = has_drafts ? draft_logits : nullptr;
-    hipError_t e = sv::launch_softmax_stats(logits, dl, rows, nr, seq, V, c, true, ws.stats, s);
-    if (e == hipSuccess)
-        e = sv::launch_accept(logits, dl, draft_tokens, seeds, rows, nr, seq, V, c, true,
-                              pass_layout(ws.stats, nr, seq.K, V), accepted_len, out_tokens, probs_at_draft, ws.info,
-                              ws.counters, s);
-    if (e == hipSuccess) e = sv::launch_residual(logits, dl, nr, V, c, ws.info, ws.sums, ws.counters, out_tokens, s);
+    // small batches: acceptance and residual draw in one launch (their
+    // latency, not their bytes, bounds the step there)
+    const bool fused = nr <= sv::kFusedAcceptMaxRows;
+    hipError_t e = sv::launch_softmax_stats(logits, dl, rows, nr, seq, V, c, true, ws.stats, s,
+                                            fused ? ws.counters : nullptr);
+    if (e == hipSuccess && fused) {
+        e = sv::launch_accept_residual(logits, dl, draft_tokens, seeds, rows, nr, seq, V, c,
+                                       pass_layout(ws.stats, nr, seq.K, V), accepted_len, out_tokens, probs_at_draft,
+                                       ws.sums, ws.counters, s);
+    } else {
+        if (e == hipSuccess)
+            e = sv::launch_accept(logits, dl, draft_tokens, seeds, rows, nr, seq, V, c, true,
+                                  pass_layout(ws.stats, nr, seq.K, V), accepted_len, out_tokens, probs_at_draft,
+                                  ws.info, ws.counters, s);
+        if (e == hipSuccess)
+            e = sv::launch_residual(logits, dl, nr, V, c, ws.info, ws.sums, ws.counters, out_tokens, s);
+    }
     return e == hipSuccess ? SPEC_OK : hip_fail(e);
 }
 

@@ -29,9 +29,11 @@ bool skinny_fits(int M, int H);
 //   jobs = (if logits) n_rows*(K+1) target slots, then (if draft_logits)
 //   n_rows*K draft slots, K = seq.K; slots past a ragged sequence's own rows
 //   are skipped.
+//   zero_counters (optional): n_rows completion counters cleared on the way,
+//   for a fused accept + residual launch that follows.
 hipError_t launch_softmax_stats(const float* logits, const float* draft_logits, const int32_t* rows, int n_rows,
                                 SeqRows seq, int V, float inv_t_log2e, bool need_sum, StatRec* stats,
-                                hipStream_t stream);
+                                hipStream_t stream, int* zero_counters = nullptr);
 
 // Where the accept kernel finds the statistics records of a sequence's rows.
 // Target rows: tgt + (tgt_by_row ? t0 + i : j*(K+1) + i) * tgt_nc (by packed
@@ -52,6 +54,14 @@ hipError_t launch_accept(const float* logits, const float* draft_logits, const i
                          float inv_t_log2e, bool sampled, RecLayout rec, int32_t* accepted_len,
                          int32_t* out_tokens, float* probs_at_draft, AcceptInfo* info, int* counters,
                          hipStream_t stream);
+
+// Acceptance and residual draw of sampled sequences in one launch (small
+// batches); needs the counters cleared by launch_softmax_stats.
+constexpr int kFusedAcceptMaxRows = 16;
+hipError_t launch_accept_residual(const float* logits, const float* draft_logits, const int32_t* draft_tokens,
+                                  const uint64_t* seeds, const int32_t* rows, int n_rows, SeqRows seq, int V,
+                                  float inv_t_log2e, RecLayout rec, int32_t* accepted_len, int32_t* out_tokens,
+                                  float* probs_at_draft, float* chunk_sums, int* counters, hipStream_t stream);
 
 // Greedy verification of draft trees (N+1 rows per sequence, statistics from
 // launch_softmax_stats over the dense layout with K = N).
