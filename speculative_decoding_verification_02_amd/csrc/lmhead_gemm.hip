@@ -509,24 +509,24 @@ __global__ __launch_bounds__(kTiledThreads) void lmhead_tiled_bf16(
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 constexpr int kBigBN = 256;
-constexpr int kBigThreads = 256;
 
 // Geometry of one k-slice of BK columns: 256 W rows then BM hidden rows, CPR
 // 16-byte chunks per row; a DMA instruction fills RPI rows (1 KB).
-template <int BK, int SLOTS, int NA, int NB>
+template <int BK, int SLOTS, int NA, int NB, int NW = 4>
 struct Big {
+    static constexpr int kThreads = NW * 64;
     static constexpr int kWN = 8 / NA;                  // waves along the vocabulary
-    static constexpr int kWM = 4 / kWN;                 // waves along the hidden rows
+    static constexpr int kWM = NW / kWN;                // waves along the hidden rows
     static constexpr int kBM = kWM * NB * 32;
     static constexpr int kCPR = BK / 8;
     static constexpr int kRPI = 64 / kCPR;
     static constexpr int kSliceChunks = (kBigBN + kBM) * kCPR;
-    static constexpr int kLoads = kSliceChunks / 64 / (kBigThreads / 64);   // DMA per lane per slice
+    static constexpr int kLoads = kSliceChunks / 64 / NW;                   // DMA per lane per slice
     static constexpr int kWLoads = kBigBN * kCPR / 64;                      // DMA blocks holding W rows
     static constexpr int kSteps = BK / 16;                                  // MFMA k-steps per slice
     static constexpr size_t kLds = (size_t)SLOTS * kSliceChunks * 16;
-    static_assert(kSliceChunks % kBigThreads == 0, "slice must split evenly over the lanes");
-    static_assert(kWN * NA == 8 && kWN * kWM == 4, "wave layout must tile 256 x BM");
+    static_assert(kSliceChunks % kThreads == 0, "slice must split evenly over the lanes");
+    static_assert(kWN * NA == 8 && kWN * kWM == NW, "wave layout must tile 256 x BM");
     static_assert(kLoads <= kSteps * NA * NB, "every load must find an MFMA to ride on");
     static_assert(kLds <= 160 * 1024, "LDS ring exceeds the 160 KB of a CU");
     // chunk c of row r sits at r*CPR + (c ^ f(r)), f(r) = (r / (16/CPR)) % CPR:
@@ -564,19 +564,34 @@ __device__ __forceinline__ void wait_slices(int after) {
 
 // With STATS, the workgroup also writes the softmax statistics of each of its
 // hidden rows over its 256 vocabulary columns: stats[m * tiles_n + tn].
-template <int BK, int SLOTS, int NA, int NB, bool STATS>
-__global__ __launch_bounds__(kBigThreads, 1) void lmhead_big_bf16(
+template <int BK, int SLOTS, int NA, int NB, bool STATS, int NW>
+__global__ __launch_bounds__(NW * 64, 1) void lmhead_big_bf16(
     const uint16_t* __restrict__ hidden, const uint16_t* __restrict__ W, float* __restrict__ logits,
-    int M, int V, int H, int tiles_n, int tiles_m, StatRec* __restrict__ stats, float c) {
-    using G = Big<BK, SLOTS, NA, NB>;
+    int M, int V, int H, int tiles_n, int tiles_m, int group_m, StatRec* __restrict__ stats, float c) {
+    using G = Big<BK, SLOTS, NA, NB, NW>;
     extern __shared__ __align__(16) unsigned char smem[];
     u32x4* lds = reinterpret_cast<u32x4*>(smem);   // [slot][W rows 0..255 | hidden rows 0..BM-1][CPR chunks]
 
-    const int total = tiles_n * tiles_m;
-    const int per_xcd = (total + 7) / 8;
-    const int seq = (blockIdx.x % 8) * per_xcd + blockIdx.x / 8;
-    if (seq >= total) return;
-    const int tn = seq / tiles_m, tm = seq - tn * tiles_m;
+    // Workgroups go to the XCDs round-robin.  XCD x owns vocabulary tiles
+    // [n_lo, n_hi) and walks them in groups of group_m hidden-row tiles:
+    // for each group, every vocabulary tile, the group's row tiles next to
+    // each other, so the workgroups running together share operand slices
+    // through the XCD's L2.
+    const int xcd = blockIdx.x % 8, local = blockIdx.x / 8;
+    const int n_lo = (int)((long)tiles_n * xcd / 8), nn = (int)((long)tiles_n * (xcd + 1) / 8) - n_lo;
+    if (local >= nn * tiles_m) return;
+    const int full = tiles_m / group_m;
+    int grp, rem, gm;
+    if (local < full * nn * group_m) {
+        grp = local / (nn * group_m);
+        rem = local - grp * nn * group_m;
+        gm = group_m;
+    } else {
+        grp = full;
+        rem = local - full * nn * group_m;
+        gm = tiles_m - full * group_m;
+    }
+    const int tn = n_lo + rem / gm, tm = grp * group_m + rem % gm;
     const int v0 = tn * kBigBN, m0 = tm * G::kBM;
 
     const int tid = threadIdx.x;
@@ -732,7 +747,7 @@ __global__ __launch_bounds__(kBigThreads, 1) void lmhead_big_bf16(
             store_rows(b);   // block b's registers are free after this
         }
         __syncthreads();
-        for (int row = threadIdx.x; row < G::kBM; row += kBigThreads) {
+        for (int row = threadIdx.x; row < G::kBM; row += G::kThreads) {
             if (m0 + row >= M) continue;
             StatRec t{-INFINITY, 0.f, INT_MAX, 0};
 #pragma unroll
@@ -750,34 +765,41 @@ __global__ __launch_bounds__(kBigThreads, 1) void lmhead_big_bf16(
     }
 }
 
-template <int BK, int SLOTS, int NA, int NB, bool STATS>
+template <int BK, int SLOTS, int NA, int NB, bool STATS, int NW = 4>
 hipError_t launch_big_cfg(const uint16_t* hidden, const uint16_t* W, float* logits, int M, int V, int H,
-                          hipStream_t stream, StatRec* stats = nullptr, float c = 0.f) {
-    using G = Big<BK, SLOTS, NA, NB>;
+                          hipStream_t stream, StatRec* stats = nullptr, float c = 0.f, int group_m = 0) {
+    using G = Big<BK, SLOTS, NA, NB, NW>;
     static_assert(!STATS || (size_t)G::kWN * G::kBM * sizeof(StatRec) <= G::kLds, "statistics exchange fits the ring");
-    auto kern = lmhead_big_bf16<BK, SLOTS, NA, NB, STATS>;
+    auto kern = lmhead_big_bf16<BK, SLOTS, NA, NB, STATS, NW>;
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)G::kLds);
     if (e != hipSuccess) return e;
     const int tiles_n = (V + kBigBN - 1) / kBigBN;
     const int tiles_m = (M + G::kBM - 1) / G::kBM;
-    const int grid = ((tiles_n * tiles_m + 7) / 8) * 8;
-    hipLaunchKernelGGL(kern, dim3(grid), dim3(kBigThreads), G::kLds, stream, hidden, W, logits, M, V, H, tiles_n,
-                       tiles_m, stats, c);
+    const int max_nn = (tiles_n + 7) / 8;    // most vocabulary tiles any XCD owns
+    const int grid = 8 * max_nn * tiles_m;
+    const int gm = group_m > 0 ? min(group_m, tiles_m) : tiles_m;
+    hipLaunchKernelGGL(kern, dim3(grid), dim3(G::kThreads), G::kLds, stream, hidden, W, logits, M, V, H, tiles_n,
+                       tiles_m, gm, stats, c);
     return hipGetLastError();
 }
 
 // Configurations the library launches, all with whole 128-byte rows per
-// slice.  The tile height follows M so that little of the tile is padding;
-// rows from 257 to 320 run as two 160-row tiles (4 waves side by side along
-// the vocabulary), whose smaller slices leave room for a third slot, i.e. two
-// slices in flight.  Measured on MI355X at H = 4096, V = 128256 (us per
-// GEMM): M = 40: 183 (64-row tile) vs 246 (128 x 128 tiled kernel); M = 96:
-// 214 vs 226; M = 130: 263 vs 362; M = 320: 395 (2 x 160) vs 535 (2 x 256)
-// vs 537 (tiled); M = 400: 546 (2 x 256) vs 679 (tiled).  256-row tiles use
-// waves of 64 x 256 (2 x 8 blocks): ~980 vs ~900 TFLOP/s for 128 x 128 waves
-// at M = 2048, H = 5120, V = 262144, and within 2% either way at M = 2304,
-// H = 8192, V = 152064.
+// slice.  The tile height follows M so that little of the tile is padding,
+// and from 65 rows up the tiles run with 8 waves (two per SIMD, each with
+// half the accumulators), so one wave's MFMAs cover the other's waits.
+// Measured on MI355X (us per GEMM, H = 4096, V = 128256 unless noted):
+//   M = 40:  183 (64-row tile, 4 waves) vs 246 for the 128 x 128 tiled kernel
+//   M = 128: 208 (128 rows, 8 waves) vs 214 (4 waves)
+//   M = 150: 230 (160 rows, 4 waves, 3 slots) vs 255 (192 rows, 8 waves)
+//   M = 192: 264 (192 rows, 8 waves) vs 269 (4 waves)
+//   M = 256: 285 (256 rows, 8 waves) vs 301-313 (4 waves)
+//   M = 320: 333-341 (one 320-row tile, 8 waves) vs 388 (2 x 160, 4 waves)
+//   M = 640: 654 (2 x 320) vs 740-764 (3 x 256)
+//   M = 2304, H = 8192, V = 152064: 5.25 ms (256 rows, 8 waves) vs 5.5-5.9
+//   M = 2048, H = 5120, V = 262144: 5.23-5.32 ms vs 5.5
+// Above 320 rows the tile is 256 or 320 rows, whichever gives the smaller
+// sum of per-tile times (measured 285 and 339 us per 256-/320-row tile here).
 constexpr int kBigBK = 64;
 constexpr int kBigMinM = 17;
 
@@ -789,13 +811,15 @@ bool big_fits(int M, int V, int H) {
 template <bool STATS>
 hipError_t launch_big(const uint16_t* hidden, const uint16_t* W, float* logits, int M, int V, int H,
                       hipStream_t stream, StatRec* stats, float c) {
-    if (M <= 64) return launch_big_cfg<kBigBK, 3, 4, 1, STATS>(hidden, W, logits, M, V, H, stream, stats, c);
-    if (M <= 128) return launch_big_cfg<kBigBK, 3, 4, 2, STATS>(hidden, W, logits, M, V, H, stream, stats, c);
-    if (M <= 160) return launch_big_cfg<kBigBK, 3, 2, 5, STATS>(hidden, W, logits, M, V, H, stream, stats, c);
-    if (M <= 192) return launch_big_cfg<kBigBK, 2, 4, 3, STATS>(hidden, W, logits, M, V, H, stream, stats, c);
-    if (M <= 256) return launch_big_cfg<kBigBK, 2, 2, 8, STATS>(hidden, W, logits, M, V, H, stream, stats, c);
-    if (M <= 320) return launch_big_cfg<kBigBK, 3, 2, 5, STATS>(hidden, W, logits, M, V, H, stream, stats, c);
-    return launch_big_cfg<kBigBK, 2, 2, 8, STATS>(hidden, W, logits, M, V, H, stream, stats, c);
+    if (M <= 64) return launch_big_cfg<kBigBK, 3, 4, 1, STATS, 4>(hidden, W, logits, M, V, H, stream, stats, c);
+    if (M <= 128) return launch_big_cfg<kBigBK, 3, 2, 2, STATS, 8>(hidden, W, logits, M, V, H, stream, stats, c);
+    if (M <= 160) return launch_big_cfg<kBigBK, 3, 2, 5, STATS, 4>(hidden, W, logits, M, V, H, stream, stats, c);
+    if (M <= 192) return launch_big_cfg<kBigBK, 2, 2, 3, STATS, 8>(hidden, W, logits, M, V, H, stream, stats, c);
+    if (M <= 256) return launch_big_cfg<kBigBK, 2, 2, 4, STATS, 8>(hidden, W, logits, M, V, H, stream, stats, c);
+    const long cost256 = (long)((M + 255) / 256) * 285, cost320 = (long)((M + 319) / 320) * 339;
+    if (cost320 < cost256)
+        return launch_big_cfg<kBigBK, 2, 2, 5, STATS, 8>(hidden, W, logits, M, V, H, stream, stats, c);
+    return launch_big_cfg<kBigBK, 2, 2, 4, STATS, 8>(hidden, W, logits, M, V, H, stream, stats, c);
 }
 
 // ------------------------------------------------------------------ fp32 ---

@@ -151,8 +151,9 @@ spec_status_t sample_impl(const float* logits, const float* draft_logits, const 
     const float c = sv::kLog2e / temperature;
     const float* dl = has_drafts ? draft_logits : nullptr;
     // small batches: acceptance and residual draw in one launch (their
-    // latency, not their bytes, bounds the step there)
-    const bool fused = nr <= sv::kFusedAcceptMaxRows;
+    // latency, not their bytes, bounds the step there); every chunk
+    // workgroup repeats the decision, so only while the rows to merge are few
+    const bool fused = (long)nr * (2 * seq.K + 1) <= sv::kFusedAcceptMaxRows;
     hipError_t e = sv::launch_softmax_stats(logits, dl, rows, nr, seq, V, c, true, ws.stats, s,
                                             fused ? ws.counters : nullptr);
     if (e == hipSuccess && fused) {
