@@ -28,7 +28,9 @@ __device__ __forceinline__ void load_chunk(const float* __restrict__ row, int v_
     for (int q = 0; q < kStatPerThread / 4; ++q) {
         const int v = v_begin + (q * kStatThreads + tid) * 4;
         if (vec && v + 3 < V) {
-            const float4 f = *reinterpret_cast<const float4*>(row + v);
+            // read once per step: stream past the caches
+            typedef float f4v __attribute__((ext_vector_type(4)));
+            const f4v f = __builtin_nontemporal_load(reinterpret_cast<const f4v*>(row + v));
             x[4 * q + 0] = f.x;
             x[4 * q + 1] = f.y;
             x[4 * q + 2] = f.z;
