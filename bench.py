@@ -66,13 +66,19 @@ _SECTIONS = {"lmhead_coop_bf16": "small M, cooperative", "lmhead_big_bf16": "big
 
 
 def kernel_source_sha(kernel: str) -> str:
-    """sha256 of the kernel's source section (kernel, configuration and its
-    launcher), so edits elsewhere in the file keep stored readings valid."""
-    lines = open(GEMM_SRC).read().splitlines(keepends=True)
+    """sha256 of the code of the kernel's source section (kernel,
+    configuration and launcher; comments and blank lines dropped), so edits
+    elsewhere in the file, or to comments, keep stored readings valid."""
+    lines = open(GEMM_SRC).read().splitlines()
     banners = [i for i, ln in enumerate(lines) if ln.startswith("// ---")]
-    i = next(i for i in banners if lines[i].strip("/ -\n") == _SECTIONS[kernel])
+    i = next(i for i in banners if lines[i].strip("/ -") == _SECTIONS[kernel])
     j = next((k for k in banners if k > i), len(lines))
-    return hashlib.sha256("".join(lines[i:j]).encode()).hexdigest()[:16]
+    code = []
+    for ln in lines[i:j]:
+        ln = ln.split("//", 1)[0].rstrip()
+        if ln.strip():
+            code.append(ln)
+    return hashlib.sha256("\n".join(code).encode()).hexdigest()[:16]
 
 
 def load_traffic(workload: str, kernel: str):

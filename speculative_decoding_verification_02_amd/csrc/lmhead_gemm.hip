@@ -6,9 +6,10 @@
 // positions ("speculative-decoding" blog, Verification mechanism; "Speculative
 // decoding" course page, Memory-bound, not compute-bound).  With M a handful of
 // rows the product is a stream over W (2 bytes per weight, 2*M flops per
-// weight), so the small-M kernel is built to keep HBM busy; with M in the
-// hundreds or thousands it becomes a dense contraction and the tiled kernel
-// keeps the matrix cores busy.
+// weight), so the small-M kernels are built to keep HBM busy; from a few
+// dozen rows up it becomes a dense contraction and the direct-to-LDS kernel
+// keeps the matrix cores busy (the LDS-tiled kernel covers hidden sizes that
+// are not a multiple of 64).
 //
 // Matrix-core mapping (v_mfma_f32_16x16x32_bf16, wave64): the A operand is a
 // 16 x 32 tile of W (16 vocabulary rows, 32 hidden columns), the B operand a
@@ -484,12 +485,14 @@ __global__ __launch_bounds__(kTiledThreads) void lmhead_tiled_bf16(
 
 // ------------------------------------------------------------- big M -----
 // Dense contraction for M from a few dozen rows up (MFMA-bound at large M).
-// A workgroup of 4 waves owns a 256 (vocab) x BM (hidden rows) tile; each
-// wave a 32*NA x 32*NB part as NA x NB blocks of v_mfma_f32_32x32x16_bf16
-// (16*NA*NB fp32 accumulators per lane, one wave per SIMD), the waves laid out
-// 8/NA along the vocabulary and 4*NA/8 along the rows, so BM = 32*NB*4*NA/8.  On MI355X the 32x32x16 form issues at about twice the rate of
-// 16x16x32 (measured ~2.0 vs ~0.8 PFLOP/s at one wave per SIMD), so the dense
-// path uses it.  Operand layout: lane l holds A[l % 32][8*(l/32) .. +8) (W
+// A workgroup of NW = 4 or 8 waves (one or two per SIMD) owns a 256 (vocab) x
+// BM (hidden rows) tile; each wave a 32*NA x 32*NB part as NA x NB blocks of
+// v_mfma_f32_32x32x16_bf16 (16*NA*NB fp32 accumulators per lane), the waves
+// laid out 8/NA along the vocabulary and NW*NA/8 along the rows, so
+// BM = 32*NB*NW*NA/8.  With two waves per SIMD each holds half the
+// accumulators and one wave's MFMAs cover the other's waits.  On MI355X the
+// 32x32x16 form issues at about twice the rate of 16x16x32 (measured ~2.0 vs
+// ~0.8 PFLOP/s at one wave per SIMD), so the dense path uses it.  Operand layout: lane l holds A[l % 32][8*(l/32) .. +8) (W
 // rows) and B[8*(l/32) .. +8)[l % 32] (hidden rows) and receives
 // D[8*(i/4) + 4*(l/32) + i%4][l % 32], i < 16: four runs of four consecutive
 // vocabulary entries of one hidden row.
@@ -504,8 +507,8 @@ __global__ __launch_bounds__(kTiledThreads) void lmhead_tiled_bf16(
 // each k-step's fragments are read from LDS during the previous k-step's
 // MFMAs, so neither a full load queue nor an LDS read stalls the matrix
 // pipe.  Synchronisation is explicit: a wait on the wave's own outstanding
-// loads (vmcnt), then one barrier per slice.  Tiles are ordered XCD-aware like
-// the tiled kernel, so the M-tiles of one vocabulary tile share an L2.
+// loads (vmcnt), then one barrier per slice.  Tiles are ordered XCD-aware, so
+// the M-tiles of one vocabulary tile share an L2.
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 constexpr int kBigBN = 256;
@@ -854,22 +857,20 @@ __global__ __launch_bounds__(kF32Threads) void lmhead_f32(
 // ------------------------------------------------------------ launchers ----
 
 hipError_t launch_lmhead_bf16(const uint16_t* hidden, const uint16_t* W, float* logits, int M, int V, int H,
-                              int num_cus, hipStream_t stream, int force_kernel, StatRec* stats, float c,
-                              int* n_rec) {
+                              int num_cus, hipStream_t stream, StatRec* stats, float c, int* n_rec) {
     if (n_rec) *n_rec = 0;
-    if (force_kernel == 0 && CoopCfg::fits(M, H)) {
+    if (CoopCfg::fits(M, H)) {
         if (stats) return launch_coop<2, 2, 8, true>(hidden, W, logits, M, V, H, num_cus, stream, 1, stats, c, n_rec);
         return launch_coop<2, 2, 8, false>(hidden, W, logits, M, V, H, num_cus, stream, 1, nullptr, 0.f, nullptr);
     }
-    if (force_kernel == 0 && big_fits(M, V, H)) {
+    if (big_fits(M, V, H)) {
         if (stats) {
             if (n_rec) *n_rec = (V + kBigBN - 1) / kBigBN;
             return launch_big<true>(hidden, W, logits, M, V, H, stream, stats, c);
         }
         return launch_big<false>(hidden, W, logits, M, V, H, stream, nullptr, 0.f);
     }
-    const bool skinny = force_kernel == 1 || (force_kernel == 0 && skinny_fits(M, H));
-    if (skinny) return launch_skinny<kSkRPL, kSkP, kSkThreads>(hidden, W, logits, M, V, H, num_cus, stream);
+    if (skinny_fits(M, H)) return launch_skinny<kSkRPL, kSkP, kSkThreads>(hidden, W, logits, M, V, H, num_cus, stream);
     const int tiles_n = (V + kTileN - 1) / kTileN;
     const int tiles_m = (M + kTileM - 1) / kTileM;
     const int total = tiles_n * tiles_m;

@@ -207,7 +207,7 @@ spec_status_t spec_verify_logits(const void* hidden, const void* w_lmhead, spec_
         e = num_cus(&cus);
         if (e != hipSuccess) return hip_fail(e);
         e = sv::launch_lmhead_bf16(static_cast<const uint16_t*>(hidden), static_cast<const uint16_t*>(w_lmhead),
-                                   logits, M, V, H, cus, s, 0);
+                                   logits, M, V, H, cus, s);
     } else {
         e = sv::launch_lmhead_f32(static_cast<const float*>(hidden), static_cast<const float*>(w_lmhead), logits, M,
                                   V, H, s);
@@ -345,7 +345,7 @@ spec_status_t spec_verify_step(const void* hidden, const void* w_lmhead, spec_dt
             e = num_cus(&cus);
             if (e == hipSuccess)
                 e = sv::launch_lmhead_bf16(static_cast<const uint16_t*>(hidden), static_cast<const uint16_t*>(w_lmhead),
-                                           logits, M, V, H, cus, s, 0, any ? tstats : nullptr, c, &nrec);
+                                           logits, M, V, H, cus, s, any ? tstats : nullptr, c, &nrec);
         } else {
             e = sv::launch_lmhead_f32(static_cast<const float*>(hidden), static_cast<const float*>(w_lmhead), logits,
                                       M, V, H, s);

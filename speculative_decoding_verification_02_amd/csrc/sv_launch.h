@@ -12,18 +12,18 @@ namespace sv {
 // Most statistics records per row the LM-head epilogue writes.
 constexpr int kMaxStatRecs = 1024;
 
-// LM-head contraction.  force_kernel: 0 = pick by shape, 1 = small-M
-// streaming kernel, 2 = LDS-tiled kernel.  With stats non-null the kernels
+// LM-head contraction, the kernel picked by shape (cooperative for M <= 16
+// and H <= 4096, small-M streaming for wider H, direct-to-LDS for M > 16
+// with H % 64 == 0, LDS-tiled otherwise).  With stats non-null the kernels
 // that have a statistics epilogue (cooperative and direct-to-LDS) also write
 // *n_rec records per row, stats[m * *n_rec + k], in vocabulary order, with
 // sums relative to c = log2(e) / T; *n_rec = 0 means the chosen kernel has no
 // epilogue and the caller runs the statistics pass.
 hipError_t launch_lmhead_bf16(const uint16_t* hidden, const uint16_t* W, float* logits, int M, int V, int H,
-                              int num_cus, hipStream_t stream, int force_kernel, StatRec* stats = nullptr,
-                              float c = 0.f, int* n_rec = nullptr);
+                              int num_cus, hipStream_t stream, StatRec* stats = nullptr, float c = 0.f,
+                              int* n_rec = nullptr);
 hipError_t launch_lmhead_f32(const float* hidden, const float* W, float* logits, int M, int V, int H,
                              hipStream_t stream);
-bool skinny_fits(int M, int H);
 
 // Softmax statistics of the rows the accept step needs, per chunk.
 //   jobs = (if logits) n_rows*(K+1) target slots, then (if draft_logits)
