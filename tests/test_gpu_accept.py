@@ -175,3 +175,28 @@ def test_accept_deterministic():
     r2 = gpu_accept_sample(ztd, zdd, dd, T, seeds, probs=True)
     for a, b in zip(r1, r2):
         assert torch.equal(a, b)
+
+
+@pytest.mark.parametrize("V", [5003, 2 * 4096 + 7])
+def test_fused_accept_residual_matches_two_kernels(V):
+    """Small sampled batches run acceptance and the residual draw in one
+    launch (sequences x (2K+1) <= 48 rows), larger ones in two.  Four
+    sequences at K = 5 (44 rows) take the fused launch; the same four plus a
+    fifth (55 rows) take the two kernels: the four must come out identical,
+    and both must meet the oracle."""
+    B, K, T = 5, 5, 0.9
+    zt, zd = _logits(B, K, V, seed=V + 11)
+    d = _sampled_drafts(zd, T, seed=V)
+    seeds = np.arange(B, dtype=np.uint64) * 7919 + 3
+    say("fused vs two-kernel accept + residual, V=%d" % V)
+    acc_f, out_f, pad_f = gpu_accept_sample(zt.to(dev()), zd.to(dev()), d.to(dev()), T, seeds, rows=[0, 1, 2, 3],
+                                            probs=True)
+    acc_s, out_s, pad_s = gpu_accept_sample(zt.to(dev()), zd.to(dev()), d.to(dev()), T, seeds,
+                                            rows=[0, 1, 2, 3, 4], probs=True)
+    acc_f, out_f, acc_s, out_s = acc_f.cpu().numpy(), out_f.cpu().numpy(), acc_s.cpu().numpy(), out_s.cpu().numpy()
+    np.testing.assert_array_equal(acc_f[:4], acc_s[:4])
+    np.testing.assert_array_equal(out_f[:4], out_s[:4])
+    np.testing.assert_array_equal(pad_f.cpu().numpy()[:4], pad_s.cpu().numpy()[:4])
+    res = oracle.accept_sample(zt.double().numpy(), zd.double().numpy(), d.numpy(), T, seeds)
+    c = compare_sample(res, acc_s, out_s, range(B))
+    say("  " + str(c))
