@@ -200,3 +200,23 @@ def test_fused_accept_residual_matches_two_kernels(V):
     res = oracle.accept_sample(zt.double().numpy(), zd.double().numpy(), d.numpy(), T, seeds)
     c = compare_sample(res, acc_s, out_s, range(B))
     say("  " + str(c))
+
+
+def test_largest_vocabulary():
+    """V at the library's limit (1024 chunks of 4096: the residual keeps one
+    prefix entry per chunk in LDS), both rules, against the oracle."""
+    B, K, V, T = 2, 2, 1024 * 4096, 1.0
+    g = torch.Generator().manual_seed(17)
+    zt = torch.randn((B, K + 1, V), generator=g) * 3.0
+    zd = zt[:, :K] + torch.randn((B, K, V), generator=g)
+    d = _sampled_drafts(zd, T, seed=5)
+    dg = _greedy_drafts(zt, seed=6)
+    seeds = np.array([11, 12], dtype=np.uint64)
+    say("largest vocabulary V=%d" % V)
+    acc, out = gpu_accept_greedy(zt.to(dev()), dg.to(dev()))
+    res = oracle.accept_greedy(zt.double().numpy(), dg.numpy())
+    c = compare_greedy(res, acc.cpu().numpy(), out.cpu().numpy(), range(B), exact=True)
+    acc, out, _ = gpu_accept_sample(zt.to(dev()), zd.to(dev()), d.to(dev()), T, seeds)
+    res = oracle.accept_sample(zt.double().numpy(), zd.double().numpy(), d.numpy(), T, seeds)
+    c.merge(compare_sample(res, acc.cpu().numpy(), out.cpu().numpy(), range(B)))
+    say("  " + str(c))
