@@ -502,13 +502,13 @@ __global__ __launch_bounds__(kTiledThreads) void lmhead_tiled_bf16(
 // then BM hidden rows, BK*2 bytes per row).  A DMA instruction writes 1 KB of
 // LDS in lane order; each lane picks the global chunk that belongs at its LDS
 // position, so the slice lands swizzled (Big::pos), which spreads any 16
-// consecutive rows read at one chunk over the 16 bank groups.  The loads of
-// slice k+SLOTS-1 are issued one per MFMA while slice k is multiplied, and
-// each k-step's fragments are read from LDS during the previous k-step's
-// MFMAs, so neither a full load queue nor an LDS read stalls the matrix
-// pipe.  Synchronisation is explicit: a wait on the wave's own outstanding
-// loads (vmcnt), then one barrier per slice.  Tiles are ordered XCD-aware, so
-// the M-tiles of one vocabulary tile share an L2.
+// consecutive rows read at one chunk over the 16 bank groups.  The loads that
+// refill a slot are issued one per MFMA, and each k-step's fragments are read
+// from LDS during the previous k-step's MFMAs (across slice boundaries too),
+// so neither a full load queue nor an LDS read stalls the matrix pipe.
+// Synchronisation is explicit: a wait on the wave's own outstanding loads
+// (vmcnt), then one barrier per slice.  Tiles are ordered XCD-aware, so the
+// M-tiles of one vocabulary tile share an L2.
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 constexpr int kBigBN = 256;
@@ -564,6 +564,12 @@ __device__ __forceinline__ void wait_slices(int after) {
     }
     wait_vmcnt<0>();
 }
+
+// loop phase of the direct-to-LDS kernel: which of a slice's loads go out
+template <bool MAIN, bool NEXT>
+struct BigPhase {
+    static constexpr bool kMain = MAIN, kNext = NEXT;
+};
 
 // With STATS, the workgroup also writes the softmax statistics of each of its
 // hidden rows over its 256 vocabulary columns: stats[m * tiles_n + tn].
@@ -636,62 +642,108 @@ __global__ __launch_bounds__(NW * 64, 1) void lmhead_big_bf16(
 #pragma unroll
             for (int e = 0; e < 16; ++e) acc[a][b][e] = 0.f;
 
+    // Pipeline.  The slice barrier sits one k-step early: before the last
+    // k-step of slice kt every wave holds that step's fragments in registers,
+    // so after the barrier slice kt+1 is visible to all and slot kt is free.
+    // Each wave then reads slice kt+1's first fragments while it multiplies
+    // the last k-step of slice kt, and no wave leaves a barrier with nothing
+    // to multiply.  The loads issued between two barriers (a window) refill
+    // the slot freed by the first of them and ride on the window's MFMAs,
+    // window-local index q = 0, 1, ...  Within a k-step the order is pinned:
+    // one MFMA, the next step's fragment reads, then the remaining MFMAs each
+    // followed by at most one load.  The slice body has no branches (which
+    // loads go out is a compile-time property of the loop phase), so the
+    // compiler's waits on fragment reads stay exact.
     const int nk = H / BK;
+    constexpr int kLast = G::kSteps - 1;
+    constexpr int kPerStep = NA * NB;
+    auto dma = [&](int q, int slice) {
+        u32x4* slot = lds + (slice % SLOTS) * G::kSliceChunks;
+        __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(src(q, slice)),
+                                         (__attribute__((address_space(3))) void*)(slot + (wave * G::kLoads + q) * 64),
+                                         16, 0, 0);
+    };
+    auto frag = [&](const u32x4* lw, int ks, bf16x8 (&xa)[NA], bf16x8 (&xb)[NB]) {
+        const u32x4* lh = lw + kBigBN * G::kCPR;
+        const int ch = ks * 2 + h;
+#pragma unroll
+        for (int a = 0; a < NA; ++a) xa[a] = as_bf16x8(lw[G::pos(wn + a * 32 + r, ch)]);
+#pragma unroll
+        for (int b = 0; b < NB; ++b) xb[b] = as_bf16x8(lh[G::pos(wm + b * 32 + r, ch)]);
+    };
+
 #pragma unroll
     for (int p = 0; p < SLOTS - 1; ++p) {
         if (p >= nk) break;
-        u32x4* slot = lds + p * G::kSliceChunks;
 #pragma unroll
-        for (int q = 0; q < G::kLoads; ++q)
-            __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(src(q, p)),
-                                             (__attribute__((address_space(3))) void*)(slot + (wave * G::kLoads + q) * 64),
-                                             16, 0, 0);
+        for (int q = 0; q < G::kLoads; ++q) dma(q, p);
+    }
+    // this lane's loads of slice 0 have landed once at most the slices issued
+    // after it are outstanding; after the barrier everyone's have
+    wait_slices<G::kLoads, SLOTS - 2>(min(SLOTS - 2, nk - 1));
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    bf16x8 fa[2][NA], fb[2][NB];
+    frag(lds, 0, fa[0], fb[0]);
+    // the loads of slice SLOTS-1 that would ride on the last k-step of the
+    // (absent) slice before slice 0; that slot has not been used yet
+    if (SLOTS - 1 < nk) {
+#pragma unroll
+        for (int q = 0; q < G::kLoads && q < kPerStep; ++q) dma(q, SLOTS - 1);
     }
 
-    for (int kt = 0; kt < nk; ++kt) {
-        // this lane's loads of slice kt have landed once at most the slices
-        // issued after it are outstanding
-        wait_slices<G::kLoads, SLOTS - 2>(min(SLOTS - 2, nk - 1 - kt));
-        // everyone's slice kt has landed and everyone has finished reading
-        // slice kt-1, whose slot the next loads reuse
-        __builtin_amdgcn_s_barrier();
-        asm volatile("" ::: "memory");
-        const bool refill = kt + SLOTS - 1 < nk;
-        const int kn = kt + SLOTS - 1;
-        u32x4* nslot = lds + (kn % SLOTS) * G::kSliceChunks;
-
+    // MAIN: this window's loads (slice kt+SLOTS-1) go out; NEXT: the next
+    // window's first loads (slice kt+SLOTS) go out after the early barrier
+    auto slice = [&](int kt, auto phase) {
+        constexpr bool MAIN = decltype(phase)::kMain, NEXT = decltype(phase)::kNext;
         const u32x4* lw = lds + (kt % SLOTS) * G::kSliceChunks;
-        const u32x4* lh = lw + kBigBN * G::kCPR;
-        bf16x8 fa[2][NA], fb[2][NB];
-        auto frag = [&](int ks, bf16x8 (&xa)[NA], bf16x8 (&xb)[NB]) {
-            const int ch = ks * 2 + h;
-#pragma unroll
-            for (int a = 0; a < NA; ++a) xa[a] = as_bf16x8(lw[G::pos(wn + a * 32 + r, ch)]);
-#pragma unroll
-            for (int b = 0; b < NB; ++b) xb[b] = as_bf16x8(lh[G::pos(wm + b * 32 + r, ch)]);
-        };
-        frag(0, fa[0], fb[0]);
 #pragma unroll
         for (int ks = 0; ks < G::kSteps; ++ks) {
-            if (ks + 1 < G::kSteps) frag(ks + 1, fa[(ks + 1) & 1], fb[(ks + 1) & 1]);
+            const int cur = ks & 1;
+            if (ks == kLast) {
+                // this wave's reads of slot kt have completed and its loads of
+                // slice kt+1 have landed (at most the slices issued after it
+                // outstanding); after the barrier the same holds for everyone.
+                // On the last slice this only costs one barrier and reads of
+                // a stale slot that nothing uses.  The scheduling fences keep
+                // every MFMA of the previous k-step ahead of the waits.
+                __builtin_amdgcn_sched_barrier(0);
+                __builtin_amdgcn_s_waitcnt((0xF) | (0x3 << 14) | (0x7 << 4) | (0x0 << 8));   // lgkmcnt(0)
+                wait_slices<G::kLoads, SLOTS - 2>(min(SLOTS - 2, nk - 2 - kt));
+                __builtin_amdgcn_s_barrier();
+                asm volatile("" ::: "memory");
+                __builtin_amdgcn_sched_barrier(0);
+            }
 #pragma unroll
-            for (int a = 0; a < NA; ++a)
-#pragma unroll
-                for (int b = 0; b < NB; ++b) {
-                    acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[ks & 1][a], fb[ks & 1][b], acc[a][b], 0,
-                                                                        0, 0);
-                    const int q = (ks * NA + a) * NB + b;
-                    if (q < G::kLoads && refill)
-                        __builtin_amdgcn_global_load_lds(
-                            reinterpret_cast<const void*>(src(q, kn)),
-                            (__attribute__((address_space(3))) void*)(nslot + (wave * G::kLoads + q) * 64), 16, 0,
-                            0);
+            for (int i = 0; i < kPerStep; ++i) {
+                const int a = i / NB, b = i % NB;
+                acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[cur][a], fb[cur][b], acc[a][b], 0, 0, 0);
+                if (i == 0) {
+                    if (ks < kLast) frag(lw, ks + 1, fa[cur ^ 1], fb[cur ^ 1]);
+                    else frag(lds + ((kt + 1) % SLOTS) * G::kSliceChunks, 0, fa[cur ^ 1], fb[cur ^ 1]);
                 }
+                const int q = ks == kLast ? i : kPerStep * (ks + 1) + i;
+                if (q < G::kLoads) {
+                    if (ks == kLast && NEXT) dma(q, kt + SLOTS);
+                    if (ks < kLast && MAIN) dma(q, kt + SLOTS - 1);
+                }
+            }
+            // pin the order: 1 MFMA, the fragment reads, then each MFMA with
+            // the load that rides on it
+#pragma unroll
+            for (int i = 0; i < kPerStep; ++i) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
+                if (i == 0) __builtin_amdgcn_sched_group_barrier(0x100, NA + NB, 0);   // LDS reads
+                const int q = ks == kLast ? i : kPerStep * (ks + 1) + i;
+                if (q < G::kLoads && ((ks == kLast && NEXT) || (ks < kLast && MAIN)))
+                    __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);   // memory load
+            }
         }
-        // the slot is refilled only after the next barrier; make sure this
-        // wave's reads of it have completed before arriving there
-        __builtin_amdgcn_s_waitcnt((0xF) | (0x3 << 14) | (0x7 << 4) | (0x0 << 8));   // lgkmcnt(0)
-    }
+    };
+    int kt = 0;
+    for (; kt + SLOTS < nk; ++kt) slice(kt, BigPhase<true, true>{});
+    if (kt + SLOTS - 1 < nk) slice(kt++, BigPhase<true, false>{});
+    for (; kt < nk; ++kt) slice(kt, BigPhase<false, false>{});
 
     // logits of row block b: four runs of four consecutive vocabulary entries
     const bool vec_ok = (V & 3) == 0;
@@ -791,7 +843,8 @@ hipError_t launch_big_cfg(const uint16_t* hidden, const uint16_t* W, float* logi
 // slice.  The tile height follows M so that little of the tile is padding,
 // and from 65 rows up the tiles run with 8 waves (two per SIMD, each with
 // half the accumulators), so one wave's MFMAs cover the other's waits.
-// Measured on MI355X (us per GEMM, H = 4096, V = 128256 unless noted):
+// Measured on MI355X (us per GEMM, H = 4096, V = 128256 unless noted; taken
+// before the loop's order was pinned, which made the large tiles 3-7% faster):
 //   M = 40:  183 (64-row tile, 4 waves) vs 246 for the 128 x 128 tiled kernel
 //   M = 128: 208 (128 rows, 8 waves) vs 214 (4 waves)
 //   M = 150: 230 (160 rows, 4 waves, 3 slots) vs 255 (192 rows, 8 waves)
