@@ -279,6 +279,21 @@ def main():
     print("bench: %d steps, %.1f us/step, LM-head kernel %.1f us" % (args.steps, step_s * 1e6, gemm_ms * 1e3),
           file=sys.stderr, flush=True)
 
+    # the distribution of single steps (HIP events around each step, in a
+    # loop of its own) and the tokens each commits: sum over sequences of
+    # accepted length + 1
+    sev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    acc_hist = torch.empty((args.steps, B), dtype=torch.int32, device=dev)
+    for k, (a, b) in enumerate(sev):
+        a.record(stream)
+        step(args.warmup + k)
+        b.record(stream)
+        acc_hist[k].copy_(acc)
+    torch.cuda.synchronize()
+    step_us = np.array([a.elapsed_time(b) * 1e3 for a, b in sev])
+    hist = acc_hist.cpu().numpy()
+    committed = np.where(hist >= 0, hist + 1, 0).sum(axis=1)   # a faulted sequence (-1) commits nothing
+
     # algorithmic bytes / flops of one LM-head launch
     wbytes = 2 if wl.dtype == "bf16" else 4
     gemm_bytes = V * H * wbytes + M * H * wbytes + M * V * 4
@@ -307,6 +322,20 @@ def main():
     roof["algorithmic_flops"] = gemm_flops
     roof["avg_kernel_us"] = gemm_ms * 1e3
 
+    # algorithmic bytes of one whole step (each tensor of the three-stage
+    # interface once: W, hidden, logits written and read back, draft logits of
+    # the sampled rows, two terminal rows per sampled sequence)
+    n_sampled = int(smask.sum())
+    if row_start is not None:
+        rs_np = row_start.cpu().numpy()
+        draft_rows = int(sum(rs_np[b + 1] - rs_np[b] - 1 for b in range(B) if smask[b]))
+    else:
+        draft_rows = 0 if tree is not None else n_sampled * K
+    step_bytes = gemm_bytes + M * V * 4 + draft_rows * V * 4 + n_sampled * 2 * V * 4
+    step_roof = {"algorithmic_bytes": step_bytes, "frac_hbm": step_bytes / step_s / (HBM_PEAK_GBS * 1e9),
+                 "fused_minimal_bytes": step_bytes - M * V * 4,
+                 "frac_hbm_fused_minimal": (step_bytes - M * V * 4) / step_s / (HBM_PEAK_GBS * 1e9)}
+
     positions = M
     res = {
         "metric": METRIC,
@@ -327,7 +356,10 @@ def main():
         **({"tree_nodes": K, "mean_kept_depth": float(np.mean(accepted))} if tree is not None else {}),
         "verify_step_us": step_s * 1e6,
         "path": "spec_verify_step (fused statistics)" if step_ws is not None else "separate calls",
-        "committed_tokens_per_step_last": float(np.mean(accepted + 1)),
+        "step_us_median": float(np.median(step_us)),
+        "step_us_p90": float(np.percentile(step_us, 90)),
+        "committed_tokens_per_s": float(np.mean(committed / (step_us * 1e-6))),
+        "step_roofline": step_roof,
         "roofline": roof,
     }
 
@@ -432,7 +464,8 @@ def bench_ngram(args, dev):
         step()
         b.record(stream)
     torch.cuda.synchronize()
-    call_ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
+    call_us = np.array([a.elapsed_time(b) * 1e3 for a, b in evs])
+    call_ms = float(np.mean(call_us)) * 1e-3
     # algorithmic bytes: every history token read once, the drafts, counts
     # and offsets written once
     alg = n_tok * 4 + wl.B * (wl.n_drafts + 2) * 4 + (wl.B + 1) * 8
@@ -446,6 +479,7 @@ def bench_ngram(args, dev):
            "dtype": "int32", "data": "synthetic",
            "config": {"workload": wl.name, "B": wl.B, "max_len": max_len, "tokens": n_tok, "V": wl.V,
                       "max_ngram": wl.max_ngram, "n_drafts": wl.n_drafts},
+           "step_us_median": float(np.median(call_us)), "step_us_p90": float(np.percentile(call_us, 90)),
            "mean_drafts": float(count.float().mean().item()), "roofline": roof}
     if not args.no_cpu_baseline:
         import oracle
