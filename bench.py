@@ -355,7 +355,7 @@ def main():
         **({"verify_rows": M, "draft_counts": "K_b ~ U{0..%d}, packed" % K} if row_start is not None else {}),
         **({"tree_nodes": K, "mean_kept_depth": float(np.mean(accepted))} if tree is not None else {}),
         "verify_step_us": step_s * 1e6,
-        "path": "spec_verify_step (fused statistics)" if step_ws is not None else "separate calls",
+        "path": "spec_verify_step" if step_ws is not None else "separate calls",
         "step_us_median": float(np.median(step_us)),
         "step_us_p90": float(np.percentile(step_us, 90)),
         "committed_tokens_per_s": float(np.mean(committed / (step_us * 1e-6))),

@@ -45,9 +45,9 @@
  *                          course page, One pass, many candidate
  *                          continuations).
  *   spec_verify_step    -- the whole step in one call: LM head, statistics
- *                          (the target rows' folded into the LM head's
- *                          epilogue, which saves a pass over the logits) and
- *                          both accept rules.
+ *                          (at large batches the target rows' folded into the
+ *                          LM head's epilogue, which saves a pass over the
+ *                          logits) and both accept rules.
  *   spec_ngram_propose  -- the step before verification for prompt lookup:
  *                          drafts copied from the most recent earlier
  *                          occurrence of the sequence's last n tokens
@@ -289,14 +289,16 @@ spec_status_t spec_tree_accept_greedy(const float* logits, const int32_t* parent
  * Same results as spec_verify_logits followed by spec_accept_greedy over
  * greedy_rows and spec_accept_sample over sampled_rows, up to the rounding
  * order of the softmax sums (so a sampled decision with a margin below about
- * 1e-6 may differ; greedy decisions and the logits are identical).  The
- * statistics of the target rows are computed in the LM-head kernel's epilogue
- * while the logits are in registers (the cooperative and direct-to-LDS
- * kernels; the other kernels fall back to the statistics pass), so the
- * logits are written once and not read back for statistics; the draft rows'
- * statistics are computed before the LM head.  Long verify blocks (K = 15 at
- * B <= 32) make the LM head compute-bound ("Inference-4", DFlash), where this
- * saves the most.
+ * 1e-6 may differ; greedy decisions and the logits are identical).  Where the
+ * direct-to-LDS LM-head kernel runs (M = B*(K+1) > 16, H % 64 == 0) and each
+ * sequence's 2K+1 rows hold at most 12288 records of 256 vocabulary entries,
+ * the statistics of the target rows are computed in the kernel's epilogue
+ * while the logits are in registers, so the logits are written once and not
+ * read back for statistics; the draft rows' statistics are computed before
+ * the LM head.  Otherwise the call enqueues exactly the kernels of the three
+ * separate calls (the statistics pass costs less than the epilogue there:
+ * at small M the step is bound by W's bytes, at long K by the merge of the
+ * epilogue's records).
  *
  *   hidden, w_lmhead, dtype, logits, B, K, V, H: as in spec_verify_logits
  *   draft_logits, draft_tokens, temperature, seeds, probs_at_draft,

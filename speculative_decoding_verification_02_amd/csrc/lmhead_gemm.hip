@@ -909,6 +909,10 @@ __global__ __launch_bounds__(kF32Threads) void lmhead_f32(
 
 // ------------------------------------------------------------ launchers ----
 
+int lmhead_big_records(int M, int V, int H) {
+    return !CoopCfg::fits(M, H) && big_fits(M, V, H) ? (V + kBigBN - 1) / kBigBN : 0;
+}
+
 hipError_t launch_lmhead_bf16(const uint16_t* hidden, const uint16_t* W, float* logits, int M, int V, int H,
                               int num_cus, hipStream_t stream, StatRec* stats, float c, int* n_rec) {
     if (n_rec) *n_rec = 0;

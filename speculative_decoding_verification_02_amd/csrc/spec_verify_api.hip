@@ -19,6 +19,7 @@ thread_local const char* g_detail = "";
 constexpr int kMaxK = 63;                          // K+1 positions scanned by one wave64
 constexpr int kMaxV = 1024 * sv::kChunk;           // the residual prefix lives in LDS
 constexpr int kMaxDevices = 64;
+constexpr long kEpilogueMaxRecs = 12288;           // epilogue records per sequence the fused step accepts
 
 std::atomic<int> g_cus[kMaxDevices];
 
@@ -175,14 +176,10 @@ spec_status_t sample_impl(const float* logits, const float* draft_logits, const 
 // bounded B*(K+1) to 31 bits)
 sv::SeqRows dense_rows(int B, int K) { return sv::SeqRows{nullptr, B, K, B * (K + 1)}; }
 
-// Records per target row the fused step may write: the cooperative kernel
-// writes one per workgroup (at most one per 16 vocabulary entries, at most
-// kMaxStatRecs), the direct-to-LDS kernel one per 256 entries, the
-// statistics pass one per 4096-entry chunk.
-size_t step_target_recs(int M, int V) {
-    const size_t by16 = ((size_t)V + 15) / 16, by256 = ((size_t)V + 255) / 256;
-    return M <= 16 ? std::min(by16, (size_t)sv::kMaxStatRecs) : by256;
-}
+// Records per target row the fused step may write: the direct-to-LDS
+// kernel's epilogue writes one per 256 vocabulary entries (it runs only for
+// M > 16; the statistics pass it may fall back to writes one per 4096).
+size_t step_target_recs(int M, int V) { return M <= 16 ? 0 : ((size_t)V + 255) / 256; }
 
 // A row list as the fused step takes it: (NULL, 0) none, (NULL, B) all,
 // (list, 0..B) those.
@@ -332,6 +329,39 @@ spec_status_t spec_verify_step(const void* hidden, const void* w_lmhead, spec_dt
     const int ng = greedy_rows ? n_greedy : (n_greedy ? B : 0);
     hipStream_t s = static_cast<hipStream_t>(stream);
     hipError_t e = hipSuccess;
+
+    // The statistics epilogue pays where the direct-to-LDS kernel runs: it
+    // removes the pass that reads the logits back, and with the loop's order
+    // pinned it costs the kernel ~2%.  The accept kernels then merge one
+    // record per 256 vocabulary entries instead of one per 4096, which
+    // outweighs the gain once a sequence has more than kEpilogueMaxRecs of
+    // them (measured on MI355X, µs per step, epilogue vs separate pass:
+    // B=256 K=8 5460 vs 5653, B=512 K=3 5466 vs 5806, B=64 K=4 399 vs 403-414,
+    // B=32 K=15 757-760 vs 739-746).  Everywhere else the step runs the
+    // kernels the separate calls run.
+    const int big_recs = dtype == SPEC_BF16 ? sv::lmhead_big_records(M, V, H) : 0;
+    const bool epilogue = any && big_recs > 0 && (long)(2 * K + 1) * big_recs <= kEpilogueMaxRecs;
+    if (!epilogue) {
+        if (dtype == SPEC_BF16) {
+            int cus = 0;
+            e = num_cus(&cus);
+            if (e == hipSuccess)
+                e = sv::launch_lmhead_bf16(static_cast<const uint16_t*>(hidden),
+                                           static_cast<const uint16_t*>(w_lmhead), logits, M, V, H, cus, s);
+        } else {
+            e = sv::launch_lmhead_f32(static_cast<const float*>(hidden), static_cast<const float*>(w_lmhead), logits,
+                                      M, V, H, s);
+        }
+        if (e != hipSuccess) return hip_fail(e);
+        spec_status_t st = SPEC_OK;
+        if (ng > 0)
+            st = greedy_impl(logits, draft_tokens, greedy_rows, n_greedy, seq, V, accepted_len, out_tokens,
+                             workspace, workspace_bytes, s);
+        if (st == SPEC_OK && ns > 0)
+            st = sample_impl(logits, draft_logits, draft_tokens, temperature, seeds, sampled_rows, n_sampled, seq, V,
+                             accepted_len, out_tokens, probs_at_draft, workspace, workspace_bytes, s);
+        return st;
+    }
 
     // draft-row statistics first: they do not depend on the LM head
     const float* dl = (ns > 0 && K > 0) ? draft_logits : nullptr;

@@ -24,6 +24,10 @@ hipError_t launch_lmhead_bf16(const uint16_t* hidden, const uint16_t* W, float* 
                               int* n_rec = nullptr);
 hipError_t launch_lmhead_f32(const float* hidden, const float* W, float* logits, int M, int V, int H,
                              hipStream_t stream);
+// Records per row the direct-to-LDS kernel's statistics epilogue writes (one
+// per 256 vocabulary entries) when launch_lmhead_bf16 picks it for this
+// shape, else 0.
+int lmhead_big_records(int M, int V, int H);
 
 // Softmax statistics of the rows the accept step needs, per chunk.
 //   jobs = (if logits) n_rows*(K+1) target slots, then (if draft_logits)

@@ -198,8 +198,10 @@ def _step(lib, hid=A, w=A, dt=0, dl=A, dtok=A, T=1.0, seeds=A, g=None, ng=0, sm=
 
 
 def test_step_validation(lib):
-    a = sv.spec_verify_step_workspace_bytes(1, 5, 128256)
-    assert a > sv.spec_workspace_bytes(1, 5, 128256) and a % 256 == 0
+    # epilogue records only where the direct-to-LDS kernel can run (M > 16)
+    assert sv.spec_verify_step_workspace_bytes(1, 5, 128256) == sv.spec_workspace_bytes(1, 5, 128256)
+    a = sv.spec_verify_step_workspace_bytes(4, 5, 128256)
+    assert a >= sv.spec_workspace_bytes(4, 5, 128256) + 24 * 501 * 16 and a % 256 == 0
     assert sv.spec_verify_step_workspace_bytes(1, 64, 100) == 0
     assert _step(lib, hid=None) == sv.SPEC_ERR_ARG
     assert _step(lib, logits=None) == sv.SPEC_ERR_ARG

@@ -1,16 +1,18 @@
-"""GPU parity of spec_verify_step (LM head with the target rows' softmax
-statistics in its epilogue, then both accept rules) against the oracle and
-against the separate calls it replaces.
+"""GPU parity of spec_verify_step (LM head, with the target rows' softmax
+statistics in its epilogue where that pays, then both accept rules) against
+the oracle and against the separate calls it replaces.
 
-Every LM-head kernel path is covered: the cooperative kernel (M <= 16) and
-the direct-to-LDS kernel in several tile heights, which both fold the
-statistics into their epilogue, and the paths that fall back to the
-statistics pass (the small-M kernel for wide hidden sizes, the tiled kernel
-for H not a multiple of 64, fp32 weights).  The logits must be bit-identical
-to spec_verify_logits, greedy outputs identical to spec_accept_greedy, and
-both sides must meet the oracle run on the same fp32 logits (sampled
-decisions by the margin rule, probabilities within 1e-5).  Full-size cases:
-the B=1 and B=64 workloads and the K = 15 long-block workload.
+Every LM-head kernel path is covered: the direct-to-LDS kernel in several
+tile heights, which folds the statistics into its epilogue, and the paths
+that run the separate calls' kernels instead (the cooperative kernel for
+M <= 16, the small-M kernel for wide hidden sizes, the tiled kernel for H not
+a multiple of 64, fp32 weights, and sequences with too many epilogue records
+to merge).  The logits must be bit-identical to spec_verify_logits, greedy
+outputs identical to spec_accept_greedy, and both sides must meet the oracle
+run on the same fp32 logits (sampled decisions by the margin rule,
+probabilities within 1e-5).  Full-size cases: the B=1 and B=64 workloads and
+the K = 15 long-block workload (the last two on either side of the record
+bound).
 """
 import numpy as np
 import pytest
@@ -89,8 +91,10 @@ def _wl(B, K, H, V, dtype="bf16", T=0.9, seed=7):
 
 
 @pytest.mark.parametrize("B,K,H,V,dtype,path", [
-    (1, 5, 512, 3001, "bf16", "cooperative, epilogue"),
-    (3, 4, 4096, 5003, "bf16", "cooperative, epilogue"),
+    (1, 5, 512, 3001, "bf16", "cooperative, statistics pass"),
+    (3, 4, 4096, 5003, "bf16", "cooperative, statistics pass"),
+    (4, 15, 256, 102400, "bf16", "direct-to-LDS, 12400 records per sequence, statistics pass"),
+    (4, 15, 256, 101120, "bf16", "direct-to-LDS, 12245 records per sequence, epilogue"),
     (2, 3, 8192, 3001, "bf16", "small-M wide H, statistics pass"),
     (8, 7, 576, 4099, "bf16", "direct-to-LDS 64-row tiles, epilogue"),
     (30, 4, 128, 2053, "bf16", "direct-to-LDS 160-row tiles, epilogue"),
