@@ -290,15 +290,14 @@ spec_status_t spec_tree_accept_greedy(const float* logits, const int32_t* parent
  * greedy_rows and spec_accept_sample over sampled_rows, up to the rounding
  * order of the softmax sums (so a sampled decision with a margin below about
  * 1e-6 may differ; greedy decisions and the logits are identical).  Where the
- * direct-to-LDS LM-head kernel runs (M = B*(K+1) > 16, H % 64 == 0) and each
- * sequence's 2K+1 rows hold at most 12288 records of 256 vocabulary entries,
- * the statistics of the target rows are computed in the kernel's epilogue
- * while the logits are in registers, so the logits are written once and not
- * read back for statistics; the draft rows' statistics are computed before
- * the LM head.  Otherwise the call enqueues exactly the kernels of the three
- * separate calls (the statistics pass costs less than the epilogue there:
- * at small M the step is bound by W's bytes, at long K by the merge of the
- * epilogue's records).
+ * direct-to-LDS LM-head kernel runs (M = B*(K+1) > 16, H % 64 == 0), the
+ * statistics of the target rows are computed in the kernel's epilogue while
+ * the logits are in registers, so the logits are written once and not read
+ * back for statistics; the draft rows' statistics are computed before the LM
+ * head, and the epilogue's records are folded into the statistics pass's
+ * layout before acceptance.  Otherwise (M <= 16, where W's bytes bound the
+ * step, other hidden sizes, fp32) the call enqueues exactly the kernels of
+ * the three separate calls.
  *
  *   hidden, w_lmhead, dtype, logits, B, K, V, H: as in spec_verify_logits
  *   draft_logits, draft_tokens, temperature, seeds, probs_at_draft,

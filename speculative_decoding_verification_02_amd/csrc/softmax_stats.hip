@@ -134,6 +134,67 @@ __global__ __launch_bounds__(kStatThreads) void softmax_stats_kernel(
     if (tid == 0) stats[blockIdx.x] = StatRec{bm, s, bi, bbad};
 }
 
+// Fold the LM-head epilogue's records (one per 256 vocabulary entries of a
+// row, in vocabulary order) into the chunk records the statistics pass
+// writes (one per kChunk entries): 16 lanes per chunk, lane t holding record
+// 16k + t, folded by a butterfly over the 16 lanes.  Both partners of a
+// butterfly step compute the same combination (the sum is commutative), so
+// every lane of a group ends with the same record; bad records contribute
+// only their flag, as in the epilogue's own fold.
+constexpr int kRecsPerChunk = kChunk / 256;
+
+__device__ __forceinline__ StatRec rec_combine(StatRec a, StatRec b, float c) {
+    StatRec r;
+    r.bad = a.bad | b.bad;
+    if (a.m == -INFINITY) {
+        r.m = b.m; r.s = b.s; r.idx = b.idx;
+    } else if (b.m == -INFINITY) {
+        r.m = a.m; r.s = a.s; r.idx = a.idx;
+    } else {
+        r.m = fmaxf(a.m, b.m);
+        r.s = a.s * exp2f((a.m - r.m) * c) + b.s * exp2f((b.m - r.m) * c);
+        r.idx = (a.m > b.m || (a.m == b.m && a.idx < b.idx)) ? a.idx : b.idx;
+    }
+    return r;
+}
+
+__global__ __launch_bounds__(kStatThreads) void fold_records_kernel(const StatRec* __restrict__ in, int recs, long items,
+                                                                    int nc, float c, StatRec* __restrict__ out) {
+    const long g = (long)blockIdx.x * (kStatThreads / kRecsPerChunk) + threadIdx.x / kRecsPerChunk;   // (row, chunk)
+    if (g >= items) return;   // whole 16-lane groups leave together
+    const int t = threadIdx.x % kRecsPerChunk;
+    const long row = g / nc;
+    const int chunk = (int)(g - row * nc);
+    const int k = chunk * kRecsPerChunk + t;
+    StatRec a{-INFINITY, 0.f, INT_MAX, 0};
+    if (k < recs) {
+        const StatRec x = in[row * recs + k];
+        a = StatRec{x.bad ? -INFINITY : x.m, x.bad ? 0.f : x.s, x.idx, x.bad};
+    }
+#pragma unroll
+    for (int o = kRecsPerChunk / 2; o > 0; o >>= 1) {
+        StatRec b;
+        b.m = __shfl_xor(a.m, o, kWave);
+        b.s = __shfl_xor(a.s, o, kWave);
+        b.idx = __shfl_xor(a.idx, o, kWave);
+        b.bad = __shfl_xor(a.bad, o, kWave);
+        a = rec_combine(a, b, c);
+    }
+    if (t == 0) out[g] = a;
+}
+
+hipError_t launch_fold_records(const StatRec* in, int recs_per_row, int rows, int V, float inv_t_log2e, StatRec* out,
+                               hipStream_t stream) {
+    const int nc = n_chunks(V);
+    const long items = (long)rows * nc;
+    if (items == 0) return hipSuccess;
+    constexpr int kGroups = kStatThreads / kRecsPerChunk;
+    const long blocks = (items + kGroups - 1) / kGroups;
+    hipLaunchKernelGGL(fold_records_kernel, dim3((unsigned)blocks), dim3(kStatThreads), 0, stream, in, recs_per_row,
+                       items, nc, inv_t_log2e, out);
+    return hipGetLastError();
+}
+
 hipError_t launch_softmax_stats(const float* logits, const float* draft_logits, const int32_t* rows, int n_rows,
                                 SeqRows seq, int V, float inv_t_log2e, bool need_sum, StatRec* stats,
                                 hipStream_t stream, int* zero_counters) {

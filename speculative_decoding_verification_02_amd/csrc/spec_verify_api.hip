@@ -19,7 +19,6 @@ thread_local const char* g_detail = "";
 constexpr int kMaxK = 63;                          // K+1 positions scanned by one wave64
 constexpr int kMaxV = 1024 * sv::kChunk;           // the residual prefix lives in LDS
 constexpr int kMaxDevices = 64;
-constexpr long kEpilogueMaxRecs = 12288;           // epilogue records per sequence the fused step accepts
 
 std::atomic<int> g_cus[kMaxDevices];
 
@@ -332,15 +331,13 @@ spec_status_t spec_verify_step(const void* hidden, const void* w_lmhead, spec_dt
 
     // The statistics epilogue pays where the direct-to-LDS kernel runs: it
     // removes the pass that reads the logits back, and with the loop's order
-    // pinned it costs the kernel ~2%.  The accept kernels then merge one
-    // record per 256 vocabulary entries instead of one per 4096, which
-    // outweighs the gain once a sequence has more than kEpilogueMaxRecs of
-    // them (measured on MI355X, µs per step, epilogue vs separate pass:
-    // B=256 K=8 5460 vs 5653, B=512 K=3 5466 vs 5806, B=64 K=4 399 vs 403-414,
-    // B=32 K=15 757-760 vs 739-746).  Everywhere else the step runs the
-    // kernels the separate calls run.
+    // pinned it costs the kernel ~2%.  Its records (one per 256 vocabulary
+    // entries) are folded into the statistics pass's chunk records before the
+    // accept kernels, which then run exactly as after the pass.  Elsewhere
+    // (the cooperative kernel at M <= 16, where W's bytes bound the step;
+    // the other kernels; fp32) the step runs the separate calls' kernels.
     const int big_recs = dtype == SPEC_BF16 ? sv::lmhead_big_records(M, V, H) : 0;
-    const bool epilogue = any && big_recs > 0 && (long)(2 * K + 1) * big_recs <= kEpilogueMaxRecs;
+    const bool epilogue = any && big_recs > 0;
     if (!epilogue) {
         if (dtype == SPEC_BF16) {
             int cus = 0;
@@ -363,38 +360,38 @@ spec_status_t spec_verify_step(const void* hidden, const void* w_lmhead, spec_dt
         return st;
     }
 
-    // draft-row statistics first: they do not depend on the LM head
+    // draft-row statistics first: they do not depend on the LM head (the pass
+    // also clears the completion counters a fused accept + residual needs)
+    const int nc = sv::n_chunks(V);
     const float* dl = (ns > 0 && K > 0) ? draft_logits : nullptr;
-    if (dl) e = sv::launch_softmax_stats(nullptr, dl, sampled_rows, ns, seq, V, c, true, ws.stats, s);
-    // LM head, with the target-row statistics in its epilogue where the
-    // chosen kernel has one; otherwise the statistics pass over all rows
-    int nrec = 0;
-    if (e == hipSuccess) {
-        if (dtype == SPEC_BF16) {
-            int cus = 0;
-            e = num_cus(&cus);
-            if (e == hipSuccess)
-                e = sv::launch_lmhead_bf16(static_cast<const uint16_t*>(hidden), static_cast<const uint16_t*>(w_lmhead),
-                                           logits, M, V, H, cus, s, any ? tstats : nullptr, c, &nrec);
-        } else {
-            e = sv::launch_lmhead_f32(static_cast<const float*>(hidden), static_cast<const float*>(w_lmhead), logits,
-                                      M, V, H, s);
-        }
-    }
-    if (e == hipSuccess && any && nrec == 0) {
-        e = sv::launch_softmax_stats(logits, nullptr, nullptr, B, seq, V, c, true, tstats, s);
-        nrec = sv::n_chunks(V);
-    }
+    const bool fused = dl && (long)ns * (2 * K + 1) <= sv::kFusedAcceptMaxRows;
+    if (dl) e = sv::launch_softmax_stats(nullptr, dl, sampled_rows, ns, seq, V, c, true, ws.stats, s,
+                                         fused ? ws.counters : nullptr);
+    int cus = 0, nrec = 0;
+    if (e == hipSuccess) e = num_cus(&cus);
+    if (e == hipSuccess)
+        e = sv::launch_lmhead_bf16(static_cast<const uint16_t*>(hidden), static_cast<const uint16_t*>(w_lmhead), logits,
+                                   M, V, H, cus, s, tstats, c, &nrec);
+    if (e == hipSuccess && nrec != big_recs) e = hipErrorInvalidValue;   // the kernel the shape rule named
+    // target chunk records after the draft slots: B*K + M rows fit the
+    // statistics area, which is sized for B*(K+1) + B*K rows
+    sv::StatRec* trec = ws.stats + (size_t)B * K * nc;
+    if (e == hipSuccess) e = sv::launch_fold_records(tstats, nrec, M, V, c, trec, s);
+    const sv::RecLayout lay{trec, nc, true, ws.stats, nc};
     if (e == hipSuccess && ng > 0)
         e = sv::launch_accept(logits, nullptr, draft_tokens, nullptr, greedy_rows, ng, seq, V, sv::kLog2e, false,
-                              sv::RecLayout{tstats, nrec, true, nullptr, 0}, accepted_len, out_tokens, nullptr,
-                              ws.info, ws.counters, s);
+                              sv::RecLayout{trec, nc, true, nullptr, 0}, accepted_len, out_tokens, nullptr, ws.info,
+                              ws.counters, s);
     if (e == hipSuccess && ns > 0) {
-        e = sv::launch_accept(logits, dl, draft_tokens, seeds, sampled_rows, ns, seq, V, c, true,
-                              sv::RecLayout{tstats, nrec, true, ws.stats, sv::n_chunks(V)}, accepted_len, out_tokens,
-                              probs_at_draft, ws.info, ws.counters, s);
-        if (e == hipSuccess)
-            e = sv::launch_residual(logits, dl, ns, V, c, ws.info, ws.sums, ws.counters, out_tokens, s);
+        if (fused) {
+            e = sv::launch_accept_residual(logits, dl, draft_tokens, seeds, sampled_rows, ns, seq, V, c, lay,
+                                           accepted_len, out_tokens, probs_at_draft, ws.sums, ws.counters, s);
+        } else {
+            e = sv::launch_accept(logits, dl, draft_tokens, seeds, sampled_rows, ns, seq, V, c, true, lay,
+                                  accepted_len, out_tokens, probs_at_draft, ws.info, ws.counters, s);
+            if (e == hipSuccess)
+                e = sv::launch_residual(logits, dl, ns, V, c, ws.info, ws.sums, ws.counters, out_tokens, s);
+        }
     }
     return e == hipSuccess ? SPEC_OK : hip_fail(e);
 }

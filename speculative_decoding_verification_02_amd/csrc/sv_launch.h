@@ -24,6 +24,11 @@ hipError_t launch_lmhead_bf16(const uint16_t* hidden, const uint16_t* W, float* 
                               int* n_rec = nullptr);
 hipError_t launch_lmhead_f32(const float* hidden, const float* W, float* logits, int M, int V, int H,
                              hipStream_t stream);
+// Fold rows x recs_per_row epilogue records (one per 256 vocabulary entries,
+// row r at in + r * recs_per_row) into rows x n_chunks(V) chunk records, the
+// layout the statistics pass writes; sums relative to inv_t_log2e.
+hipError_t launch_fold_records(const StatRec* in, int recs_per_row, int rows, int V, float inv_t_log2e, StatRec* out,
+                               hipStream_t stream);
 // Records per row the direct-to-LDS kernel's statistics epilogue writes (one
 // per 256 vocabulary entries) when launch_lmhead_bf16 picks it for this
 // shape, else 0.

@@ -3,16 +3,16 @@ statistics in its epilogue where that pays, then both accept rules) against
 the oracle and against the separate calls it replaces.
 
 Every LM-head kernel path is covered: the direct-to-LDS kernel in several
-tile heights, which folds the statistics into its epilogue, and the paths
-that run the separate calls' kernels instead (the cooperative kernel for
-M <= 16, the small-M kernel for wide hidden sizes, the tiled kernel for H not
-a multiple of 64, fp32 weights, and sequences with too many epilogue records
-to merge).  The logits must be bit-identical to spec_verify_logits, greedy
-outputs identical to spec_accept_greedy, and both sides must meet the oracle
-run on the same fp32 logits (sampled decisions by the margin rule,
-probabilities within 1e-5).  Full-size cases: the B=1 and B=64 workloads and
-the K = 15 long-block workload (the last two on either side of the record
-bound).
+tile heights, which folds the statistics into its epilogue (records then
+folded to the statistics pass's chunks, small sampled batches accepted and
+drawn in one launch), and the paths that run the separate calls' kernels
+instead (the cooperative kernel for M <= 16, the small-M kernel for wide
+hidden sizes, the tiled kernel for H not a multiple of 64, fp32 weights).
+The logits must be bit-identical to spec_verify_logits, greedy outputs
+identical to spec_accept_greedy, and both sides must meet the oracle run on
+the same fp32 logits (sampled decisions by the margin rule, probabilities
+within 1e-5).  Full-size cases: the B=1 and B=64 workloads and the K = 15
+long-block workload.
 """
 import numpy as np
 import pytest
@@ -93,8 +93,8 @@ def _wl(B, K, H, V, dtype="bf16", T=0.9, seed=7):
 @pytest.mark.parametrize("B,K,H,V,dtype,path", [
     (1, 5, 512, 3001, "bf16", "cooperative, statistics pass"),
     (3, 4, 4096, 5003, "bf16", "cooperative, statistics pass"),
-    (4, 15, 256, 102400, "bf16", "direct-to-LDS, 12400 records per sequence, statistics pass"),
-    (4, 15, 256, 101120, "bf16", "direct-to-LDS, 12245 records per sequence, epilogue"),
+    (4, 15, 256, 102400, "bf16", "direct-to-LDS, K=15, epilogue records folded to chunks"),
+    (2, 8, 256, 3001, "bf16", "direct-to-LDS, epilogue, accept and residual in one launch"),
     (2, 3, 8192, 3001, "bf16", "small-M wide H, statistics pass"),
     (8, 7, 576, 4099, "bf16", "direct-to-LDS 64-row tiles, epilogue"),
     (30, 4, 128, 2053, "bf16", "direct-to-LDS 160-row tiles, epilogue"),
