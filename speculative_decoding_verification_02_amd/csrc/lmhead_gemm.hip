@@ -224,26 +224,19 @@ struct Coop {
     static constexpr int kSlice = MAXST * kKS;    // k elements per wave
     static constexpr int kBufChunks = 16 * kCPR;
     static constexpr int kThreads = NW * 64;
-    static size_t lds_bytes() { return (size_t)NW * kBufChunks * 16 + 2 * (size_t)NW * 64 * 16 + (size_t)NW * 16 * 16; }
+    static size_t lds_bytes() { return (size_t)NW * kBufChunks * 16 + 2 * (size_t)NW * 64 * 16; }
     static bool fits(int M, int H) { return M <= 16 && H <= NW * kSlice; }
 };
 
-// With STATS, the workgroup also folds each stored tile into running softmax
-// statistics of its rows (max, lowest argmax, sum of 2^((z - max) c)) and
-// writes one record per row for its whole tile range: stats[r * gridDim.x +
-// blockIdx.x].  Workgroups own contiguous ranges in order, so the records of
-// a row are in vocabulary order.
-template <int RPL, int MAXST, int NW, bool STATS>
+template <int RPL, int MAXST, int NW>
 __global__ __launch_bounds__(NW * 64) void lmhead_coop_bf16(
     const uint16_t* __restrict__ hidden, const uint16_t* __restrict__ W, float* __restrict__ logits,
-    int M, int V, int H, int n_tiles, StatRec* __restrict__ stats, float c) {
+    int M, int V, int H, int n_tiles) {
     using S = Coop<RPL, MAXST, NW>;
     extern __shared__ __align__(16) unsigned char smem[];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     u32x4* buf = reinterpret_cast<u32x4*>(smem) + wave * S::kBufChunks;
     f32x4* red = reinterpret_cast<f32x4*>(smem + (size_t)NW * S::kBufChunks * 16);   // [2][NW][64]
-    StatRec* run = reinterpret_cast<StatRec*>(smem + (size_t)NW * S::kBufChunks * 16 + 2 * (size_t)NW * 64 * 16);
-    StatRec own{-INFINITY, 0.f, INT_MAX, 0};   // this wave's running record of row lane % 16
 
     const int la = lane / S::kLanesPerRow, lc = lane % S::kLanesPerRow;
     const int r = lane & 15, g = lane >> 4;
@@ -314,54 +307,15 @@ __global__ __launch_bounds__(NW * 64) void lmhead_coop_bf16(
 #pragma unroll
             for (int w = 1; w < NW; ++w) s += rb[w * 64 + lane];
             if (r < M) store_row4(logits + (size_t)r * V, (t << 4) + 4 * g, V, s, vec_ok);
-            if constexpr (STATS) {
-                // row r of the tile: lanes r, r+16, r+32, r+48 hold entries
-                // 4g .. 4g+3 in ascending order; folded into this wave's
-                // running record (kept by the lanes with g == 0)
-                const int vb = (t << 4) + 4 * g;
-                float m = -INFINITY;
-                int mi = INT_MAX;
-                float ze[4];
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    ze[e] = vb + e < V ? s[e] : -INFINITY;
-                    mi = ze[e] > m ? vb + e : mi;
-                    m = fmaxf(m, ze[e]);
-                }
-#pragma unroll
-                for (int o = 16; o < 64; o <<= 1) argmax_combine(m, mi, __shfl_xor(m, o, kWave), __shfl_xor(mi, o, kWave));
-                const float mc = (m == -INFINITY ? 0.f : m) * c;
-                float sum = 0.f;
-#pragma unroll
-                for (int e = 0; e < 4; ++e) sum += __builtin_amdgcn_exp2f(fmaf(ze[e], c, -mc));
-                sum += __shfl_xor(sum, 16, kWave);
-                sum += __shfl_xor(sum, 32, kWave);
-                const int bad = m == INFINITY || sum != sum;
-                stat_fold(own, bad ? -INFINITY : m, sum, mi, bad, c);
-            }
-        }
-    }
-    if constexpr (STATS) {
-        // the waves' records of each row, folded in wave order
-        __syncthreads();
-        if (lane < 16) run[wave * 16 + lane] = own;
-        __syncthreads();
-        if (threadIdx.x < M) {
-            StatRec a{-INFINITY, 0.f, INT_MAX, 0};
-            for (int w = 0; w < NW; ++w) {
-                const StatRec x = run[w * 16 + threadIdx.x];
-                stat_fold(a, x.m, x.s, x.idx, x.bad, c);
-            }
-            stats[(size_t)threadIdx.x * gridDim.x + blockIdx.x] = a;
         }
     }
 }
 
-template <int RPL, int MAXST, int NW, bool STATS>
+template <int RPL, int MAXST, int NW>
 hipError_t launch_coop(const uint16_t* hidden, const uint16_t* W, float* logits, int M, int V, int H, int num_cus,
-                       hipStream_t stream, int blocks_per_cu, StatRec* stats, float c, int* n_rec) {
+                       hipStream_t stream, int blocks_per_cu) {
     using S = Coop<RPL, MAXST, NW>;
-    auto kern = lmhead_coop_bf16<RPL, MAXST, NW, STATS>;
+    auto kern = lmhead_coop_bf16<RPL, MAXST, NW>;
     const int n_tiles = (V + 15) / 16;
     const size_t lds = S::lds_bytes();
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
@@ -371,10 +325,8 @@ hipError_t launch_coop(const uint16_t* hidden, const uint16_t* W, float* logits,
     e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, kern, S::kThreads, lds);
     if (e != hipSuccess) return e;
     occ = max(1, min(occ, blocks_per_cu));
-    const int grid = (int)min(min((long)n_tiles, (long)num_cus * occ), (long)kMaxStatRecs);
-    hipLaunchKernelGGL(kern, dim3(grid), dim3(S::kThreads), lds, stream, hidden, W, logits, M, V, H, n_tiles, stats,
-                       c);
-    if (n_rec) *n_rec = grid;
+    const int grid = (int)min((long)n_tiles, (long)num_cus * occ);
+    hipLaunchKernelGGL(kern, dim3(grid), dim3(S::kThreads), lds, stream, hidden, W, logits, M, V, H, n_tiles);
     return hipGetLastError();
 }
 
@@ -916,10 +868,7 @@ int lmhead_big_records(int M, int V, int H) {
 hipError_t launch_lmhead_bf16(const uint16_t* hidden, const uint16_t* W, float* logits, int M, int V, int H,
                               int num_cus, hipStream_t stream, StatRec* stats, float c, int* n_rec) {
     if (n_rec) *n_rec = 0;
-    if (CoopCfg::fits(M, H)) {
-        if (stats) return launch_coop<2, 2, 8, true>(hidden, W, logits, M, V, H, num_cus, stream, 1, stats, c, n_rec);
-        return launch_coop<2, 2, 8, false>(hidden, W, logits, M, V, H, num_cus, stream, 1, nullptr, 0.f, nullptr);
-    }
+    if (CoopCfg::fits(M, H)) return launch_coop<2, 2, 8>(hidden, W, logits, M, V, H, num_cus, stream, 1);
     if (big_fits(M, V, H)) {
         if (stats) {
             if (n_rec) *n_rec = (V + kBigBN - 1) / kBigBN;

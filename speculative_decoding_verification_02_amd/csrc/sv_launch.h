@@ -9,16 +9,13 @@
 
 namespace sv {
 
-// Most statistics records per row the LM-head epilogue writes.
-constexpr int kMaxStatRecs = 1024;
-
 // LM-head contraction, the kernel picked by shape (cooperative for M <= 16
 // and H <= 4096, small-M streaming for wider H, direct-to-LDS for M > 16
-// with H % 64 == 0, LDS-tiled otherwise).  With stats non-null the kernels
-// that have a statistics epilogue (cooperative and direct-to-LDS) also write
-// *n_rec records per row, stats[m * *n_rec + k], in vocabulary order, with
-// sums relative to c = log2(e) / T; *n_rec = 0 means the chosen kernel has no
-// epilogue and the caller runs the statistics pass.
+// with H % 64 == 0, LDS-tiled otherwise).  With stats non-null the
+// direct-to-LDS kernel also writes its statistics epilogue's *n_rec records
+// per row (one per 256 vocabulary entries), stats[m * *n_rec + k], in
+// vocabulary order, with sums relative to c = log2(e) / T; *n_rec = 0 means
+// the chosen kernel has no epilogue and the caller runs the statistics pass.
 hipError_t launch_lmhead_bf16(const uint16_t* hidden, const uint16_t* W, float* logits, int M, int V, int H,
                               int num_cus, hipStream_t stream, StatRec* stats = nullptr, float c = 0.f,
                               int* n_rec = nullptr);
