@@ -11,8 +11,8 @@ hidden sizes, the tiled kernel for H not a multiple of 64, fp32 weights).
 The logits must be bit-identical to spec_verify_logits, greedy outputs
 identical to spec_accept_greedy, and both sides must meet the oracle run on
 the same fp32 logits (sampled decisions by the margin rule, probabilities
-within 1e-5).  Full-size cases: the B=1 and B=64 workloads and the K = 15
-long-block workload.
+within 1e-5).  Full-size cases: every dense workload (B=1, B=64, the K = 15
+long blocks, B=256, B=512).
 """
 import numpy as np
 import pytest
@@ -118,7 +118,8 @@ def test_step_row_list_forms():
     _check(wl, None, [5, 0, 2])
 
 
-@pytest.mark.parametrize("name", ["b1_k5_h4096_v128256", "b64_k4_h4096_v128256", "b32_k15_h4096_v151936"])
+@pytest.mark.parametrize("name", ["b1_k5_h4096_v128256", "b64_k4_h4096_v128256", "b32_k15_h4096_v151936",
+                                  "b256_k8_h8192_v152064", "b512_k3_h5120_v262144"])
 def test_step_full_size(name):
     wl = synth.WORKLOADS[name]
     say("fused step, full-size workload %s" % name)
