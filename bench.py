@@ -391,7 +391,7 @@ def cpu_baseline(wl, W, hidden, zd, drafts, smask, budget_s, rs=None, parents=No
     ds = [d.cpu().numpy() for d in drafts]
     g_rows = np.nonzero(~smask)[0]
     s_rows = np.nonzero(smask)[0]
-    times = []
+    times, t_logits = [], []
     with threadpool_limits(limits=cores):
         used = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
         t_start = time.perf_counter()
@@ -399,6 +399,7 @@ def cpu_baseline(wl, W, hidden, zd, drafts, smask, budget_s, rs=None, parents=No
         while True:
             t0 = time.perf_counter()
             z = oracle.lm_head_logits(h64, w64)
+            t_logits.append(time.perf_counter() - t0)
             d = ds[r % len(ds)]
             if parents is not None:
                 oracle.tree_accept_greedy(z.reshape(wl.B, wl.K + 1, wl.V), parents, d)
@@ -419,7 +420,9 @@ def cpu_baseline(wl, W, hidden, zd, drafts, smask, budget_s, rs=None, parents=No
             if time.perf_counter() - t_start > budget_s:
                 break
     t = float(np.mean(times))
+    tl = float(np.mean(t_logits))
     return {"value": M / t, "unit": "verified positions/s", "cores": int(min(used, cores)), "kind": "oracle",
+            "logits_s_per_step": tl, "accept_s_per_step": t - tl,
             "sample": "%d whole verify steps of %s (fp64 logits of all %d positions over V=%d, then acceptance), "
                       "same inputs as the GPU run; %.2f s per step" % (len(times), wl.name, M, wl.V, t)}
 
