@@ -25,11 +25,19 @@ namespace sv {
 
 constexpr int kMaxChunks = 1024;  // V <= kMaxChunks * kChunk (checked on the host)
 
-// w_v for the terminal row: q_n(v) - p_n(v) clipped at 0, or q_n(v) itself.
-__device__ __forceinline__ float term_weight(float zt, float zd, const AcceptInfo& a, float c, bool use_q) {
-    const float q = exp2f((zt - a.mt) * c) / a.st;
+// w_v for the terminal row: q_n(v) - p_n(v) clipped at 0, or q_n(v) itself,
+// each probability as one exp2 with its normaliser folded into the exponent:
+// q = 2^((z - M) c - log2 S).
+struct TermNorm {
+    float mt, lst, md, lsd;   // maxima and log2 of the sums of the terminal rows
+};
+__device__ __forceinline__ TermNorm term_norm(const AcceptInfo& a) {
+    return TermNorm{a.mt, log2f(a.st), a.md, a.sd > 0.f ? log2f(a.sd) : 0.f};
+}
+__device__ __forceinline__ float term_weight(float zt, float zd, const TermNorm& t, float c, bool use_q) {
+    const float q = exp2f(fmaf(zt - t.mt, c, -t.lst));
     if (use_q) return q;
-    const float p = exp2f((zd - a.md) * c) / a.sd;
+    const float p = exp2f(fmaf(zd - t.md, c, -t.lsd));
     return fmaxf(q - p, 0.f);
 }
 
@@ -38,6 +46,7 @@ __device__ __forceinline__ float term_weight(float zt, float zd, const AcceptInf
 __device__ __forceinline__ void chunk_weights(const float* __restrict__ zt_row, const float* __restrict__ zd_row,
                                               int v_begin, int V, bool vec, int tid, const AcceptInfo& a, float c,
                                               bool use_q, float w[kStatPerThread]) {
+    const TermNorm tn = term_norm(a);
 #pragma unroll
     for (int q = 0; q < kStatPerThread / 4; ++q) {
         const int v = v_begin + (q * kStatThreads + tid) * 4;
@@ -57,7 +66,7 @@ __device__ __forceinline__ void chunk_weights(const float* __restrict__ zt_row, 
             }
         }
 #pragma unroll
-        for (int e = 0; e < 4; ++e) w[4 * q + e] = (v + e < V) ? term_weight(zt[e], zd[e], a, c, use_q) : 0.f;
+        for (int e = 0; e < 4; ++e) w[4 * q + e] = (v + e < V) ? term_weight(zt[e], zd[e], tn, c, use_q) : 0.f;
     }
 }
 
@@ -100,12 +109,7 @@ __device__ __forceinline__ void chunk_prefix(const float* src, int nc, int lane,
             v = from_global ? __hip_atomic_fetch_add(const_cast<float*>(src) + k, 0.f, __ATOMIC_RELAXED,
                                                      __HIP_MEMORY_SCOPE_AGENT)
                             : src[k];
-#pragma unroll
-        for (int o = 1; o < kWave; o <<= 1) {
-            const float y = __shfl_up(v, o, kWave);
-            if (lane >= o) v += y;
-        }
-        v += carry;
+        v = wave_inclusive_scan(v) + carry;
         if (k < nc) pre[k + 1] = v;
         carry = __shfl(v, kWave - 1, kWave);
     }
@@ -191,12 +195,7 @@ __device__ void select_terminal(const float* __restrict__ logits, const float* _
         s += mine[e];
     }
     // inclusive scan of the thread sums: within the wave, then across waves
-    float incl = s;
-#pragma unroll
-    for (int o = 1; o < kWave; o <<= 1) {
-        const float y = __shfl_up(incl, o, kWave);
-        if (lane >= o) incl += y;
-    }
+    float incl = wave_inclusive_scan(s);
     if (lane == kWave - 1) wtot[wave] = incl;
     __syncthreads();
     float base = 0.f;

@@ -22,15 +22,23 @@ namespace sv {
 
 // Thread tid of a chunk workgroup owns elements v_begin + (q * kStatThreads + tid) * 4 + e,
 // q < 4, e < 4: each load instruction of a wavefront covers 1 KB contiguous.
+// STREAM: the logits are read once per step, so large passes stream past the
+// caches; small ones keep them cached for the accept kernels' reads of the
+// terminal rows that follow.
+template <bool STREAM>
 __device__ __forceinline__ void load_chunk(const float* __restrict__ row, int v_begin, int V, bool vec, int tid,
                                            float x[kStatPerThread]) {
 #pragma unroll
     for (int q = 0; q < kStatPerThread / 4; ++q) {
         const int v = v_begin + (q * kStatThreads + tid) * 4;
         if (vec && v + 3 < V) {
-            // read once per step: stream past the caches
             typedef float f4v __attribute__((ext_vector_type(4)));
-            const f4v f = __builtin_nontemporal_load(reinterpret_cast<const f4v*>(row + v));
+            const f4v* p = reinterpret_cast<const f4v*>(row + v);
+            f4v f;
+            if constexpr (STREAM)
+                f = __builtin_nontemporal_load(p);
+            else
+                f = *p;
             x[4 * q + 0] = f.x;
             x[4 * q + 1] = f.y;
             x[4 * q + 2] = f.z;
@@ -46,7 +54,7 @@ __device__ __forceinline__ int chunk_index(int v_begin, int tid, int k) {
     return v_begin + ((k >> 2) * kStatThreads + tid) * 4 + (k & 3);
 }
 
-template <bool NEED_SUM>
+template <bool NEED_SUM, bool STREAM>
 __global__ __launch_bounds__(kStatThreads) void softmax_stats_kernel(
     const float* __restrict__ logits, const float* __restrict__ draft_logits, const int32_t* __restrict__ rows,
     int n_rows, SeqRows seq, int V, int nc, float c, StatRec* __restrict__ stats, int* __restrict__ zero_counters) {
@@ -83,7 +91,7 @@ __global__ __launch_bounds__(kStatThreads) void softmax_stats_kernel(
 
     const int v_begin = chunk * kChunk;
     float x[kStatPerThread];
-    load_chunk(row, v_begin, V, (V & 3) == 0, tid, x);
+    load_chunk<STREAM>(row, v_begin, V, (V & 3) == 0, tid, x);
 
     float m = -INFINITY;
     int mi = INT_MAX;
@@ -202,12 +210,12 @@ hipError_t launch_softmax_stats(const float* logits, const float* draft_logits, 
     const long jobs = (logits ? (long)n_rows * (seq.K + 1) : 0) + (draft_logits ? (long)n_rows * seq.K : 0);
     const long blocks = jobs * nc;
     if (blocks == 0) return hipSuccess;
-    if (need_sum)
-        hipLaunchKernelGGL(softmax_stats_kernel<true>, dim3((unsigned)blocks), dim3(kStatThreads), 0, stream, logits,
-                           draft_logits, rows, n_rows, seq, V, nc, inv_t_log2e, stats, zero_counters);
-    else
-        hipLaunchKernelGGL(softmax_stats_kernel<false>, dim3((unsigned)blocks), dim3(kStatThreads), 0, stream,
-                           logits, draft_logits, rows, n_rows, seq, V, nc, inv_t_log2e, stats, zero_counters);
+    // stream past the caches above 64 MB of logits (4096 chunks of 16 KB)
+    const bool stream_hint = blocks > 4096;
+    auto kern = need_sum ? (stream_hint ? softmax_stats_kernel<true, true> : softmax_stats_kernel<true, false>)
+                         : (stream_hint ? softmax_stats_kernel<false, true> : softmax_stats_kernel<false, false>);
+    hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(kStatThreads), 0, stream, logits, draft_logits, rows, n_rows,
+                       seq, V, nc, inv_t_log2e, stats, zero_counters);
     return hipGetLastError();
 }
 

@@ -54,6 +54,30 @@ __device__ __forceinline__ Merged wave_merge(const StatRec* rec, int nc, float c
     return Merged{m, s, idx, bad};
 }
 
+// The same merge by the 16 lanes of a DPP row (gl = lane % 16), so a
+// wavefront merges four rows at once with DPP reductions.
+__device__ __forceinline__ Merged row16_merge(const StatRec* rec, int nc, float c, bool need_sum, int gl) {
+    float m = -INFINITY;
+    int idx = INT_MAX;
+    int bad = 0;
+    for (int k = gl; k < nc; k += 16) {
+        const StatRec x = rec[k];
+        argmax_combine(m, idx, x.m, x.idx);
+        bad |= x.bad;
+    }
+    row16_argmax(m, idx);
+    bad = row16_or(bad) != 0;
+    float s = 0.f;
+    if (need_sum && m != -INFINITY) {
+        for (int k = gl; k < nc; k += 16) {
+            const StatRec x = rec[k];
+            if (x.m != -INFINITY) s += x.s * exp2f((x.m - m) * c);
+        }
+        s = row16_sum(s);
+    }
+    return Merged{m, s, idx, bad};
+}
+
 // Merge the records of n consecutive rows (nc records each, row r at
 // base + r*nc) into merged[out0 + r], one wavefront per row.  Rows are staged
 // through LDS with every load in flight at once when they fit; rows longer
@@ -136,9 +160,10 @@ __device__ AcceptInfo accept_sequence(const float* __restrict__ logits, const fl
         for (int e = tid; e < (kb + 1 + n_drf) * nc; e += kAcceptThreads)
             recs[e] = e < n_tgt ? tgt0[e] : drf0[e - n_tgt];
         __syncthreads();
-        for (int rr = wave; rr < kb + 1 + n_drf; rr += kAcceptWaves) {
-            const Merged x = wave_merge(recs + rr * nc, nc, c, SAMPLED, lane);
-            if (lane == 0) merged[rr] = x;
+        // four rows per wavefront, one per 16-lane DPP row
+        for (int rr = wave * 4 + (lane >> 4); rr < kb + 1 + n_drf; rr += kAcceptWaves * 4) {
+            const Merged x = row16_merge(recs + rr * nc, nc, c, SAMPLED, lane & 15);
+            if ((lane & 15) == 0) merged[rr] = x;
         }
         __syncthreads();
     } else {

@@ -79,12 +79,6 @@ struct SeqRows {
 
 // ---------------------------------------------------------- reductions ----
 
-__device__ __forceinline__ float wave_sum(float x) {
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o, kWave);
-    return x;
-}
-
 // max with lowest-index tie break; NaN never enters (callers mask it).
 __device__ __forceinline__ void argmax_combine(float& m, int& i, float m2, int i2) {
     if (m2 > m || (m2 == m && i2 < i)) {
@@ -93,13 +87,70 @@ __device__ __forceinline__ void argmax_combine(float& m, int& i, float m2, int i
     }
 }
 
+// Reductions over the 16 lanes of a DPP row (lanes 16r .. 16r+15) with DPP
+// moves, a few cycles each instead of a shuffle's LDS round trip: xor 1 and
+// xor 2 (quad permutes), then the half-row mirror and the row mirror.  Every
+// step combines a lane with a partner holding an equally reduced value and
+// the combinations are symmetric, so all 16 lanes end with the same result.
+__device__ __forceinline__ int dpp_xor1(int x) { return __builtin_amdgcn_mov_dpp(x, 0xB1, 0xF, 0xF, false); }
+__device__ __forceinline__ int dpp_xor2(int x) { return __builtin_amdgcn_mov_dpp(x, 0x4E, 0xF, 0xF, false); }
+__device__ __forceinline__ int dpp_half_mirror(int x) { return __builtin_amdgcn_mov_dpp(x, 0x141, 0xF, 0xF, false); }
+__device__ __forceinline__ int dpp_mirror(int x) { return __builtin_amdgcn_mov_dpp(x, 0x140, 0xF, 0xF, false); }
+
+__device__ __forceinline__ float as_f(int x) { return __builtin_bit_cast(float, x); }
+__device__ __forceinline__ int as_i(float x) { return __builtin_bit_cast(int, x); }
+
+__device__ __forceinline__ void row16_argmax(float& m, int& i) {
+    argmax_combine(m, i, as_f(dpp_xor1(as_i(m))), dpp_xor1(i));
+    argmax_combine(m, i, as_f(dpp_xor2(as_i(m))), dpp_xor2(i));
+    argmax_combine(m, i, as_f(dpp_half_mirror(as_i(m))), dpp_half_mirror(i));
+    argmax_combine(m, i, as_f(dpp_mirror(as_i(m))), dpp_mirror(i));
+}
+__device__ __forceinline__ float row16_sum(float x) {
+    x += as_f(dpp_xor1(as_i(x)));
+    x += as_f(dpp_xor2(as_i(x)));
+    x += as_f(dpp_half_mirror(as_i(x)));
+    x += as_f(dpp_mirror(as_i(x)));
+    return x;
+}
+__device__ __forceinline__ int row16_or(int x) {
+    x |= dpp_xor1(x);
+    x |= dpp_xor2(x);
+    x |= dpp_half_mirror(x);
+    x |= dpp_mirror(x);
+    return x;
+}
+
+// Whole-wavefront reductions: the 16-lane DPP reduction, then two shuffles
+// across the rows (xor 16, xor 32); every lane ends with the result.
+__device__ __forceinline__ float wave_sum(float x) {
+    x = row16_sum(x);
+    x += __shfl_xor(x, 16, kWave);
+    x += __shfl_xor(x, 32, kWave);
+    return x;
+}
+
 __device__ __forceinline__ void wave_argmax(float& m, int& i) {
+    row16_argmax(m, i);
 #pragma unroll
-    for (int o = 32; o > 0; o >>= 1) {
-        float m2 = __shfl_xor(m, o, kWave);
-        int i2 = __shfl_xor(i, o, kWave);
+    for (int o = 16; o < kWave; o <<= 1) {
+        const float m2 = __shfl_xor(m, o, kWave);
+        const int i2 = __shfl_xor(i, o, kWave);
         argmax_combine(m, i, m2, i2);
     }
+}
+
+// Inclusive prefix sum over the wavefront with DPP: row shifts by 1, 2, 4, 8
+// (zero-filled at the row start) give each 16-lane row its prefix, then the
+// row broadcasts of lane 15 and lane 31 carry the earlier rows' totals.
+__device__ __forceinline__ float wave_inclusive_scan(float x) {
+    x += as_f(__builtin_amdgcn_update_dpp(0, as_i(x), 0x111, 0xF, 0xF, true));   // row_shr:1
+    x += as_f(__builtin_amdgcn_update_dpp(0, as_i(x), 0x112, 0xF, 0xF, true));   // row_shr:2
+    x += as_f(__builtin_amdgcn_update_dpp(0, as_i(x), 0x114, 0xF, 0xF, true));   // row_shr:4
+    x += as_f(__builtin_amdgcn_update_dpp(0, as_i(x), 0x118, 0xF, 0xF, true));   // row_shr:8
+    x += as_f(__builtin_amdgcn_update_dpp(0, as_i(x), 0x142, 0xA, 0xF, false));  // row_bcast:15 into rows 1, 3
+    x += as_f(__builtin_amdgcn_update_dpp(0, as_i(x), 0x143, 0xC, 0xF, false));  // row_bcast:31 into rows 2, 3
+    return x;
 }
 
 // Fold the statistics (m, s, i, bad) of one span of a row into a running
