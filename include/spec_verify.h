@@ -45,9 +45,9 @@
  *                          course page, One pass, many candidate
  *                          continuations).
  *   spec_verify_step    -- the whole step in one call: LM head, statistics
- *                          (at large batches the target rows' folded into the
- *                          LM head's epilogue, which saves a pass over the
- *                          logits) and both accept rules.
+ *                          (computed by the LM-head kernel itself wherever a
+ *                          bf16 kernel with that option runs, which saves a
+ *                          pass over the logits) and both accept rules.
  *   spec_ngram_propose  -- the step before verification for prompt lookup:
  *                          drafts copied from the most recent earlier
  *                          occurrence of the sequence's last n tokens
@@ -289,15 +289,19 @@ spec_status_t spec_tree_accept_greedy(const float* logits, const int32_t* parent
  * Same results as spec_verify_logits followed by spec_accept_greedy over
  * greedy_rows and spec_accept_sample over sampled_rows, up to the rounding
  * order of the softmax sums (so a sampled decision with a margin below about
- * 1e-6 may differ; greedy decisions and the logits are identical).  Where the
- * direct-to-LDS LM-head kernel runs (M = B*(K+1) > 16, H % 64 == 0), the
- * statistics of the target rows are computed in the kernel's epilogue while
- * the logits are in registers, so the logits are written once and not read
- * back for statistics; the draft rows' statistics are computed before the LM
- * head, and the epilogue's records are folded into the statistics pass's
- * layout before acceptance.  Otherwise (M <= 16, where W's bytes bound the
- * step, other hidden sizes, fp32) the call enqueues exactly the kernels of
- * the three separate calls.
+ * 1e-6 may differ; greedy decisions and the logits are identical).  The
+ * logits are written once and not read back for statistics where a bf16
+ * LM-head kernel computes them itself:
+ *   - M = B*(K+1) <= 16, H <= 4096 (the cooperative kernel): each workgroup
+ *     keeps the logits of its vocabulary range in LDS and writes one record
+ *     per target row, plus one per draft row from the draft logits it loads
+ *     while the weights stream; the accept kernels merge these records;
+ *   - M > 16, H % 64 == 0 (the direct-to-LDS kernel): the target rows'
+ *     statistics come from the kernel's epilogue while the logits are in
+ *     registers, the draft rows' from a pass before the LM head, and the
+ *     epilogue's records are folded into that pass's layout.
+ * Otherwise (other hidden sizes, fp32) the call enqueues exactly the kernels
+ * of the three separate calls.
  *
  *   hidden, w_lmhead, dtype, logits, B, K, V, H: as in spec_verify_logits
  *   draft_logits, draft_tokens, temperature, seeds, probs_at_draft,

@@ -214,6 +214,15 @@ hipError_t launch_skinny(const uint16_t* hidden, const uint16_t* W, float* logit
 // stage st of tile t is consumed, stage st of the next tile is issued.  Each
 // workgroup takes a contiguous, balanced range of tiles, so it streams one
 // contiguous region of W and its output rows fill whole cache lines.
+//
+// With STATS the kernel also writes softmax statistics records (see
+// CoopStats) over each workgroup's vocabulary range.  The wave that sums a
+// tile also keeps its logits in LDS (one 16-byte write per lane, nothing on
+// the tile's critical path).  The draft rows' entries are loaded at the
+// start, ahead of W, and written next to them after the last tile.  Then one
+// 32-lane group per row reduces its row from LDS: max, first index of the
+// max, sum of 2^((z - max) c).  No per-entry checks: a NaN or +inf shows in
+// the maximum or the sum and marks the record bad.
 template <int RPL, int MAXST, int NW>
 struct Coop {
     static constexpr int kLanesPerRow = 64 / RPL;
@@ -224,14 +233,44 @@ struct Coop {
     static constexpr int kSlice = MAXST * kKS;    // k elements per wave
     static constexpr int kBufChunks = 16 * kCPR;
     static constexpr int kThreads = NW * 64;
-    static size_t lds_bytes() { return (size_t)NW * kBufChunks * 16 + 2 * (size_t)NW * 64 * 16; }
+    static constexpr size_t kLdsBase = (size_t)NW * kBufChunks * 16 + 2 * (size_t)NW * 64 * 16;
+    static size_t lds_bytes() { return kLdsBase; }
+    // LDS with the statistics stash: M target and n_draft draft rows, each
+    // as long as the most columns a workgroup owns (whole tiles of 16) plus
+    // 16 floats, which puts the two rows a wavefront reads at once 16 banks
+    // apart
+    static int stash_stride(int n_tiles, int grid) { return ((n_tiles + grid - 1) / grid) * 16 + 16; }
+    static size_t lds_bytes_stats(int n_tiles, int grid, int rows) {
+        return lds_bytes() + (size_t)rows * stash_stride(n_tiles, grid) * sizeof(float);
+    }
     static bool fits(int M, int H) { return M <= 16 && H <= NW * kSlice; }
 };
 
-template <int RPL, int MAXST, int NW>
+// Records of the entries z[0..n) at vocabulary indices v0 + j*step: max,
+// sum of 2^((z - max) c), first index attaining the max, bad flag.  The
+// sum runs over every entry (with the max taken as 0 when there is none),
+// so a NaN anywhere makes it NaN.
+template <int N>
+__device__ __forceinline__ void coop_fold(StatRec& a, const float (&z)[N], int v0, int step, float c) {
+    float bm = -INFINITY;
+    int bi = INT_MAX;
+#pragma unroll
+    for (int j = 0; j < N; ++j)
+        if (z[j] > bm) {   // indices ascend with j: strict > keeps the first
+            bm = z[j];
+            bi = v0 + j * step;
+        }
+    const float mc = (bm == -INFINITY ? 0.f : bm) * c;
+    float bs = 0.f;
+#pragma unroll
+    for (int j = 0; j < N; ++j) bs += exp2f(fmaf(z[j], c, -mc));
+    stat_fold(a, bm, bs, bi, (bs != bs) | (bm == INFINITY), c);
+}
+
+template <int RPL, int MAXST, int NW, bool STATS>
 __global__ __launch_bounds__(NW * 64) void lmhead_coop_bf16(
     const uint16_t* __restrict__ hidden, const uint16_t* __restrict__ W, float* __restrict__ logits,
-    int M, int V, int H, int n_tiles) {
+    int M, int V, int H, int n_tiles, CoopStats cs) {
     using S = Coop<RPL, MAXST, NW>;
     extern __shared__ __align__(16) unsigned char smem[];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -270,9 +309,32 @@ __global__ __launch_bounds__(NW * 64) void lmhead_coop_bf16(
     const int t_begin = (int)(((long)n_tiles * blockIdx.x) / gridDim.x);
     const int t_end = (int)(((long)n_tiles * (blockIdx.x + 1)) / gridDim.x);
 
+    // draft row `wave` over this workgroup's vocabulary range: the first
+    // kDraftPer * 64 entries are loaded now, ahead of W, and reduced after
+    // the tiles, so the statistics never hold up the weight stream
+    constexpr int kDraftPer = 8;
+    const int dcb = t_begin << 4, dce = min(t_end << 4, V);
+    float dz[kDraftPer];
+    if constexpr (STATS) {
+        if (blockIdx.x == 0 && (int)threadIdx.x < cs.n_zero) cs.zero[threadIdx.x] = 0;
+        if (wave < cs.n_draft) {
+            const float* row = cs.draft + (size_t)wave * V;
+#pragma unroll
+            for (int j = 0; j < kDraftPer; ++j) {
+                const int v = dcb + j * 64 + lane;
+                dz[j] = v < dce ? row[v] : -INFINITY;
+            }
+        }
+    }
+
     u32x4 pipe[MAXST][S::kLoads];
 #pragma unroll
     for (int st = 0; st < MAXST; ++st) issue(t_begin < t_end ? t_begin : n_tiles, st, pipe[st]);
+
+    // logits of this workgroup's tiles, [row][column - dcb], kept for the
+    // statistics (STATS only; sized by the launcher)
+    float* stash = reinterpret_cast<float*>(smem + S::kLdsBase);   // [M + n_draft][stash_cols]
+    const int stash_cols = ((n_tiles + (int)gridDim.x - 1) / (int)gridDim.x) * 16 + 16;
 
     const bool vec_ok = (V & 3) == 0;
     for (int t = t_begin, it = 0; t < t_end; ++t, ++it) {
@@ -306,27 +368,114 @@ __global__ __launch_bounds__(NW * 64) void lmhead_coop_bf16(
             f32x4 s = rb[lane];
 #pragma unroll
             for (int w = 1; w < NW; ++w) s += rb[w * 64 + lane];
-            if (r < M) store_row4(logits + (size_t)r * V, (t << 4) + 4 * g, V, s, vec_ok);
+            const int v0 = (t << 4) + 4 * g;
+            if (r < M) store_row4(logits + (size_t)r * V, v0, V, s, vec_ok);
+            if constexpr (STATS) {
+                if (r < M) {
+                    f32x4 z = s;
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                        if (v0 + i >= V) z[i] = -INFINITY;
+                    *reinterpret_cast<f32x4*>(stash + r * stash_cols + (v0 - dcb)) = z;
+                }
+            }
+        }
+    }
+
+    if constexpr (STATS) {
+        // Rows are reduced over span = stash_cols - 16 columns, -inf past
+        // this workgroup's range: the target rows' columns past its tiles,
+        // and draft row d (stash row M + d) written here, row `wave` from
+        // the registers loaded at the start.
+        const int span = stash_cols - 16, n = dce - dcb;
+        for (int row = wave; row < M; row += NW)
+            for (int k = (t_end - t_begin) * 16 + lane; k < span; k += 64) stash[row * stash_cols + k] = -INFINITY;
+        for (int d = wave; d < cs.n_draft; d += NW) {
+            const float* drow = cs.draft + (size_t)d * V + dcb;
+            float* dst = stash + (M + d) * stash_cols;
+            for (int k0 = 0; k0 < span; k0 += kDraftPer * 64) {
+#pragma unroll
+                for (int j = 0; j < kDraftPer; ++j) {
+                    const int k = k0 + j * 64 + lane;
+                    if (k < span) dst[k] = k >= n ? -INFINITY : (d == wave && k0 == 0 ? dz[j] : drow[k]);
+                }
+            }
+        }
+        __syncthreads();   // the stash is complete
+        // one 32-lane group per row (target rows 0..M-1, then the draft
+        // rows); lane l holds columns 4l + 128j + i, ascending in (j, i)
+        const int l32 = lane & 31;
+        for (int q = wave * 2 + (lane >> 5); q < M + cs.n_draft; q += NW * 2) {
+            const float* src = stash + q * stash_cols;
+            StatRec a{-INFINITY, 0.f, INT_MAX, 0};
+            for (int c0 = 0; c0 < span; c0 += 512) {   // span is a multiple of 16: whole float4s
+                float z[16];
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const int k = c0 + 128 * j + 4 * l32;
+                    const f32x4 x = k < span ? *reinterpret_cast<const f32x4*>(src + k)
+                                             : f32x4{-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) z[4 * j + i] = x[i];
+                }
+                float bm = -INFINITY;
+                int bi = INT_MAX;
+#pragma unroll
+                for (int k = 0; k < 16; ++k)
+                    if (z[k] > bm) {
+                        bm = z[k];
+                        bi = dcb + c0 + 128 * (k / 4) + 4 * l32 + (k % 4);
+                    }
+                const float mc = (bm == -INFINITY ? 0.f : bm) * cs.c;
+                float bs = 0.f;
+#pragma unroll
+                for (int k = 0; k < 16; ++k) bs += __builtin_amdgcn_exp2f(fmaf(z[k], cs.c, -mc));
+                stat_fold(a, bm, bs, bi, (bs != bs) | (bm == INFINITY), cs.c);
+            }
+            // the 32 lanes of the group: DPP within each 16-lane row, then
+            // the two rows (lane ^ 16)
+            float m = a.m;
+            int idx = a.idx;
+            row16_argmax(m, idx);
+            argmax_combine(m, idx, __shfl_xor(m, 16, kWave), __shfl_xor(idx, 16, kWave));
+            float sum = row16_sum(a.m == -INFINITY ? 0.f : a.s * exp2f((a.m - m) * cs.c));
+            sum += __shfl_xor(sum, 16, kWave);
+            int bad = row16_or(a.bad);
+            bad |= __shfl_xor(bad, 16, kWave);
+            bad |= (m == INFINITY) | (sum != sum);
+            if (l32 == 0) {
+                StatRec* out = q < M ? cs.tgt + (size_t)q * gridDim.x : cs.drf + (size_t)(q - M) * gridDim.x;
+                out[blockIdx.x] = StatRec{m, sum, idx, bad};
+            }
         }
     }
 }
 
-template <int RPL, int MAXST, int NW>
-hipError_t launch_coop(const uint16_t* hidden, const uint16_t* W, float* logits, int M, int V, int H, int num_cus,
-                       hipStream_t stream, int blocks_per_cu) {
-    using S = Coop<RPL, MAXST, NW>;
-    auto kern = lmhead_coop_bf16<RPL, MAXST, NW>;
+// Workgroups of the cooperative kernel: one per compute unit, as many as
+// there are tiles at most (and at most kCoopMaxRecs with statistics, so the
+// records fit the caller's workspace).
+inline int coop_grid(int V, int num_cus, bool stats) {
     const int n_tiles = (V + 15) / 16;
-    const size_t lds = S::lds_bytes();
+    const int g = min(n_tiles, max(1, num_cus));
+    return stats ? min(g, kCoopMaxRecs) : g;
+}
+
+template <int RPL, int MAXST, int NW, bool STATS>
+hipError_t launch_coop(const uint16_t* hidden, const uint16_t* W, float* logits, int M, int V, int H, int num_cus,
+                       hipStream_t stream, CoopStats st = CoopStats{}) {
+    using S = Coop<RPL, MAXST, NW>;
+    auto kern = lmhead_coop_bf16<RPL, MAXST, NW, STATS>;
+    const int n_tiles = (V + 15) / 16;
+    const int grid = coop_grid(V, num_cus, STATS);
+    const size_t lds = STATS ? S::lds_bytes_stats(n_tiles, grid, M + st.n_draft) : S::lds_bytes();
+    if (lds > 160 * 1024) return hipErrorInvalidValue;
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
-    int occ = 0;
-    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, kern, S::kThreads, lds);
-    if (e != hipSuccess) return e;
-    occ = max(1, min(occ, blocks_per_cu));
-    const int grid = (int)min((long)n_tiles, (long)num_cus * occ);
-    hipLaunchKernelGGL(kern, dim3(grid), dim3(S::kThreads), lds, stream, hidden, W, logits, M, V, H, n_tiles);
+    if (STATS && (st.n_zero > S::kThreads || st.n_zero < 0 || st.n_draft < 0 || M > 16 || !st.tgt ||
+                  (st.n_draft > 0 && (!st.draft || !st.drf)) || (st.n_zero > 0 && !st.zero)))
+        return hipErrorInvalidValue;
+    hipLaunchKernelGGL(kern, dim3(grid), dim3(S::kThreads), lds, stream, hidden, W, logits, M, V, H, n_tiles, st);
     return hipGetLastError();
 }
 
@@ -861,6 +1010,18 @@ __global__ __launch_bounds__(kF32Threads) void lmhead_f32(
 
 // ------------------------------------------------------------ launchers ----
 
+int lmhead_coop_records(int M, int V, int H, int n_draft, int num_cus) {
+    if (!CoopCfg::fits(M, H) || n_draft < 0) return 0;
+    const int grid = coop_grid(V, num_cus, true);
+    return CoopCfg::lds_bytes_stats((V + 15) / 16, grid, M + n_draft) <= 160 * 1024 ? grid : 0;
+}
+
+hipError_t launch_lmhead_coop_stats(const uint16_t* hidden, const uint16_t* W, float* logits, int M, int V, int H,
+                                    int num_cus, hipStream_t stream, const CoopStats& st) {
+    if (!CoopCfg::fits(M, H)) return hipErrorInvalidValue;
+    return launch_coop<2, 2, 8, true>(hidden, W, logits, M, V, H, num_cus, stream, st);
+}
+
 int lmhead_big_records(int M, int V, int H) {
     return !CoopCfg::fits(M, H) && big_fits(M, V, H) ? (V + kBigBN - 1) / kBigBN : 0;
 }
@@ -868,7 +1029,7 @@ int lmhead_big_records(int M, int V, int H) {
 hipError_t launch_lmhead_bf16(const uint16_t* hidden, const uint16_t* W, float* logits, int M, int V, int H,
                               int num_cus, hipStream_t stream, StatRec* stats, float c, int* n_rec) {
     if (n_rec) *n_rec = 0;
-    if (CoopCfg::fits(M, H)) return launch_coop<2, 2, 8>(hidden, W, logits, M, V, H, num_cus, stream, 1);
+    if (CoopCfg::fits(M, H)) return launch_coop<2, 2, 8, false>(hidden, W, logits, M, V, H, num_cus, stream);
     if (big_fits(M, V, H)) {
         if (stats) {
             if (n_rec) *n_rec = (V + kBigBN - 1) / kBigBN;

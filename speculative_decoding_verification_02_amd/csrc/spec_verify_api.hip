@@ -110,7 +110,7 @@ spec_status_t check_ragged(const int32_t* row_start, int total_rows, int B, int 
 // records written by the statistics pass: target slots, then draft slots
 sv::RecLayout pass_layout(const sv::StatRec* stats, int n_rows, int K, int V) {
     const int nc = sv::n_chunks(V);
-    return sv::RecLayout{stats, nc, false, stats + (size_t)n_rows * (K + 1) * nc, nc};
+    return sv::RecLayout{stats, nc, false, stats + (size_t)n_rows * (K + 1) * nc, nc, false};
 }
 
 spec_status_t greedy_impl(const float* logits, const int32_t* draft_tokens, const int32_t* rows, int n_rows,
@@ -178,7 +178,14 @@ sv::SeqRows dense_rows(int B, int K) { return sv::SeqRows{nullptr, B, K, B * (K 
 // Records per target row the fused step may write: the direct-to-LDS
 // kernel's epilogue writes one per 256 vocabulary entries (it runs only for
 // M > 16; the statistics pass it may fall back to writes one per 4096).
-size_t step_target_recs(int M, int V) { return M <= 16 ? 0 : ((size_t)V + 255) / 256; }
+// Records the fused step keeps beyond the accept calls' workspace: at
+// M <= 16 one per cooperative-kernel workgroup for each target and draft
+// row, above that one per 256 vocabulary entries for each target row.
+size_t step_extra_records(int B, int K, int V) {
+    const size_t M = (size_t)B * (K + 1);
+    if (M <= 16) return (M + (size_t)B * K) * sv::kCoopMaxRecs;
+    return M * (((size_t)V + 255) / 256);
+}
 
 // A row list as the fused step takes it: (NULL, 0) none, (NULL, B) all,
 // (list, 0..B) those.
@@ -329,18 +336,55 @@ spec_status_t spec_verify_step(const void* hidden, const void* w_lmhead, spec_dt
     hipStream_t s = static_cast<hipStream_t>(stream);
     hipError_t e = hipSuccess;
 
+    // At M <= 16 the cooperative kernel computes the statistics of the
+    // target rows as it sums each tile and those of the draft rows while its
+    // first loads are in flight, one record per workgroup and row; the accept
+    // kernels merge those records straight from memory.  No pass reads the
+    // logits back and no statistics kernel runs.
+    const float* dl = (ns > 0 && K > 0) ? draft_logits : nullptr;
+    const bool fused = dl && (long)ns * (2 * K + 1) <= sv::kFusedAcceptMaxRows;
+    int cus = 0;
+    if (any && dtype == SPEC_BF16) {
+        e = num_cus(&cus);
+        if (e != hipSuccess) return hip_fail(e);
+        const int crec = sv::lmhead_coop_records(M, V, H, dl ? B * K : 0, cus);
+        if (crec > 0) {
+            sv::StatRec* trec = tstats;                          // M x crec
+            sv::StatRec* drec = tstats + (size_t)M * crec;       // B*K x crec
+            const sv::CoopStats cs{trec, dl, dl ? B * K : 0, drec, c, fused ? ws.counters : nullptr, fused ? ns : 0};
+            e = sv::launch_lmhead_coop_stats(static_cast<const uint16_t*>(hidden),
+                                             static_cast<const uint16_t*>(w_lmhead), logits, M, V, H, cus, s, cs);
+            if (e == hipSuccess && ng > 0)
+                e = sv::launch_accept(logits, nullptr, draft_tokens, nullptr, greedy_rows, ng, seq, V, sv::kLog2e,
+                                      false, sv::RecLayout{trec, crec, true, nullptr, 0, false}, accepted_len,
+                                      out_tokens, nullptr, ws.info, ws.counters, s);
+            const sv::RecLayout lay{trec, crec, true, drec, crec, true};
+            if (e == hipSuccess && ns > 0) {
+                if (fused) {
+                    e = sv::launch_accept_residual(logits, dl, draft_tokens, seeds, sampled_rows, ns, seq, V, c, lay,
+                                                   accepted_len, out_tokens, probs_at_draft, ws.sums, ws.counters, s);
+                } else {
+                    e = sv::launch_accept(logits, dl, draft_tokens, seeds, sampled_rows, ns, seq, V, c, true, lay,
+                                          accepted_len, out_tokens, probs_at_draft, ws.info, ws.counters, s);
+                    if (e == hipSuccess)
+                        e = sv::launch_residual(logits, dl, ns, V, c, ws.info, ws.sums, ws.counters, out_tokens, s);
+                }
+            }
+            return e == hipSuccess ? SPEC_OK : hip_fail(e);
+        }
+    }
+
     // The statistics epilogue pays where the direct-to-LDS kernel runs: it
     // removes the pass that reads the logits back, and with the loop's order
     // pinned it costs the kernel ~2%.  Its records (one per 256 vocabulary
     // entries) are folded into the statistics pass's chunk records before the
     // accept kernels, which then run exactly as after the pass.  Elsewhere
-    // (the cooperative kernel at M <= 16, where W's bytes bound the step;
-    // the other kernels; fp32) the step runs the separate calls' kernels.
+    // (the skinny and tiled kernels, fp32) the step runs the separate calls'
+    // kernels.
     const int big_recs = dtype == SPEC_BF16 ? sv::lmhead_big_records(M, V, H) : 0;
     const bool epilogue = any && big_recs > 0;
     if (!epilogue) {
         if (dtype == SPEC_BF16) {
-            int cus = 0;
             e = num_cus(&cus);
             if (e == hipSuccess)
                 e = sv::launch_lmhead_bf16(static_cast<const uint16_t*>(hidden),
@@ -363,12 +407,10 @@ spec_status_t spec_verify_step(const void* hidden, const void* w_lmhead, spec_dt
     // draft-row statistics first: they do not depend on the LM head (the pass
     // also clears the completion counters a fused accept + residual needs)
     const int nc = sv::n_chunks(V);
-    const float* dl = (ns > 0 && K > 0) ? draft_logits : nullptr;
-    const bool fused = dl && (long)ns * (2 * K + 1) <= sv::kFusedAcceptMaxRows;
     if (dl) e = sv::launch_softmax_stats(nullptr, dl, sampled_rows, ns, seq, V, c, true, ws.stats, s,
                                          fused ? ws.counters : nullptr);
-    int cus = 0, nrec = 0;
-    if (e == hipSuccess) e = num_cus(&cus);
+    int nrec = 0;
+    if (e == hipSuccess && cus == 0) e = num_cus(&cus);
     if (e == hipSuccess)
         e = sv::launch_lmhead_bf16(static_cast<const uint16_t*>(hidden), static_cast<const uint16_t*>(w_lmhead), logits,
                                    M, V, H, cus, s, tstats, c, &nrec);
@@ -377,10 +419,10 @@ spec_status_t spec_verify_step(const void* hidden, const void* w_lmhead, spec_dt
     // statistics area, which is sized for B*(K+1) + B*K rows
     sv::StatRec* trec = ws.stats + (size_t)B * K * nc;
     if (e == hipSuccess) e = sv::launch_fold_records(tstats, nrec, M, V, c, trec, s);
-    const sv::RecLayout lay{trec, nc, true, ws.stats, nc};
+    const sv::RecLayout lay{trec, nc, true, ws.stats, nc, false};
     if (e == hipSuccess && ng > 0)
         e = sv::launch_accept(logits, nullptr, draft_tokens, nullptr, greedy_rows, ng, seq, V, sv::kLog2e, false,
-                              sv::RecLayout{trec, nc, true, nullptr, 0}, accepted_len, out_tokens, nullptr, ws.info,
+                              sv::RecLayout{trec, nc, true, nullptr, 0, false}, accepted_len, out_tokens, nullptr, ws.info,
                               ws.counters, s);
     if (e == hipSuccess && ns > 0) {
         if (fused) {
@@ -398,8 +440,7 @@ spec_status_t spec_verify_step(const void* hidden, const void* w_lmhead, spec_dt
 
 size_t spec_verify_step_workspace_bytes(int B, int K, int V) {
     if (!sizes_ok(B, K, V)) return 0;
-    const size_t M = (size_t)B * (K + 1);
-    return workspace_layout(B, K, V, nullptr, nullptr) + align256(M * step_target_recs((int)M, V) * sizeof(sv::StatRec));
+    return workspace_layout(B, K, V, nullptr, nullptr) + align256(step_extra_records(B, K, V) * sizeof(sv::StatRec));
 }
 
 size_t spec_workspace_bytes(int B, int K, int V) {

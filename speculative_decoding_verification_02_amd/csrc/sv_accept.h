@@ -78,6 +78,47 @@ __device__ __forceinline__ Merged row16_merge(const StatRec* rec, int nc, float 
     return Merged{m, s, idx, bad};
 }
 
+// The same merge by the 16 lanes of a DPP row, reading the records straight
+// from global memory (rows with many records, such as one per LM-head
+// workgroup): each lane keeps a running record over its batches of loads,
+// all loads of a batch in flight at once, then the 16 lanes combine.
+__device__ __forceinline__ Merged row16_merge_global(const StatRec* __restrict__ rec, int nc, float c, bool need_sum,
+                                                     int gl) {
+    constexpr int kBatch = 16;
+    float m = -INFINITY, s = 0.f;
+    int idx = INT_MAX, bad = 0;
+    for (int k0 = 0; k0 < nc; k0 += 16 * kBatch) {
+        StatRec x[kBatch];
+#pragma unroll
+        for (int j = 0; j < kBatch; ++j) {
+            const int k = k0 + j * 16 + gl;
+            x[j] = k < nc ? rec[k] : StatRec{-INFINITY, 0.f, INT_MAX, 0};
+        }
+        float bm = m;
+        int bi = idx;
+#pragma unroll
+        for (int j = 0; j < kBatch; ++j) {
+            argmax_combine(bm, bi, x[j].m, x[j].idx);
+            bad |= x[j].bad;
+        }
+        if (need_sum && bm != -INFINITY) {
+            s = m == -INFINITY ? 0.f : s * exp2f((m - bm) * c);
+#pragma unroll
+            for (int j = 0; j < kBatch; ++j)
+                if (x[j].m != -INFINITY) s += x[j].s * exp2f((x[j].m - bm) * c);
+        }
+        m = bm;
+        idx = bi;
+    }
+    float M = m;
+    int I = idx;
+    row16_argmax(M, I);
+    bad = row16_or(bad) != 0;
+    float S = 0.f;
+    if (need_sum && M != -INFINITY) S = row16_sum(m == -INFINITY ? 0.f : s * exp2f((m - M) * c));
+    return Merged{M, S, I, bad};
+}
+
 // Merge the records of n consecutive rows (nc records each, row r at
 // base + r*nc) into merged[out0 + r], one wavefront per row.  Rows are staged
 // through LDS with every load in flight at once when they fit; rows longer
@@ -151,7 +192,7 @@ __device__ AcceptInfo accept_sequence(const float* __restrict__ logits, const fl
     // merged statistics of the target rows 0..kb, then (sampled) the draft
     // rows 0..kb-1 (merged[kb+1+i])
     const StatRec* tgt0 = rec.tgt + (size_t)(rec.tgt_by_row ? t0 : j * (K + 1)) * rec.tgt_nc;
-    const StatRec* drf0 = rec.drf + (size_t)j * K * rec.drf_nc;
+    const StatRec* drf0 = rec.drf + (rec.drf_by_row ? d0 : (size_t)j * K) * rec.drf_nc;
     const int n_drf = SAMPLED ? kb : 0;
     if (rec.tgt_nc == rec.drf_nc && (kb + 1 + n_drf) * rec.tgt_nc <= kRecBuf) {
         // everything in one pass: all record loads of both groups in flight
@@ -163,6 +204,18 @@ __device__ AcceptInfo accept_sequence(const float* __restrict__ logits, const fl
         // four rows per wavefront, one per 16-lane DPP row
         for (int rr = wave * 4 + (lane >> 4); rr < kb + 1 + n_drf; rr += kAcceptWaves * 4) {
             const Merged x = row16_merge(recs + rr * nc, nc, c, SAMPLED, lane & 15);
+            if ((lane & 15) == 0) merged[rr] = x;
+        }
+        __syncthreads();
+    } else if (kb + 1 + n_drf <= kAcceptWaves * 4) {
+        // few rows with many records each: one row per 16-lane DPP row,
+        // straight from global memory
+        const int rr = wave * 4 + (lane >> 4);
+        if (rr < kb + 1 + n_drf) {
+            const bool tgt_row = rr <= kb;
+            const StatRec* src = tgt_row ? tgt0 + (size_t)rr * rec.tgt_nc : drf0 + (size_t)(rr - kb - 1) * rec.drf_nc;
+            const Merged x = row16_merge_global(src, tgt_row ? rec.tgt_nc : rec.drf_nc, c, !tgt_row || SAMPLED,
+                                                lane & 15);
             if ((lane & 15) == 0) merged[rr] = x;
         }
         __syncthreads();

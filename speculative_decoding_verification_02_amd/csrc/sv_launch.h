@@ -21,6 +21,27 @@ hipError_t launch_lmhead_bf16(const uint16_t* hidden, const uint16_t* W, float* 
                               int* n_rec = nullptr);
 hipError_t launch_lmhead_f32(const float* hidden, const float* W, float* logits, int M, int V, int H,
                              hipStream_t stream);
+// Statistics the cooperative LM-head kernel (M <= 16) computes on the side:
+// per workgroup w of n_rec, the record of hidden row m over the workgroup's
+// contiguous vocabulary range at tgt[m * n_rec + w], and likewise of draft
+// row d (n_draft rows of V fp32 logits at draft) at drf[d * n_rec + w], sums
+// relative to c = log2(e) / T; workgroup 0 also clears n_zero counters.
+struct CoopStats {
+    StatRec* tgt;
+    const float* draft;
+    int n_draft;
+    StatRec* drf;
+    float c;
+    int* zero;
+    int n_zero;
+};
+constexpr int kCoopMaxRecs = 1024;   // records per row at most (workgroups of the cooperative kernel)
+// Records per row the cooperative kernel writes for this shape with n_draft
+// draft rows (its workgroup count), else 0 (it does not run for this shape,
+// or the rows' logits would not fit its LDS).
+int lmhead_coop_records(int M, int V, int H, int n_draft, int num_cus);
+hipError_t launch_lmhead_coop_stats(const uint16_t* hidden, const uint16_t* W, float* logits, int M, int V, int H,
+                                    int num_cus, hipStream_t stream, const CoopStats& st);
 // Fold rows x recs_per_row epilogue records (one per 256 vocabulary entries,
 // row r at in + r * recs_per_row) into rows x n_chunks(V) chunk records, the
 // layout the statistics pass writes; sums relative to inv_t_log2e.
@@ -44,13 +65,15 @@ hipError_t launch_softmax_stats(const float* logits, const float* draft_logits, 
 // Where the accept kernel finds the statistics records of a sequence's rows.
 // Target rows: tgt + (tgt_by_row ? t0 + i : j*(K+1) + i) * tgt_nc (by packed
 // row for the LM-head epilogue's records, by selection slot for the
-// statistics pass).  Draft rows: drf + (j*K + i) * drf_nc.
+// statistics pass).  Draft rows: drf + (drf_by_row ? t0 - b + i : j*K + i) *
+// drf_nc.
 struct RecLayout {
     const StatRec* tgt;
     int tgt_nc;
     bool tgt_by_row;
     const StatRec* drf;
     int drf_nc;
+    bool drf_by_row;
 };
 
 // Greedy or sampled acceptance: one workgroup per selected sequence.  The

@@ -198,8 +198,10 @@ def _step(lib, hid=A, w=A, dt=0, dl=A, dtok=A, T=1.0, seeds=A, g=None, ng=0, sm=
 
 
 def test_step_validation(lib):
-    # epilogue records only where the direct-to-LDS kernel can run (M > 16)
-    assert sv.spec_verify_step_workspace_bytes(1, 5, 128256) == sv.spec_workspace_bytes(1, 5, 128256)
+    # M <= 16: one record per cooperative-kernel workgroup (at most 1024) for
+    # each of the M target and B*K draft rows; M > 16: one per 256 vocabulary
+    # entries for each target row
+    assert sv.spec_verify_step_workspace_bytes(1, 5, 128256) == sv.spec_workspace_bytes(1, 5, 128256) + 11 * 1024 * 16
     a = sv.spec_verify_step_workspace_bytes(4, 5, 128256)
     assert a >= sv.spec_workspace_bytes(4, 5, 128256) + 24 * 501 * 16 and a % 256 == 0
     assert sv.spec_verify_step_workspace_bytes(1, 64, 100) == 0

@@ -2,12 +2,16 @@
 statistics in its epilogue where that pays, then both accept rules) against
 the oracle and against the separate calls it replaces.
 
-Every LM-head kernel path is covered: the direct-to-LDS kernel in several
-tile heights, which folds the statistics into its epilogue (records then
-folded to the statistics pass's chunks, small sampled batches accepted and
-drawn in one launch), and the paths that run the separate calls' kernels
-instead (the cooperative kernel for M <= 16, the small-M kernel for wide
-hidden sizes, the tiled kernel for H not a multiple of 64, fp32 weights).
+Every LM-head kernel path is covered: the cooperative kernel for M <= 16,
+which computes the target and draft rows' statistics itself (one record per
+workgroup, merged by the accept kernels straight from memory); the
+direct-to-LDS kernel in several tile heights, which folds the statistics into
+its epilogue (records then folded to the statistics pass's chunks, small
+sampled batches accepted and drawn in one launch); and the paths that run the
+separate calls' kernels instead (the small-M kernel for wide hidden sizes, the
+tiled kernel for H not a multiple of 64, fp32 weights).  Data faults (a NaN
+in a target row, +inf in a draft row) must mark the same sequences on both
+sides.
 The logits must be bit-identical to spec_verify_logits, greedy outputs
 identical to spec_accept_greedy, and both sides must meet the oracle run on
 the same fp32 logits (sampled decisions by the margin rule, probabilities
@@ -91,8 +95,12 @@ def _wl(B, K, H, V, dtype="bf16", T=0.9, seed=7):
 
 
 @pytest.mark.parametrize("B,K,H,V,dtype,path", [
-    (1, 5, 512, 3001, "bf16", "cooperative, statistics pass"),
-    (3, 4, 4096, 5003, "bf16", "cooperative, statistics pass"),
+    (1, 5, 512, 3001, "bf16", "cooperative, statistics in the LM-head kernel"),
+    (3, 4, 4096, 5003, "bf16", "cooperative, statistics in the LM-head kernel, mixed rules"),
+    (2, 7, 1024, 2053, "bf16", "cooperative, 15 rows per sequence merged from memory"),
+    (1, 15, 256, 3001, "bf16", "cooperative, K=15 (31 rows: staged merge)"),
+    (16, 0, 256, 1000, "bf16", "cooperative, K=0 (bonus draws only)"),
+    (2, 3, 256, 262147, "bf16", "cooperative, 64+ tiles per workgroup (rows reduced in several passes)"),
     (4, 15, 256, 102400, "bf16", "direct-to-LDS, K=15, epilogue records folded to chunks"),
     (2, 8, 256, 3001, "bf16", "direct-to-LDS, epilogue, accept and residual in one launch"),
     (2, 3, 8192, 3001, "bf16", "small-M wide H, statistics pass"),
@@ -110,12 +118,40 @@ def test_step_paths(B, K, H, V, dtype, path):
     _check(wl, list(range(half)), list(range(half, B)))
 
 
-def test_step_row_list_forms():
-    wl = _wl(6, 3, 256, 2000, seed=3)
-    say("fused step: all greedy, all sampled, sampled subset only")
+@pytest.mark.parametrize("B,K", [(6, 3), (4, 3)])
+def test_step_row_list_forms(B, K):
+    wl = _wl(B, K, 256, 2000, seed=3)
+    say("fused step B=%d K=%d: all greedy, all sampled, sampled subset only" % (B, K))
     _check(wl, "all", None)
     _check(wl, None, "all")
-    _check(wl, None, [5, 0, 2])
+    _check(wl, None, [B - 1, 0, 2])
+
+
+@pytest.mark.parametrize("B,K,H,V", [(4, 3, 256, 2000), (6, 3, 256, 2000)])
+def test_step_faults(B, K, H, V):
+    """A NaN in a target row and +inf in a draft row fault exactly the
+    sequences they belong to, as in the separate calls."""
+    wl = _wl(B, K, H, V, seed=11)
+    say("fused step faults B=%d K=%d H=%d V=%d" % (B, K, H, V))
+    inp = _inputs(wl, dev())
+    inp["hidden"][1, 2, 5] = float("nan")           # sequence 1: target row 2 all NaN
+    inp["draft_logits"][2, 1, 17] = float("inf")    # sequence 2: draft row 1
+    # sequence 1 verified greedily, then by sampling; sequence 2 always sampled
+    for greedy_rows, sampled_rows in (([0, 1], list(range(2, B))), ([0], list(range(1, B)))):
+        logits, acc, out, pad = _step(inp, wl.temperature, greedy_rows, sampled_rows, K, V)
+        torch.cuda.synchronize()
+        ref = gpu_logits(inp["hidden"], inp["W"])
+        assert torch.equal(torch.nan_to_num(logits, nan=7.0), torch.nan_to_num(ref, nan=7.0))
+        acc_c, out_c = acc.cpu().numpy(), out.cpu().numpy()
+        for b in (1, 2):
+            assert acc_c[b] == -1 and (out_c[b] == -1).all(), (b, acc_c[b], out_c[b])
+        acc_g, out_g = gpu_accept_greedy(ref, inp["drafts"], rows=np.asarray(greedy_rows))
+        np.testing.assert_array_equal(acc_c[greedy_rows], acc_g.cpu().numpy()[greedy_rows])
+        np.testing.assert_array_equal(out_c[greedy_rows], out_g.cpu().numpy()[greedy_rows])
+        acc_s, out_s, _ = gpu_accept_sample(ref, inp["draft_logits"], inp["drafts"], wl.temperature, inp["seeds"],
+                                            rows=np.asarray(sampled_rows))
+        np.testing.assert_array_equal(acc_c[sampled_rows], acc_s.cpu().numpy()[sampled_rows])
+        np.testing.assert_array_equal(out_c[sampled_rows], out_s.cpu().numpy()[sampled_rows])
 
 
 @pytest.mark.parametrize("name", ["b1_k5_h4096_v128256", "b64_k4_h4096_v128256", "b32_k15_h4096_v151936",
