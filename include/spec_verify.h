@@ -366,7 +366,7 @@ spec_status_t spec_ngram_propose(const int32_t* history, const int64_t* hist_sta
                                  spec_stream_t stream);
 
 /* Bytes of workspace spec_ngram_propose needs for B histories of at most
- * max_len tokens (one 8-byte slot per 8192-position segment; 0 if B < 1 or
+ * max_len tokens (one 8-byte slot per 4096-position segment; 0 if B < 1 or
  * max_len is out of range). */
 size_t spec_ngram_workspace_bytes(int B, int max_len);
 

@@ -15,10 +15,12 @@
 //
 // Two launches: one workgroup per (sequence, segment of kNgSeg end positions)
 // stages its segment with coalesced loads, scores every position and stores
-// the segment's best key (m << 32 | e); one workgroup takes the best key of
-// each sequence, copies the drafts and prefix-sums the verify-row offsets
-// row_start[b+1] = row_start[b] + count_b + 1.  The history is read once, so
-// the scan is bound by HBM bandwidth.
+// the segment's best key (m << 32 | e); one workgroup, four threads per
+// sequence, takes the best key of each sequence, copies the drafts and
+// prefix-sums the verify-row offsets row_start[b+1] = row_start[b] +
+// count_b + 1.  The history is read once, so the scan is bound by HBM
+// bandwidth; the second launch is two dependent rounds of loads (span and
+// keys, then the drafts).
 #include "sv_common.h"
 #include "sv_launch.h"
 
@@ -27,6 +29,8 @@ namespace sv {
 constexpr int kNgThreads = 256;
 constexpr int kNgPerThread = kNgSeg / kNgThreads;   // end positions per thread
 constexpr int kNgFinThreads = 1024;
+constexpr int kNgFinLanes = 4;                            // threads per sequence
+constexpr int kNgFinSeqs = kNgFinThreads / kNgFinLanes;   // sequences per pass
 static_assert(kNgSeg % kNgThreads == 0, "segment must split evenly");
 
 // history span of sequence b, or false if its offsets are malformed
@@ -96,62 +100,86 @@ __global__ __launch_bounds__(kNgThreads) void ngram_scan_kernel(const int32_t* _
     }
 }
 
-// One workgroup: per sequence, the best key over its segments, the drafts
-// that follow the chosen window, and the prefix sum of the verify rows.
+// One workgroup: per sequence (four threads, a DPP quad), the best key over
+// its segments, the drafts that follow the chosen window, and the prefix sum
+// of the verify rows.  The span and the keys are loaded together (thread q
+// takes segments q, q+4, ...), then the drafts (thread q takes positions q,
+// q+4, ...).
+__device__ __forceinline__ unsigned long long quad_max_u64(unsigned long long x) {
+#pragma unroll
+    for (int step = 0; step < 2; ++step) {
+        const int lo = (int)(unsigned)x, hi = (int)(unsigned)(x >> 32);
+        const int plo = step ? dpp_xor2(lo) : dpp_xor1(lo), phi = step ? dpp_xor2(hi) : dpp_xor1(hi);
+        const unsigned long long y = ((unsigned long long)(unsigned)phi << 32) | (unsigned)plo;
+        x = y > x ? y : x;
+    }
+    return x;
+}
+
 __global__ __launch_bounds__(kNgFinThreads) void ngram_finalize_kernel(
     const int32_t* __restrict__ hist, const int64_t* __restrict__ hist_start, int B, int max_len, int n_drafts,
     int segs, const unsigned long long* __restrict__ keys, int32_t* __restrict__ drafts, int32_t* __restrict__ count,
     int32_t* __restrict__ row_start) {
     __shared__ int wsum[kNgFinThreads / kWave];
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, q = tid & (kNgFinLanes - 1);
+    constexpr int kKeyBatch = 8;
+    constexpr int kDraftPer = (kNgMaxDrafts + kNgFinLanes - 1) / kNgFinLanes;
     int carry = 0;
     if (row_start && tid == 0) row_start[0] = 0;
-    for (int base = 0; base < B; base += kNgFinThreads) {
-        const int b = base + tid;
-        int c = 0;
-        if (b < B) {
-            int64_t s0;
-            int L;
-            int32_t* drow = drafts + (size_t)b * n_drafts;
-            if (!ng_span(hist_start, b, max_len, s0, L)) {
-                count[b] = -1;
-                for (int i = 0; i < n_drafts; ++i) drow[i] = -1;
-            } else {
-                // loads in batches of 8, each batch in flight at once
-                unsigned long long key = 0ull;
-                for (int g0 = 0; g0 < segs; g0 += 8) {
-                    unsigned long long k[8];
+    for (int base = 0; base < B; base += kNgFinSeqs) {
+        const int b = base + tid / kNgFinLanes;
+        const bool live = b < B;   // whole quads
+        int64_t s0 = 0;
+        int L = 0;
+        bool ok = false;
+        unsigned long long key = 0ull;
+        if (live) {
+            ok = ng_span(hist_start, b, max_len, s0, L);
+            const unsigned long long* kb = keys + (size_t)b * segs;
+            for (int g0 = q; g0 < segs; g0 += kNgFinLanes * kKeyBatch) {
+                unsigned long long k[kKeyBatch];
 #pragma unroll
-                    for (int g = 0; g < 8; ++g) k[g] = g0 + g < segs ? keys[(size_t)b * segs + g0 + g] : 0ull;
-#pragma unroll
-                    for (int g = 0; g < 8; ++g) key = k[g] > key ? k[g] : key;
+                for (int g = 0; g < kKeyBatch; ++g) {
+                    const int idx = g0 + g * kNgFinLanes;
+                    k[g] = idx < segs ? kb[idx] : 0ull;
                 }
+#pragma unroll
+                for (int g = 0; g < kKeyBatch; ++g) key = k[g] > key ? k[g] : key;
+            }
+        }
+        key = quad_max_u64(key);
+        int c = 0;
+        if (live) {
+            int32_t* drow = drafts + (size_t)b * n_drafts;
+            if (!ok) {
+                for (int i = q; i < n_drafts; i += kNgFinLanes) drow[i] = -1;
+                if (q == 0) count[b] = -1;
+            } else {
                 const int start = (int)(key & 0xffffffffull) + 1;   // after the matched window
                 if (key >> 32) c = min(n_drafts, L - start);          // a match: L - start >= 1
-                for (int i0 = 0; i0 < n_drafts; i0 += 8) {
-                    int32_t t[8];
+                int32_t t[kDraftPer];
 #pragma unroll
-                    for (int i = 0; i < 8; ++i) t[i] = i0 + i < c ? hist[s0 + start + i0 + i] : -1;
-#pragma unroll
-                    for (int i = 0; i < 8; ++i)
-                        if (i0 + i < n_drafts) drow[i0 + i] = t[i];
+                for (int j = 0; j < kDraftPer; ++j) {
+                    const int i = q + j * kNgFinLanes;
+                    t[j] = i < c ? hist[s0 + start + i] : -1;
                 }
-                count[b] = c;
+#pragma unroll
+                for (int j = 0; j < kDraftPer; ++j) {
+                    const int i = q + j * kNgFinLanes;
+                    if (i < n_drafts) drow[i] = t[j];
+                }
+                if (q == 0) count[b] = c;
             }
         }
         if (row_start) {
-            // inclusive scan of c + 1 over the chunk, then the running carry
-            int x = b < B ? c + 1 : 0;
-#pragma unroll
-            for (int o = 1; o < kWave; o <<= 1) {
-                const int y = __shfl_up(x, o, kWave);
-                if (lane >= o) x += y;
-            }
+            // inclusive scan of count + 1 (one value per quad, at its first
+            // thread) over the pass, then the running carry
+            const int x = wave_inclusive_scan_int(live && q == 0 ? c + 1 : 0);
             if (lane == kWave - 1) wsum[wave] = x;
             __syncthreads();
             int pre = carry;
             for (int w = 0; w < wave; ++w) pre += wsum[w];
-            if (b < B) row_start[b + 1] = pre + x;
+            if (live && q == 0) row_start[b + 1] = pre + x;
             int tot = 0;
             for (int w = 0; w < kNgFinThreads / kWave; ++w) tot += wsum[w];
             carry += tot;
@@ -163,6 +191,7 @@ __global__ __launch_bounds__(kNgFinThreads) void ngram_finalize_kernel(
 hipError_t launch_ngram(const int32_t* hist, const int64_t* hist_start, int B, int max_len, int G, int n_drafts,
                         int32_t* drafts, int32_t* count, int32_t* row_start, unsigned long long* keys,
                         hipStream_t stream) {
+    if (n_drafts < 0 || n_drafts > kNgMaxDrafts) return hipErrorInvalidValue;
     const int segs = ngram_segments(max_len);
     if (segs > 0) {
         hipLaunchKernelGGL(ngram_scan_kernel, dim3((unsigned)((long)B * segs)), dim3(kNgThreads), 0, stream, hist,

@@ -285,7 +285,7 @@ spec_status_t spec_ngram_propose(const int32_t* history, const int64_t* hist_sta
                                  int max_ngram, int n_drafts, int32_t* drafts, int32_t* draft_count,
                                  int32_t* row_start, void* workspace, size_t workspace_bytes, spec_stream_t stream) {
     if (B < 1 || max_len < 0 || max_len == 0x7fffffff || max_ngram < 1 || max_ngram > sv::kNgMaxGram ||
-        n_drafts < 0 || n_drafts > kMaxK)
+        n_drafts < 0 || n_drafts > sv::kNgMaxDrafts)
         return SPEC_ERR_ARG;
     if (!hist_start || !draft_count || (n_drafts > 0 && !drafts) || (max_len > 0 && !history)) return SPEC_ERR_ARG;
     if ((long long)B * sv::ngram_segments(max_len) > 0x7fffffffLL) return SPEC_ERR_ARG;

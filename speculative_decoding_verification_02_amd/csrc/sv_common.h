@@ -153,6 +153,17 @@ __device__ __forceinline__ float wave_inclusive_scan(float x) {
     return x;
 }
 
+// The same inclusive prefix sum over 32-bit integers.
+__device__ __forceinline__ int wave_inclusive_scan_int(int x) {
+    x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xF, 0xF, true);   // row_shr:1
+    x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xF, 0xF, true);   // row_shr:2
+    x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xF, 0xF, true);   // row_shr:4
+    x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xF, 0xF, true);   // row_shr:8
+    x += __builtin_amdgcn_update_dpp(0, x, 0x142, 0xA, 0xF, false);  // row_bcast:15 into rows 1, 3
+    x += __builtin_amdgcn_update_dpp(0, x, 0x143, 0xC, 0xF, false);  // row_bcast:31 into rows 2, 3
+    return x;
+}
+
 // Fold the statistics (m, s, i, bad) of one span of a row into a running
 // record a, both relative to c = log2(e) / T:
 //   M = max(a.m, m),  S = a.s * 2^((a.m - M) c) + s * 2^((m - M) c),

@@ -170,9 +170,9 @@ def _ngram(lib, hist=A, hs=A, B=2, max_len=100, g=3, k=5, drafts=A, count=A, ws=
 def test_ngram_validation(lib):
     assert sv.spec_ngram_workspace_bytes(0, 10) == 0 and sv.spec_ngram_workspace_bytes(3, 100) == 256
     assert sv.spec_ngram_workspace_bytes(3, -1) == 0
-    assert sv.spec_ngram_workspace_bytes(64, 8193) == 64 * 8         # 8192 end positions: one segment
-    assert sv.spec_ngram_workspace_bytes(64, 8194) == 64 * 8 * 2
-    assert sv.spec_ngram_workspace_bytes(64, 16386) == 64 * 8 * 3
+    assert sv.spec_ngram_workspace_bytes(64, 4097) == 64 * 8         # 4096 end positions: one segment
+    assert sv.spec_ngram_workspace_bytes(64, 4098) == 64 * 8 * 2
+    assert sv.spec_ngram_workspace_bytes(64, 8194) == 64 * 8 * 3
     assert _ngram(lib, B=0) == sv.SPEC_ERR_ARG
     assert _ngram(lib, max_len=-1) == sv.SPEC_ERR_ARG
     assert _ngram(lib, g=0) == sv.SPEC_ERR_ARG

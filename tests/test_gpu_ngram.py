@@ -1,7 +1,7 @@
 """GPU parity of spec_ngram_propose (prompt-lookup drafts) against the
 oracle, which follows the pages' search n = max_ngram .. 1 directly.  Token
 equality only, so drafts, counts and verify-row offsets must match exactly:
-histories from empty to several scan segments long (8192 end positions per
+histories from empty to several scan segments long (4096 end positions per
 workgroup) with matches on either side of segment borders, tiny and large
 vocabularies (every position matching, or almost none), the n-gram and
 draft-count limits, malformed offsets, the full 256 x 128K-token workload,
@@ -52,7 +52,7 @@ def _check(hist, G, k):
 @pytest.mark.parametrize("G,k", [(1, 1), (3, 7), (8, 63), (16, 4)])
 def test_ngram_exact(V, G, k):
     rng = np.random.default_rng(V + 10 * G + k)
-    lengths = np.concatenate([[0, 1, 2, 3, 8193, 8194, 16385], rng.integers(0, 30000, 33)])
+    lengths = np.concatenate([[0, 1, 2, 3, 4097, 4098, 8193, 8194, 16385], rng.integers(0, 30000, 31)])
     hist = synth.histories(len(lengths), 0, V, seed=V + G, copy_frac=0.5, lengths=lengths)
     say("ngram exact B=%d V=%d max_ngram=%d n_drafts=%d" % (len(hist), V, G, k))
     oc, om = _check(hist, G, k)
@@ -61,10 +61,11 @@ def test_ngram_exact(V, G, k):
 
 def test_matches_at_segment_borders():
     # the only earlier occurrence of the final trigram ends exactly at, just
-    # before, or just after a segment border (end positions 8191 | 8192)
+    # before, or just after a segment border (end positions 4095 | 4096,
+    # 8191 | 8192, ...)
     V = 1 << 20
     hist = []
-    for e in (8190, 8191, 8192, 8193, 16383, 16384):
+    for e in (4094, 4095, 4096, 4097, 8190, 8191, 8192, 8193, 16383, 16384):
         s = np.arange(20000, dtype=np.int64) + 1000      # all distinct
         s[e - 2:e + 1] = [7, 8, 9]
         s[-3:] = [7, 8, 9]
