@@ -43,6 +43,34 @@ __global__ __launch_bounds__(kAcceptThreads) void accept_kernel(
     if (SAMPLED && threadIdx.x == 0) info[j] = a;
 }
 
+// Both rules in one launch: workgroup j < n_greedy decides greedy_rows[j],
+// the others sampled_rows[j - n_greedy] (their AcceptInfo and residual
+// counter in slot j - n_greedy), each exactly as accept_kernel does.
+__global__ __launch_bounds__(kAcceptThreads) void accept_both_kernel(
+    const float* __restrict__ logits, const float* __restrict__ draft_logits, const int32_t* __restrict__ draft_tokens,
+    const uint64_t* __restrict__ seeds, const int32_t* __restrict__ greedy_rows, int n_greedy,
+    const int32_t* __restrict__ sampled_rows, SeqRows seq, int V, float c, RecLayout rec_greedy,
+    RecLayout rec_sampled, int32_t* __restrict__ accepted_len, int32_t* __restrict__ out_tokens,
+    float* __restrict__ probs_at_draft, AcceptInfo* __restrict__ info, int* __restrict__ counters) {
+    __shared__ StatRec recs[kRecBuf];
+    __shared__ Merged merged[kMaxRows];
+    __shared__ AcceptInfo sinfo;
+    const int j = blockIdx.x;
+    if (j < n_greedy) {
+        const int b = greedy_rows ? greedy_rows[j] : j;
+        accept_sequence<false>(logits, nullptr, draft_tokens, nullptr, j, b, seq, V, kLog2e, rec_greedy, true,
+                               accepted_len, out_tokens, nullptr, recs, merged, &sinfo);
+        return;
+    }
+    const int js = j - n_greedy;
+    const int b = sampled_rows ? sampled_rows[js] : js;
+    if (threadIdx.x == 0) counters[js] = 0;   // the residual kernel counts its chunk blocks from zero
+    const AcceptInfo a = accept_sequence<true>(logits, draft_logits, draft_tokens, seeds, js, b, seq, V, c,
+                                               rec_sampled, true, accepted_len, out_tokens, probs_at_draft, recs,
+                                               merged, &sinfo);
+    if (threadIdx.x == 0) info[js] = a;
+}
+
 // ----------------------------------------------------------- draft trees --
 // Greedy verification of a draft tree of N <= 63 nodes per sequence
 // ("Inference-4", Medusa; "speculative-decoding" blog, EAGLE-2's dynamic
@@ -176,6 +204,19 @@ hipError_t launch_accept(const float* logits, const float* draft_logits, const i
         hipLaunchKernelGGL(accept_kernel<false>, dim3(n_rows), dim3(kAcceptThreads), 0, stream, logits, draft_logits,
                            draft_tokens, seeds, rows, n_rows, seq, V, inv_t_log2e, rec, accepted_len,
                            out_tokens, probs_at_draft, info, counters);
+    return hipGetLastError();
+}
+
+hipError_t launch_accept_both(const float* logits, const float* draft_logits, const int32_t* draft_tokens,
+                              const uint64_t* seeds, const int32_t* greedy_rows, int n_greedy,
+                              const int32_t* sampled_rows, int n_sampled, SeqRows seq, int V, float inv_t_log2e,
+                              RecLayout rec_greedy, RecLayout rec_sampled, int32_t* accepted_len,
+                              int32_t* out_tokens, float* probs_at_draft, AcceptInfo* info, int* counters,
+                              hipStream_t stream) {
+    if (n_greedy + n_sampled == 0) return hipSuccess;
+    hipLaunchKernelGGL(accept_both_kernel, dim3(n_greedy + n_sampled), dim3(kAcceptThreads), 0, stream, logits,
+                       draft_logits, draft_tokens, seeds, greedy_rows, n_greedy, sampled_rows, seq, V, inv_t_log2e,
+                       rec_greedy, rec_sampled, accepted_len, out_tokens, probs_at_draft, info, counters);
     return hipGetLastError();
 }
 

@@ -377,10 +377,11 @@ spec_status_t spec_verify_step(const void* hidden, const void* w_lmhead, spec_dt
     // The statistics epilogue pays where the direct-to-LDS kernel runs: it
     // removes the pass that reads the logits back, and with the loop's order
     // pinned it costs the kernel ~2%.  Its records (one per 256 vocabulary
-    // entries) are folded into the statistics pass's chunk records before the
-    // accept kernels, which then run exactly as after the pass.  Elsewhere
-    // (the skinny and tiled kernels, fp32) the step runs the separate calls'
-    // kernels.
+    // entries) are merged by the accept kernels straight from memory when a
+    // sequence has at most kAcceptRowsDirect rows, else folded into the
+    // statistics pass's chunk records first.  Greedy and sampled rows are
+    // accepted in one launch.  Elsewhere (the skinny and tiled kernels, fp32)
+    // the step runs the separate calls' kernels.
     const int big_recs = dtype == SPEC_BF16 ? sv::lmhead_big_records(M, V, H) : 0;
     const bool epilogue = any && big_recs > 0;
     if (!epilogue) {
@@ -417,13 +418,22 @@ spec_status_t spec_verify_step(const void* hidden, const void* w_lmhead, spec_dt
     if (e == hipSuccess && nrec != big_recs) e = hipErrorInvalidValue;   // the kernel the shape rule named
     // target chunk records after the draft slots: B*K + M rows fit the
     // statistics area, which is sized for B*(K+1) + B*K rows
+    const bool direct = (ns > 0 ? 2 * K + 1 : K + 1) <= sv::kAcceptRowsDirect;
     sv::StatRec* trec = ws.stats + (size_t)B * K * nc;
-    if (e == hipSuccess) e = sv::launch_fold_records(tstats, nrec, M, V, c, trec, s);
-    const sv::RecLayout lay{trec, nc, true, ws.stats, nc, false};
+    if (e == hipSuccess && !direct) e = sv::launch_fold_records(tstats, nrec, M, V, c, trec, s);
+    const sv::RecLayout tgt = direct ? sv::RecLayout{tstats, nrec, true, nullptr, 0, false}
+                                     : sv::RecLayout{trec, nc, true, nullptr, 0, false};
+    const sv::RecLayout lay{tgt.tgt, tgt.tgt_nc, true, ws.stats, nc, false};
+    if (e == hipSuccess && ng > 0 && ns > 0 && !fused) {
+        e = sv::launch_accept_both(logits, dl, draft_tokens, seeds, greedy_rows, ng, sampled_rows, ns, seq, V, c, tgt,
+                                   lay, accepted_len, out_tokens, probs_at_draft, ws.info, ws.counters, s);
+        if (e == hipSuccess)
+            e = sv::launch_residual(logits, dl, ns, V, c, ws.info, ws.sums, ws.counters, out_tokens, s);
+        return e == hipSuccess ? SPEC_OK : hip_fail(e);
+    }
     if (e == hipSuccess && ng > 0)
-        e = sv::launch_accept(logits, nullptr, draft_tokens, nullptr, greedy_rows, ng, seq, V, sv::kLog2e, false,
-                              sv::RecLayout{trec, nc, true, nullptr, 0, false}, accepted_len, out_tokens, nullptr, ws.info,
-                              ws.counters, s);
+        e = sv::launch_accept(logits, nullptr, draft_tokens, nullptr, greedy_rows, ng, seq, V, sv::kLog2e, false, tgt,
+                              accepted_len, out_tokens, nullptr, ws.info, ws.counters, s);
     if (e == hipSuccess && ns > 0) {
         if (fused) {
             e = sv::launch_accept_residual(logits, dl, draft_tokens, seeds, sampled_rows, ns, seq, V, c, lay,

@@ -22,6 +22,7 @@ constexpr int kAcceptThreads = 256;          // one workgroup per sequence
 constexpr int kAcceptWaves = kAcceptThreads / kWave;
 constexpr int kRecBuf = 2048;                // chunk records staged in LDS per pass (32 KB)
 constexpr int kMaxRows = 2 * 63 + 1;         // target rows 0..K plus draft rows 0..K-1
+static_assert(kAcceptRowsDirect == kAcceptWaves * 4, "one 16-lane group per row merged from memory");
 
 struct Merged {
     float m;
@@ -207,7 +208,7 @@ __device__ AcceptInfo accept_sequence(const float* __restrict__ logits, const fl
             if ((lane & 15) == 0) merged[rr] = x;
         }
         __syncthreads();
-    } else if (kb + 1 + n_drf <= kAcceptWaves * 4) {
+    } else if (kb + 1 + n_drf <= kAcceptRowsDirect) {
         // few rows with many records each: one row per 16-lane DPP row,
         // straight from global memory
         const int rr = wave * 4 + (lane >> 4);

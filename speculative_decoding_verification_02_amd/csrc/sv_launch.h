@@ -76,6 +76,12 @@ struct RecLayout {
     bool drf_by_row;
 };
 
+// Rows per sequence (target plus draft) up to which the accept kernels merge
+// records straight from memory, one 16-lane group per row, however many
+// records a row has; longer sequences want the statistics pass's layout
+// (4096-entry chunk records).
+constexpr int kAcceptRowsDirect = 16;
+
 // Greedy or sampled acceptance: one workgroup per selected sequence.  The
 // sampled variant also zeroes the sequence's residual counter.
 hipError_t launch_accept(const float* logits, const float* draft_logits, const int32_t* draft_tokens,
@@ -83,6 +89,16 @@ hipError_t launch_accept(const float* logits, const float* draft_logits, const i
                          float inv_t_log2e, bool sampled, RecLayout rec, int32_t* accepted_len,
                          int32_t* out_tokens, float* probs_at_draft, AcceptInfo* info, int* counters,
                          hipStream_t stream);
+
+// Greedy and sampled acceptance in one launch: workgroups 0 .. n_greedy-1
+// take greedy_rows, the rest sampled_rows (AcceptInfo and residual counter
+// of sampled slot j at info[j], counters[j]); each with its own layout.
+hipError_t launch_accept_both(const float* logits, const float* draft_logits, const int32_t* draft_tokens,
+                              const uint64_t* seeds, const int32_t* greedy_rows, int n_greedy,
+                              const int32_t* sampled_rows, int n_sampled, SeqRows seq, int V, float inv_t_log2e,
+                              RecLayout rec_greedy, RecLayout rec_sampled, int32_t* accepted_len,
+                              int32_t* out_tokens, float* probs_at_draft, AcceptInfo* info, int* counters,
+                              hipStream_t stream);
 
 // Acceptance and residual draw of sampled sequences in one launch (small
 // batches); needs the counters cleared by launch_softmax_stats.  Used while
