@@ -21,6 +21,8 @@
 // the same (lane group, element) slot, which both loads below guarantee.
 #include <limits.h>
 
+#include <type_traits>
+
 #include "sv_common.h"
 #include "sv_launch.h"
 
@@ -608,7 +610,11 @@ __global__ __launch_bounds__(kTiledThreads) void lmhead_tiled_bf16(
 // from LDS during the previous k-step's MFMAs (across slice boundaries too),
 // so neither a full load queue nor an LDS read stalls the matrix pipe.
 // Synchronisation is explicit: a wait on the wave's own outstanding loads
-// (vmcnt), then one barrier per slice.  Tiles are ordered XCD-aware, so the
+// (vmcnt), then one barrier per slice.  Where several row tiles share each
+// vocabulary tile (M > 320), the hidden rows are the operand fetched again
+// from the last-level cache in every round, so they get a ring of three
+// slots of their own beside the weights' two (160 KB at 256 rows): the waves
+// that load hidden rows run one slice further ahead.  Tiles are ordered XCD-aware, so the
 // M-tiles of one vocabulary tile share an L2.
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
@@ -674,7 +680,7 @@ struct BigPhase {
 
 // With STATS, the workgroup also writes the softmax statistics of each of its
 // hidden rows over its 256 vocabulary columns: stats[m * tiles_n + tn].
-template <int BK, int SLOTS, int NA, int NB, bool STATS, int NW>
+template <int BK, int SLOTS, int NA, int NB, bool STATS, int NW, int HS>
 __global__ __launch_bounds__(NW * 64, 1) void lmhead_big_bf16(
     const uint16_t* __restrict__ hidden, const uint16_t* __restrict__ W, float* __restrict__ logits,
     int M, int V, int H, int tiles_n, int tiles_m, int group_m, StatRec* __restrict__ stats, float c) {
@@ -758,14 +764,30 @@ __global__ __launch_bounds__(NW * 64, 1) void lmhead_big_bf16(
     const int nk = H / BK;
     constexpr int kLast = G::kSteps - 1;
     constexpr int kPerStep = NA * NB;
-    auto dma = [&](int q, int slice) {
-        u32x4* slot = lds + (slice % SLOTS) * G::kSliceChunks;
-        __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(src(q, slice)),
-                                         (__attribute__((address_space(3))) void*)(slot + (wave * G::kLoads + q) * 64),
-                                         16, 0, 0);
+    // Rings: HS == 0, one ring of SLOTS slices [W rows | hidden rows]; HS > 0,
+    // the W rows in a ring of SLOTS slots and the hidden rows in a ring of HS
+    // slots of their own.  Waves 0 .. kWWaves-1 load only W blocks and the
+    // others only hidden blocks, so each role runs its own prefetch depth.
+    constexpr int kWChunks = kBigBN * G::kCPR, kHChunks = G::kBM * G::kCPR;
+    constexpr int kWWaves = G::kWLoads / G::kLoads;
+    static_assert(HS == 0 || (G::kWLoads % G::kLoads == 0 && kWWaves < NW), "roles split by wave");
+    auto wslot = [&](int slice) -> u32x4* {
+        return HS ? lds + (slice % SLOTS) * kWChunks : lds + (slice % SLOTS) * G::kSliceChunks;
     };
-    auto frag = [&](const u32x4* lw, int ks, bf16x8 (&xa)[NA], bf16x8 (&xb)[NB]) {
-        const u32x4* lh = lw + kBigBN * G::kCPR;
+    auto hslot = [&](int slice) -> u32x4* {
+        return HS ? lds + SLOTS * kWChunks + (slice % (HS ? HS : 1)) * kHChunks
+                  : lds + (slice % SLOTS) * G::kSliceChunks + kWChunks;
+    };
+    auto dma = [&](int q, int slice) {
+        const int bi = wave_u * G::kLoads + q;
+        u32x4* dst = HS ? (bi < G::kWLoads ? wslot(slice) + bi * 64 : hslot(slice) + (bi - G::kWLoads) * 64)
+                        : lds + (slice % SLOTS) * G::kSliceChunks + bi * 64;
+        __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(src(q, slice)),
+                                         (__attribute__((address_space(3))) void*)dst, 16, 0, 0);
+    };
+    auto frag = [&](int slice, int ks, bf16x8 (&xa)[NA], bf16x8 (&xb)[NB]) {
+        const u32x4* lw = wslot(slice);
+        const u32x4* lh = hslot(slice);
         const int ch = ks * 2 + h;
 #pragma unroll
         for (int a = 0; a < NA; ++a) xa[a] = as_bf16x8(lw[G::pos(wn + a * 32 + r, ch)]);
@@ -773,78 +795,88 @@ __global__ __launch_bounds__(NW * 64, 1) void lmhead_big_bf16(
         for (int b = 0; b < NB; ++b) xb[b] = as_bf16x8(lh[G::pos(wm + b * 32 + r, ch)]);
     };
 
-#pragma unroll
-    for (int p = 0; p < SLOTS - 1; ++p) {
-        if (p >= nk) break;
-#pragma unroll
-        for (int q = 0; q < G::kLoads; ++q) dma(q, p);
-    }
-    // this lane's loads of slice 0 have landed once at most the slices issued
-    // after it are outstanding; after the barrier everyone's have
-    wait_slices<G::kLoads, SLOTS - 2>(min(SLOTS - 2, nk - 1));
-    __builtin_amdgcn_s_barrier();
-    asm volatile("" ::: "memory");
     bf16x8 fa[2][NA], fb[2][NB];
-    frag(lds, 0, fa[0], fb[0]);
-    // the loads of slice SLOTS-1 that would ride on the last k-step of the
-    // (absent) slice before slice 0; that slot has not been used yet
-    if (SLOTS - 1 < nk) {
+    // prologue and loop of a wave whose loads run SL slices deep
+    auto run = [&](auto sl_tag) {
+        constexpr int SL = decltype(sl_tag)::value;
 #pragma unroll
-        for (int q = 0; q < G::kLoads && q < kPerStep; ++q) dma(q, SLOTS - 1);
-    }
-
-    // MAIN: this window's loads (slice kt+SLOTS-1) go out; NEXT: the next
-    // window's first loads (slice kt+SLOTS) go out after the early barrier
-    auto slice = [&](int kt, auto phase) {
-        constexpr bool MAIN = decltype(phase)::kMain, NEXT = decltype(phase)::kNext;
-        const u32x4* lw = lds + (kt % SLOTS) * G::kSliceChunks;
+        for (int p = 0; p < SL - 1; ++p) {
+            if (p >= nk) break;
 #pragma unroll
-        for (int ks = 0; ks < G::kSteps; ++ks) {
-            const int cur = ks & 1;
-            if (ks == kLast) {
-                // this wave's reads of slot kt have completed and its loads of
-                // slice kt+1 have landed (at most the slices issued after it
-                // outstanding); after the barrier the same holds for everyone.
-                // On the last slice this only costs one barrier and reads of
-                // a stale slot that nothing uses.  The scheduling fences keep
-                // every MFMA of the previous k-step ahead of the waits.
-                __builtin_amdgcn_sched_barrier(0);
-                __builtin_amdgcn_s_waitcnt((0xF) | (0x3 << 14) | (0x7 << 4) | (0x0 << 8));   // lgkmcnt(0)
-                wait_slices<G::kLoads, SLOTS - 2>(min(SLOTS - 2, nk - 2 - kt));
-                __builtin_amdgcn_s_barrier();
-                asm volatile("" ::: "memory");
-                __builtin_amdgcn_sched_barrier(0);
-            }
-#pragma unroll
-            for (int i = 0; i < kPerStep; ++i) {
-                const int a = i / NB, b = i % NB;
-                acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[cur][a], fb[cur][b], acc[a][b], 0, 0, 0);
-                if (i == 0) {
-                    if (ks < kLast) frag(lw, ks + 1, fa[cur ^ 1], fb[cur ^ 1]);
-                    else frag(lds + ((kt + 1) % SLOTS) * G::kSliceChunks, 0, fa[cur ^ 1], fb[cur ^ 1]);
-                }
-                const int q = ks == kLast ? i : kPerStep * (ks + 1) + i;
-                if (q < G::kLoads) {
-                    if (ks == kLast && NEXT) dma(q, kt + SLOTS);
-                    if (ks < kLast && MAIN) dma(q, kt + SLOTS - 1);
-                }
-            }
-            // pin the order: 1 MFMA, the fragment reads, then each MFMA with
-            // the load that rides on it
-#pragma unroll
-            for (int i = 0; i < kPerStep; ++i) {
-                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
-                if (i == 0) __builtin_amdgcn_sched_group_barrier(0x100, NA + NB, 0);   // LDS reads
-                const int q = ks == kLast ? i : kPerStep * (ks + 1) + i;
-                if (q < G::kLoads && ((ks == kLast && NEXT) || (ks < kLast && MAIN)))
-                    __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);   // memory load
-            }
+            for (int q = 0; q < G::kLoads; ++q) dma(q, p);
         }
+        // this lane's loads of slice 0 have landed once at most the slices
+        // issued after it are outstanding; after the barrier everyone's have
+        wait_slices<G::kLoads, SL - 2>(min(SL - 2, nk - 1));
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
+        frag(0, 0, fa[0], fb[0]);
+        // the loads of slice SL-1 that would ride on the last k-step of the
+        // (absent) slice before slice 0; that slot has not been used yet
+        if (SL - 1 < nk) {
+#pragma unroll
+            for (int q = 0; q < G::kLoads && q < kPerStep; ++q) dma(q, SL - 1);
+        }
+
+        // MAIN: this window's loads (slice kt+SL-1) go out; NEXT: the next
+        // window's first loads (slice kt+SL) go out after the early barrier
+        auto slice = [&](int kt, auto phase) {
+            constexpr bool MAIN = decltype(phase)::kMain, NEXT = decltype(phase)::kNext;
+#pragma unroll
+            for (int ks = 0; ks < G::kSteps; ++ks) {
+                const int cur = ks & 1;
+                if (ks == kLast) {
+                    // this wave's reads of slot kt have completed and its loads
+                    // of slice kt+1 have landed (at most the slices issued after
+                    // it outstanding); after the barrier the same holds for
+                    // everyone.  On the last slice this only costs one barrier
+                    // and reads of a stale slot that nothing uses.  The
+                    // scheduling fences keep every MFMA of the previous k-step
+                    // ahead of the waits.
+                    __builtin_amdgcn_sched_barrier(0);
+                    __builtin_amdgcn_s_waitcnt((0xF) | (0x3 << 14) | (0x7 << 4) | (0x0 << 8));   // lgkmcnt(0)
+                    wait_slices<G::kLoads, SL - 2>(min(SL - 2, nk - 2 - kt));
+                    __builtin_amdgcn_s_barrier();
+                    asm volatile("" ::: "memory");
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+#pragma unroll
+                for (int i = 0; i < kPerStep; ++i) {
+                    const int a = i / NB, b = i % NB;
+                    acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[cur][a], fb[cur][b], acc[a][b], 0, 0, 0);
+                    if (i == 0) {
+                        if (ks < kLast) frag(kt, ks + 1, fa[cur ^ 1], fb[cur ^ 1]);
+                        else frag(kt + 1, 0, fa[cur ^ 1], fb[cur ^ 1]);
+                    }
+                    const int q = ks == kLast ? i : kPerStep * (ks + 1) + i;
+                    if (q < G::kLoads) {
+                        if (ks == kLast && NEXT) dma(q, kt + SL);
+                        if (ks < kLast && MAIN) dma(q, kt + SL - 1);
+                    }
+                }
+                // pin the order: 1 MFMA, the fragment reads, then each MFMA
+                // with the load that rides on it
+#pragma unroll
+                for (int i = 0; i < kPerStep; ++i) {
+                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
+                    if (i == 0) __builtin_amdgcn_sched_group_barrier(0x100, NA + NB, 0);   // LDS reads
+                    const int q = ks == kLast ? i : kPerStep * (ks + 1) + i;
+                    if (q < G::kLoads && ((ks == kLast && NEXT) || (ks < kLast && MAIN)))
+                        __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);   // memory load
+                }
+            }
+        };
+        int kt = 0;
+        for (; kt + SL < nk; ++kt) slice(kt, BigPhase<true, true>{});
+        if (kt + SL - 1 < nk) slice(kt++, BigPhase<true, false>{});
+        for (; kt < nk; ++kt) slice(kt, BigPhase<false, false>{});
     };
-    int kt = 0;
-    for (; kt + SLOTS < nk; ++kt) slice(kt, BigPhase<true, true>{});
-    if (kt + SLOTS - 1 < nk) slice(kt++, BigPhase<true, false>{});
-    for (; kt < nk; ++kt) slice(kt, BigPhase<false, false>{});
+    if constexpr (HS > 0) {
+        if (wave_u < kWWaves) run(std::integral_constant<int, SLOTS>{});
+        else run(std::integral_constant<int, HS>{});
+    } else {
+        run(std::integral_constant<int, SLOTS>{});
+    }
 
     // logits of row block b: four runs of four consecutive vocabulary entries
     const bool vec_ok = (V & 3) == 0;
@@ -921,21 +953,23 @@ __global__ __launch_bounds__(NW * 64, 1) void lmhead_big_bf16(
     }
 }
 
-template <int BK, int SLOTS, int NA, int NB, bool STATS, int NW = 4>
+template <int BK, int SLOTS, int NA, int NB, bool STATS, int NW = 4, int HS = 0>
 hipError_t launch_big_cfg(const uint16_t* hidden, const uint16_t* W, float* logits, int M, int V, int H,
                           hipStream_t stream, StatRec* stats = nullptr, float c = 0.f, int group_m = 0) {
     using G = Big<BK, SLOTS, NA, NB, NW>;
-    static_assert(!STATS || (size_t)G::kWN * G::kBM * sizeof(StatRec) <= G::kLds, "statistics exchange fits the ring");
-    auto kern = lmhead_big_bf16<BK, SLOTS, NA, NB, STATS, NW>;
+    constexpr size_t kLds = HS ? (size_t)(SLOTS * kBigBN + HS * G::kBM) * G::kCPR * 16 : G::kLds;
+    static_assert(kLds <= 160 * 1024, "rings exceed the 160 KB of a CU");
+    static_assert(!STATS || (size_t)G::kWN * G::kBM * sizeof(StatRec) <= kLds, "statistics exchange fits the ring");
+    auto kern = lmhead_big_bf16<BK, SLOTS, NA, NB, STATS, NW, HS>;
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)G::kLds);
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLds);
     if (e != hipSuccess) return e;
     const int tiles_n = (V + kBigBN - 1) / kBigBN;
     const int tiles_m = (M + G::kBM - 1) / G::kBM;
     const int max_nn = (tiles_n + 7) / 8;    // most vocabulary tiles any XCD owns
     const int grid = 8 * max_nn * tiles_m;
     const int gm = group_m > 0 ? min(group_m, tiles_m) : tiles_m;
-    hipLaunchKernelGGL(kern, dim3(grid), dim3(G::kThreads), G::kLds, stream, hidden, W, logits, M, V, H, tiles_n,
+    hipLaunchKernelGGL(kern, dim3(grid), dim3(G::kThreads), kLds, stream, hidden, W, logits, M, V, H, tiles_n,
                        tiles_m, gm, stats, c);
     return hipGetLastError();
 }
@@ -956,7 +990,10 @@ hipError_t launch_big_cfg(const uint16_t* hidden, const uint16_t* W, float* logi
 //   M = 2304, H = 8192, V = 152064: 5.25 ms (256 rows, 8 waves) vs 5.5-5.9
 //   M = 2048, H = 5120, V = 262144: 5.23-5.32 ms vs 5.5
 // Above 320 rows the tile is 256 or 320 rows, whichever gives the smaller
-// sum of per-tile times (measured 285 and 339 us per 256-/320-row tile here).
+// sum of per-tile times (measured 285 and 339 us per 256-/320-row tile here);
+// the 256-row tiles there use the split rings: M = 2048, H = 5120, V = 262144
+// 5.01 vs 5.18 ms and M = 2304, H = 8192 5.11 vs 5.17 ms (interleaved, one
+// box), M = 512 unchanged.
 constexpr int kBigBK = 64;
 constexpr int kBigMinM = 17;
 
@@ -976,7 +1013,7 @@ hipError_t launch_big(const uint16_t* hidden, const uint16_t* W, float* logits, 
     const long cost256 = (long)((M + 255) / 256) * 285, cost320 = (long)((M + 319) / 320) * 339;
     if (cost320 < cost256)
         return launch_big_cfg<kBigBK, 2, 2, 5, STATS, 8>(hidden, W, logits, M, V, H, stream, stats, c);
-    return launch_big_cfg<kBigBK, 2, 2, 4, STATS, 8>(hidden, W, logits, M, V, H, stream, stats, c);
+    return launch_big_cfg<kBigBK, 2, 2, 4, STATS, 8, 3>(hidden, W, logits, M, V, H, stream, stats, c);
 }
 
 // ------------------------------------------------------------------ fp32 ---
