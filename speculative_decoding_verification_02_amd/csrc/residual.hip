@@ -7,10 +7,11 @@
 // speculative decoding works).  The draw is an inverse CDF:
 //     t = min{v : C_v > u' * Z},  C_v = w_0 + ... + w_v,  Z = C_{V-1}.
 //
-// One kernel, one workgroup per (sequence, chunk): each sums the weights of
-// its chunk (fixed-order reduction); the workgroup that finishes last for a
-// sequence then runs a sequential prefix over the chunk sums to find the
-// chunk c* holding u'Z, and a workgroup scan over c*'s weights to find t.
+// One workgroup per (sequence, chunk) sums the weights of its chunk
+// (fixed-order reduction); then, for a sequence, a prefix over the chunk sums
+// finds the chunk c* holding u'Z and a workgroup scan over c*'s weights finds
+// t.  Small batches run the selection in the workgroup that finishes last
+// (one launch); large ones in a second launch, one workgroup per sequence.
 // Both phases evaluate a weight with the same function from the same inputs,
 // so a chunk's elements agree bitwise between them; only the order of the
 // within-chunk sum differs, and the selection falls back to the last (or first)
@@ -24,6 +25,10 @@
 namespace sv {
 
 constexpr int kMaxChunks = 1024;  // V <= kMaxChunks * kChunk (checked on the host)
+// Above this many (sequence, chunk) blocks the draw runs in two launches
+// (sums, then selection) instead of one with a last-block selection: at
+// B = 256 64 + 8 us against 84, at B = 512 117 + 8 against 140.
+constexpr long kResidualSplitBlocks = 4096;
 
 // w_v for the terminal row: q_n(v) - p_n(v) clipped at 0, or q_n(v) itself,
 // each probability as one exp2 with its normaliser folded into the exponent:
@@ -121,7 +126,7 @@ __device__ __forceinline__ void chunk_prefix(const float* src, int nc, int lane,
 // per-chunk weight sums published by all of them (read back with atomics).
 __device__ void select_terminal(const float* __restrict__ logits, const float* __restrict__ draft_logits,
                                 int V, int nc, float c, const AcceptInfo& a, const float* chunk_sums,
-                                int32_t* __restrict__ out_tokens) {
+                                int32_t* __restrict__ out_tokens, bool sums_by_atomics = true) {
     __shared__ float pre[kMaxChunks + 1];   // prefix over chunk sums
     __shared__ float wl[kChunk];            // weights of the selected chunk, token order
     __shared__ float red[kStatThreads / kWave];
@@ -134,7 +139,7 @@ __device__ void select_terminal(const float* __restrict__ logits, const float* _
     const bool vec = (V & 3) == 0;
 
     bool use_q = tr.bonus;
-    if (wave == 0) chunk_prefix(chunk_sums, nc, lane, pre, true);
+    if (wave == 0) chunk_prefix(chunk_sums, nc, lane, pre, sums_by_atomics);
     __syncthreads();
     if (!(pre[nc] > 0.f) && !use_q) {
         // residual without mass: draw from q_n, recomputing the chunk sums
@@ -282,6 +287,37 @@ __global__ __launch_bounds__(kStatThreads) void residual_kernel(
     select_terminal(logits, draft_logits, V, nc, c, a, chunk_sums + (size_t)j * nc, out_tokens);
 }
 
+// The same draw in two launches, for large batches: the chunk sums with
+// plain stores (a workgroup retires as soon as its chunk is summed, with no
+// device-scope atomics to wait for), then one workgroup per sequence selects
+// (the sums are visible to the next launch).
+__global__ __launch_bounds__(kStatThreads) void residual_sums_kernel(
+    const float* __restrict__ logits, const float* __restrict__ draft_logits, int V, int nc, float c,
+    const AcceptInfo* __restrict__ info, float* __restrict__ chunk_sums) {
+    __shared__ float red[kStatThreads / kWave];
+    const int j = blockIdx.x / nc;
+    const int chunk = blockIdx.x - j * nc;
+    const AcceptInfo a = info[j];
+    if (a.n < 0) return;
+    const TermRows tr = term_rows(logits, draft_logits, a, V);
+    float w[kStatPerThread];
+    chunk_weights(tr.zt, tr.zd, chunk * kChunk, V, (V & 3) == 0, threadIdx.x, a, c, tr.bonus, w);
+    float s = 0.f;
+#pragma unroll
+    for (int k = 0; k < kStatPerThread; ++k) s += w[k];
+    s = block_sum(s, red);
+    if (threadIdx.x == 0) chunk_sums[blockIdx.x] = s;
+}
+
+__global__ __launch_bounds__(kStatThreads) void residual_select_kernel(
+    const float* __restrict__ logits, const float* __restrict__ draft_logits, int V, int nc, float c,
+    const AcceptInfo* __restrict__ info, const float* __restrict__ chunk_sums, int32_t* __restrict__ out_tokens) {
+    const int j = blockIdx.x;
+    const AcceptInfo a = info[j];
+    if (a.n < 0) return;
+    select_terminal(logits, draft_logits, V, nc, c, a, chunk_sums + (size_t)j * nc, out_tokens, false);
+}
+
 // Acceptance and residual draw in one launch, for small batches where the
 // two kernels' latency dominates: one workgroup per (sampled sequence, chunk).
 // Every workgroup of a sequence takes the acceptance decision itself (a few
@@ -344,7 +380,17 @@ hipError_t launch_residual(const float* logits, const float* draft_logits, int n
                            int32_t* out_tokens, hipStream_t stream) {
     if (n_rows == 0) return hipSuccess;
     const int nc = n_chunks(V);
-    hipLaunchKernelGGL(residual_kernel, dim3((unsigned)((long)n_rows * nc)), dim3(kStatThreads), 0, stream, logits,
+    const long blocks = (long)n_rows * nc;
+    if (blocks > kResidualSplitBlocks) {
+        hipLaunchKernelGGL(residual_sums_kernel, dim3((unsigned)blocks), dim3(kStatThreads), 0, stream, logits,
+                           draft_logits, V, nc, inv_t_log2e, info, chunk_sums);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        hipLaunchKernelGGL(residual_select_kernel, dim3((unsigned)n_rows), dim3(kStatThreads), 0, stream, logits,
+                           draft_logits, V, nc, inv_t_log2e, info, chunk_sums, out_tokens);
+        return hipGetLastError();
+    }
+    hipLaunchKernelGGL(residual_kernel, dim3((unsigned)blocks), dim3(kStatThreads), 0, stream, logits,
                        draft_logits, V, nc, inv_t_log2e, info, chunk_sums, counters, out_tokens);
     return hipGetLastError();
 }
