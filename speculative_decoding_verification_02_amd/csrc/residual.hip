@@ -47,31 +47,54 @@ __device__ __forceinline__ float term_weight(float zt, float zd, const TermNorm&
 }
 
 // The thread's weights of one chunk, in the coalesced order of the statistics
-// pass: element (q * kStatThreads + tid) * 4 + e of the chunk.
-__device__ __forceinline__ void chunk_weights(const float* __restrict__ zt_row, const float* __restrict__ zd_row,
-                                              int v_begin, int V, bool vec, int tid, const AcceptInfo& a, float c,
-                                              bool use_q, float w[kStatPerThread]) {
-    const TermNorm tn = term_norm(a);
+// pass: element (q * kStatThreads + tid) * 4 + e of the chunk.  VEC (V % 4 ==
+// 0): 128-bit loads, else 32-bit ones; USE_Q: the target row only.  No load
+// sits in a branch (entries past V read an in-range address and get weight
+// 0), so all of a thread's loads are in flight together.
+template <bool VEC, bool USE_Q>
+__device__ __forceinline__ void chunk_weights_impl(const float* __restrict__ zt_row, const float* __restrict__ zd_row,
+                                                   int v_begin, int V, int tid, const TermNorm& tn, float c,
+                                                   float w[kStatPerThread]) {
+    float zt[kStatPerThread], zd[kStatPerThread];
 #pragma unroll
     for (int q = 0; q < kStatPerThread / 4; ++q) {
         const int v = v_begin + (q * kStatThreads + tid) * 4;
-        float zt[4], zd[4] = {0.f, 0.f, 0.f, 0.f};
-        if (vec && v + 3 < V) {
-            const float4 f = *reinterpret_cast<const float4*>(zt_row + v);
-            zt[0] = f.x; zt[1] = f.y; zt[2] = f.z; zt[3] = f.w;
-            if (!use_q) {
-                const float4 g = *reinterpret_cast<const float4*>(zd_row + v);
-                zd[0] = g.x; zd[1] = g.y; zd[2] = g.z; zd[3] = g.w;
+        if constexpr (VEC) {
+            const int vc = min(v, V - 4);
+            const float4 f = *reinterpret_cast<const float4*>(zt_row + vc);
+            zt[4 * q] = f.x; zt[4 * q + 1] = f.y; zt[4 * q + 2] = f.z; zt[4 * q + 3] = f.w;
+            if constexpr (!USE_Q) {
+                const float4 g = *reinterpret_cast<const float4*>(zd_row + vc);
+                zd[4 * q] = g.x; zd[4 * q + 1] = g.y; zd[4 * q + 2] = g.z; zd[4 * q + 3] = g.w;
             }
         } else {
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                zt[e] = (v + e < V) ? zt_row[v + e] : -INFINITY;
-                if (!use_q) zd[e] = (v + e < V) ? zd_row[v + e] : 0.f;
+                const int vc = min(v + e, V - 1);
+                zt[4 * q + e] = zt_row[vc];
+                if constexpr (!USE_Q) zd[4 * q + e] = zd_row[vc];
             }
         }
+    }
 #pragma unroll
-        for (int e = 0; e < 4; ++e) w[4 * q + e] = (v + e < V) ? term_weight(zt[e], zd[e], tn, c, use_q) : 0.f;
+    for (int k = 0; k < kStatPerThread; ++k) {
+        // computed for every entry (past V from a valid duplicate), then masked
+        const int v = v_begin + ((k >> 2) * kStatThreads + tid) * 4 + (k & 3);
+        const float tw = term_weight(zt[k], USE_Q ? 0.f : zd[k], tn, c, USE_Q);
+        w[k] = v < V ? tw : 0.f;
+    }
+}
+
+__device__ __forceinline__ void chunk_weights(const float* __restrict__ zt_row, const float* __restrict__ zd_row,
+                                              int v_begin, int V, bool vec, int tid, const AcceptInfo& a, float c,
+                                              bool use_q, float w[kStatPerThread]) {
+    const TermNorm tn = term_norm(a);
+    if (vec) {
+        if (use_q) chunk_weights_impl<true, true>(zt_row, zd_row, v_begin, V, tid, tn, c, w);
+        else chunk_weights_impl<true, false>(zt_row, zd_row, v_begin, V, tid, tn, c, w);
+    } else {
+        if (use_q) chunk_weights_impl<false, true>(zt_row, zd_row, v_begin, V, tid, tn, c, w);
+        else chunk_weights_impl<false, false>(zt_row, zd_row, v_begin, V, tid, tn, c, w);
     }
 }
 

@@ -24,28 +24,36 @@ namespace sv {
 // q < 4, e < 4: each load instruction of a wavefront covers 1 KB contiguous.
 // STREAM: the logits are read once per step, so large passes stream past the
 // caches; small ones keep them cached for the accept kernels' reads of the
-// terminal rows that follow.
-template <bool STREAM>
-__device__ __forceinline__ void load_chunk(const float* __restrict__ row, int v_begin, int V, bool vec, int tid,
+// terminal rows that follow.  VEC (V % 4 == 0): four 128-bit loads, else
+// sixteen 32-bit loads.  No load sits in a branch: entries past V read an
+// in-range address and become -inf.  (With a vector/scalar branch per load
+// the compiler waited for the first loads before issuing the last one, which
+// halved the bytes in flight.)
+template <bool STREAM, bool VEC>
+__device__ __forceinline__ void load_chunk(const float* __restrict__ row, int v_begin, int V, int tid,
                                            float x[kStatPerThread]) {
 #pragma unroll
     for (int q = 0; q < kStatPerThread / 4; ++q) {
         const int v = v_begin + (q * kStatThreads + tid) * 4;
-        if (vec && v + 3 < V) {
+        if constexpr (VEC) {
             typedef float f4v __attribute__((ext_vector_type(4)));
-            const f4v* p = reinterpret_cast<const f4v*>(row + v);
+            const f4v* p = reinterpret_cast<const f4v*>(row + min(v, V - 4));
             f4v f;
             if constexpr (STREAM)
                 f = __builtin_nontemporal_load(p);
             else
                 f = *p;
-            x[4 * q + 0] = f.x;
-            x[4 * q + 1] = f.y;
-            x[4 * q + 2] = f.z;
-            x[4 * q + 3] = f.w;
+            const bool in = v < V;   // V % 4 == 0: all four entries or none
+            x[4 * q + 0] = in ? f.x : -INFINITY;
+            x[4 * q + 1] = in ? f.y : -INFINITY;
+            x[4 * q + 2] = in ? f.z : -INFINITY;
+            x[4 * q + 3] = in ? f.w : -INFINITY;
         } else {
 #pragma unroll
-            for (int e = 0; e < 4; ++e) x[4 * q + e] = (v + e < V) ? row[v + e] : -INFINITY;
+            for (int e = 0; e < 4; ++e) {
+                const float f = row[min(v + e, V - 1)];
+                x[4 * q + e] = v + e < V ? f : -INFINITY;
+            }
         }
     }
 }
@@ -54,7 +62,7 @@ __device__ __forceinline__ int chunk_index(int v_begin, int tid, int k) {
     return v_begin + ((k >> 2) * kStatThreads + tid) * 4 + (k & 3);
 }
 
-template <bool NEED_SUM, bool STREAM>
+template <bool NEED_SUM, bool STREAM, bool VEC>
 __global__ __launch_bounds__(kStatThreads) void softmax_stats_kernel(
     const float* __restrict__ logits, const float* __restrict__ draft_logits, const int32_t* __restrict__ rows,
     int n_rows, SeqRows seq, int V, int nc, float c, StatRec* __restrict__ stats, int* __restrict__ zero_counters) {
@@ -91,7 +99,7 @@ __global__ __launch_bounds__(kStatThreads) void softmax_stats_kernel(
 
     const int v_begin = chunk * kChunk;
     float x[kStatPerThread];
-    load_chunk<STREAM>(row, v_begin, V, (V & 3) == 0, tid, x);
+    load_chunk<STREAM, VEC>(row, v_begin, V, tid, x);
 
     float m = -INFINITY;
     int mi = INT_MAX;
@@ -212,8 +220,15 @@ hipError_t launch_softmax_stats(const float* logits, const float* draft_logits, 
     if (blocks == 0) return hipSuccess;
     // stream past the caches above 64 MB of logits (4096 chunks of 16 KB)
     const bool stream_hint = blocks > 4096;
-    auto kern = need_sum ? (stream_hint ? softmax_stats_kernel<true, true> : softmax_stats_kernel<true, false>)
-                         : (stream_hint ? softmax_stats_kernel<false, true> : softmax_stats_kernel<false, false>);
+    const bool vec = (V & 3) == 0;
+    auto kern = need_sum ? (stream_hint ? (vec ? softmax_stats_kernel<true, true, true>
+                                               : softmax_stats_kernel<true, true, false>)
+                                        : (vec ? softmax_stats_kernel<true, false, true>
+                                               : softmax_stats_kernel<true, false, false>))
+                         : (stream_hint ? (vec ? softmax_stats_kernel<false, true, true>
+                                               : softmax_stats_kernel<false, true, false>)
+                                        : (vec ? softmax_stats_kernel<false, false, true>
+                                               : softmax_stats_kernel<false, false, false>));
     hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(kStatThreads), 0, stream, logits, draft_logits, rows, n_rows,
                        seq, V, nc, inv_t_log2e, stats, zero_counters);
     return hipGetLastError();
