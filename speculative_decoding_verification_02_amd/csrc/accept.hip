@@ -109,10 +109,8 @@ __global__ __launch_bounds__(kAcceptThreads) void tree_accept_kernel(
     const int rows_per_pass = max(1, min(N + 1, kRecBuf / nc));
     for (int r0 = 0; r0 <= N; r0 += rows_per_pass) {
         const int nr = min(rows_per_pass, N + 1 - r0);
-        for (int e = tid; e < nr * nc; e += kAcceptThreads) {
-            const int rr = r0 + e / nc, k = e - (e / nc) * nc;
-            recs[e] = stats[((size_t)j * (N + 1) + rr) * nc + k];
-        }
+        const StatRec* src = stats + ((size_t)j * (N + 1) + r0) * nc;   // rows r0 .. r0+nr-1, contiguous
+        stage_records(recs, nr * nc, tid, [&](int e) { return src + e; });
         __syncthreads();
         for (int rr = wave; rr < nr; rr += kAcceptWaves) {
             const Merged x = wave_merge(recs + rr * nc, nc, 0.f, false, lane);

@@ -89,11 +89,14 @@ __device__ __forceinline__ Merged row16_merge_global(const StatRec* __restrict__
     float m = -INFINITY, s = 0.f;
     int idx = INT_MAX, bad = 0;
     for (int k0 = 0; k0 < nc; k0 += 16 * kBatch) {
+        // every load goes out (an index past nc reads the last record and is
+        // masked), so a batch is one round trip
         StatRec x[kBatch];
 #pragma unroll
         for (int j = 0; j < kBatch; ++j) {
             const int k = k0 + j * 16 + gl;
-            x[j] = k < nc ? rec[k] : StatRec{-INFINITY, 0.f, INT_MAX, 0};
+            const StatRec y = rec[min(k, nc - 1)];
+            x[j] = k < nc ? y : StatRec{-INFINITY, 0.f, INT_MAX, 0};
         }
         float bm = m;
         int bi = idx;
@@ -120,6 +123,22 @@ __device__ __forceinline__ Merged row16_merge_global(const StatRec* __restrict__
     return Merged{M, S, I, bad};
 }
 
+// Copy records 0 .. n-1 (record e at src(e)) into LDS: each thread's loads
+// in batches of kStageBatch, all of a batch in flight at once (an index past
+// n reads the last record and is not stored).  Called by the whole workgroup.
+constexpr int kStageBatch = 4;
+template <typename Src>
+__device__ __forceinline__ void stage_records(StatRec* recs, int n, int tid, Src src) {
+    for (int e0 = tid; e0 < n; e0 += kStageBatch * kAcceptThreads) {
+        StatRec t[kStageBatch];
+#pragma unroll
+        for (int u = 0; u < kStageBatch; ++u) t[u] = *src(min(e0 + u * kAcceptThreads, n - 1));
+#pragma unroll
+        for (int u = 0; u < kStageBatch; ++u)
+            if (e0 + u * kAcceptThreads < n) recs[e0 + u * kAcceptThreads] = t[u];
+    }
+}
+
 // Merge the records of n consecutive rows (nc records each, row r at
 // base + r*nc) into merged[out0 + r], one wavefront per row.  Rows are staged
 // through LDS with every load in flight at once when they fit; rows longer
@@ -140,7 +159,7 @@ __device__ inline void merge_rows(const StatRec* __restrict__ base, int n, int n
     for (int r0 = 0; r0 < n; r0 += rows_per_pass) {
         const int nr = min(rows_per_pass, n - r0);
         const StatRec* src = base + (size_t)r0 * nc;
-        for (int e = tid; e < nr * nc; e += kAcceptThreads) recs[e] = src[e];
+        stage_records(recs, nr * nc, tid, [&](int e) { return src + e; });
         __syncthreads();
         for (int rr = wave; rr < nr; rr += kAcceptWaves) {
             const Merged x = wave_merge(recs + rr * nc, nc, c, need_sum, lane);
@@ -198,9 +217,8 @@ __device__ AcceptInfo accept_sequence(const float* __restrict__ logits, const fl
     if (rec.tgt_nc == rec.drf_nc && (kb + 1 + n_drf) * rec.tgt_nc <= kRecBuf) {
         // everything in one pass: all record loads of both groups in flight
         const int nc = rec.tgt_nc;
-        const int n_tgt = (kb + 1) * nc;
-        for (int e = tid; e < (kb + 1 + n_drf) * nc; e += kAcceptThreads)
-            recs[e] = e < n_tgt ? tgt0[e] : drf0[e - n_tgt];
+        const int n_tgt = (kb + 1) * nc, n_all = (kb + 1 + n_drf) * nc;
+        stage_records(recs, n_all, tid, [&](int e) { return e < n_tgt ? tgt0 + e : drf0 + (e - n_tgt); });
         __syncthreads();
         // four rows per wavefront, one per 16-lane DPP row
         for (int rr = wave * 4 + (lane >> 4); rr < kb + 1 + n_drf; rr += kAcceptWaves * 4) {
