@@ -1,9 +1,12 @@
 """Benchmark of the speculative-decoding verify step on one MI355X.
 
 One step = one pass of the whole verify path over one batch: the LM-head
-contraction of the K+1 verify positions (spec_verify_logits) and the
-acceptance of every sequence (spec_accept_sample / spec_accept_greedy, by the
-workload's per-row mode), including the residual or bonus draw.  Inputs
+contraction of the K+1 verify positions, the softmax statistics, and the
+acceptance of every sequence (greedy or sampled, by the workload's per-row
+mode), including the residual or bonus draw.  By default the step is one
+spec_verify_step call (--path fused); --path separate runs spec_verify_logits
+then spec_accept_sample / spec_accept_greedy (ragged and tree workloads
+always run separately).  Inputs
 (weights, hidden states, draft logits, per-round draft tokens and seeds) are
 resident in HBM before the timed region; each timed step uses the next
 pre-drawn draft set and seed.
@@ -42,9 +45,9 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="b1_k5_h4096_v128256")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--path", choices=["fused", "separate"], default="separate",
-                    help="fused: spec_verify_step (statistics in the LM-head epilogue); separate: "
-                         "spec_verify_logits then the accept calls")
+    ap.add_argument("--path", choices=["fused", "separate"], default="fused",
+                    help="fused: spec_verify_step, the one-call step (statistics in the LM-head kernel where "
+                         "it can compute them); separate: spec_verify_logits then the accept calls")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle sample")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="before the run, copy a buffer of this many MiB 3 times (untimed), so a counter "
@@ -121,7 +124,9 @@ def ingest_traffic(args):
     # the calibration copy is a contiguous same-type copy: the runtime's blit
     # kernel; take its largest dispatches (the calibration is the biggest copy)
     is_copy = lambda n: "copyBuffer" in n
-    is_gemm = lambda n: "sv::lmhead" in n
+    # the LM-head launches without the statistics option: the ones the
+    # event-timed loop measures (the fused step runs the other variant)
+    is_gemm = lambda n: "sv::lmhead" in n and "true" not in n.split("(")[0]
 
     def calib(rows):
         vals = sorted((v for n, v in rows if is_copy(n)), reverse=True)[:3]
