@@ -157,7 +157,7 @@ def main():
         ingest_traffic(args)
         return
     if args.gpus != 1:
-        print("bench.py measures one GPU: this build has no multi-GPU path (run with --gpus 1)", file=sys.stderr)
+        print("bench.py measures one GPU: the verify path here has no multi-GPU mode (run with --gpus 1)", file=sys.stderr)
         sys.exit(2)
 
     import torch
