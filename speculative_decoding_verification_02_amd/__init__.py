@@ -114,7 +114,11 @@ def declared_symbols(header: str = HEADER_PATH) -> list[str]:
 # ------------------------------------------------------------ marshalling --
 
 def _ptr(t):
-    return None if t is None else ctypes.c_void_p(t.data_ptr())
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError("every tensor argument must be on the GPU (got one on %s)" % t.device)
+    return ctypes.c_void_p(t.data_ptr())
 
 
 def _stream(stream):
@@ -138,9 +142,54 @@ def _dtype_code(t):
     raise TypeError("hidden/w_lmhead must be bfloat16 or float32, got %s" % t.dtype)
 
 
+def _arg(t, name, dtypes, shape=None, optional=False):
+    """A device tensor the library reads or writes through a bare pointer:
+    the kernels trust its dtype and extent, so they are checked here (shape
+    entries of None match any size; _ptr checks the device).  Returns t."""
+    import torch
+    if t is None:
+        if optional:
+            return None
+        raise ValueError("%s is required" % name)
+    if not isinstance(t, torch.Tensor):
+        raise TypeError("%s must be a torch.Tensor" % name)
+    if not isinstance(dtypes, tuple):
+        dtypes = (dtypes,)
+    if t.dtype not in dtypes:
+        raise TypeError("%s must be %s, got %s" % (name, " or ".join(str(d) for d in dtypes), t.dtype))
+    if shape is not None and (t.dim() != len(shape) or
+                              any(w is not None and int(d) != int(w) for d, w in zip(t.shape, shape))):
+        raise ValueError("%s has shape %s, expected %s" % (name, tuple(t.shape),
+                                                            tuple("*" if w is None else w for w in shape)))
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+    return t
+
+
+def _i32():
+    import torch
+    return torch.int32
+
+
+def _f32():
+    import torch
+    return torch.float32
+
+
+def _seed_types():
+    import torch
+    return (torch.int64, torch.uint64) if hasattr(torch, "uint64") else (torch.int64,)
+
+
+def _ws(workspace):
+    import torch
+    return _arg(workspace, "workspace", (torch.uint8, torch.int8, torch.int32, torch.int64, torch.float32))
+
+
 def _rows(rows):
     if rows is None:
         return None, 0
+    _arg(rows, "rows", _i32(), (None,))
     return rows, int(rows.numel())
 
 
@@ -165,9 +214,10 @@ def spec_verify_logits(hidden, w_lmhead, logits, stream=None) -> None:
     if tuple(logits.shape) != (B, P, V) or w_lmhead.shape[1] != H:
         raise ValueError("shape mismatch: hidden %s, w_lmhead %s, logits %s"
                          % (tuple(hidden.shape), tuple(w_lmhead.shape), tuple(logits.shape)))
-    for t in (hidden, w_lmhead, logits):
-        if not t.is_contiguous():
-            raise ValueError("tensors must be contiguous")
+    _dtype_code(hidden)
+    for t, n in ((hidden, "hidden"), (w_lmhead, "w_lmhead")):
+        _arg(t, n, hidden.dtype)
+    _arg(logits, "logits", _f32(), (B, P, V))
     lib = load_library()
     _check("spec_verify_logits",
            lib.spec_verify_logits(_ptr(hidden), _ptr(w_lmhead), _dtype_code(hidden), _ptr(logits),
@@ -176,7 +226,11 @@ def spec_verify_logits(hidden, w_lmhead, logits, stream=None) -> None:
 
 def spec_accept_greedy(logits, draft_tokens, accepted_len, out_tokens, workspace, rows=None, stream=None) -> None:
     """Greedy acceptance of the selected rows (all rows if ``rows`` is None)."""
-    B, P, V = logits.shape
+    B, P, V = _arg(logits, "logits", _f32(), (None, None, None)).shape
+    _arg(draft_tokens, "draft_tokens", _i32(), (B, P - 1), optional=P == 1)
+    _arg(accepted_len, "accepted_len", _i32(), (B,))
+    _arg(out_tokens, "out_tokens", _i32(), (B, P))
+    _ws(workspace)
     rows_t, n_rows = _rows(rows)
     lib = load_library()
     _check("spec_accept_greedy",
@@ -188,7 +242,14 @@ def spec_accept_greedy(logits, draft_tokens, accepted_len, out_tokens, workspace
 def spec_accept_sample(logits, draft_logits, draft_tokens, temperature, seeds, accepted_len, out_tokens, workspace,
                        rows=None, probs_at_draft=None, stream=None) -> None:
     """Speculative sampling of the selected rows (all rows if ``rows`` is None)."""
-    B, P, V = logits.shape
+    B, P, V = _arg(logits, "logits", _f32(), (None, None, None)).shape
+    _arg(draft_logits, "draft_logits", _f32(), (B, P - 1, V), optional=P == 1)
+    _arg(draft_tokens, "draft_tokens", _i32(), (B, P - 1), optional=P == 1)
+    _arg(seeds, "seeds", _seed_types(), (B,))
+    _arg(accepted_len, "accepted_len", _i32(), (B,))
+    _arg(out_tokens, "out_tokens", _i32(), (B, P))
+    _arg(probs_at_draft, "probs_at_draft", _f32(), (B, P - 1, 2), optional=True)
+    _ws(workspace)
     rows_t, n_rows = _rows(rows)
     lib = load_library()
     _check("spec_accept_sample",
@@ -202,8 +263,12 @@ def spec_accept_sample(logits, draft_logits, draft_tokens, temperature, seeds, a
 def spec_accept_greedy_ragged(logits, draft_tokens, row_start, K_max, accepted_len, out_tokens, workspace, rows=None,
                               stream=None) -> None:
     """Greedy acceptance of a ragged batch: logits [R, V] packed by row_start [B+1]."""
-    R, V = logits.shape
-    B = row_start.numel() - 1
+    R, V = _arg(logits, "logits", _f32(), (None, None)).shape
+    B = _arg(row_start, "row_start", _i32(), (None,)).numel() - 1
+    _arg(draft_tokens, "draft_tokens", _i32(), (R - B,), optional=R <= B)
+    _arg(accepted_len, "accepted_len", _i32(), (B,))
+    _arg(out_tokens, "out_tokens", _i32(), (R,))
+    _ws(workspace)
     rows_t, n_rows = _rows(rows)
     lib = load_library()
     _check("spec_accept_greedy_ragged",
@@ -217,8 +282,15 @@ def spec_accept_sample_ragged(logits, draft_logits, draft_tokens, row_start, K_m
                               out_tokens, workspace, rows=None, probs_at_draft=None, stream=None) -> None:
     """Speculative sampling of a ragged batch: logits [R, V], draft_logits [R-B, V]
     packed by row_start [B+1]."""
-    R, V = logits.shape
-    B = row_start.numel() - 1
+    R, V = _arg(logits, "logits", _f32(), (None, None)).shape
+    B = _arg(row_start, "row_start", _i32(), (None,)).numel() - 1
+    _arg(draft_logits, "draft_logits", _f32(), (R - B, V), optional=R <= B)
+    _arg(draft_tokens, "draft_tokens", _i32(), (R - B,), optional=R <= B)
+    _arg(seeds, "seeds", _seed_types(), (B,))
+    _arg(accepted_len, "accepted_len", _i32(), (B,))
+    _arg(out_tokens, "out_tokens", _i32(), (R,))
+    _arg(probs_at_draft, "probs_at_draft", _f32(), (R - B, 2), optional=True)
+    _ws(workspace)
     rows_t, n_rows = _rows(rows)
     lib = load_library()
     _check("spec_accept_sample_ragged",
@@ -234,7 +306,13 @@ def spec_tree_accept_greedy(logits, parents, tokens, accepted_len, out_tokens, w
                             stream=None) -> None:
     """Greedy verification of draft trees: logits [B, N+1, V], parents and
     tokens [B, N+1] (entry 0 of each row is the root and is ignored)."""
-    B, P, V = logits.shape
+    B, P, V = _arg(logits, "logits", _f32(), (None, None, None)).shape
+    _arg(parents, "parents", _i32(), (B, P), optional=P == 1)
+    _arg(tokens, "tokens", _i32(), (B, P), optional=P == 1)
+    _arg(accepted_len, "accepted_len", _i32(), (B,))
+    _arg(out_tokens, "out_tokens", _i32(), (B, P))
+    _arg(out_nodes, "out_nodes", _i32(), (B, P), optional=True)
+    _ws(workspace)
     rows_t, n_rows = _rows(rows)
     lib = load_library()
     _check("spec_tree_accept_greedy",
@@ -253,7 +331,14 @@ def spec_ngram_propose(history, hist_start, max_len, max_ngram, n_drafts, drafts
     """Prompt-lookup drafts: history int32 (packed), hist_start int64 [B+1];
     drafts [B, n_drafts] and draft_count [B] int32 (row_start [B+1] int32
     optional)."""
-    B = hist_start.numel() - 1
+    import torch
+    _arg(history, "history", _i32(), (None,))
+    B = _arg(hist_start, "hist_start", torch.int64, (None,)).numel() - 1
+    # drafts[b, i] lives at b * n_drafts + i: with n_drafts = 0 nothing is written
+    _arg(drafts, "drafts", _i32(), (B, int(n_drafts)) if n_drafts else None, optional=not n_drafts)
+    _arg(draft_count, "draft_count", _i32(), (B,))
+    _arg(row_start, "row_start", _i32(), (B + 1,), optional=True)
+    _ws(workspace)
     lib = load_library()
     _check("spec_ngram_propose",
            lib.spec_ngram_propose(_ptr(history) if history.numel() else None, _ptr(hist_start), B, int(max_len),
@@ -273,6 +358,7 @@ def _row_list(rows, B):
         return None, 0
     if isinstance(rows, str) and rows == "all":
         return None, B
+    _arg(rows, "rows", _i32(), (None,))
     return rows, int(rows.numel())
 
 
@@ -286,6 +372,18 @@ def spec_verify_step(hidden, w_lmhead, logits, accepted_len, out_tokens, workspa
     V = w_lmhead.shape[0]
     if w_lmhead.dtype != hidden.dtype or tuple(logits.shape) != (B, P, V) or w_lmhead.shape[1] != H:
         raise ValueError("shape or dtype mismatch")
+    _dtype_code(hidden)
+    _arg(hidden, "hidden", hidden.dtype)
+    _arg(w_lmhead, "w_lmhead", hidden.dtype)
+    _arg(logits, "logits", _f32(), (B, P, V))
+    sampled = sampled_rows is not None
+    _arg(draft_logits, "draft_logits", _f32(), (B, P - 1, V), optional=P == 1 or not sampled)
+    _arg(draft_tokens, "draft_tokens", _i32(), (B, P - 1), optional=P == 1)
+    _arg(seeds, "seeds", _seed_types(), (B,), optional=not sampled)
+    _arg(accepted_len, "accepted_len", _i32(), (B,))
+    _arg(out_tokens, "out_tokens", _i32(), (B, P))
+    _arg(probs_at_draft, "probs_at_draft", _f32(), (B, P - 1, 2), optional=True)
+    _ws(workspace)
     g, ng = _row_list(greedy_rows, B)
     sm, ns = _row_list(sampled_rows, B)
     lib = load_library()

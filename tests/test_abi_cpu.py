@@ -253,3 +253,40 @@ def test_product_never_touches_the_oracle():
             if fn.endswith((".py", ".hip", ".h", ".cpp")):
                 text = open(os.path.join(dirpath, fn)).read()
                 assert not re.search(r"\boracle\b", text), fn
+
+
+def test_binding_checks_tensors_before_any_launch():
+    """The kernels trust the dtype and extent behind every pointer, so the
+    binding rejects a wrong dtype, a wrong shape, a strided view or a host
+    tensor before it reaches the library."""
+    import torch
+    B, K, V = 2, 3, 64
+    z = torch.zeros((B, K + 1, V))
+    d32 = torch.zeros((B, K), dtype=torch.int32)
+    acc = torch.zeros((B,), dtype=torch.int32)
+    out = torch.zeros((B, K + 1), dtype=torch.int32)
+    ws = torch.zeros((64,), dtype=torch.uint8)
+    with pytest.raises(TypeError, match="logits"):
+        sv.spec_accept_greedy(z.double(), d32, acc, out, ws)
+    with pytest.raises(TypeError, match="draft_tokens"):
+        sv.spec_accept_greedy(z, d32.long(), acc, out, ws)                  # int64 tokens
+    with pytest.raises(ValueError, match="draft_tokens has shape"):
+        sv.spec_accept_greedy(z, torch.zeros((B, K + 1), dtype=torch.int32), acc, out, ws)
+    with pytest.raises(ValueError, match="out_tokens has shape"):
+        sv.spec_accept_greedy(z, d32, acc, out[:, :K].contiguous(), ws)
+    with pytest.raises(ValueError, match="contiguous"):
+        sv.spec_accept_greedy(z, torch.zeros((K, B), dtype=torch.int32).t(), acc, out, ws)
+    with pytest.raises(ValueError, match="on the GPU"):
+        sv.spec_accept_greedy(z, d32, acc, out, ws)
+    with pytest.raises(TypeError, match="seeds"):
+        sv.spec_accept_sample(z, torch.zeros((B, K, V)), d32, 1.0, torch.zeros((B,), dtype=torch.int32), acc, out,
+                              ws)
+    with pytest.raises(ValueError, match="draft_logits has shape"):
+        sv.spec_verify_step(torch.zeros((B, K + 1, 8), dtype=torch.bfloat16),
+                            torch.zeros((V, 8), dtype=torch.bfloat16), z, acc, out, ws,
+                            draft_logits=torch.zeros((B, K + 1, V)), draft_tokens=d32,
+                            seeds=torch.zeros((B,), dtype=torch.int64), sampled_rows="all")
+    with pytest.raises(ValueError, match="row_start"):
+        sv.spec_accept_greedy_ragged(torch.zeros((6, V)), torch.zeros((4,), dtype=torch.int32),
+                                     torch.zeros((2, 2), dtype=torch.int32), K, acc, torch.zeros((6,), dtype=torch.int32),
+                                     ws)
