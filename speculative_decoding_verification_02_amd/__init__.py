@@ -142,48 +142,77 @@ def _dtype_code(t):
     raise TypeError("hidden/w_lmhead must be bfloat16 or float32, got %s" % t.dtype)
 
 
+_T = None   # torch, imported on first use (importing the package does not need it)
+
+
+def _torch():
+    global _T
+    if _T is None:
+        import torch
+        _T = torch
+    return _T
+
+
 def _arg(t, name, dtypes, shape=None, optional=False):
     """A device tensor the library reads or writes through a bare pointer:
     the kernels trust its dtype and extent, so they are checked here (shape
     entries of None match any size; _ptr checks the device).  Returns t."""
-    import torch
     if t is None:
         if optional:
             return None
         raise ValueError("%s is required" % name)
-    if not isinstance(t, torch.Tensor):
-        raise TypeError("%s must be a torch.Tensor" % name)
-    if not isinstance(dtypes, tuple):
-        dtypes = (dtypes,)
-    if t.dtype not in dtypes:
-        raise TypeError("%s must be %s, got %s" % (name, " or ".join(str(d) for d in dtypes), t.dtype))
-    if shape is not None and (t.dim() != len(shape) or
-                              any(w is not None and int(d) != int(w) for d, w in zip(t.shape, shape))):
-        raise ValueError("%s has shape %s, expected %s" % (name, tuple(t.shape),
-                                                            tuple("*" if w is None else w for w in shape)))
+    try:
+        dt = t.dtype
+    except AttributeError:
+        raise TypeError("%s must be a torch.Tensor" % name) from None
+    if dt is not dtypes and (type(dtypes) is not tuple or dt not in dtypes):
+        want = dtypes if type(dtypes) is tuple else (dtypes,)
+        raise TypeError("%s must be %s, got %s" % (name, " or ".join(str(d) for d in want), dt))
+    if shape is not None:
+        ts = t.shape
+        ok = len(ts) == len(shape)
+        if ok:
+            for d, w in zip(ts, shape):
+                if w is not None and d != w:
+                    ok = False
+                    break
+        if not ok:
+            raise ValueError("%s has shape %s, expected %s" % (name, tuple(ts),
+                                                                tuple("*" if w is None else w for w in shape)))
     if not t.is_contiguous():
         raise ValueError("%s must be contiguous" % name)
     return t
 
 
+_DT = {}
+
+
+def _dt(key):
+    """Cached dtype (or dtype tuple) by name."""
+    v = _DT.get(key)
+    if v is None:
+        torch = _torch()
+        v = {"i32": torch.int32, "f32": torch.float32, "i64": torch.int64,
+             "seed": (torch.int64, torch.uint64) if hasattr(torch, "uint64") else torch.int64,
+             "ws": (torch.uint8, torch.int8, torch.int32, torch.int64, torch.float32)}[key]
+        _DT[key] = v
+    return v
+
+
 def _i32():
-    import torch
-    return torch.int32
+    return _dt("i32")
 
 
 def _f32():
-    import torch
-    return torch.float32
+    return _dt("f32")
 
 
 def _seed_types():
-    import torch
-    return (torch.int64, torch.uint64) if hasattr(torch, "uint64") else (torch.int64,)
+    return _dt("seed")
 
 
 def _ws(workspace):
-    import torch
-    return _arg(workspace, "workspace", (torch.uint8, torch.int8, torch.int32, torch.int64, torch.float32))
+    return _arg(workspace, "workspace", _dt("ws"))
 
 
 def _rows(rows):
@@ -331,9 +360,8 @@ def spec_ngram_propose(history, hist_start, max_len, max_ngram, n_drafts, drafts
     """Prompt-lookup drafts: history int32 (packed), hist_start int64 [B+1];
     drafts [B, n_drafts] and draft_count [B] int32 (row_start [B+1] int32
     optional)."""
-    import torch
     _arg(history, "history", _i32(), (None,))
-    B = _arg(hist_start, "hist_start", torch.int64, (None,)).numel() - 1
+    B = _arg(hist_start, "hist_start", _dt("i64"), (None,)).numel() - 1
     # drafts[b, i] lives at b * n_drafts + i: with n_drafts = 0 nothing is written
     _arg(drafts, "drafts", _i32(), (B, int(n_drafts)) if n_drafts else None, optional=not n_drafts)
     _arg(draft_count, "draft_count", _i32(), (B,))
