@@ -404,7 +404,7 @@ def spec_verify_step(hidden, w_lmhead, logits, accepted_len, out_tokens, workspa
     _arg(hidden, "hidden", hidden.dtype)
     _arg(w_lmhead, "w_lmhead", hidden.dtype)
     _arg(logits, "logits", _f32(), (B, P, V))
-    sampled = sampled_rows is not None
+    sampled = sampled_rows is not None and (isinstance(sampled_rows, str) or sampled_rows.numel() > 0)
     _arg(draft_logits, "draft_logits", _f32(), (B, P - 1, V), optional=P == 1 or not sampled)
     _arg(draft_tokens, "draft_tokens", _i32(), (B, P - 1), optional=P == 1)
     _arg(seeds, "seeds", _seed_types(), (B,), optional=not sampled)
