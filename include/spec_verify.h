@@ -339,6 +339,8 @@ size_t spec_verify_step_workspace_bytes(int B, int K, int V);
  * no drafts.  Only token equality is used, so the result is exact.
  *
  *   history       device, int32 tokens of all histories, packed
+ *   history_len   number of int32 entries behind `history` (>= 0); no
+ *                 kernel reads past it
  *   hist_start    device, [B+1] int64, 8-byte aligned: history b is
  *                 history[hist_start[b] .. hist_start[b+1]-1]
  *   B             number of histories, >= 1
@@ -354,12 +356,11 @@ size_t spec_verify_step_workspace_bytes(int B, int K, int V);
  *                 offsets counts as 0 drafts there)
  *   workspace     device scratch of spec_ngram_workspace_bytes(B, max_len)
  *                 bytes, 8-byte aligned; contents on entry do not matter
- * The caller guarantees that every well-formed span lies inside history.
- * A history whose offsets are malformed (negative start, negative length or
- * a length above max_len) gets draft_count[b] = -1 and drafts of -1, and is
- * not read.
+ * A history whose offsets are malformed (negative start, negative length, a
+ * length above max_len, or an end past history_len) gets draft_count[b] = -1
+ * and drafts of -1, and is not read.
  */
-spec_status_t spec_ngram_propose(const int32_t* history, const int64_t* hist_start, int B,
+spec_status_t spec_ngram_propose(const int32_t* history, int64_t history_len, const int64_t* hist_start, int B,
                                  int max_len, int max_ngram, int n_drafts,
                                  int32_t* drafts, int32_t* draft_count, int32_t* row_start,
                                  void* workspace, size_t workspace_bytes,

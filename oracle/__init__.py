@@ -35,4 +35,4 @@ from .verify import (  # noqa: F401
     ragged_sequences, softmax, widen_bf16,
 )
 from .tree import TreeResult, tree_accept_greedy  # noqa: F401,E402
-from .ngram import ngram_propose, ngram_propose_one  # noqa: F401,E402
+from .ngram import ngram_propose, ngram_propose_one, trailing_runs  # noqa: F401,E402

@@ -61,8 +61,8 @@ _SIGNATURES = {
                                            _c_void_p, _c_void_p, _c_size_t, _c_void_p]),
     "spec_tree_accept_greedy": (_c_int, [_c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_int, _c_int, _c_int, _c_int,
                                          _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_size_t, _c_void_p]),
-    "spec_ngram_propose": (_c_int, [_c_void_p, _c_void_p, _c_int, _c_int, _c_int, _c_int, _c_void_p, _c_void_p,
-                                    _c_void_p, _c_void_p, _c_size_t, _c_void_p]),
+    "spec_ngram_propose": (_c_int, [_c_void_p, ctypes.c_int64, _c_void_p, _c_int, _c_int, _c_int, _c_int, _c_void_p,
+                                    _c_void_p, _c_void_p, _c_void_p, _c_size_t, _c_void_p]),
     "spec_ngram_workspace_bytes": (_c_size_t, [_c_int, _c_int]),
     "spec_verify_step": (_c_int, [_c_void_p, _c_void_p, _c_int, _c_void_p, _c_void_p, _c_float, _c_void_p, _c_void_p,
                                   _c_int, _c_void_p, _c_int, _c_int, _c_int, _c_int, _c_int, _c_void_p, _c_void_p,
@@ -369,7 +369,8 @@ def spec_ngram_propose(history, hist_start, max_len, max_ngram, n_drafts, drafts
     _ws(workspace)
     lib = load_library()
     _check("spec_ngram_propose",
-           lib.spec_ngram_propose(_ptr(history) if history.numel() else None, _ptr(hist_start), B, int(max_len),
+           lib.spec_ngram_propose(_ptr(history) if history.numel() else None, int(history.numel()),
+                                  _ptr(hist_start), B, int(max_len),
                                   int(max_ngram), int(n_drafts), _ptr(drafts) if n_drafts else None,
                                   _ptr(draft_count), _ptr(row_start), _ptr(workspace),
                                   workspace.numel() * workspace.element_size(), _stream(stream)))

@@ -33,11 +33,14 @@ constexpr int kNgFinLanes = 4;                            // threads per sequenc
 constexpr int kNgFinSeqs = kNgFinThreads / kNgFinLanes;   // sequences per pass
 static_assert(kNgSeg % kNgThreads == 0, "segment must split evenly");
 
-// history span of sequence b, or false if its offsets are malformed
-__device__ __forceinline__ bool ng_span(const int64_t* hist_start, int b, int max_len, int64_t& s0, int& L) {
+// history span of sequence b, or false if its offsets are malformed (a
+// negative start or length, a length above max_len, or an end past the
+// hist_len entries behind the history pointer)
+__device__ __forceinline__ bool ng_span(const int64_t* hist_start, int b, int max_len, int64_t hist_len, int64_t& s0,
+                                        int& L) {
     s0 = hist_start[b];
     const int64_t len = hist_start[b + 1] - s0;
-    if (s0 < 0 || len < 0 || len > max_len) return false;
+    if (s0 < 0 || len < 0 || len > max_len || s0 > hist_len - len) return false;
     L = (int)len;
     return true;
 }
@@ -50,6 +53,7 @@ __device__ __forceinline__ bool ng_span(const int64_t* hist_start, int b, int ma
 // (rare unless the vocabulary is tiny or the text repeats) reads the earlier
 // tokens of its window, from the cache the segment was just streamed through.
 __global__ __launch_bounds__(kNgThreads) void ngram_scan_kernel(const int32_t* __restrict__ hist,
+                                                                int64_t hist_len,
                                                                 const int64_t* __restrict__ hist_start, int max_len,
                                                                 int G, int segs, unsigned long long* keys) {
     __shared__ unsigned long long red[kNgThreads / kWave];
@@ -59,7 +63,7 @@ __global__ __launch_bounds__(kNgThreads) void ngram_scan_kernel(const int32_t* _
     const int tid = threadIdx.x;
     int64_t s0 = 0;
     int L = 0;
-    const bool ok = ng_span(hist_start, b, max_len, s0, L);
+    const bool ok = ng_span(hist_start, b, max_len, hist_len, s0, L);
     const int e0 = seg * kNgSeg;                 // end positions e0 .. e1-1, e <= L-2
     const int e1 = ok ? min(e0 + kNgSeg, L - 1) : 0;
     if (e0 >= e1) {
@@ -117,7 +121,8 @@ __device__ __forceinline__ unsigned long long quad_max_u64(unsigned long long x)
 }
 
 __global__ __launch_bounds__(kNgFinThreads) void ngram_finalize_kernel(
-    const int32_t* __restrict__ hist, const int64_t* __restrict__ hist_start, int B, int max_len, int n_drafts,
+    const int32_t* __restrict__ hist, int64_t hist_len, const int64_t* __restrict__ hist_start, int B, int max_len,
+    int n_drafts,
     int segs, const unsigned long long* __restrict__ keys, int32_t* __restrict__ drafts, int32_t* __restrict__ count,
     int32_t* __restrict__ row_start) {
     __shared__ int wsum[kNgFinThreads / kWave];
@@ -134,7 +139,7 @@ __global__ __launch_bounds__(kNgFinThreads) void ngram_finalize_kernel(
         bool ok = false;
         unsigned long long key = 0ull;
         if (live) {
-            ok = ng_span(hist_start, b, max_len, s0, L);
+            ok = ng_span(hist_start, b, max_len, hist_len, s0, L);
             const unsigned long long* kb = keys + (size_t)b * segs;
             for (int g0 = q; g0 < segs; g0 += kNgFinLanes * kKeyBatch) {
                 unsigned long long k[kKeyBatch];
@@ -188,19 +193,20 @@ __global__ __launch_bounds__(kNgFinThreads) void ngram_finalize_kernel(
     }
 }
 
-hipError_t launch_ngram(const int32_t* hist, const int64_t* hist_start, int B, int max_len, int G, int n_drafts,
+hipError_t launch_ngram(const int32_t* hist, int64_t hist_len, const int64_t* hist_start, int B, int max_len, int G,
+                        int n_drafts,
                         int32_t* drafts, int32_t* count, int32_t* row_start, unsigned long long* keys,
                         hipStream_t stream) {
     if (n_drafts < 0 || n_drafts > kNgMaxDrafts) return hipErrorInvalidValue;
     const int segs = ngram_segments(max_len);
     if (segs > 0) {
         hipLaunchKernelGGL(ngram_scan_kernel, dim3((unsigned)((long)B * segs)), dim3(kNgThreads), 0, stream, hist,
-                           hist_start, max_len, G, segs, keys);
+                           hist_len, hist_start, max_len, G, segs, keys);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
-    hipLaunchKernelGGL(ngram_finalize_kernel, dim3(1), dim3(kNgFinThreads), 0, stream, hist, hist_start, B, max_len,
-                       n_drafts, segs, keys, drafts, count, row_start);
+    hipLaunchKernelGGL(ngram_finalize_kernel, dim3(1), dim3(kNgFinThreads), 0, stream, hist, hist_len, hist_start, B,
+                       max_len, n_drafts, segs, keys, drafts, count, row_start);
     return hipGetLastError();
 }
 

@@ -281,18 +281,20 @@ spec_status_t spec_tree_accept_greedy(const float* logits, const int32_t* parent
     return e == hipSuccess ? SPEC_OK : hip_fail(e);
 }
 
-spec_status_t spec_ngram_propose(const int32_t* history, const int64_t* hist_start, int B, int max_len,
-                                 int max_ngram, int n_drafts, int32_t* drafts, int32_t* draft_count,
+spec_status_t spec_ngram_propose(const int32_t* history, int64_t history_len, const int64_t* hist_start, int B,
+                                 int max_len, int max_ngram, int n_drafts, int32_t* drafts, int32_t* draft_count,
                                  int32_t* row_start, void* workspace, size_t workspace_bytes, spec_stream_t stream) {
     if (B < 1 || max_len < 0 || max_len == 0x7fffffff || max_ngram < 1 || max_ngram > sv::kNgMaxGram ||
-        n_drafts < 0 || n_drafts > sv::kNgMaxDrafts)
+        n_drafts < 0 || n_drafts > sv::kNgMaxDrafts || history_len < 0)
         return SPEC_ERR_ARG;
-    if (!hist_start || !draft_count || (n_drafts > 0 && !drafts) || (max_len > 0 && !history)) return SPEC_ERR_ARG;
+    if (!hist_start || !draft_count || (n_drafts > 0 && !drafts) || (history_len > 0 && !history))
+        return SPEC_ERR_ARG;
     if ((long long)B * sv::ngram_segments(max_len) > 0x7fffffffLL) return SPEC_ERR_ARG;
     if ((reinterpret_cast<uintptr_t>(hist_start) & 7u) != 0) return SPEC_ERR_ALIGN;
     if (!workspace || workspace_bytes < spec_ngram_workspace_bytes(B, max_len)) return SPEC_ERR_WORKSPACE;
     if ((reinterpret_cast<uintptr_t>(workspace) & 7u) != 0) return SPEC_ERR_ALIGN;
-    hipError_t e = sv::launch_ngram(history, hist_start, B, max_len, max_ngram, n_drafts, drafts, draft_count,
+    hipError_t e = sv::launch_ngram(history, history_len, hist_start, B, max_len, max_ngram, n_drafts, drafts,
+                                    draft_count,
                                     row_start, static_cast<unsigned long long*>(workspace),
                                     static_cast<hipStream_t>(stream));
     return e == hipSuccess ? SPEC_OK : hip_fail(e);

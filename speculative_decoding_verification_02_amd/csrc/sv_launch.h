@@ -123,12 +123,14 @@ hipError_t launch_residual(const float* logits, const float* draft_logits, int n
                            int32_t* out_tokens, hipStream_t stream);
 
 // Prompt-lookup drafter: per-sequence best (match length, end position) keys
-// (B x 8 bytes of scratch), then drafts, counts and verify-row offsets.
+// (B x 8 bytes of scratch), then drafts, counts and verify-row offsets.  A
+// span reaching past hist_len entries of hist is malformed and never read.
 constexpr int kNgMaxGram = 16;                     // longest n-gram tried
 constexpr int kNgMaxDrafts = 63;                   // drafts per history at most
 constexpr int kNgSeg = 4096;                       // end positions per scan workgroup
 inline int ngram_segments(int max_len) { return max_len >= 2 ? (max_len - 2) / kNgSeg + 1 : 0; }
-hipError_t launch_ngram(const int32_t* hist, const int64_t* hist_start, int B, int max_len, int G, int n_drafts,
+hipError_t launch_ngram(const int32_t* hist, int64_t hist_len, const int64_t* hist_start, int B, int max_len, int G,
+                        int n_drafts,
                         int32_t* drafts, int32_t* count, int32_t* row_start, unsigned long long* keys,
                         hipStream_t stream);
 

@@ -161,10 +161,10 @@ def test_tree_validation(lib):
     assert _tree(lib, rows=A, n_rows=0) == sv.SPEC_OK
 
 
-def _ngram(lib, hist=A, hs=A, B=2, max_len=100, g=3, k=5, drafts=A, count=A, ws=A, wsb=None):
+def _ngram(lib, hist=A, hl=100, hs=A, B=2, max_len=100, g=3, k=5, drafts=A, count=A, ws=A, wsb=None):
     if wsb is None:
         wsb = sv.spec_ngram_workspace_bytes(B, max_len) or 256
-    return lib.spec_ngram_propose(hist, hs, B, max_len, g, k, drafts, count, None, ws, wsb, None)
+    return lib.spec_ngram_propose(hist, hl, hs, B, max_len, g, k, drafts, count, None, ws, wsb, None)
 
 
 def test_ngram_validation(lib):
@@ -180,6 +180,8 @@ def test_ngram_validation(lib):
     assert _ngram(lib, k=64) == sv.SPEC_ERR_ARG
     assert _ngram(lib, k=-1) == sv.SPEC_ERR_ARG
     assert _ngram(lib, hist=None) == sv.SPEC_ERR_ARG
+    assert _ngram(lib, hl=-1) == sv.SPEC_ERR_ARG                      # negative history length
+    assert _ngram(lib, hist=None, hl=1) == sv.SPEC_ERR_ARG            # entries declared behind a null pointer
     assert _ngram(lib, hs=None) == sv.SPEC_ERR_ARG
     assert _ngram(lib, drafts=None) == sv.SPEC_ERR_ARG
     assert _ngram(lib, count=None) == sv.SPEC_ERR_ARG

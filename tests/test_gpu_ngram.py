@@ -1,5 +1,6 @@
 """GPU parity of spec_ngram_propose (prompt-lookup drafts) against the
-oracle, which follows the pages' search n = max_ngram .. 1 directly.  Token
+oracle, which takes the longest earlier match of the sequence's end directly
+from the rule (its own formulation, checked against string search).  Token
 equality only, so drafts, counts and verify-row offsets must match exactly:
 histories from empty to several scan segments long (4096 end positions per
 workgroup) with matches on either side of segment borders, tiny and large
@@ -90,6 +91,23 @@ def test_ngram_malformed_offsets():
         assert c[b] == len(od) and d[b, :len(od)].tolist() == od.tolist()
     cnt = np.where(c < 0, 0, c)
     np.testing.assert_array_equal(rs, np.concatenate([[0], np.cumsum(cnt + 1)]))
+
+
+def test_span_past_history_end():
+    """Offsets that reach past the history buffer (the binding passes its
+    length) mark exactly those histories -1; nothing past the buffer is read."""
+    hist = synth.histories(5, 0, 40, seed=4, lengths=[120, 90, 60, 30, 75])
+    flat, starts = _pack(hist)
+    n = len(flat)
+    bad = starts.copy()
+    bad[4] = n - 10            # history 3 grows to end 10 entries before the buffer's end: well formed
+    bad[5] = n + 4096          # history 4 ends 4096 entries past it: malformed
+    say("ngram span past the history buffer (%d entries)" % n)
+    d, c, rs = _run(hist, 3, 4, starts=bad, max_len=5000)
+    assert c[4] == -1 and np.all(d[4] == -1)
+    for b in range(4):
+        od, _ = oracle.ngram_propose_one(flat[bad[b]:bad[b + 1]], 4, 3)
+        assert c[b] == len(od) and d[b, :len(od)].tolist() == od.tolist()
 
 
 def test_full_size_workload():

@@ -91,3 +91,21 @@ def test_invariants_and_batch_form():
         for m in range(n + 1, 5):      # no longer suffix occurs earlier
             if L > m:
                 assert not any(np.array_equal(s[j:j + m], s[L - m:]) for j in range(0, L - m))
+
+
+@pytest.mark.parametrize("seed", range(4))
+def test_trailing_runs_brute_force(seed):
+    """run(e) against a direct count of agreeing tokens, walking back from e
+    and from the sequence's end one token at a time."""
+    rng = np.random.default_rng(100 + seed)
+    for _ in range(60):
+        L = int(rng.integers(0, 40))
+        s = rng.integers(0, int(rng.choice([2, 3, 6])), L)
+        g = int(rng.integers(1, 7))
+        want = []
+        for e in range(L - 1):
+            k = 0
+            while k < g and e - k >= 0 and s[e - k] == s[L - 1 - k]:
+                k += 1
+            want.append(k)
+        assert oracle.trailing_runs(s, g).tolist() == want, (s.tolist(), g)
