@@ -56,7 +56,8 @@
  * Conventions shared by every entry point
  *   - Every pointer argument is DEVICE memory on the current HIP device, owned
  *     by the caller.  The library allocates nothing and keeps no state between
- *     calls other than a per-device cache of the compute-unit count.
+ *     calls other than a per-device cache of the compute-unit count and of
+ *     the address of spec_verify_step_noalloc's scratch array.
  *   - Every call is asynchronous: it validates its arguments on the host,
  *     enqueues kernels on `stream` and returns.  It never synchronises.  The
  *     caller synchronises (event or stream) before reading outputs.
@@ -330,6 +331,36 @@ spec_status_t spec_verify_step(const void* hidden, const void* w_lmhead, spec_dt
 size_t spec_verify_step_workspace_bytes(int B, int K, int V);
 
 /*
+ * spec_verify_step_noalloc -- spec_verify_step for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc.
+ *
+ * Same arguments, kernels and results as spec_verify_step, without the
+ * workspace: the step's scratch is a 64 MiB array the library holds per GPU
+ * (in its code object, for the life of the process), so every workload with
+ * spec_verify_step_workspace_bytes(B, K, V) <= 67108864 fits (the largest
+ * benchmark workload, B = 512, K = 3, V = 262144, needs 36 MiB).  Larger
+ * sizes return SPEC_ERR_WORKSPACE before anything is enqueued, and
+ * spec_last_error_detail() says why.  The first call on a device looks up
+ * that device's copy of the array (hipGetSymbolAddress, with the device
+ * current); no call allocates or frees memory.
+ *
+ * Every call on one GPU uses that GPU's one array.  Calls ordered on one
+ * stream are safe (each clears what its kernels count on, so what an earlier
+ * call left there does not matter); calls that may overlap on one GPU (other
+ * streams, other threads without ordering) race on it and must use
+ * spec_verify_step with workspaces of their own.
+ */
+spec_status_t spec_verify_step_noalloc(const void* hidden, const void* w_lmhead, spec_dtype_t dtype,
+                                       const float* draft_logits, const int32_t* draft_tokens,
+                                       float temperature, const uint64_t* seeds,
+                                       const int32_t* greedy_rows, int n_greedy,
+                                       const int32_t* sampled_rows, int n_sampled,
+                                       int B, int K, int V, int H,
+                                       float* logits, int32_t* accepted_len, int32_t* out_tokens,
+                                       float* probs_at_draft, spec_stream_t stream);
+
+/*
  * spec_ngram_propose -- prompt-lookup drafts for B token histories.
  *
  * For history s of length L: for n = max_ngram, ..., 1, look for the window
@@ -379,7 +410,8 @@ size_t spec_workspace_bytes(int B, int K, int V);
 const char* spec_status_string(spec_status_t status);
 
 /* Detail of the last SPEC_ERR_HIP returned on the calling thread (a static
- * string owned by the HIP runtime), or "" if none. */
+ * string owned by the HIP runtime), or of spec_verify_step_noalloc's
+ * SPEC_ERR_WORKSPACE (a static string of the library); "" if none. */
 const char* spec_last_error_detail(void);
 
 #ifdef __cplusplus

@@ -20,6 +20,9 @@ in the library's HIP kernels; if the library is missing, every call raises.
     spec_verify_step(hidden, w_lmhead, logits, accepted_len, out_tokens, workspace, draft_logits=None,
                      draft_tokens=None, temperature=1.0, seeds=None, greedy_rows=None, sampled_rows=None,
                      probs_at_draft=None)
+    spec_verify_step_noalloc(hidden, w_lmhead, logits, accepted_len, out_tokens, draft_logits=None,
+                             draft_tokens=None, temperature=1.0, seeds=None, greedy_rows=None, sampled_rows=None,
+                             probs_at_draft=None)
     spec_workspace_bytes(B, K, V), spec_ngram_workspace_bytes(B, max_len), spec_verify_step_workspace_bytes(B, K, V)
 """
 from __future__ import annotations
@@ -33,7 +36,7 @@ __all__ = [
     "SPEC_ERR_WORKSPACE", "SPEC_ERR_HIP", "SPEC_BF16", "SPEC_F32", "LIB_PATH", "HEADER_PATH",
     "load_library", "declared_symbols", "spec_verify_logits", "spec_accept_greedy",
     "spec_accept_sample", "spec_accept_greedy_ragged", "spec_accept_sample_ragged", "spec_tree_accept_greedy", "spec_ngram_propose", "spec_ngram_workspace_bytes",
-    "spec_verify_step", "spec_verify_step_workspace_bytes",
+    "spec_verify_step", "spec_verify_step_workspace_bytes", "spec_verify_step_noalloc",
     "spec_workspace_bytes", "spec_status_string", "spec_last_error_detail",
 ]
 
@@ -68,6 +71,9 @@ _SIGNATURES = {
                                   _c_int, _c_void_p, _c_int, _c_int, _c_int, _c_int, _c_int, _c_void_p, _c_void_p,
                                   _c_void_p, _c_void_p, _c_void_p, _c_size_t, _c_void_p]),
     "spec_verify_step_workspace_bytes": (_c_size_t, [_c_int, _c_int, _c_int]),
+    "spec_verify_step_noalloc": (_c_int, [_c_void_p, _c_void_p, _c_int, _c_void_p, _c_void_p, _c_float, _c_void_p,
+                                          _c_void_p, _c_int, _c_void_p, _c_int, _c_int, _c_int, _c_int, _c_int,
+                                          _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p]),
     "spec_workspace_bytes": (_c_size_t, [_c_int, _c_int, _c_int]),
     "spec_status_string": (ctypes.c_char_p, [_c_int]),
     "spec_last_error_detail": (ctypes.c_char_p, []),
@@ -391,12 +397,9 @@ def _row_list(rows, B):
     return rows, int(rows.numel())
 
 
-def spec_verify_step(hidden, w_lmhead, logits, accepted_len, out_tokens, workspace, draft_logits=None,
-                     draft_tokens=None, temperature=1.0, seeds=None, greedy_rows=None, sampled_rows=None,
-                     probs_at_draft=None, stream=None) -> None:
-    """The whole verify step: logits[B, K+1, V] = hidden . w_lmheadᵀ, then greedy
-    acceptance of ``greedy_rows`` and speculative sampling of ``sampled_rows``
-    (each None, "all", or an int32 device tensor of sequence indices)."""
+def _step_args(hidden, w_lmhead, logits, accepted_len, out_tokens, draft_logits, draft_tokens, seeds, greedy_rows,
+               sampled_rows, probs_at_draft):
+    """Checks of the step's tensors; returns (B, P, V, H, greedy, n_greedy, sampled, n_sampled)."""
     B, P, H = hidden.shape
     V = w_lmhead.shape[0]
     if w_lmhead.dtype != hidden.dtype or tuple(logits.shape) != (B, P, V) or w_lmhead.shape[1] != H:
@@ -412,9 +415,20 @@ def spec_verify_step(hidden, w_lmhead, logits, accepted_len, out_tokens, workspa
     _arg(accepted_len, "accepted_len", _i32(), (B,))
     _arg(out_tokens, "out_tokens", _i32(), (B, P))
     _arg(probs_at_draft, "probs_at_draft", _f32(), (B, P - 1, 2), optional=True)
-    _ws(workspace)
     g, ng = _row_list(greedy_rows, B)
     sm, ns = _row_list(sampled_rows, B)
+    return B, P, V, H, g, ng, sm, ns
+
+
+def spec_verify_step(hidden, w_lmhead, logits, accepted_len, out_tokens, workspace, draft_logits=None,
+                     draft_tokens=None, temperature=1.0, seeds=None, greedy_rows=None, sampled_rows=None,
+                     probs_at_draft=None, stream=None) -> None:
+    """The whole verify step: logits[B, K+1, V] = hidden . w_lmheadᵀ, then greedy
+    acceptance of ``greedy_rows`` and speculative sampling of ``sampled_rows``
+    (each None, "all", or an int32 device tensor of sequence indices)."""
+    B, P, V, H, g, ng, sm, ns = _step_args(hidden, w_lmhead, logits, accepted_len, out_tokens, draft_logits,
+                                           draft_tokens, seeds, greedy_rows, sampled_rows, probs_at_draft)
+    _ws(workspace)
     lib = load_library()
     _check("spec_verify_step",
            lib.spec_verify_step(_ptr(hidden), _ptr(w_lmhead), _dtype_code(hidden),
@@ -422,3 +436,20 @@ def spec_verify_step(hidden, w_lmhead, logits, accepted_len, out_tokens, workspa
                                 float(temperature), _ptr(seeds), _ptr(g), ng, _ptr(sm), ns, B, P - 1, V, H,
                                 _ptr(logits), _ptr(accepted_len), _ptr(out_tokens), _ptr(probs_at_draft),
                                 _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream)))
+
+
+def spec_verify_step_noalloc(hidden, w_lmhead, logits, accepted_len, out_tokens, draft_logits=None,
+                             draft_tokens=None, temperature=1.0, seeds=None, greedy_rows=None, sampled_rows=None,
+                             probs_at_draft=None, stream=None) -> None:
+    """spec_verify_step without a workspace: the library's own per-GPU
+    scratch (64 MiB) takes its place.  Calls that may overlap on one GPU race
+    on that scratch."""
+    B, P, V, H, g, ng, sm, ns = _step_args(hidden, w_lmhead, logits, accepted_len, out_tokens, draft_logits,
+                                           draft_tokens, seeds, greedy_rows, sampled_rows, probs_at_draft)
+    lib = load_library()
+    _check("spec_verify_step_noalloc",
+           lib.spec_verify_step_noalloc(_ptr(hidden), _ptr(w_lmhead), _dtype_code(hidden),
+                                        _ptr(draft_logits) if P > 1 else None, _ptr(draft_tokens) if P > 1 else None,
+                                        float(temperature), _ptr(seeds), _ptr(g), ng, _ptr(sm), ns, B, P - 1, V, H,
+                                        _ptr(logits), _ptr(accepted_len), _ptr(out_tokens), _ptr(probs_at_draft),
+                                        _stream(stream)))

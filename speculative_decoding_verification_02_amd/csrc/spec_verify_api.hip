@@ -12,6 +12,14 @@
 #include "sv_common.h"
 #include "sv_launch.h"
 
+// Scratch of spec_verify_step_noalloc, for callers that cannot allocate:
+// one copy per GPU in the library's code object, held until the process
+// ends.  Host code never passes the array's name to a kernel (on the host it
+// is a stand-in, not a device address): the address comes from
+// hipGetSymbolAddress, once per device, with that device current.
+constexpr size_t kNoAllocScratchBytes = size_t(64) << 20;
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+
 namespace {
 
 thread_local const char* g_detail = "";
@@ -21,6 +29,7 @@ constexpr int kMaxV = 1024 * sv::kChunk;           // the residual prefix lives 
 constexpr int kMaxDevices = 64;
 
 std::atomic<int> g_cus[kMaxDevices];
+std::atomic<void*> g_scratch[kMaxDevices];   // device address of `scratch`, per device
 
 spec_status_t hip_fail(hipError_t e) {
     g_detail = hipGetErrorString(e);
@@ -54,6 +63,25 @@ hipError_t num_cus(int* out) {
     if (n < 1) n = 1;
     if (dev >= 0 && dev < kMaxDevices) g_cus[dev].store(n, std::memory_order_relaxed);
     *out = n;
+    return hipSuccess;
+}
+
+// The current device's copy of `scratch`: looked up on the first call made
+// with that device current, then cached (two threads racing on the first
+// call store the same address).
+hipError_t scratch_ptr(void** out) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    void* p = g_scratch[dev].load(std::memory_order_acquire);
+    if (!p) {
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        if (!p) return hipErrorInvalidSymbol;
+        g_scratch[dev].store(p, std::memory_order_release);
+    }
+    *out = p;
     return hipSuccess;
 }
 
@@ -448,6 +476,27 @@ spec_status_t spec_verify_step(const void* hidden, const void* w_lmhead, spec_dt
         }
     }
     return e == hipSuccess ? SPEC_OK : hip_fail(e);
+}
+
+spec_status_t spec_verify_step_noalloc(const void* hidden, const void* w_lmhead, spec_dtype_t dtype,
+                                       const float* draft_logits, const int32_t* draft_tokens, float temperature,
+                                       const uint64_t* seeds, const int32_t* greedy_rows, int n_greedy,
+                                       const int32_t* sampled_rows, int n_sampled, int B, int K, int V, int H,
+                                       float* logits, int32_t* accepted_len, int32_t* out_tokens,
+                                       float* probs_at_draft, spec_stream_t stream) {
+    const size_t need = spec_verify_step_workspace_bytes(B, K, V);
+    if (need == 0) return SPEC_ERR_ARG;
+    if (need > kNoAllocScratchBytes) {
+        g_detail = "spec_verify_step_noalloc: these sizes need more than the 64 MiB of scratch the library holds "
+                   "per GPU (spec_verify_step_workspace_bytes(B, K, V) > 67108864); use spec_verify_step";
+        return SPEC_ERR_WORKSPACE;
+    }
+    void* ws = nullptr;
+    hipError_t e = scratch_ptr(&ws);
+    if (e != hipSuccess) return hip_fail(e);
+    return spec_verify_step(hidden, w_lmhead, dtype, draft_logits, draft_tokens, temperature, seeds, greedy_rows,
+                            n_greedy, sampled_rows, n_sampled, B, K, V, H, logits, accepted_len, out_tokens,
+                            probs_at_draft, ws, kNoAllocScratchBytes, stream);
 }
 
 size_t spec_verify_step_workspace_bytes(int B, int K, int V) {

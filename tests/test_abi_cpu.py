@@ -29,7 +29,7 @@ def test_exports_every_declared_symbol(lib):
     assert set(names) == {"spec_verify_logits", "spec_accept_greedy", "spec_accept_sample",
                           "spec_accept_greedy_ragged", "spec_accept_sample_ragged", "spec_tree_accept_greedy",
                           "spec_ngram_propose", "spec_ngram_workspace_bytes",
-                          "spec_verify_step", "spec_verify_step_workspace_bytes",
+                          "spec_verify_step", "spec_verify_step_workspace_bytes", "spec_verify_step_noalloc",
                           "spec_workspace_bytes", "spec_status_string", "spec_last_error_detail"}
     for n in names:
         assert hasattr(lib, n), n
@@ -292,3 +292,19 @@ def test_binding_checks_tensors_before_any_launch():
         sv.spec_accept_greedy_ragged(torch.zeros((6, V)), torch.zeros((4,), dtype=torch.int32),
                                      torch.zeros((2, 2), dtype=torch.int32), K, acc, torch.zeros((6,), dtype=torch.int32),
                                      ws)
+
+
+def test_noalloc_step_size_limit(lib):
+    """spec_verify_step_noalloc refuses, before any HIP call, sizes whose
+    workspace would exceed the library's 64 MiB scratch, and names the
+    limit; sizes out of range are argument errors."""
+    def call(B, K, V, H=64):
+        return lib.spec_verify_step_noalloc(A, A, sv.SPEC_BF16, A, A, 1.0, A, None, B, None, 0, B, K, V, H,
+                                            A, A, A, None, None)
+    assert sv.spec_verify_step_workspace_bytes(256, 63, 262144) > 64 << 20
+    assert call(256, 63, 262144) == sv.SPEC_ERR_WORKSPACE
+    assert "64 MiB" in sv.spec_last_error_detail()
+    assert call(0, 4, 1000) == sv.SPEC_ERR_ARG
+    assert call(1, 64, 1000) == sv.SPEC_ERR_ARG
+    for B, K, V in ((1, 5, 128256), (64, 4, 128256), (256, 8, 152064), (512, 3, 262144), (32, 15, 151936)):
+        assert 0 < sv.spec_verify_step_workspace_bytes(B, K, V) <= 64 << 20, (B, K, V)
