@@ -30,8 +30,8 @@ search and hand-worked sequences.
 """
 from .philox import philox4x32_10, uniform24, verify_uniforms  # noqa: F401
 from .verify import (  # noqa: F401
-    GreedyResult, SampleResult, accept_greedy, accept_greedy_ragged, accept_ratio, accept_sample,
-    accept_sample_ragged, expected_tokens, expected_tokens_positional, inverse_cdf, lm_head_logits,
+    GreedyResult, SampleProbs, SampleResult, accept_greedy, accept_greedy_ragged, accept_ratio, accept_sample,
+    accept_sample_probs, accept_sample_ragged, accept_sample_rounds, sample_probs, expected_tokens, expected_tokens_positional, inverse_cdf, lm_head_logits,
     ragged_sequences, softmax, widen_bf16,
 )
 from .tree import TreeResult, tree_accept_greedy  # noqa: F401,E402

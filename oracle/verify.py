@@ -214,17 +214,67 @@ def accept_sample(logits, draft_logits, draft_tokens, temperature, seeds, rows=N
     Accept d_i iff u_i < r_i = min(1, q_i(d_i)/p_i(d_i)); n = first rejected i, else K.
     Terminal weights: w = max(0, q_n - p_n) if n < K, else q_K (bonus).
     Terminal token: inverse CDF of w at u'_n.  Emitted: d_0..d_{n-1}, t.
-    Vectorised over the selected rows.
+    The two halves are ``sample_probs`` (the distributions) and
+    ``accept_sample_probs`` (the decisions), for callers that verify many
+    rounds over the same logits.
     """
+    z = np.asarray(logits)
+    B, P, V = z.shape
+    rows = _rows_arg(rows, B)
+    probs = sample_probs(logits, draft_logits, draft_tokens, temperature, rows)
+    return accept_sample_probs(probs, draft_tokens, seeds, slots)
+
+
+@dataclass
+class SampleProbs:
+    """The distributions of the selected, well-formed rows of a sampled
+    batch: q [R, K+1, V] and p [R, K, V] for the rows ``good`` (in order),
+    and alpha [R, K] = sum_v min(q_i, p_i), the probability that a draft
+    drawn from p_i is accepted; ``bad`` lists the selected rows marked as
+    faulted."""
+    B: int
+    K: int
+    V: int
+    good: np.ndarray
+    bad: np.ndarray
+    q: np.ndarray
+    p: np.ndarray
+    alpha: np.ndarray
+
+
+def sample_probs(logits, draft_logits, draft_tokens, temperature, rows=None) -> SampleProbs:
+    """q_i = softmax(logits[b, i] / T) and p_i = softmax(draft_logits[b, i] / T)
+    of the selected rows; rows with bad data (NaN or +inf, a row without a
+    finite entry, a draft token outside [0, V)) are set apart as faulted."""
     z = np.asarray(logits, dtype=np.float64)
     B, P, V = z.shape
     K = P - 1
     zd = np.asarray(draft_logits, dtype=np.float64) if K else np.zeros((B, 0, V))
     d = np.asarray(draft_tokens, dtype=np.int64).reshape(B, K)
-    seeds = np.asarray(seeds, dtype=np.uint64)
-    slot = np.arange(B) if slots is None else np.asarray(slots, dtype=np.int64).reshape(B)
     T = float(temperature)
     rows = _rows_arg(rows, B)
+    if len(rows) == 0:
+        e = np.zeros(0, np.int64)
+        return SampleProbs(B, K, V, e, e, np.zeros((0, P, V)), np.zeros((0, K, V)), np.zeros((0, K)))
+    zr, zdr, dr = z[rows], zd[rows], d[rows]
+    bad = np.any(_bad_rows(zr), axis=-1)
+    if K:
+        bad |= np.any(_bad_rows(zdr), axis=-1)
+        bad |= np.any((dr < 0) | (dr >= V), axis=-1)
+    good = rows[~bad]
+    q = softmax(z[good], T) if len(good) else np.zeros((0, P, V))
+    p = softmax(zd[good], T) if (K and len(good)) else np.zeros((len(good), K, V))
+    alpha = np.sum(np.minimum(q[:, :K], p), axis=-1)
+    return SampleProbs(B, K, V, good, rows[bad], q, p, alpha)
+
+
+def accept_sample_probs(probs: SampleProbs, draft_tokens, seeds, slots=None) -> SampleResult:
+    """The sampled decisions of the rows in ``probs`` for one round of draft
+    tokens [B, K] and seeds [B] (see accept_sample)."""
+    B, K, V = probs.B, probs.K, probs.V
+    d = np.asarray(draft_tokens, dtype=np.int64).reshape(B, K)
+    seeds = np.asarray(seeds, dtype=np.uint64).reshape(B)
+    slot = np.arange(B) if slots is None else np.asarray(slots, dtype=np.int64).reshape(B)
 
     acc = np.full(B, -2, np.int32)
     out = np.full((B, K + 1), -1, np.int32)
@@ -236,23 +286,12 @@ def accept_sample(logits, draft_logits, draft_tokens, temperature, seeds, rows=N
     tm = np.full(B, np.inf)
     zz = np.full(B, np.nan)
     alpha = np.full((B, K), np.nan)
-    if len(rows) == 0:
-        return SampleResult(acc, out, pad, ratio, ua, ut, am, tm, zz, alpha)
-
-    zr, zdr, dr = z[rows], zd[rows], d[rows]
-    bad = np.any(_bad_rows(zr), axis=-1)
-    if K:
-        bad |= np.any(_bad_rows(zdr), axis=-1)
-        bad |= np.any((dr < 0) | (dr >= V), axis=-1)
-    acc[rows[bad]] = -1
-    good = rows[~bad]
+    acc[probs.bad] = -1
+    good = probs.good
     if len(good) == 0:
         return SampleResult(acc, out, pad, ratio, ua, ut, am, tm, zz, alpha)
     R = len(good)
-    zr, zdr, dr = z[good], zd[good], d[good]
-
-    q = softmax(zr, T)                                   # [R, K+1, V]
-    p = softmax(zdr, T) if K else np.zeros((R, 0, V))    # [R, K, V]
+    q, p, dr = probs.q, probs.p, d[good]
     u, u2 = verify_uniforms(seeds[good][:, None], slot[good][:, None], np.arange(K + 1)[None, :])
     ua[good], ut[good] = u, u2
 
@@ -263,7 +302,7 @@ def accept_sample(logits, draft_logits, draft_tokens, temperature, seeds, rows=N
     r = accept_ratio(q_d, p_d)
     pad[good] = np.stack([q_d, p_d], axis=-1)
     ratio[good] = r
-    alpha[good] = np.sum(np.minimum(q[:, :K], p), axis=-1)
+    alpha[good] = probs.alpha
     am[good] = np.abs(u[:, :K] - r)
 
     # n = index of the first rejection (u_i >= r_i), scanning left to right; K if none
@@ -285,6 +324,82 @@ def accept_sample(logits, draft_logits, draft_tokens, temperature, seeds, rows=N
     acc[good] = n
     tm[good] = margin
     zz[good] = Z
+    return SampleResult(acc, out, pad, ratio, ua, ut, am, tm, zz, alpha)
+
+
+def accept_sample_rounds(probs: SampleProbs, draft_tokens, seeds, slots=None) -> SampleResult:
+    """accept_sample_probs over R rounds of the same distributions, with
+    draft_tokens [R, B, K] and seeds [R, B]; every result field gains a
+    leading round axis.
+
+    Only the draft tokens and the uniforms change from round to round, so
+    the terminal weights of each (row, terminal position) and their in-order
+    cumulative sums C are formed once; each round then finds its draw in
+    them by the same rule, t = min{v : C_v > u' Z} (C is nondecreasing, so
+    that is the number of entries C_v <= u' Z), with the same margin.
+    """
+    B, K, V = probs.B, probs.K, probs.V
+    sd = np.asarray(seeds, dtype=np.uint64).reshape(-1, B)
+    R = sd.shape[0]
+    d = np.asarray(draft_tokens, dtype=np.int64).reshape(R, B, K)
+    slot = np.arange(B) if slots is None else np.asarray(slots, dtype=np.int64).reshape(B)
+    good = probs.good
+    G = len(good)
+    q, p = probs.q, probs.p
+
+    # C[j, n]: cumulative terminal weights of good row j when the first
+    # rejection is at n (n = K: the bonus draw from q_K)
+    C = np.empty((G, K + 1, V))
+    for j in range(G):
+        for n in range(K + 1):
+            w = q[j, n] if n == K else terminal_weights(q[j, n], p[j, n])
+            np.cumsum(w, out=C[j, n])
+    Ztab = C[:, :, -1]
+
+    acc = np.full((R, B), -2, np.int32)
+    out = np.full((R, B, K + 1), -1, np.int32)
+    pad = np.full((R, B, K, 2), np.nan)
+    ratio = np.full((R, B, K), np.nan)
+    ua = np.full((R, B, K + 1), np.nan)
+    ut = np.full((R, B, K + 1), np.nan)
+    am = np.full((R, B, K), np.inf)
+    tm = np.full((R, B), np.inf)
+    zz = np.full((R, B), np.nan)
+    alpha = np.full((R, B, K), np.nan)
+    acc[:, probs.bad] = -1
+    if G == 0:
+        return SampleResult(acc, out, pad, ratio, ua, ut, am, tm, zz, alpha)
+    gi = np.arange(G)[:, None]
+    ki = np.arange(K)[None, :]
+    for r in range(R):
+        dr = d[r, good]
+        u, u2 = verify_uniforms(sd[r, good][:, None], slot[good][:, None], np.arange(K + 1)[None, :])
+        q_d = q[gi, ki, dr]
+        p_d = p[gi, ki, dr]
+        rr = accept_ratio(q_d, p_d)
+        rejected = ~(u[:, :K] < rr)
+        n = np.where(rejected.any(axis=-1), np.argmax(rejected, axis=-1), K) if K else np.zeros(G, np.int64)
+        Z = Ztab[np.arange(G), n]
+        x = u2[np.arange(G), n] * Z
+        t = np.empty(G, np.int64)
+        marg = np.empty(G)
+        for j in range(G):
+            Cj = C[j, n[j]]
+            tj = min(int(np.searchsorted(Cj, x[j], side="right")), V - 1)
+            lo = Cj[tj - 1] if tj > 0 else 0.0
+            t[j] = tj
+            marg[j] = min(x[j] - lo, Cj[tj] - x[j]) / Z[j] if Z[j] > 0 else 0.0
+        for j, b in enumerate(good):
+            out[r, b, :n[j]] = dr[j, :n[j]]
+        out[r, good, n] = t
+        acc[r, good] = n
+        ua[r, good], ut[r, good] = u, u2
+        pad[r, good] = np.stack([q_d, p_d], axis=-1)
+        ratio[r, good] = rr
+        am[r, good] = np.abs(u[:, :K] - rr)
+        tm[r, good] = marg
+        zz[r, good] = Z
+        alpha[r, good] = probs.alpha
     return SampleResult(acc, out, pad, ratio, ua, ut, am, tm, zz, alpha)
 
 

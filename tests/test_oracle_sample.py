@@ -24,6 +24,7 @@ import numpy as np
 import pytest
 from scipy import special, stats
 
+import oracle.verify as ov
 from oracle.verify import (accept_ratio, accept_sample, expected_tokens,
                            expected_tokens_positional, inverse_cdf, terminal_weights)
 
@@ -299,3 +300,27 @@ def test_inverse_cdf_never_draws_zero_weight():
     grid = np.arange(2 ** 12) / 2 ** 12          # includes 0 and exact steps
     t, _, _ = inverse_cdf(np.broadcast_to(w, (len(grid), len(w))), grid)
     assert np.all(w[t] > 0)
+
+
+@pytest.mark.parametrize("K", [0, 1, 4])
+def test_rounds_form_equals_round_by_round(K):
+    """accept_sample_rounds (terminal CDFs formed once, draws looked up) gives
+    field for field what accept_sample_probs gives round by round, faulted
+    rows, residuals without mass and bonus draws included."""
+    rng = np.random.default_rng(40 + K)
+    B, V, T, R = 7, 300, 0.8, 12
+    z = rng.normal(0, 2, (B, K + 1, V))
+    zd = z[:, :K] + rng.normal(0, 0.7, (B, K, V))
+    if K:
+        zd[1] = z[1, :K]                       # p = q: every draft accepted, bonus draws
+        zd[2, 0, :] = z[2, 0, :]               # residual without mass at position 0
+    z[3, 0, 5] = np.nan                        # a faulted row
+    d = rng.integers(0, V, (R, B, K))
+    seeds = rng.integers(0, 2**63, (R, B)).astype(np.uint64)
+    probs = ov.sample_probs(z, zd, d[0], T, rows=[0, 1, 2, 3, 4, 6])
+    got = ov.accept_sample_rounds(probs, d, seeds)
+    for r in range(R):
+        want = ov.accept_sample_probs(probs, d[r], seeds[r])
+        for f in ("accepted_len", "out_tokens", "probs_at_draft", "ratio", "u_accept", "u_terminal",
+                  "accept_margin", "terminal_margin", "residual_mass", "alpha"):
+            np.testing.assert_array_equal(getattr(got, f)[r], getattr(want, f), err_msg="%s round %d" % (f, r))
