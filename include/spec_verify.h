@@ -108,12 +108,15 @@ typedef enum spec_status {
     SPEC_ERR_DTYPE = 2,      /* unsupported element type */
     SPEC_ERR_ALIGN = 3,      /* a pointer is not 16-byte aligned */
     SPEC_ERR_WORKSPACE = 4,  /* workspace NULL or smaller than spec_workspace_bytes() */
-    SPEC_ERR_HIP = 5         /* a HIP call or kernel launch failed */
+    SPEC_ERR_HIP = 5,        /* a HIP call or kernel launch failed */
+    SPEC_STATUS_MAX_ENUM = 0x7fffffff   /* not a status: makes every non-negative int a value
+                                           of the type, so an unknown code is well defined */
 } spec_status_t;
 
 typedef enum spec_dtype {
     SPEC_BF16 = 0,           /* bfloat16, storage as uint16 bit patterns */
-    SPEC_F32 = 1             /* IEEE binary32 */
+    SPEC_F32 = 1,            /* IEEE binary32 */
+    SPEC_DTYPE_MAX_ENUM = 0x7fffffff    /* not a type: as above (rejected with SPEC_ERR_DTYPE) */
 } spec_dtype_t;
 
 /* A hipStream_t.  NULL selects the null stream of the current device. */

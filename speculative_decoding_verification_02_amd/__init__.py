@@ -41,7 +41,9 @@ __all__ = [
 ]
 
 PKG_DIR = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(PKG_DIR, "libspecverify.so")
+# the in-tree build; SPECVERIFY_LIBRARY names another build of the same
+# sources (the host-sanitized copy the CPU tests load)
+LIB_PATH = os.environ.get("SPECVERIFY_LIBRARY") or os.path.join(PKG_DIR, "libspecverify.so")
 HEADER_PATH = os.path.join(os.path.dirname(PKG_DIR), "include", "spec_verify.h")
 
 SPEC_OK, SPEC_ERR_ARG, SPEC_ERR_DTYPE, SPEC_ERR_ALIGN, SPEC_ERR_WORKSPACE, SPEC_ERR_HIP = range(6)

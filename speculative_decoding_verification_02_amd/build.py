@@ -49,5 +49,36 @@ def build(verbose: bool = False) -> str:
     return LIB_PATH
 
 
+def sanitized_command(out: str) -> list[str]:
+    """The same library with AddressSanitizer and UndefinedBehaviorSanitizer
+    on its host code only (argument checks, workspace layout, launch set-up):
+    every -fsanitize= goes to the host pass (-Xarch_host), the device code is
+    built as usual."""
+    srcs = sorted(glob.glob(os.path.join(CSRC, "*.hip")))
+    return [hipcc(), f"--offload-arch={ARCH}", "-O1", "-g", "-std=c++17", "-fPIC", "-shared",
+            "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+            "-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+            "-Xarch_host", "-fno-sanitize-recover=undefined", "-Xarch_host", "-shared-libasan",
+            *srcs, "-o", out]
+
+
+def asan_runtime() -> str:
+    """Path of the shared AddressSanitizer runtime of the HIP toolchain (to
+    preload into a process that loads the sanitized library)."""
+    pats = glob.glob("/opt/rocm/llvm/lib/clang/*/lib/linux/libclang_rt.asan-x86_64.so")
+    if not pats:
+        raise RuntimeError("no libclang_rt.asan-x86_64.so under /opt/rocm/llvm")
+    return sorted(pats)[-1]
+
+
+def build_sanitized(out: str) -> str:
+    """Compile the host-sanitized library to `out` and return its path."""
+    cmd = sanitized_command(out)
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        raise RuntimeError("building the sanitized library failed:\n%s\n%s" % (" ".join(cmd), res.stderr[-8000:]))
+    return out
+
+
 if __name__ == "__main__":
     print(build(verbose=True))

@@ -517,6 +517,7 @@ const char* spec_status_string(spec_status_t status) {
         case SPEC_ERR_ALIGN: return "SPEC_ERR_ALIGN: pointer not 16-byte aligned";
         case SPEC_ERR_WORKSPACE: return "SPEC_ERR_WORKSPACE: workspace missing or too small";
         case SPEC_ERR_HIP: return "SPEC_ERR_HIP: HIP call or kernel launch failed";
+        default: break;
     }
     return "unknown spec_status_t";
 }
