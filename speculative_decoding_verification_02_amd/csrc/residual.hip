@@ -46,18 +46,19 @@ __device__ __forceinline__ float term_weight(float zt, float zd, const TermNorm&
     return fmaxf(q - p, 0.f);
 }
 
-// The thread's weights of one chunk, in the coalesced order of the statistics
-// pass: element (q * kStatThreads + tid) * 4 + e of the chunk.  VEC (V % 4 ==
+// The thread's PER weights of one chunk of PER * kStatThreads entries, in the
+// coalesced order of the statistics pass: element (q * kStatThreads + tid) * 4
+// + e of the chunk.  VEC (V % 4 ==
 // 0): 128-bit loads, else 32-bit ones; USE_Q: the target row only.  No load
 // sits in a branch (entries past V read an in-range address and get weight
 // 0), so all of a thread's loads are in flight together.
-template <bool VEC, bool USE_Q>
+template <bool VEC, bool USE_Q, int PER>
 __device__ __forceinline__ void chunk_weights_impl(const float* __restrict__ zt_row, const float* __restrict__ zd_row,
                                                    int v_begin, int V, int tid, const TermNorm& tn, float c,
-                                                   float w[kStatPerThread]) {
-    float zt[kStatPerThread], zd[kStatPerThread];
+                                                   float w[PER]) {
+    float zt[PER], zd[PER];
 #pragma unroll
-    for (int q = 0; q < kStatPerThread / 4; ++q) {
+    for (int q = 0; q < PER / 4; ++q) {
         const int v = v_begin + (q * kStatThreads + tid) * 4;
         if constexpr (VEC) {
             const int vc = min(v, V - 4);
@@ -77,7 +78,7 @@ __device__ __forceinline__ void chunk_weights_impl(const float* __restrict__ zt_
         }
     }
 #pragma unroll
-    for (int k = 0; k < kStatPerThread; ++k) {
+    for (int k = 0; k < PER; ++k) {
         // computed for every entry (past V from a valid duplicate), then masked
         const int v = v_begin + ((k >> 2) * kStatThreads + tid) * 4 + (k & 3);
         const float tw = term_weight(zt[k], USE_Q ? 0.f : zd[k], tn, c, USE_Q);
@@ -85,16 +86,17 @@ __device__ __forceinline__ void chunk_weights_impl(const float* __restrict__ zt_
     }
 }
 
+template <int PER = kStatPerThread>
 __device__ __forceinline__ void chunk_weights(const float* __restrict__ zt_row, const float* __restrict__ zd_row,
                                               int v_begin, int V, bool vec, int tid, const AcceptInfo& a, float c,
-                                              bool use_q, float w[kStatPerThread]) {
+                                              bool use_q, float w[PER]) {
     const TermNorm tn = term_norm(a);
     if (vec) {
-        if (use_q) chunk_weights_impl<true, true>(zt_row, zd_row, v_begin, V, tid, tn, c, w);
-        else chunk_weights_impl<true, false>(zt_row, zd_row, v_begin, V, tid, tn, c, w);
+        if (use_q) chunk_weights_impl<true, true, PER>(zt_row, zd_row, v_begin, V, tid, tn, c, w);
+        else chunk_weights_impl<true, false, PER>(zt_row, zd_row, v_begin, V, tid, tn, c, w);
     } else {
-        if (use_q) chunk_weights_impl<false, true>(zt_row, zd_row, v_begin, V, tid, tn, c, w);
-        else chunk_weights_impl<false, false>(zt_row, zd_row, v_begin, V, tid, tn, c, w);
+        if (use_q) chunk_weights_impl<false, true, PER>(zt_row, zd_row, v_begin, V, tid, tn, c, w);
+        else chunk_weights_impl<false, false, PER>(zt_row, zd_row, v_begin, V, tid, tn, c, w);
     }
 }
 
@@ -147,11 +149,13 @@ __device__ __forceinline__ void chunk_prefix(const float* src, int nc, int lane,
 // Inverse-CDF selection of the terminal token of one sequence, by the block
 // that finished last among the sequence's chunk blocks.  chunk_sums holds the
 // per-chunk weight sums published by all of them (read back with atomics).
+template <int PER = kStatPerThread>
 __device__ void select_terminal(const float* __restrict__ logits, const float* __restrict__ draft_logits,
                                 int V, int nc, float c, const AcceptInfo& a, const float* chunk_sums,
                                 int32_t* __restrict__ out_tokens, bool sums_by_atomics = true) {
-    __shared__ float pre[kMaxChunks + 1];   // prefix over chunk sums
-    __shared__ float wl[kChunk];            // weights of the selected chunk, token order
+    constexpr int CH = PER * kStatThreads;               // entries per chunk
+    __shared__ float pre[kMaxChunks * kChunk / CH + 1];  // prefix over chunk sums
+    __shared__ float wl[CH];                             // weights of the selected chunk, token order
     __shared__ float red[kStatThreads / kWave];
     __shared__ float wtot[kStatThreads / kWave];
     __shared__ int sel[2];                  // selected chunk, selected token
@@ -168,11 +172,11 @@ __device__ void select_terminal(const float* __restrict__ logits, const float* _
         // residual without mass: draw from q_n, recomputing the chunk sums
         use_q = true;
         for (int k = 0; k < nc; ++k) {
-            float w[kStatPerThread];
-            chunk_weights(tr.zt, tr.zd, k * kChunk, V, vec, tid, a, c, true, w);
+            float w[PER];
+            chunk_weights<PER>(tr.zt, tr.zd, k * CH, V, vec, tid, a, c, true, w);
             float s = 0.f;
 #pragma unroll
-            for (int e = 0; e < kStatPerThread; ++e) s += w[e];
+            for (int e = 0; e < PER; ++e) s += w[e];
             s = block_sum(s, red);
             if (tid == 0) pre[k + 1] = s;
         }
@@ -201,25 +205,25 @@ __device__ void select_terminal(const float* __restrict__ logits, const float* _
     }
     __syncthreads();
     const int cs = sel[0];
-    const int v_begin = cs * kChunk;
+    const int v_begin = cs * CH;
 
     // weights of chunk cs into LDS in token order
     {
-        float w[kStatPerThread];
-        chunk_weights(tr.zt, tr.zd, v_begin, V, vec, tid, a, c, use_q, w);
+        float w[PER];
+        chunk_weights<PER>(tr.zt, tr.zd, v_begin, V, vec, tid, a, c, use_q, w);
 #pragma unroll
-        for (int q = 0; q < kStatPerThread / 4; ++q)
+        for (int q = 0; q < PER / 4; ++q)
 #pragma unroll
             for (int e = 0; e < 4; ++e) wl[(q * kStatThreads + tid) * 4 + e] = w[4 * q + e];
     }
     __syncthreads();
 
-    // thread tid owns tokens [tid*16, tid*16+16) of the chunk
-    float mine[kStatPerThread];
+    // thread tid owns tokens [tid*PER, tid*PER+PER) of the chunk
+    float mine[PER];
     float s = 0.f;
 #pragma unroll
-    for (int e = 0; e < kStatPerThread; ++e) {
-        mine[e] = wl[tid * kStatPerThread + e];
+    for (int e = 0; e < PER; ++e) {
+        mine[e] = wl[tid * PER + e];
         s += mine[e];
     }
     // inclusive scan of the thread sums: within the wave, then across waves
@@ -237,13 +241,13 @@ __device__ void select_terminal(const float* __restrict__ logits, const float* _
         float run = excl;
         int tok = -1, lastp = -1;
 #pragma unroll
-        for (int e = 0; e < kStatPerThread; ++e) {
+        for (int e = 0; e < PER; ++e) {
             if (mine[e] > 0.f) lastp = e;
             run += mine[e];
             if (tok < 0 && run > xr && mine[e] > 0.f) tok = e;
         }
         if (tok < 0) tok = lastp;
-        sel[1] = v_begin + tid * kStatPerThread + tok;
+        sel[1] = v_begin + tid * PER + tok;
     }
     __syncthreads();
     if (sel[1] < 0) {  // block-uniform: read after the barrier
@@ -252,8 +256,8 @@ __device__ void select_terminal(const float* __restrict__ logits, const float* _
         const bool low = xr < 0.f;
         int cand = low ? INT_MAX : -1;
 #pragma unroll
-        for (int e = 0; e < kStatPerThread; ++e) {
-            const int idx = tid * kStatPerThread + e;
+        for (int e = 0; e < PER; ++e) {
+            const int idx = tid * PER + e;
             if (mine[e] > 0.f) cand = low ? min(cand, idx) : max(cand, idx);
         }
 #pragma unroll
@@ -348,6 +352,7 @@ __global__ __launch_bounds__(kStatThreads) void residual_select_kernel(
 // streams), the one of chunk 0 writes it out, each sums its chunk of the
 // terminal weights, and the last to finish selects the token as above.  The
 // completion counters are zeroed by the statistics pass that runs first.
+template <int PER>
 __global__ __launch_bounds__(kStatThreads) void accept_residual_kernel(
     const float* __restrict__ logits, const float* __restrict__ draft_logits, const int32_t* __restrict__ draft_tokens,
     const uint64_t* __restrict__ seeds, const int32_t* __restrict__ rows, SeqRows seq, int V, int nc, float c,
@@ -367,11 +372,11 @@ __global__ __launch_bounds__(kStatThreads) void accept_residual_kernel(
                                                &sinfo);
     if (a.n < 0) return;
     const TermRows tr = term_rows(logits, draft_logits, a, V);
-    float w[kStatPerThread];
-    chunk_weights(tr.zt, tr.zd, chunk * kChunk, V, (V & 3) == 0, threadIdx.x, a, c, tr.bonus, w);
+    float w[PER];
+    chunk_weights<PER>(tr.zt, tr.zd, chunk * (PER * kStatThreads), V, (V & 3) == 0, threadIdx.x, a, c, tr.bonus, w);
     float s = 0.f;
 #pragma unroll
-    for (int k = 0; k < kStatPerThread; ++k) s += w[k];
+    for (int k = 0; k < PER; ++k) s += w[k];
     s = block_sum(s, red);
     if (threadIdx.x == 0) {
         // published as in residual_kernel: an exchange whose result is waited
@@ -383,7 +388,7 @@ __global__ __launch_bounds__(kStatThreads) void accept_residual_kernel(
     }
     __syncthreads();
     if (!last) return;
-    select_terminal(logits, draft_logits, V, nc, c, a, chunk_sums + (size_t)j * nc, out_tokens);
+    select_terminal<PER>(logits, draft_logits, V, nc, c, a, chunk_sums + (size_t)j * nc, out_tokens);
 }
 
 hipError_t launch_accept_residual(const float* logits, const float* draft_logits, const int32_t* draft_tokens,
@@ -391,8 +396,11 @@ hipError_t launch_accept_residual(const float* logits, const float* draft_logits
                                   float inv_t_log2e, RecLayout rec, int32_t* accepted_len, int32_t* out_tokens,
                                   float* probs_at_draft, float* chunk_sums, int* counters, hipStream_t stream) {
     if (n_rows == 0) return hipSuccess;
-    const int nc = n_chunks(V);
-    hipLaunchKernelGGL(accept_residual_kernel, dim3((unsigned)((long)n_rows * nc)), dim3(kStatThreads), 0, stream,
+    // small chunks: every workgroup sums (and the selecting one re-reads) a
+    // quarter of a statistics chunk, one memory round trip each
+    const int nc = n_fused_chunks(V);
+    hipLaunchKernelGGL(accept_residual_kernel<kFusedPer>, dim3((unsigned)((long)n_rows * nc)), dim3(kStatThreads), 0,
+                       stream,
                        logits, draft_logits, draft_tokens, seeds, rows, seq, V, nc, inv_t_log2e, rec, accepted_len,
                        out_tokens, probs_at_draft, chunk_sums, counters);
     return hipGetLastError();

@@ -101,7 +101,9 @@ size_t workspace_layout(int B, int K, int V, void* base, Workspace* ws) {
     const size_t nc = (size_t)sv::n_chunks(V);
     const size_t stats = align256(((size_t)B * (K + 1) + (size_t)B * K) * nc * sizeof(sv::StatRec));
     const size_t info = align256((size_t)B * sizeof(sv::AcceptInfo));
-    const size_t sums = align256((size_t)B * nc * sizeof(float));
+    // residual chunk sums: one per statistics chunk, or per (smaller) chunk of
+    // the one-launch accept + residual, whichever is more
+    const size_t sums = align256((size_t)B * std::max(nc, (size_t)sv::n_fused_chunks(V)) * sizeof(float));
     const size_t counters = align256((size_t)B * sizeof(int));
     if (ws) {
         char* p = static_cast<char*>(base);

@@ -105,6 +105,10 @@ hipError_t launch_accept_both(const float* logits, const float* draft_logits, co
 // sequences x (2K+1) rows stay within this bound (measured: 17 vs 20 us at
 // one sequence with K = 5; 45 vs 35 us at 16 sequences with K = 15).
 constexpr int kFusedAcceptMaxRows = 48;
+// The one-launch accept + residual splits the terminal rows into chunks of
+// kFusedPer entries per thread (1024 entries), a quarter of a statistics chunk.
+constexpr int kFusedPer = 4;
+inline int n_fused_chunks(int V) { return (V + kFusedPer * kStatThreads - 1) / (kFusedPer * kStatThreads); }
 hipError_t launch_accept_residual(const float* logits, const float* draft_logits, const int32_t* draft_tokens,
                                   const uint64_t* seeds, const int32_t* rows, int n_rows, SeqRows seq, int V,
                                   float inv_t_log2e, RecLayout rec, int32_t* accepted_len, int32_t* out_tokens,
