@@ -174,7 +174,8 @@ def main():
     torch.cuda.set_device(dev)
     sv.load_library()
     if args.workload in synth.NGRAM_WORKLOADS:
-        bench_ngram(args, dev)
+        print(json.dumps(bench_ngram(args, dev, synth.NGRAM_WORKLOADS[args.workload],
+                                     cpu=not args.no_cpu_baseline, steps=args.steps)), flush=True)
         return
     res = measure(synth.WORKLOADS[args.workload], args, dev, args.steps, args.warmup,
                   cpu=not args.no_cpu_baseline, record_rounds=512)
@@ -188,11 +189,23 @@ def main():
                                                "step_roofline", "roofline", "path")})
             torch.cuda.empty_cache()
         res["other_configs"] = others
+        # the rows built beyond the five workloads: long blocks, per-sequence
+        # draft counts, draft trees, and the prompt-lookup drafter
+        widened = []
+        for name in WIDENED:
+            r = measure(synth.WORKLOADS[name], args, dev, min(args.steps, 10), 3, cpu=False)
+            widened.append({k: r[k] for k in ("config", "ms_per_step", "value", "unit", "step_us_median",
+                                               "step_roofline", "roofline", "path")})
+            torch.cuda.empty_cache()
+        r = bench_ngram(args, dev, synth.NGRAM_WORKLOADS["ngram_b256_l131072"], cpu=False, steps=min(args.steps, 20))
+        widened.append({k: r[k] for k in ("config", "ms_per_step", "value", "unit", "step_us_median", "roofline")})
+        res["widened_rows"] = widened
     print(json.dumps(res), flush=True)
 
 
 HEADLINE = "b1_k5_h4096_v128256"
 OTHER_CONFIGS = ("b64_k4_h4096_v128256", "b256_k8_h8192_v152064", "b512_k3_h5120_v262144")
+WIDENED = ("b32_k15_h4096_v151936", "b64_k0to7_h4096_v128256", "b8_tree63_h4096_v128256")
 
 
 def measure(wl, args, dev, n_steps, n_warmup, cpu=False, record_rounds=0):
@@ -572,7 +585,7 @@ def cpu_baseline(wl, W, hidden, zd, drafts, smask, budget_s, rs=None, parents=No
     return out
 
 
-def bench_ngram(args, dev):
+def bench_ngram(args, dev, wl, cpu=True, steps=50):
     """The prompt-lookup drafter on its own: one step = one
     spec_ngram_propose call over every history of the workload."""
     import torch
@@ -580,7 +593,6 @@ def bench_ngram(args, dev):
     import speculative_decoding_verification_02_amd as sv
     import synth
 
-    wl = synth.NGRAM_WORKLOADS[args.workload]
     print("bench: %s, generating histories" % wl.name, file=sys.stderr, flush=True)
     hist = synth.histories(wl.B, wl.L, wl.V, wl.data_seed, wl.copy_frac)
     starts = np.concatenate([[0], np.cumsum([len(h) for h in hist])]).astype(np.int64)
@@ -607,11 +619,11 @@ def bench_ngram(args, dev):
         step(i)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for i in range(args.steps):
+    for i in range(steps):
         step(i)
     torch.cuda.synchronize()
-    step_s = (time.perf_counter() - t0) / args.steps
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    step_s = (time.perf_counter() - t0) / steps
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
     for i, (a, b) in enumerate(evs):
         a.record(stream)
         step(i)
@@ -629,14 +641,14 @@ def bench_ngram(args, dev):
                       "last-level cache) between calls" % (set_bytes / 1e6, n_copies, n_copies * set_bytes / 1e6)}
     roof["frac"] = roof["achieved"] / roof["peak"]
     res = {"metric": "history tokens scanned/s (prompt-lookup drafter)", "value": n_tok / step_s,
-           "unit": "tokens/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+           "unit": "tokens/s", "n_gpus": 1, "steps": steps, "warmup": args.warmup,
            "ms_per_step": step_s * 1e3, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
            "dtype": "int32", "data": "synthetic",
            "config": {"workload": wl.name, "B": wl.B, "max_len": max_len, "tokens": n_tok, "V": wl.V,
                       "max_ngram": wl.max_ngram, "n_drafts": wl.n_drafts},
            "step_us_median": float(np.median(call_us)), "step_us_p90": float(np.percentile(call_us, 90)),
            "mean_drafts": float(count.float().mean().item()), "roofline": roof}
-    if not args.no_cpu_baseline:
+    if cpu:
         import oracle
         t0 = time.perf_counter()
         n = 0
@@ -649,7 +661,7 @@ def bench_ngram(args, dev):
         scanned = sum(len(h) for h in hist[:n])
         res["cpu_baseline"] = {"value": scanned / t, "unit": "tokens/s", "cores": 1, "kind": "oracle",
                                "sample": "%d of the %d histories (%d tokens), one thread (numpy)" % (n, wl.B, scanned)}
-    print(json.dumps(res), flush=True)
+    return res
 
 
 def synth_seeds(wl, r):
