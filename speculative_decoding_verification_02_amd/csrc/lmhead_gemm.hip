@@ -43,6 +43,21 @@ __device__ __forceinline__ u32x4 load_stream(const uint16_t* p) {
     return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
 }
 
+// Raw buffer resource over `bytes` bytes from `base` (stride 0; the fourth
+// word sets the 32-bit data format a raw load needs to be valid).  A load
+// whose per-lane byte offset is at or past `bytes` returns zero and does not
+// access memory.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const uint16_t* base, unsigned bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(base), 0, (int)bytes, 0x00020000);
+}
+constexpr unsigned kOutOfRange = 0xFFFFFFF0u;   // past any resource built here (16 rows of at most 8 KB)
+
+// 16 bytes at byte offset `off` of the resource, non-temporal (the whole
+// offset is the range-checked per-lane offset; the scalar offset is 0)
+__device__ __forceinline__ u32x4 load_stream_buf(__amdgpu_buffer_rsrc_t rs, unsigned off) {
+    return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, 2));
+}
+
 __device__ __forceinline__ void store_row4(float* __restrict__ out, int v, int V, f32x4 acc, bool vec_ok) {
     if (vec_ok && v + 3 < V) {
         *reinterpret_cast<float4*>(out + v) = make_float4(acc[0], acc[1], acc[2], acc[3]);
@@ -215,16 +230,26 @@ hipError_t launch_skinny(const uint16_t* hidden, const uint16_t* W, float* logit
 // order (fixed order: bitwise reproducible).  Loads run one tile ahead: while
 // stage st of tile t is consumed, stage st of the next tile is issued.  Each
 // workgroup takes a contiguous, balanced range of tiles, so it streams one
-// contiguous region of W and its output rows fill whole cache lines.
+// contiguous region of W.
 //
-// With STATS the kernel also writes softmax statistics records (see
-// CoopStats) over each workgroup's vocabulary range.  The wave that sums a
-// tile also keeps its logits in LDS (one 16-byte write per lane, nothing on
-// the tile's critical path).  The draft rows' entries are loaded at the
-// start, ahead of W, and written next to them after the last tile.  Then one
-// 32-lane group per row reduces its row from LDS: max, first index of the
-// max, sum of 2^((z - max) c).  No per-entry checks: a NaN or +inf shows in
-// the maximum or the sum and marks the record bad.
+// The weight loads are buffer loads, exactly kLoads per stage with no branch
+// around them: the vector-memory counter of gfx9 counts in issue order, and
+// only when the compiler can count the loads issued after the ones a stage
+// needs can it wait for those alone (with a load skipped on some path, or a
+// store between them, it must wait for every load in flight, and the next
+// tile's loads would never overlap this tile's work).  For the same reason
+// the loop stores nothing to memory: with STASH the wave that sums a tile
+// keeps its logits in LDS, and the workgroup writes its rows out after the
+// last tile, one contiguous run per row.  Without STASH (a vocabulary range
+// too long for LDS) it stores each tile's logits as it goes.
+//
+// With STATS (which needs STASH) the kernel also writes softmax statistics
+// records (see CoopStats) over each workgroup's vocabulary range.  The draft
+// rows' entries are loaded at the start, ahead of W, and written next to the
+// logits after the last tile.  Then one 32-lane group per row reduces its
+// row from LDS: max, first index of the max, sum of 2^((z - max) c).  No
+// per-entry checks: a NaN or +inf shows in the maximum or the sum and marks
+// the record bad.
 template <int RPL, int MAXST, int NW>
 struct Coop {
     static constexpr int kLanesPerRow = 64 / RPL;
@@ -237,10 +262,9 @@ struct Coop {
     static constexpr int kThreads = NW * 64;
     static constexpr size_t kLdsBase = (size_t)NW * kBufChunks * 16 + 2 * (size_t)NW * 64 * 16;
     static size_t lds_bytes() { return kLdsBase; }
-    // LDS with the statistics stash: M target and n_draft draft rows, each
-    // as long as the most columns a workgroup owns (whole tiles of 16) plus
-    // 16 floats, which puts the two rows a wavefront reads at once 16 banks
-    // apart
+    // LDS with the stash: M target and n_draft draft rows, each as long as
+    // the most columns a workgroup owns (whole tiles of 16) plus 16 floats,
+    // which puts the two rows a wavefront reads at once 16 banks apart
     static int stash_stride(int n_tiles, int grid) { return ((n_tiles + grid - 1) / grid) * 16 + 16; }
     static size_t lds_bytes_stats(int n_tiles, int grid, int rows) {
         return lds_bytes() + (size_t)rows * stash_stride(n_tiles, grid) * sizeof(float);
@@ -269,11 +293,12 @@ __device__ __forceinline__ void coop_fold(StatRec& a, const float (&z)[N], int v
     stat_fold(a, bm, bs, bi, (bs != bs) | (bm == INFINITY), c);
 }
 
-template <int RPL, int MAXST, int NW, bool STATS>
+template <int RPL, int MAXST, int NW, bool STATS, bool STASH>
 __global__ __launch_bounds__(NW * 64) void lmhead_coop_bf16(
     const uint16_t* __restrict__ hidden, const uint16_t* __restrict__ W, float* __restrict__ logits,
     int M, int V, int H, int n_tiles, CoopStats cs) {
     using S = Coop<RPL, MAXST, NW>;
+    static_assert(STASH || !STATS, "the statistics are taken from the stash");
     extern __shared__ __align__(16) unsigned char smem[];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     u32x4* buf = reinterpret_cast<u32x4*>(smem) + wave * S::kBufChunks;
@@ -296,20 +321,28 @@ __global__ __launch_bounds__(NW * 64) void lmhead_coop_bf16(
                 (r < M && k < H) ? *reinterpret_cast<const u32x4*>(hidden + (size_t)r * H + k) : zero;
         }
 
-    auto issue = [&](int t, int st, u32x4 (&dst)[S::kLoads]) {
-        const int k = k_lo + st * S::kKS + lc * 8;
-        const bool ok = t < n_tiles && st < n_st && k < H;
-        const int v0 = t << 4;
-#pragma unroll
-        for (int q = 0; q < S::kLoads; ++q) {
-            const int row = min(v0 + q * RPL + la, V - 1);
-            dst[q] = ok ? load_stream(W + (size_t)row * H + k) : zero;
-        }
-    };
-
     // this workgroup's tiles: a contiguous, balanced range [t_begin, t_end)
     const int t_begin = (int)(((long)n_tiles * blockIdx.x) / gridDim.x);
     const int t_end = (int)(((long)n_tiles * (blockIdx.x + 1)) / gridDim.x);
+
+    // The loads of stage st of tile t: the buffer resource spans the tile's
+    // rows below V (none for a tile at or past t_end), and the whole offset
+    // is the range-checked per-lane offset, so a row past the resource reads
+    // zero without touching memory; so does a column past H, whose offset is
+    // set beyond any resource.  A stage past this wave's slice (H < NW *
+    // SLICE) loads and is not used.
+    auto issue = [&](int t, int st, u32x4 (&dst)[S::kLoads]) {
+        const int k = k_lo + st * S::kKS + lc * 8;
+        const int v0 = t << 4;
+        const int rows = t < t_end ? min(16, V - v0) : 0;
+        const __amdgpu_buffer_rsrc_t rs = make_rsrc(W + (size_t)(t < t_end ? v0 : 0) * H, (unsigned)(rows * H * 2));
+        const unsigned vo = (unsigned)(la * H + k) * 2u;
+#pragma unroll
+        for (int q = 0; q < S::kLoads; ++q) {
+            const unsigned o = k < H ? vo + (unsigned)(q * RPL * H * 2) : kOutOfRange;
+            dst[q] = load_stream_buf(rs, o);
+        }
+    };
 
     // draft row `wave` over this workgroup's vocabulary range: the first
     // kDraftPer * 64 entries are loaded now, ahead of W, and reduced after
@@ -331,27 +364,36 @@ __global__ __launch_bounds__(NW * 64) void lmhead_coop_bf16(
 
     u32x4 pipe[MAXST][S::kLoads];
 #pragma unroll
-    for (int st = 0; st < MAXST; ++st) issue(t_begin < t_end ? t_begin : n_tiles, st, pipe[st]);
+    for (int st = 0; st < MAXST; ++st) {
+        issue(t_begin, st, pipe[st]);
+        // issue order kept: the loop waits for stage 0 with stage 1 in flight
+        __builtin_amdgcn_sched_barrier(0);
+    }
 
-    // logits of this workgroup's tiles, [row][column - dcb], kept for the
-    // statistics (STATS only; sized by the launcher)
+    // logits of this workgroup's tiles, [row][column - dcb] (STASH only;
+    // sized by the launcher)
     float* stash = reinterpret_cast<float*>(smem + S::kLdsBase);   // [M + n_draft][stash_cols]
     const int stash_cols = ((n_tiles + (int)gridDim.x - 1) / (int)gridDim.x) * 16 + 16;
 
     const bool vec_ok = (V & 3) == 0;
     for (int t = t_begin, it = 0; t < t_end; ++t, ++it) {
-        const int tn = t + 1 < t_end ? t + 1 : n_tiles;   // next tile (n_tiles: nothing to load)
         f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int st = 0; st < MAXST; ++st) {
-            if (st < n_st) {
+            const bool live = st < n_st;   // this wave's slice reaches stage st
+            if (live) {
+                // columns past H are zeroed (their hidden values are zero too,
+                // but the bytes loaded there may be anything)
+                const bool k_in = k_lo + st * S::kKS + lc * 8 < H;
 #pragma unroll
                 for (int q = 0; q < S::kLoads; ++q) {
                     const int R = q * RPL + la;
-                    buf[R * S::kCPR + (lc ^ (R % S::kCPR))] = pipe[st][q];
+                    buf[R * S::kCPR + (lc ^ (R % S::kCPR))] = k_in ? pipe[st][q] : zero;
                 }
-                __builtin_amdgcn_wave_barrier();
-                issue(tn, st, pipe[st]);
+            }
+            __builtin_amdgcn_wave_barrier();
+            issue(t + 1, st, pipe[st]);
+            if (live) {
 #pragma unroll
                 for (int j = 0; j < S::kSteps; ++j) {
                     const int c = j * 4 + g;
@@ -359,8 +401,8 @@ __global__ __launch_bounds__(NW * 64) void lmhead_coop_bf16(
                     acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(wv), as_bf16x8(hreg[st * S::kSteps + j]),
                                                                   acc, 0, 0, 0);
                 }
-                __builtin_amdgcn_wave_barrier();
             }
+            __builtin_amdgcn_wave_barrier();
         }
         // cross-wave sum of the tile's partial accumulators, in wave order
         f32x4* rb = red + (it & 1) * NW * 64;
@@ -371,15 +413,32 @@ __global__ __launch_bounds__(NW * 64) void lmhead_coop_bf16(
 #pragma unroll
             for (int w = 1; w < NW; ++w) s += rb[w * 64 + lane];
             const int v0 = (t << 4) + 4 * g;
-            if (r < M) store_row4(logits + (size_t)r * V, v0, V, s, vec_ok);
-            if constexpr (STATS) {
-                if (r < M) {
+            if (r < M) {
+                if constexpr (STASH) {
                     f32x4 z = s;
 #pragma unroll
                     for (int i = 0; i < 4; ++i)
                         if (v0 + i >= V) z[i] = -INFINITY;
                     *reinterpret_cast<f32x4*>(stash + r * stash_cols + (v0 - dcb)) = z;
+                } else {
+                    store_row4(logits + (size_t)r * V, v0, V, s, vec_ok);
                 }
+            }
+        }
+    }
+
+    if constexpr (STASH) {
+        // this workgroup's logits, one contiguous run per row
+        __syncthreads();   // every tile's logits are in the stash
+        const int n = dce - dcb;
+        for (int row = wave; row < M; row += NW) {
+            const float* src = stash + row * stash_cols;
+            float* dst = logits + (size_t)row * V + dcb;
+            if (vec_ok) {   // dcb and n are multiples of 4 when V is
+                for (int k = lane * 4; k < n; k += 256)
+                    *reinterpret_cast<f32x4*>(dst + k) = *reinterpret_cast<const f32x4*>(src + k);
+            } else {
+                for (int k = lane; k < n; k += 64) dst[k] = src[k];
             }
         }
     }
@@ -462,14 +521,19 @@ inline int coop_grid(int V, int num_cus, bool stats) {
     return stats ? min(g, kCoopMaxRecs) : g;
 }
 
+// The logits go through the stash whenever it fits in LDS (always with the
+// statistics; their launcher checks that first).
 template <int RPL, int MAXST, int NW, bool STATS>
 hipError_t launch_coop(const uint16_t* hidden, const uint16_t* W, float* logits, int M, int V, int H, int num_cus,
                        hipStream_t stream, CoopStats st = CoopStats{}) {
     using S = Coop<RPL, MAXST, NW>;
-    auto kern = lmhead_coop_bf16<RPL, MAXST, NW, STATS>;
     const int n_tiles = (V + 15) / 16;
     const int grid = coop_grid(V, num_cus, STATS);
-    const size_t lds = STATS ? S::lds_bytes_stats(n_tiles, grid, M + st.n_draft) : S::lds_bytes();
+    const size_t lds_stash = S::lds_bytes_stats(n_tiles, grid, M + (STATS ? st.n_draft : 0));
+    const bool stash = STATS || lds_stash <= 160 * 1024;
+    auto kern = !stash ? lmhead_coop_bf16<RPL, MAXST, NW, false, false>
+                       : lmhead_coop_bf16<RPL, MAXST, NW, STATS, true>;
+    const size_t lds = stash ? lds_stash : S::lds_bytes();
     if (lds > 160 * 1024) return hipErrorInvalidValue;
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);

@@ -48,6 +48,15 @@ def test_bf16_small_m(B, K, H, V):
     _check(h, W)
 
 
+@pytest.mark.parametrize("B,K", [(1, 0), (4, 3)])
+def test_bf16_small_m_long_vocabulary(B, K):
+    """A vocabulary range per workgroup too long for the logits to wait in LDS
+    at M = 16 (the cooperative kernel stores each tile as it goes), and at
+    M = 1 still short enough (it writes them out after the last tile)."""
+    W, h = _case(B, K, 264, 400003, "bf16", 0.02, seed=B + 400003)
+    _check(h, W)
+
+
 @pytest.mark.parametrize("B,K,H,V", [(1, 0, 8192, 3001), (2, 1, 6144, 4099), (1, 3, 4104, 130)])
 def test_bf16_small_m_wide_hidden(B, K, H, V):
     """M <= 16 with a hidden size beyond the register-resident slices of the
