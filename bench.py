@@ -107,6 +107,21 @@ def _counter_rows(path, counter):
     return out
 
 
+# position of the statistics flag among each LM-head kernel's template
+# arguments (cooperative <RPL, MAXST, NW, STATS, STASH>; direct-to-LDS
+# <BK, SLOTS, NA, NB, STATS, NW, HS>)
+_STATS_ARG = {"lmhead_coop_bf16": 3, "lmhead_big_bf16": 4}
+
+
+def _stats_variant(name):
+    base = name.split("(")[0]
+    for k, i in _STATS_ARG.items():
+        if k in base and "<" in base:
+            args = [a.strip() for a in base[base.index("<") + 1:base.rindex(">")].split(",")]
+            return len(args) > i and args[i] == "true"
+    return False
+
+
 def ingest_traffic(args):
     """HBM bytes per launch of the LM-head kernel from FETCH_SIZE / WRITE_SIZE
     (KiB per dispatch), each scaled so that the calibration copy of known size
@@ -128,7 +143,7 @@ def ingest_traffic(args):
     is_copy = lambda n: "copyBuffer" in n
     # the LM-head launches without the statistics option: the ones the
     # event-timed loop measures (the fused step runs the other variant)
-    is_gemm = lambda n: "sv::lmhead" in n and "true" not in n.split("(")[0]
+    is_gemm = lambda n: "sv::lmhead" in n and not _stats_variant(n)
 
     def calib(rows):
         vals = sorted((v for n, v in rows if is_copy(n)), reverse=True)[:3]

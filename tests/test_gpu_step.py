@@ -101,6 +101,7 @@ def _wl(B, K, H, V, dtype="bf16", T=0.9, seed=7):
     (1, 15, 256, 3001, "bf16", "cooperative, K=15 (31 rows: staged merge)"),
     (16, 0, 256, 1000, "bf16", "cooperative, K=0 (bonus draws only)"),
     (2, 3, 256, 262147, "bf16", "cooperative, 64+ tiles per workgroup (rows reduced in several passes)"),
+    (1, 5, 264, 600001, "bf16", "cooperative logits, statistics pass (the rows do not fit in LDS)"),
     (2, 3, 64, 37, "bf16", "cooperative, V=37: three workgroups, partial tile, odd row length"),
     (1, 1, 64, 1, "bf16", "cooperative, V=1: one entry per row"),
     (4, 15, 256, 102400, "bf16", "direct-to-LDS, K=15, epilogue records folded to chunks"),
