@@ -246,10 +246,11 @@ hipError_t launch_skinny(const uint16_t* hidden, const uint16_t* W, float* logit
 // With STATS (which needs STASH) the kernel also writes softmax statistics
 // records (see CoopStats) over each workgroup's vocabulary range.  The draft
 // rows' entries are loaded at the start, ahead of W, and written next to the
-// logits after the last tile.  Then one 32-lane group per row reduces its
-// row from LDS: max, first index of the max, sum of 2^((z - max) c).  No
-// per-entry checks: a NaN or +inf shows in the maximum or the sum and marks
-// the record bad.
+// logits' rows before the first tile (with the -inf padding of the target
+// rows), so after the last tile one barrier leaves the stash complete.  Then
+// one 32-lane group per row reduces its row from LDS: max, first index of
+// the max, sum of 2^((z - max) c).  No per-entry checks: a NaN or +inf shows
+// in the maximum or the sum and marks the record bad.
 template <int RPL, int MAXST, int NW>
 struct Coop {
     static constexpr int kLanesPerRow = 64 / RPL;
@@ -374,6 +375,25 @@ __global__ __launch_bounds__(NW * 64) void lmhead_coop_bf16(
     // sized by the launcher)
     float* stash = reinterpret_cast<float*>(smem + S::kLdsBase);   // [M + n_draft][stash_cols]
     const int stash_cols = ((n_tiles + (int)gridDim.x - 1) / (int)gridDim.x) * 16 + 16;
+    if constexpr (STATS) {
+        // before the tiles: the target rows' columns past this workgroup's
+        // tiles (-inf) and the draft rows (row `wave`'s first entries from the
+        // registers loaded above, the oldest loads in flight)
+        const int span = stash_cols - 16, n = dce - dcb;
+        for (int row = wave; row < M; row += NW)
+            for (int k = (t_end - t_begin) * 16 + lane; k < span; k += 64) stash[row * stash_cols + k] = -INFINITY;
+        for (int d = wave; d < cs.n_draft; d += NW) {
+            const float* drow = cs.draft + (size_t)d * V + dcb;
+            float* dst = stash + (M + d) * stash_cols;
+            for (int k0 = 0; k0 < span; k0 += kDraftPer * 64) {
+#pragma unroll
+                for (int j = 0; j < kDraftPer; ++j) {
+                    const int k = k0 + j * 64 + lane;
+                    if (k < span) dst[k] = k >= n ? -INFINITY : (d == wave && k0 == 0 ? dz[j] : drow[k]);
+                }
+            }
+        }
+    }
 
     const bool vec_ok = (V & 3) == 0;
     for (int t = t_begin, it = 0; t < t_end; ++t, ++it) {
@@ -444,25 +464,9 @@ __global__ __launch_bounds__(NW * 64) void lmhead_coop_bf16(
     }
 
     if constexpr (STATS) {
-        // Rows are reduced over span = stash_cols - 16 columns, -inf past
-        // this workgroup's range: the target rows' columns past its tiles,
-        // and draft row d (stash row M + d) written here, row `wave` from
-        // the registers loaded at the start.
-        const int span = stash_cols - 16, n = dce - dcb;
-        for (int row = wave; row < M; row += NW)
-            for (int k = (t_end - t_begin) * 16 + lane; k < span; k += 64) stash[row * stash_cols + k] = -INFINITY;
-        for (int d = wave; d < cs.n_draft; d += NW) {
-            const float* drow = cs.draft + (size_t)d * V + dcb;
-            float* dst = stash + (M + d) * stash_cols;
-            for (int k0 = 0; k0 < span; k0 += kDraftPer * 64) {
-#pragma unroll
-                for (int j = 0; j < kDraftPer; ++j) {
-                    const int k = k0 + j * 64 + lane;
-                    if (k < span) dst[k] = k >= n ? -INFINITY : (d == wave && k0 == 0 ? dz[j] : drow[k]);
-                }
-            }
-        }
-        __syncthreads();   // the stash is complete
+        // rows reduced over span = stash_cols - 16 columns (the stash is
+        // complete after the barrier above)
+        const int span = stash_cols - 16;
         // one 32-lane group per row (target rows 0..M-1, then the draft
         // rows); lane l holds columns 4l + 128j + i, ascending in (j, i)
         const int l32 = lane & 31;
