@@ -853,17 +853,24 @@ __global__ __launch_bounds__(NW * 64, 1) void lmhead_big_bf16(
         __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(src(q, slice)),
                                          (__attribute__((address_space(3))) void*)dst, 16, 0, 0);
     };
-    auto frag = [&](int slice, int ks, bf16x8 (&xa)[NA], bf16x8 (&xb)[NB]) {
+    // fragments of k-step ks of a slice: the NA weight ones, and hidden one b
+    auto frag_a = [&](int slice, int ks, bf16x8 (&xa)[NA]) {
         const u32x4* lw = wslot(slice);
-        const u32x4* lh = hslot(slice);
         const int ch = ks * 2 + h;
 #pragma unroll
         for (int a = 0; a < NA; ++a) xa[a] = as_bf16x8(lw[G::pos(wn + a * 32 + r, ch)]);
-#pragma unroll
-        for (int b = 0; b < NB; ++b) xb[b] = as_bf16x8(lh[G::pos(wm + b * 32 + r, ch)]);
+    };
+    auto frag_b = [&](int slice, int ks, int b) {
+        return as_bf16x8(hslot(slice)[G::pos(wm + b * 32 + r, ks * 2 + h)]);
     };
 
-    bf16x8 fa[2][NA], fb[2][NB];
+    // The weight fragments are double-buffered (every product of a k-step
+    // uses them); the hidden ones are not: a k-step runs its products
+    // b-major, hidden fragment b is dead after its NA products, and the next
+    // k-step's fragment b is read into its registers right then.  (With both
+    // double-buffered the 320-row tile spilled registers, and each reload was
+    // a vector-memory load the loop had to wait for behind every DMA.)
+    bf16x8 fa[2][NA], fb[NB];
     // prologue and loop of a wave whose loads run SL slices deep
     auto run = [&](auto sl_tag) {
         constexpr int SL = decltype(sl_tag)::value;
@@ -878,7 +885,9 @@ __global__ __launch_bounds__(NW * 64, 1) void lmhead_big_bf16(
         wait_slices<G::kLoads, SL - 2>(min(SL - 2, nk - 1));
         __builtin_amdgcn_s_barrier();
         asm volatile("" ::: "memory");
-        frag(0, 0, fa[0], fb[0]);
+        frag_a(0, 0, fa[0]);
+#pragma unroll
+        for (int b = 0; b < NB; ++b) fb[b] = frag_b(0, 0, b);
         // the loads of slice SL-1 that would ride on the last k-step of the
         // (absent) slice before slice 0; that slot has not been used yet
         if (SL - 1 < nk) {
@@ -908,26 +917,30 @@ __global__ __launch_bounds__(NW * 64, 1) void lmhead_big_bf16(
                     asm volatile("" ::: "memory");
                     __builtin_amdgcn_sched_barrier(0);
                 }
+                // the next k-step: the next one of this slice, or the first of
+                // slice kt+1 (visible after the barrier above)
+                const int nsl = ks < kLast ? kt : kt + 1, nks = ks < kLast ? ks + 1 : 0;
 #pragma unroll
                 for (int i = 0; i < kPerStep; ++i) {
-                    const int a = i / NB, b = i % NB;
-                    acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[cur][a], fb[cur][b], acc[a][b], 0, 0, 0);
-                    if (i == 0) {
-                        if (ks < kLast) frag(kt, ks + 1, fa[cur ^ 1], fb[cur ^ 1]);
-                        else frag(kt + 1, 0, fa[cur ^ 1], fb[cur ^ 1]);
-                    }
+                    const int b = i / NA, a = i % NA;
+                    acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[cur][a], fb[b], acc[a][b], 0, 0, 0);
+                    if (i == 0) frag_a(nsl, nks, fa[cur ^ 1]);
+                    if (a == NA - 1) fb[b] = frag_b(nsl, nks, b);
                     const int q = ks == kLast ? i : kPerStep * (ks + 1) + i;
                     if (q < G::kLoads) {
                         if (ks == kLast && NEXT) dma(q, kt + SL);
                         if (ks < kLast && MAIN) dma(q, kt + SL - 1);
                     }
                 }
-                // pin the order: 1 MFMA, the fragment reads, then each MFMA
-                // with the load that rides on it
+                // pin the order: each MFMA, then the fragment reads it frees
+                // (after the first, the next step's weight fragments), then
+                // the load that rides on it
 #pragma unroll
                 for (int i = 0; i < kPerStep; ++i) {
+                    const int a = i % NA;
                     __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
-                    if (i == 0) __builtin_amdgcn_sched_group_barrier(0x100, NA + NB, 0);   // LDS reads
+                    if (i == 0) __builtin_amdgcn_sched_group_barrier(0x100, NA, 0);   // LDS reads (weights)
+                    if (a == NA - 1) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // LDS read (hidden)
                     const int q = ks == kLast ? i : kPerStep * (ks + 1) + i;
                     if (q < G::kLoads && ((ks == kLast && NEXT) || (ks < kLast && MAIN)))
                         __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);   // memory load
