@@ -16,7 +16,7 @@ the step time, with the roofline of the dominant kernel (the LM-head
 contraction, timed with HIP events on the stream it runs on) and the CPU
 oracle timed on a bounded sample of the same workload.
 
-    python bench.py [--gpus 1] [--steps 50] [--warmup 5] [--workload b1_k5_h4096_v128256]
+    python bench.py [--gpus 1] [--steps 200] [--warmup 20] [--workload b1_k5_h4096_v128256]
 """
 from __future__ import annotations
 
@@ -41,8 +41,8 @@ GEMM_SRC = os.path.join(ROOT, "speculative_decoding_verification_02_amd", "csrc"
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="b1_k5_h4096_v128256")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-other-configs", action="store_true",
