@@ -47,6 +47,9 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-other-configs", action="store_true",
                     help="headline workload only (by default its line also carries the other benchmark workloads)")
+    ap.add_argument("--record-rounds", type=int, default=512,
+                    help="further rounds, drafts redrawn each, whose accepted lengths give the acceptance by "
+                         "position (0 leaves it out, e.g. for profiler runs)")
     ap.add_argument("--path", choices=["fused", "separate"], default="fused",
                     help="fused: spec_verify_step, the one-call step (statistics in the LM-head kernel where "
                          "it can compute them); separate: spec_verify_logits then the accept calls")
@@ -193,7 +196,7 @@ def main():
                                      cpu=not args.no_cpu_baseline, steps=args.steps)), flush=True)
         return
     res = measure(synth.WORKLOADS[args.workload], args, dev, args.steps, args.warmup,
-                  cpu=not args.no_cpu_baseline, record_rounds=512)
+                  cpu=not args.no_cpu_baseline, record_rounds=args.record_rounds)
     if args.workload == HEADLINE and not args.no_other_configs:
         # the other benchmark workloads, under the same clock: a few steps
         # each, no CPU baseline
