@@ -296,7 +296,7 @@ spec_status_t spec_tree_accept_greedy(const float* logits, const int32_t* parent
  * 1e-6 may differ; greedy decisions and the logits are identical).  The
  * logits are written once and not read back for statistics where a bf16
  * LM-head kernel computes them itself:
- *   - M = B*(K+1) <= 16, H <= 4096 (the cooperative kernel): each workgroup
+ *   - M = B*(K+1) <= 16, H <= 8192 (the cooperative kernel): each workgroup
  *     keeps the logits of its vocabulary range in LDS and writes one record
  *     per target row, plus one per draft row from the draft logits it loads
  *     while the weights stream; the accept kernels merge these records;

@@ -294,12 +294,13 @@ __device__ __forceinline__ void coop_fold(StatRec& a, const float (&z)[N], int v
     stat_fold(a, bm, bs, bi, (bs != bs) | (bm == INFINITY), c);
 }
 
-template <int RPL, int MAXST, int NW, bool STATS, bool STASH>
+template <int RPL, int MAXST, int NW, bool STATS, bool STASH, int PIPE>
 __global__ __launch_bounds__(NW * 64) void lmhead_coop_bf16(
     const uint16_t* __restrict__ hidden, const uint16_t* __restrict__ W, float* __restrict__ logits,
     int M, int V, int H, int n_tiles, CoopStats cs) {
     using S = Coop<RPL, MAXST, NW>;
     static_assert(STASH || !STATS, "the statistics are taken from the stash");
+    static_assert(PIPE >= 1 && MAXST % PIPE == 0, "stages in flight divide the stages of a tile");
     extern __shared__ __align__(16) unsigned char smem[];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     u32x4* buf = reinterpret_cast<u32x4*>(smem) + wave * S::kBufChunks;
@@ -336,18 +337,22 @@ __global__ __launch_bounds__(NW * 64) void lmhead_coop_bf16(
         const int k = k_lo + st * S::kKS + lc * 8;
         const int v0 = t << 4;
         const int rows = t < t_end ? min(16, V - v0) : 0;
-        const __amdgpu_buffer_rsrc_t rs = make_rsrc(W + (size_t)(t < t_end ? v0 : 0) * H, (unsigned)(rows * H * 2));
-        const unsigned vo = (unsigned)(la * H + k) * 2u;
+        const unsigned vo = k < H ? (unsigned)(la * H + k) * 2u : kOutOfRange;
 #pragma unroll
         for (int q = 0; q < S::kLoads; ++q) {
-            const unsigned o = k < H ? vo + (unsigned)(q * RPL * H * 2) : kOutOfRange;
-            dst[q] = load_stream_buf(rs, o);
+            // load q covers tile rows q * RPL .. q * RPL + RPL - 1: its own
+            // resource (scalar registers), so one per-lane offset serves all
+            const int rq = min(max(rows - q * RPL, 0), RPL);
+            const __amdgpu_buffer_rsrc_t rs =
+                make_rsrc(W + (rq ? (size_t)(v0 + q * RPL) * H : 0), (unsigned)(rq * H * 2));
+            dst[q] = load_stream_buf(rs, vo);
         }
     };
 
     // draft row `wave` over this workgroup's vocabulary range: the first
-    // kDraftPer * 64 entries are loaded now, ahead of W, and reduced after
-    // the tiles, so the statistics never hold up the weight stream
+    // kDraftPer * 64 entries are loaded now, ahead of W, and go into the
+    // stash before the first tile, so the statistics never hold up the
+    // weight stream
     constexpr int kDraftPer = 8;
     const int dcb = t_begin << 4, dce = min(t_end << 4, V);
     float dz[kDraftPer];
@@ -363,11 +368,11 @@ __global__ __launch_bounds__(NW * 64) void lmhead_coop_bf16(
         }
     }
 
-    u32x4 pipe[MAXST][S::kLoads];
+    u32x4 pipe[PIPE][S::kLoads];
 #pragma unroll
-    for (int st = 0; st < MAXST; ++st) {
+    for (int st = 0; st < PIPE; ++st) {
         issue(t_begin, st, pipe[st]);
-        // issue order kept: the loop waits for stage 0 with stage 1 in flight
+        // issue order kept: the loop waits for stage 0 with the later ones in flight
         __builtin_amdgcn_sched_barrier(0);
     }
 
@@ -408,11 +413,13 @@ __global__ __launch_bounds__(NW * 64) void lmhead_coop_bf16(
 #pragma unroll
                 for (int q = 0; q < S::kLoads; ++q) {
                     const int R = q * RPL + la;
-                    buf[R * S::kCPR + (lc ^ (R % S::kCPR))] = k_in ? pipe[st][q] : zero;
+                    buf[R * S::kCPR + (lc ^ (R % S::kCPR))] = k_in ? pipe[st % PIPE][q] : zero;
                 }
             }
             __builtin_amdgcn_wave_barrier();
-            issue(t + 1, st, pipe[st]);
+            // the step PIPE stages on: later in this tile, or in the next one
+            if (st + PIPE < MAXST) issue(t, st + PIPE, pipe[st % PIPE]);
+            else issue(t + 1, st + PIPE - MAXST, pipe[st % PIPE]);
             if (live) {
 #pragma unroll
                 for (int j = 0; j < S::kSteps; ++j) {
@@ -527,7 +534,7 @@ inline int coop_grid(int V, int num_cus, bool stats) {
 
 // The logits go through the stash whenever it fits in LDS (always with the
 // statistics; their launcher checks that first).
-template <int RPL, int MAXST, int NW, bool STATS>
+template <int RPL, int MAXST, int NW, int PIPE, bool STATS>
 hipError_t launch_coop(const uint16_t* hidden, const uint16_t* W, float* logits, int M, int V, int H, int num_cus,
                        hipStream_t stream, CoopStats st = CoopStats{}) {
     using S = Coop<RPL, MAXST, NW>;
@@ -535,8 +542,8 @@ hipError_t launch_coop(const uint16_t* hidden, const uint16_t* W, float* logits,
     const int grid = coop_grid(V, num_cus, STATS);
     const size_t lds_stash = S::lds_bytes_stats(n_tiles, grid, M + (STATS ? st.n_draft : 0));
     const bool stash = STATS || lds_stash <= 160 * 1024;
-    auto kern = !stash ? lmhead_coop_bf16<RPL, MAXST, NW, false, false>
-                       : lmhead_coop_bf16<RPL, MAXST, NW, STATS, true>;
+    auto kern = !stash ? lmhead_coop_bf16<RPL, MAXST, NW, false, false, PIPE>
+                       : lmhead_coop_bf16<RPL, MAXST, NW, STATS, true, PIPE>;
     const size_t lds = stash ? lds_stash : S::lds_bytes();
     if (lds > 160 * 1024) return hipErrorInvalidValue;
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
@@ -549,9 +556,15 @@ hipError_t launch_coop(const uint16_t* hidden, const uint16_t* W, float* logits,
     return hipGetLastError();
 }
 
-// Small-M configuration of the cooperative kernel (measured best on MI355X
-// for B = 1, K = 5, H = 4096: 2 rows per load, 2 stages, 8 waves).
+// Small-M configurations of the cooperative kernel: up to H = 4096 (measured
+// best on MI355X for B = 1, K = 5: 2 rows per load, 2 stages, 8 waves), and
+// up to H = 8192 with 4 stages per tile, 2 of them in flight (each wave's
+// hidden slice takes 128 registers).
 using CoopCfg = Coop<2, 2, 8>;
+using CoopWideCfg = Coop<2, 4, 8>;
+constexpr int kCoopWidePipe = 2;
+// 1: the H <= 4096 configuration, 2: the wide one, 0: neither fits
+inline int coop_kind(int M, int H) { return CoopCfg::fits(M, H) ? 1 : CoopWideCfg::fits(M, H) ? 2 : 0; }
 
 // ------------------------------------------------------------ large M ------
 // Classic LDS-tiled contraction: a workgroup of 4 waves computes a 128 (vocab)
@@ -1129,25 +1142,31 @@ __global__ __launch_bounds__(kF32Threads) void lmhead_f32(
 // ------------------------------------------------------------ launchers ----
 
 int lmhead_coop_records(int M, int V, int H, int n_draft, int num_cus) {
-    if (!CoopCfg::fits(M, H) || n_draft < 0) return 0;
+    if (!coop_kind(M, H) || n_draft < 0) return 0;
     const int grid = coop_grid(V, num_cus, true);
+    // both configurations have the same LDS layout
     return CoopCfg::lds_bytes_stats((V + 15) / 16, grid, M + n_draft) <= 160 * 1024 ? grid : 0;
 }
 
 hipError_t launch_lmhead_coop_stats(const uint16_t* hidden, const uint16_t* W, float* logits, int M, int V, int H,
                                     int num_cus, hipStream_t stream, const CoopStats& st) {
-    if (!CoopCfg::fits(M, H)) return hipErrorInvalidValue;
-    return launch_coop<2, 2, 8, true>(hidden, W, logits, M, V, H, num_cus, stream, st);
+    switch (coop_kind(M, H)) {
+    case 1: return launch_coop<2, 2, 8, 2, true>(hidden, W, logits, M, V, H, num_cus, stream, st);
+    case 2: return launch_coop<2, 4, 8, kCoopWidePipe, true>(hidden, W, logits, M, V, H, num_cus, stream, st);
+    default: return hipErrorInvalidValue;
+    }
 }
 
 int lmhead_big_records(int M, int V, int H) {
-    return !CoopCfg::fits(M, H) && big_fits(M, V, H) ? (V + kBigBN - 1) / kBigBN : 0;
+    return !coop_kind(M, H) && big_fits(M, V, H) ? (V + kBigBN - 1) / kBigBN : 0;
 }
 
 hipError_t launch_lmhead_bf16(const uint16_t* hidden, const uint16_t* W, float* logits, int M, int V, int H,
                               int num_cus, hipStream_t stream, StatRec* stats, float c, int* n_rec) {
     if (n_rec) *n_rec = 0;
-    if (CoopCfg::fits(M, H)) return launch_coop<2, 2, 8, false>(hidden, W, logits, M, V, H, num_cus, stream);
+    if (CoopCfg::fits(M, H)) return launch_coop<2, 2, 8, 2, false>(hidden, W, logits, M, V, H, num_cus, stream);
+    if (CoopWideCfg::fits(M, H))
+        return launch_coop<2, 4, 8, kCoopWidePipe, false>(hidden, W, logits, M, V, H, num_cus, stream);
     if (big_fits(M, V, H)) {
         if (stats) {
             if (n_rec) *n_rec = (V + kBigBN - 1) / kBigBN;

@@ -57,11 +57,25 @@ def test_bf16_small_m_long_vocabulary(B, K):
     _check(h, W)
 
 
-@pytest.mark.parametrize("B,K,H,V", [(1, 0, 8192, 3001), (2, 1, 6144, 4099), (1, 3, 4104, 130)])
+@pytest.mark.parametrize("B,K,H,V", [(1, 0, 8192, 3001), (2, 1, 6144, 4099), (1, 3, 4104, 130), (4, 3, 8192, 128256)])
 def test_bf16_small_m_wide_hidden(B, K, H, V):
-    """M <= 16 with a hidden size beyond the register-resident slices of the
-    cooperative kernel: the LDS-staged streaming kernel."""
+    """M <= 16 with 4096 < H <= 8192: the cooperative kernel with four stages
+    per tile, two of them in flight across the tile boundary."""
     W, h = _case(B, K, H, V, "bf16", 0.02, seed=H + V)
+    _check(h, W)
+
+
+@pytest.mark.parametrize("B,K,H,V", [(1, 0, 8200, 3001), (2, 1, 12288, 1000), (1, 5, 16384, 517)])
+def test_bf16_small_m_beyond_cooperative(B, K, H, V):
+    """M <= 16 with H > 8192 and the hidden rows fitting in LDS: the LDS-staged
+    streaming kernel."""
+    W, h = _case(B, K, H, V, "bf16", 0.02, seed=H + V + 1)
+    _check(h, W)
+
+
+def test_bf16_small_m_tiled():
+    """M = 16 with H = 8200: neither small-M kernel fits, the tiled kernel."""
+    W, h = _case(4, 3, 8200, 1000, "bf16", 0.02, seed=8201)
     _check(h, W)
 
 

@@ -106,7 +106,9 @@ def _wl(B, K, H, V, dtype="bf16", T=0.9, seed=7):
     (1, 1, 64, 1, "bf16", "cooperative, V=1: one entry per row"),
     (4, 15, 256, 102400, "bf16", "direct-to-LDS, K=15, epilogue records folded to chunks"),
     (2, 8, 256, 3001, "bf16", "direct-to-LDS, epilogue, accept and residual in one launch"),
-    (2, 3, 8192, 3001, "bf16", "small-M wide H, statistics pass"),
+    (2, 3, 8192, 3001, "bf16", "cooperative wide H (4 stages per tile), statistics in the LM-head kernel"),
+    (1, 5, 6144, 40000, "bf16", "cooperative wide H, B=1 K=5, statistics in the LM-head kernel"),
+    (1, 5, 8200, 3001, "bf16", "small-M streaming kernel (H beyond the cooperative slices), statistics pass"),
     (8, 7, 576, 4099, "bf16", "direct-to-LDS 64-row tiles, epilogue"),
     (30, 4, 128, 2053, "bf16", "direct-to-LDS 160-row tiles, epilogue"),
     (64, 4, 576, 1000, "bf16", "direct-to-LDS 2 x 160-row tiles, epilogue"),
