@@ -850,6 +850,7 @@ __global__ __launch_bounds__(NW * 64, 1) void lmhead_big_bf16(
     // slots of their own.  Waves 0 .. kWWaves-1 load only W blocks and the
     // others only hidden blocks, so each role runs its own prefetch depth.
     constexpr int kWChunks = kBigBN * G::kCPR, kHChunks = G::kBM * G::kCPR;
+    constexpr size_t kPartBytes = (size_t)G::kWN * G::kBM * sizeof(StatRec);   // statistics exchange (STATS)
     constexpr int kWWaves = G::kWLoads / G::kLoads;
     static_assert(HS == 0 || (G::kWLoads % G::kLoads == 0 && kWWaves < NW), "roles split by wave");
     auto wslot = [&](int slice) -> u32x4* {
@@ -972,19 +973,45 @@ __global__ __launch_bounds__(NW * 64, 1) void lmhead_big_bf16(
         run(std::integral_constant<int, SLOTS>{});
     }
 
-    // logits of row block b: four runs of four consecutive vocabulary entries
+    // Logits out through LDS (the ring is free once every wave is past its
+    // last slice), one row block at a time: the kWM * 32 rows that all waves'
+    // block b covers land in LDS as whole 256-entry rows, then each store
+    // instruction writes one row's 1 KB run.  Stored straight from the MFMA
+    // layout, an instruction wrote 16-byte pieces of 32 rows.
     const bool vec_ok = (V & 3) == 0;
-    auto store_rows = [&](int b) {
-        const int m = m0 + wm + b * 32 + r;
-        if (m >= M) return;
-        float* out = logits + (size_t)m * V;
+    auto store_logits = [&](auto off_tag) {
+        constexpr size_t kOff = decltype(off_tag)::value;   // bytes of LDS in use below the staging rows
+        constexpr int kRowF = kBigBN + 4;                  // floats per staged row (16-byte pad)
+        constexpr int kRows = G::kWM * 32;                 // rows per row block
+        float* stg = reinterpret_cast<float*>(smem + kOff);
+        const int lr0 = (wave / G::kWN) * 32;              // this wave's first staged row
+        const bool full_v = vec_ok && v0 + kBigBN <= V;
 #pragma unroll
-        for (int a = 0; a < NA; ++a)
+        for (int b = 0; b < NB; ++b) {
+            __syncthreads();
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const f32x4 v4 = {acc[a][b][4 * q], acc[a][b][4 * q + 1], acc[a][b][4 * q + 2], acc[a][b][4 * q + 3]};
-                store_row4(out, v0 + wn + a * 32 + 8 * q + 4 * h, V, v4, vec_ok);
+            for (int a = 0; a < NA; ++a)
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const f32x4 v4 = {acc[a][b][4 * q], acc[a][b][4 * q + 1], acc[a][b][4 * q + 2],
+                                      acc[a][b][4 * q + 3]};
+                    *reinterpret_cast<f32x4*>(stg + (lr0 + r) * kRowF + wn + a * 32 + 8 * q + 4 * h) = v4;
+                }
+            __syncthreads();
+            for (int lr = wave; lr < kRows; lr += NW) {
+                const int m = m0 + (lr / 32) * (32 * NB) + 32 * b + (lr % 32);
+                if (m >= M) continue;
+                const f32x4 v4 = *reinterpret_cast<const f32x4*>(stg + lr * kRowF + 4 * lane);
+                float* out = logits + (size_t)m * V + v0;
+                if (full_v) {
+                    *reinterpret_cast<f32x4*>(out + 4 * lane) = v4;
+                } else {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        if (v0 + 4 * lane + e < V) out[4 * lane + e] = v4[e];
+                }
             }
+        }
     };
 
     if constexpr (STATS) {
@@ -992,7 +1019,7 @@ __global__ __launch_bounds__(NW * 64, 1) void lmhead_big_bf16(
         // index), then its partner lane^32 (the other half of the columns),
         // then the kWN waves side by side along the vocabulary, in order,
         // through the LDS ring (free once every wave is past its last slice);
-        // each row block's logits are stored right after its statistics.
+        // the logits follow, staged above these records.
         // No per-entry checks: fmaxf skips NaN and a NaN or +inf shows in the
         // maximum or the sum, which marks the row bad; entries past V are
         // masked only in the last vocabulary tile.
@@ -1026,7 +1053,6 @@ __global__ __launch_bounds__(NW * 64, 1) void lmhead_big_bf16(
             sum += __shfl_xor(sum, 32, kWave);
             const int bad = mx == INFINITY || sum != sum;
             if (h == 0) part[(wave % G::kWN) * G::kBM + wm + b * 32 + r] = StatRec{mx, sum, mi, bad};
-            store_rows(b);   // block b's registers are free after this
         }
         __syncthreads();
         for (int row = threadIdx.x; row < G::kBM; row += G::kThreads) {
@@ -1039,12 +1065,10 @@ __global__ __launch_bounds__(NW * 64, 1) void lmhead_big_bf16(
             }
             stats[(size_t)(m0 + row) * tiles_n + tn] = t;
         }
+        store_logits(std::integral_constant<size_t, kPartBytes>{});   // staged above the records
     }
 
-    if constexpr (!STATS) {
-#pragma unroll
-        for (int b = 0; b < NB; ++b) store_rows(b);
-    }
+    if constexpr (!STATS) store_logits(std::integral_constant<size_t, 0>{});
 }
 
 template <int BK, int SLOTS, int NA, int NB, bool STATS, int NW = 4, int HS = 0>
@@ -1054,6 +1078,9 @@ hipError_t launch_big_cfg(const uint16_t* hidden, const uint16_t* W, float* logi
     constexpr size_t kLds = HS ? (size_t)(SLOTS * kBigBN + HS * G::kBM) * G::kCPR * 16 : G::kLds;
     static_assert(kLds <= 160 * 1024, "rings exceed the 160 KB of a CU");
     static_assert(!STATS || (size_t)G::kWN * G::kBM * sizeof(StatRec) <= kLds, "statistics exchange fits the ring");
+    static_assert((STATS ? (size_t)G::kWN * G::kBM * sizeof(StatRec) : 0) + (size_t)G::kWM * 32 * (kBigBN + 4) * 4 <=
+                      kLds,
+                  "a staged row block of logits fits the ring");
     auto kern = lmhead_big_bf16<BK, SLOTS, NA, NB, STATS, NW, HS>;
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLds);
