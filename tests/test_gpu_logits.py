@@ -65,6 +65,32 @@ def test_bf16_small_m_wide_hidden(B, K, H, V):
     _check(h, W)
 
 
+def test_bf16_wide_hidden_long_vocabulary_sampled():
+    """M = 16, H = 4160 (the four-stage cooperative configuration) and a
+    vocabulary range per workgroup too long for the logits to wait in LDS:
+    the tiles store as they go.  Sampled entries (the weights are 2.7 GB)."""
+    B, K, H, V = 4, 3, 4160, 330011
+    W, h = _case(B, K, H, V, "bf16", 0.02, seed=V + H, device=dev())
+    say("wide-hidden long-vocabulary logits B=%d K=%d H=%d V=%d (sampled)" % (B, K, H, V))
+    g = gpu_logits(h, W)
+    torch.cuda.synchronize()
+    M = B * (K + 1)
+    rng = np.random.default_rng(7)
+    vs = np.concatenate([rng.integers(0, V, 400), [0, 1, 15, 16, V - 17, V - 16, V - 2, V - 1]])
+    ms = rng.integers(0, M, len(vs))
+    x = f64(h.reshape(M, H)[torch.as_tensor(ms, device=dev())])
+    w = f64(W[torch.as_tensor(vs, device=dev())])
+    o = np.sum(x * w, axis=1)
+    absdot = np.sum(np.abs(x * w), axis=1)
+    gv = g.reshape(M, V)[torch.as_tensor(ms, device=dev()), torch.as_tensor(vs, device=dev())].cpu().numpy()
+    u = 2.0 ** -24
+    gam = (H + 1) * u / (1 - (H + 1) * u)
+    err = np.abs(gv.astype(np.float64) - o)
+    assert np.all(err <= gam * absdot), np.max(err / (gam * absdot))
+    assert not torch.isnan(g).any().item()
+    say("  %d entries, max err / fp32 bound = %.3g" % (len(vs), np.max(err / (gam * absdot))))
+
+
 @pytest.mark.parametrize("B,K,H,V", [(1, 0, 8200, 3001), (2, 1, 12288, 1000), (1, 5, 16384, 517)])
 def test_bf16_small_m_beyond_cooperative(B, K, H, V):
     """M <= 16 with H > 8192 and the hidden rows fitting in LDS: the LDS-staged
