@@ -37,7 +37,7 @@ __all__ = [
     "load_library", "declared_symbols", "spec_verify_logits", "spec_accept_greedy",
     "spec_accept_sample", "spec_accept_greedy_ragged", "spec_accept_sample_ragged", "spec_tree_accept_greedy", "spec_ngram_propose", "spec_ngram_workspace_bytes",
     "spec_verify_step", "spec_verify_step_workspace_bytes", "spec_verify_step_noalloc",
-    "spec_workspace_bytes", "spec_status_string", "spec_last_error_detail",
+    "spec_workspace_bytes", "spec_status_string", "spec_last_error_detail", "spec_set_poll_limit",
 ]
 
 PKG_DIR = os.path.dirname(os.path.abspath(__file__))
@@ -79,6 +79,7 @@ _SIGNATURES = {
     "spec_workspace_bytes": (_c_size_t, [_c_int, _c_int, _c_int]),
     "spec_status_string": (ctypes.c_char_p, [_c_int]),
     "spec_last_error_detail": (ctypes.c_char_p, []),
+    "spec_set_poll_limit": (_c_int, [_c_int]),
 }
 
 _lib = None
@@ -240,6 +241,12 @@ def spec_status_string(status: int) -> str:
 
 def spec_last_error_detail() -> str:
     return load_library().spec_last_error_detail().decode()
+
+
+def spec_set_poll_limit(rounds: int) -> int:
+    """Bound the chunk-sum wait of the one-launch accept + residual draw
+    (negative: the library default); returns the previous bound."""
+    return int(load_library().spec_set_poll_limit(int(rounds)))
 
 
 def spec_verify_logits(hidden, w_lmhead, logits, stream=None) -> None:

@@ -357,7 +357,8 @@ __global__ __launch_bounds__(NW * 64) void lmhead_coop_bf16(
     const int dcb = t_begin << 4, dce = min(t_end << 4, V);
     float dz[kDraftPer];
     if constexpr (STATS) {
-        if (blockIdx.x == 0 && (int)threadIdx.x < cs.n_zero) cs.zero[threadIdx.x] = 0;
+        if (blockIdx.x == 0)
+            for (int i = threadIdx.x; i < cs.n_zero; i += NW * 64) cs.zero[i] = 0;
         if (wave < cs.n_draft) {
             const float* row = cs.draft + (size_t)wave * V;
 #pragma unroll
@@ -549,7 +550,7 @@ hipError_t launch_coop(const uint16_t* hidden, const uint16_t* W, float* logits,
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
-    if (STATS && (st.n_zero > S::kThreads || st.n_zero < 0 || st.n_draft < 0 || M > 16 || !st.tgt ||
+    if (STATS && (st.n_zero > (1 << 20) || st.n_zero < 0 || st.n_draft < 0 || M > 16 || !st.tgt ||
                   (st.n_draft > 0 && (!st.draft || !st.drf)) || (st.n_zero > 0 && !st.zero)))
         return hipErrorInvalidValue;
     hipLaunchKernelGGL(kern, dim3(grid), dim3(S::kThreads), lds, stream, hidden, W, logits, M, V, H, n_tiles, st);

@@ -146,86 +146,34 @@ __device__ __forceinline__ void chunk_prefix(const float* src, int nc, int lane,
     if (lane == 0) pre[0] = 0.f;
 }
 
-// Inverse-CDF selection of the terminal token of one sequence, by the block
-// that finished last among the sequence's chunk blocks.  chunk_sums holds the
-// per-chunk weight sums published by all of them (read back with atomics).
-template <int PER = kStatPerThread>
-__device__ void select_terminal(const float* __restrict__ logits, const float* __restrict__ draft_logits,
-                                int V, int nc, float c, const AcceptInfo& a, const float* chunk_sums,
-                                int32_t* __restrict__ out_tokens, bool sums_by_atomics = true) {
-    constexpr int CH = PER * kStatThreads;               // entries per chunk
-    __shared__ float pre[kMaxChunks * kChunk / CH + 1];  // prefix over chunk sums
-    __shared__ float wl[CH];                             // weights of the selected chunk, token order
-    __shared__ float red[kStatThreads / kWave];
-    __shared__ float wtot[kStatThreads / kWave];
-    __shared__ int sel[2];                  // selected chunk, selected token
-    __shared__ int redi[kStatThreads / kWave];
+// c* = the first chunk whose inclusive prefix exceeds x; if rounding leaves
+// none, the last chunk with positive mass.  One wavefront; every lane gets it.
+__device__ __forceinline__ int choose_chunk(const float* pre, int nc, float x, int lane) {
+    int cs = -1, last_pos = 0;
+    for (int base = 0; base < nc && cs < 0; base += kWave) {
+        const int k = base + lane;
+        const bool in = k < nc;
+        const unsigned long long over = __ballot(in && pre[k + 1] > x);
+        const unsigned long long pos = __ballot(in && pre[k + 1] > pre[k]);
+        if (over) cs = base + __ffsll((long long)over) - 1;
+        if (pos) last_pos = base + 63 - __clzll((long long)pos);
+    }
+    return cs < 0 ? last_pos : cs;
+}
 
-    const TermRows tr = term_rows(logits, draft_logits, a, V);
+// The token of one chunk at which the running sum of its weights first
+// exceeds xr.  Thread tid owns tokens [tid*PER, tid*PER+PER) of the chunk,
+// weights mine[]; a token of zero weight is never taken, and if rounding puts
+// xr outside the chunk's scanned range the first (xr < 0) or last token of
+// positive weight is.  Called by the whole workgroup; the returned index
+// (relative to v_begin, plus v_begin) is the same in every thread.
+template <int PER>
+__device__ int pick_in_chunk(const float (&mine)[PER], float xr, int v_begin, int* sel, float* wtot, int* redi) {
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const bool vec = (V & 3) == 0;
-
-    bool use_q = tr.bonus;
-    if (wave == 0) chunk_prefix(chunk_sums, nc, lane, pre, sums_by_atomics);
-    __syncthreads();
-    if (!(pre[nc] > 0.f) && !use_q) {
-        // residual without mass: draw from q_n, recomputing the chunk sums
-        use_q = true;
-        for (int k = 0; k < nc; ++k) {
-            float w[PER];
-            chunk_weights<PER>(tr.zt, tr.zd, k * CH, V, vec, tid, a, c, true, w);
-            float s = 0.f;
-#pragma unroll
-            for (int e = 0; e < PER; ++e) s += w[e];
-            s = block_sum(s, red);
-            if (tid == 0) pre[k + 1] = s;
-        }
-        __syncthreads();
-        if (wave == 0) chunk_prefix(pre + 1, nc, lane, pre, false);
-        __syncthreads();
-    }
-    const float Z = pre[nc];
-    const float x = a.u_term * Z;
-    if (wave == 0) {
-        // c* = first chunk whose inclusive prefix exceeds x; if rounding leaves
-        // none, the last chunk with positive mass
-        int cs = -1, last_pos = 0;
-        for (int base = 0; base < nc && cs < 0; base += kWave) {
-            const int k = base + lane;
-            const bool in = k < nc;
-            const unsigned long long over = __ballot(in && pre[k + 1] > x);
-            const unsigned long long pos = __ballot(in && pre[k + 1] > pre[k]);
-            if (over) cs = base + __ffsll((long long)over) - 1;
-            if (pos) last_pos = base + 63 - __clzll((long long)pos);
-        }
-        if (lane == 0) {
-            sel[0] = cs < 0 ? last_pos : cs;
-            sel[1] = -1;
-        }
-    }
-    __syncthreads();
-    const int cs = sel[0];
-    const int v_begin = cs * CH;
-
-    // weights of chunk cs into LDS in token order
-    {
-        float w[PER];
-        chunk_weights<PER>(tr.zt, tr.zd, v_begin, V, vec, tid, a, c, use_q, w);
-#pragma unroll
-        for (int q = 0; q < PER / 4; ++q)
-#pragma unroll
-            for (int e = 0; e < 4; ++e) wl[(q * kStatThreads + tid) * 4 + e] = w[4 * q + e];
-    }
-    __syncthreads();
-
-    // thread tid owns tokens [tid*PER, tid*PER+PER) of the chunk
-    float mine[PER];
+    if (tid == 0) sel[1] = -1;
     float s = 0.f;
 #pragma unroll
-    for (int e = 0; e < PER; ++e) {
-        mine[e] = wl[tid * PER + e];
-        s += mine[e];
-    }
+    for (int e = 0; e < PER; ++e) s += mine[e];
     // inclusive scan of the thread sums: within the wave, then across waves
     float incl = wave_inclusive_scan(s);
     if (lane == kWave - 1) wtot[wave] = incl;
@@ -236,7 +184,6 @@ __device__ void select_terminal(const float* __restrict__ logits, const float* _
     float excl = __shfl_up(incl, 1, kWave);
     if (lane == 0) excl = base;
 
-    const float xr = x - pre[cs];
     if (excl <= xr && xr < incl) {  // exactly one thread's interval can hold xr
         float run = excl;
         int tok = -1, lastp = -1;
@@ -251,8 +198,6 @@ __device__ void select_terminal(const float* __restrict__ logits, const float* _
     }
     __syncthreads();
     if (sel[1] < 0) {  // block-uniform: read after the barrier
-        // rounding put xr outside the scanned range: take the first token of
-        // positive weight in the chunk if xr < 0, else the last one
         const bool low = xr < 0.f;
         int cand = low ? INT_MAX : -1;
 #pragma unroll
@@ -274,7 +219,124 @@ __device__ void select_terminal(const float* __restrict__ logits, const float* _
         }
         __syncthreads();
     }
-    if (tid == 0) out_tokens[(size_t)a.t0 + a.n] = sel[1];
+    return sel[1];
+}
+
+// Where select_terminal finds the chunk sums: published by the chunk
+// workgroups and read back with atomic read-modify-writes, written by an
+// earlier launch (plain loads), or not at all (the workgroup sums every chunk
+// itself, with the same function and reduction order as the chunk workgroups,
+// so the sums are the same bits).
+enum class SumSrc { Atomic, Plain, Local };
+
+// Inverse-CDF selection of the terminal token of one sequence.  With
+// writer >= 0 the token is written only if it falls in chunk `writer` (so
+// several workgroups may run the selection and exactly one writes).
+template <int PER = kStatPerThread>
+__device__ void select_terminal(const float* __restrict__ logits, const float* __restrict__ draft_logits,
+                                int V, int nc, float c, const AcceptInfo& a, const float* chunk_sums,
+                                int32_t* __restrict__ out_tokens, SumSrc src = SumSrc::Atomic, int writer = -1) {
+    constexpr int CH = PER * kStatThreads;               // entries per chunk
+    __shared__ float pre[kMaxChunks * kChunk / CH + 1];  // prefix over chunk sums
+    __shared__ float wl[CH];                             // weights of the selected chunk, token order
+    __shared__ float red[kStatThreads / kWave];
+    __shared__ float wtot[kStatThreads / kWave];
+    __shared__ int sel[2];                  // selected chunk, selected token
+    __shared__ int redi[kStatThreads / kWave];
+
+    const TermRows tr = term_rows(logits, draft_logits, a, V);
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const bool vec = (V & 3) == 0;
+
+    // pre[k+1] = the sum of chunk k, summed here, then the prefix in place
+    auto local_prefix = [&](bool q_only) {
+        for (int k = 0; k < nc; ++k) {
+            float w[PER];
+            chunk_weights<PER>(tr.zt, tr.zd, k * CH, V, vec, tid, a, c, q_only, w);
+            float s = 0.f;
+#pragma unroll
+            for (int e = 0; e < PER; ++e) s += w[e];
+            s = block_sum(s, red);
+            if (tid == 0) pre[k + 1] = s;
+        }
+        __syncthreads();
+        if (wave == 0) chunk_prefix(pre + 1, nc, lane, pre, false);
+        __syncthreads();
+    };
+
+    bool use_q = tr.bonus;
+    if (src == SumSrc::Local) {
+        local_prefix(use_q);
+    } else {
+        if (wave == 0) chunk_prefix(chunk_sums, nc, lane, pre, src == SumSrc::Atomic);
+        __syncthreads();
+    }
+    if (!(pre[nc] > 0.f) && !use_q) {
+        // residual without mass: draw from q_n, recomputing the chunk sums
+        use_q = true;
+        local_prefix(true);
+    }
+    const float Z = pre[nc];
+    const float x = a.u_term * Z;
+    if (wave == 0) {
+        const int cs = choose_chunk(pre, nc, x, lane);
+        if (lane == 0) sel[0] = cs;
+    }
+    __syncthreads();
+    const int cs = sel[0];
+    if (writer >= 0 && cs != writer) return;   // block-uniform
+    const int v_begin = cs * CH;
+
+    // weights of chunk cs into LDS in token order
+    {
+        float w[PER];
+        chunk_weights<PER>(tr.zt, tr.zd, v_begin, V, vec, tid, a, c, use_q, w);
+#pragma unroll
+        for (int q = 0; q < PER / 4; ++q)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) wl[(q * kStatThreads + tid) * 4 + e] = w[4 * q + e];
+    }
+    __syncthreads();
+    float mine[PER];
+#pragma unroll
+    for (int e = 0; e < PER; ++e) mine[e] = wl[tid * PER + e];
+    const int tok = pick_in_chunk<PER>(mine, x - pre[cs], v_begin, sel, wtot, redi);
+    if (tid == 0) out_tokens[(size_t)a.t0 + a.n] = tok;
+}
+
+// The selection of the one-launch accept + residual for small launches, by
+// every chunk workgroup of the sequence once it has seen all the chunk sums
+// (psum, in LDS): the prefix, the chunk, and, in the workgroup that owns the
+// chosen chunk only, the token, from the weights it still holds in
+// registers.  Same arithmetic and order as select_terminal, so the same
+// token.  Without residual mass the workgroup of chunk 0 draws from q alone.
+template <int PER>
+__device__ void select_polled(const float* __restrict__ logits, const float* __restrict__ draft_logits, int V,
+                              int nc, float c, const AcceptInfo& a, int chunk, const float (&w)[PER],
+                              const float* psum, int32_t* __restrict__ out_tokens) {
+    static_assert(PER == 4, "one float4 per thread: the registers hold the chunk in token order");
+    constexpr int CH = PER * kStatThreads;
+    __shared__ float pre[kPollMaxBlocks + 1];
+    __shared__ float wtot[kStatThreads / kWave];
+    __shared__ int sel[2];
+    __shared__ int redi[kStatThreads / kWave];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    if (wave == 0) chunk_prefix(psum, nc, lane, pre, false);
+    __syncthreads();
+    if (!(pre[nc] > 0.f) && a.n != a.kb) {
+        if (chunk == 0) select_terminal<PER>(logits, draft_logits, V, nc, c, a, nullptr, out_tokens, SumSrc::Local);
+        return;
+    }
+    const float x = a.u_term * pre[nc];
+    if (wave == 0) {
+        const int cs = choose_chunk(pre, nc, x, lane);
+        if (lane == 0) sel[0] = cs;
+    }
+    __syncthreads();
+    const int cs = sel[0];
+    if (cs != chunk) return;   // block-uniform
+    const int tok = pick_in_chunk<PER>(w, x - pre[cs], cs * CH, sel, wtot, redi);
+    if (tid == 0) out_tokens[(size_t)a.t0 + a.n] = tok;
 }
 
 // One workgroup per (sampled sequence, chunk): the sum of the terminal weights
@@ -342,22 +404,32 @@ __global__ __launch_bounds__(kStatThreads) void residual_select_kernel(
     const int j = blockIdx.x;
     const AcceptInfo a = info[j];
     if (a.n < 0) return;
-    select_terminal(logits, draft_logits, V, nc, c, a, chunk_sums + (size_t)j * nc, out_tokens, false);
+    select_terminal(logits, draft_logits, V, nc, c, a, chunk_sums + (size_t)j * nc, out_tokens, SumSrc::Plain);
 }
 
 // Acceptance and residual draw in one launch, for small batches where the
 // two kernels' latency dominates: one workgroup per (sampled sequence, chunk).
 // Every workgroup of a sequence takes the acceptance decision itself (a few
 // hundred statistics records and K token logits: cheap next to the chunk it
-// streams), the one of chunk 0 writes it out, each sums its chunk of the
-// terminal weights, and the last to finish selects the token as above.  The
-// completion counters are zeroed by the statistics pass that runs first.
-template <int PER>
+// streams), the one of chunk 0 writes it out, and each sums its chunk of the
+// terminal weights.  Then, with POLL (at most kPollMaxBlocks workgroups, so
+// all of them are resident together), each publishes its sum in a 64-bit
+// slot tagged as written and reads all the slots of its sequence until every
+// one is tagged; the workgroup owning the chosen chunk picks the token from
+// its registers (select_polled).  The wait is bounded by spin_limit rounds;
+// a workgroup that runs out sums every chunk itself and writes the token if
+// it owns the chosen chunk, so the result does not depend on the bound.
+// Without POLL the sums are counted in with an atomic and the last workgroup
+// to finish selects, re-reading the chosen chunk.  The counters and slots are
+// zeroed by the kernel that runs first (the statistics pass or the
+// cooperative LM head).
+template <int PER, bool POLL>
 __global__ __launch_bounds__(kStatThreads) void accept_residual_kernel(
     const float* __restrict__ logits, const float* __restrict__ draft_logits, const int32_t* __restrict__ draft_tokens,
     const uint64_t* __restrict__ seeds, const int32_t* __restrict__ rows, SeqRows seq, int V, int nc, float c,
     RecLayout rec, int32_t* __restrict__ accepted_len, int32_t* __restrict__ out_tokens,
-    float* __restrict__ probs_at_draft, float* __restrict__ chunk_sums, int* __restrict__ counters) {
+    float* __restrict__ probs_at_draft, float* __restrict__ chunk_sums, int* __restrict__ counters,
+    unsigned long long* __restrict__ slots, int spin_limit) {
     static_assert(kStatThreads == kAcceptThreads, "one workgroup shape for both phases");
     __shared__ StatRec recs[kRecBuf];
     __shared__ Merged merged[kMaxRows];
@@ -378,6 +450,48 @@ __global__ __launch_bounds__(kStatThreads) void accept_residual_kernel(
 #pragma unroll
     for (int k = 0; k < PER; ++k) s += w[k];
     s = block_sum(s, red);
+    if constexpr (POLL) {
+        __shared__ float psum[kPollMaxBlocks];
+        __shared__ int seen;
+        constexpr int kPer = kPollMaxBlocks / kWave;
+        unsigned long long* mine = slots + (size_t)j * nc;
+        const int lane = threadIdx.x & 63;
+        if (threadIdx.x == 0)
+            __hip_atomic_store(mine + chunk, kPollTag | __float_as_uint(s), __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT);
+        if (threadIdx.x < kWave) {
+            bool all = false;
+            for (int round = 0;; ++round) {
+                // every load goes out (a slot past nc re-reads the last one),
+                // so a round is one memory round trip
+                unsigned long long v[kPer];
+#pragma unroll
+                for (int i = 0; i < kPer; ++i)
+                    v[i] = __hip_atomic_load(mine + min(lane + i * kWave, nc - 1), __ATOMIC_RELAXED,
+                                             __HIP_MEMORY_SCOPE_AGENT);
+                bool miss = false;
+#pragma unroll
+                for (int i = 0; i < kPer; ++i) miss |= (v[i] >> 32) != (kPollTag >> 32);
+                if (__ballot(miss) == 0ull) {
+#pragma unroll
+                    for (int i = 0; i < kPer; ++i)
+                        if (lane + i * kWave < nc) psum[lane + i * kWave] = __uint_as_float((uint32_t)v[i]);
+                    all = true;
+                    break;
+                }
+                if (round >= spin_limit) break;
+                __builtin_amdgcn_s_sleep(1);
+            }
+            if (lane == 0) seen = all;
+        }
+        __syncthreads();
+        if (seen) {
+            select_polled<PER>(logits, draft_logits, V, nc, c, a, chunk, w, psum, out_tokens);
+        } else {
+            select_terminal<PER>(logits, draft_logits, V, nc, c, a, nullptr, out_tokens, SumSrc::Local, chunk);
+        }
+        return;
+    }
     if (threadIdx.x == 0) {
         // published as in residual_kernel: an exchange whose result is waited
         // for, then the count
@@ -394,15 +508,18 @@ __global__ __launch_bounds__(kStatThreads) void accept_residual_kernel(
 hipError_t launch_accept_residual(const float* logits, const float* draft_logits, const int32_t* draft_tokens,
                                   const uint64_t* seeds, const int32_t* rows, int n_rows, SeqRows seq, int V,
                                   float inv_t_log2e, RecLayout rec, int32_t* accepted_len, int32_t* out_tokens,
-                                  float* probs_at_draft, float* chunk_sums, int* counters, hipStream_t stream) {
+                                  float* probs_at_draft, float* chunk_sums, int* counters,
+                                  unsigned long long* slots, int spin_limit, hipStream_t stream) {
     if (n_rows == 0) return hipSuccess;
     // small chunks: every workgroup sums (and the selecting one re-reads) a
     // quarter of a statistics chunk, one memory round trip each
     const int nc = n_fused_chunks(V);
-    hipLaunchKernelGGL(accept_residual_kernel<kFusedPer>, dim3((unsigned)((long)n_rows * nc)), dim3(kStatThreads), 0,
-                       stream,
-                       logits, draft_logits, draft_tokens, seeds, rows, seq, V, nc, inv_t_log2e, rec, accepted_len,
-                       out_tokens, probs_at_draft, chunk_sums, counters);
+    const long blocks = (long)n_rows * nc;
+    auto kern = blocks <= kPollMaxBlocks ? accept_residual_kernel<kFusedPer, true>
+                                         : accept_residual_kernel<kFusedPer, false>;
+    hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(kStatThreads), 0, stream, logits, draft_logits,
+                       draft_tokens, seeds, rows, seq, V, nc, inv_t_log2e, rec, accepted_len, out_tokens,
+                       probs_at_draft, chunk_sums, counters, slots, max(spin_limit, 0));
     return hipGetLastError();
 }
 

@@ -65,14 +65,16 @@ __device__ __forceinline__ int chunk_index(int v_begin, int tid, int k) {
 template <bool NEED_SUM, bool STREAM, bool VEC>
 __global__ __launch_bounds__(kStatThreads) void softmax_stats_kernel(
     const float* __restrict__ logits, const float* __restrict__ draft_logits, const int32_t* __restrict__ rows,
-    int n_rows, SeqRows seq, int V, int nc, float c, StatRec* __restrict__ stats, int* __restrict__ zero_counters) {
+    int n_rows, SeqRows seq, int V, int nc, float c, StatRec* __restrict__ stats, int* __restrict__ zero, int n_zero) {
     __shared__ float sm[kStatThreads / kWave];
     __shared__ int si[kStatThreads / kWave];
     __shared__ int sb[kStatThreads / kWave];
 
     const int K = seq.K;
-    // completion counters of a fused accept + residual launch that follows
-    if (zero_counters && blockIdx.x < n_rows && threadIdx.x == 0) zero_counters[blockIdx.x] = 0;
+    // completion counters and poll slots of a fused accept + residual launch
+    // that follows
+    if (blockIdx.x == 0)
+        for (int i = threadIdx.x; i < n_zero; i += kStatThreads) zero[i] = 0;
     const int job = blockIdx.x / nc;
     const int chunk = blockIdx.x - job * nc;
     const int tgt_jobs = logits ? n_rows * (K + 1) : 0;   // no target rows: draft rows only
@@ -213,7 +215,7 @@ hipError_t launch_fold_records(const StatRec* in, int recs_per_row, int rows, in
 
 hipError_t launch_softmax_stats(const float* logits, const float* draft_logits, const int32_t* rows, int n_rows,
                                 SeqRows seq, int V, float inv_t_log2e, bool need_sum, StatRec* stats,
-                                hipStream_t stream, int* zero_counters) {
+                                hipStream_t stream, int* zero, int n_zero) {
     const int nc = n_chunks(V);
     const long jobs = (logits ? (long)n_rows * (seq.K + 1) : 0) + (draft_logits ? (long)n_rows * seq.K : 0);
     const long blocks = jobs * nc;
@@ -230,7 +232,7 @@ hipError_t launch_softmax_stats(const float* logits, const float* draft_logits, 
                                         : (vec ? softmax_stats_kernel<false, false, true>
                                                : softmax_stats_kernel<false, false, false>));
     hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(kStatThreads), 0, stream, logits, draft_logits, rows, n_rows,
-                       seq, V, nc, inv_t_log2e, stats, zero_counters);
+                       seq, V, nc, inv_t_log2e, stats, zero, zero ? n_zero : 0);
     return hipGetLastError();
 }
 

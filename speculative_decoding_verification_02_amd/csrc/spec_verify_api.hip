@@ -30,6 +30,10 @@ constexpr int kMaxDevices = 64;
 
 std::atomic<int> g_cus[kMaxDevices];
 std::atomic<void*> g_scratch[kMaxDevices];   // device address of `scratch`, per device
+// rounds a workgroup of the one-launch accept + residual polls for its
+// sequence's chunk sums before it sums every chunk itself
+std::atomic<int> g_poll_limit{sv::kDefaultPollLimit};
+int poll_limit() { return g_poll_limit.load(std::memory_order_relaxed); }
 
 spec_status_t hip_fail(hipError_t e) {
     g_detail = hipGetErrorString(e);
@@ -92,11 +96,13 @@ struct Workspace {
     sv::AcceptInfo* info;
     float* sums;
     int* counters;
+    unsigned long long* slots;   // poll slots of the one-launch accept + residual, right after the counters' block
 };
 
 // Layout for up to B selected rows: chunk statistics of B*(K+1) target rows and
 // B*K draft rows, one AcceptInfo per row, the residual chunk sums, and one
-// completion counter per row (zeroed by the accept kernel before use).
+// completion counter per row followed by the poll slots of the one-launch
+// accept + residual (both zeroed by the kernel that runs before it).
 size_t workspace_layout(int B, int K, int V, void* base, Workspace* ws) {
     const size_t nc = (size_t)sv::n_chunks(V);
     const size_t stats = align256(((size_t)B * (K + 1) + (size_t)B * K) * nc * sizeof(sv::StatRec));
@@ -104,13 +110,15 @@ size_t workspace_layout(int B, int K, int V, void* base, Workspace* ws) {
     // residual chunk sums: one per statistics chunk, or per (smaller) chunk of
     // the one-launch accept + residual, whichever is more
     const size_t sums = align256((size_t)B * std::max(nc, (size_t)sv::n_fused_chunks(V)) * sizeof(float));
-    const size_t counters = align256((size_t)B * sizeof(int));
+    const size_t counter_block = align256((size_t)B * sizeof(int));
+    const size_t counters = counter_block + align256((size_t)sv::kPollMaxBlocks * sizeof(unsigned long long));
     if (ws) {
         char* p = static_cast<char*>(base);
         ws->stats = reinterpret_cast<sv::StatRec*>(p);
         ws->info = reinterpret_cast<sv::AcceptInfo*>(p + stats);
         ws->sums = reinterpret_cast<float*>(p + stats + info);
         ws->counters = reinterpret_cast<int*>(p + stats + info + sums);
+        ws->slots = reinterpret_cast<unsigned long long*>(p + stats + info + sums + counter_block);
     }
     return stats + info + sums + counters;
 }
@@ -185,11 +193,11 @@ spec_status_t sample_impl(const float* logits, const float* draft_logits, const 
     // workgroup repeats the decision, so only while the rows to merge are few
     const bool fused = (long)nr * (2 * seq.K + 1) <= sv::kFusedAcceptMaxRows;
     hipError_t e = sv::launch_softmax_stats(logits, dl, rows, nr, seq, V, c, true, ws.stats, s,
-                                            fused ? ws.counters : nullptr);
+                                            fused ? ws.counters : nullptr, sv::accept_zero_ints(seq.B, nr, V));
     if (e == hipSuccess && fused) {
         e = sv::launch_accept_residual(logits, dl, draft_tokens, seeds, rows, nr, seq, V, c,
                                        pass_layout(ws.stats, nr, seq.K, V), accepted_len, out_tokens, probs_at_draft,
-                                       ws.sums, ws.counters, s);
+                                       ws.sums, ws.counters, ws.slots, poll_limit(), s);
     } else {
         if (e == hipSuccess)
             e = sv::launch_accept(logits, dl, draft_tokens, seeds, rows, nr, seq, V, c, true,
@@ -224,6 +232,10 @@ bool rows_ok(const int32_t* rows, int n, int B) { return rows ? (n >= 0 && n <= 
 }  // namespace
 
 extern "C" {
+
+int spec_set_poll_limit(int rounds) {
+    return g_poll_limit.exchange(rounds < 0 ? sv::kDefaultPollLimit : rounds, std::memory_order_relaxed);
+}
 
 spec_status_t spec_verify_logits(const void* hidden, const void* w_lmhead, spec_dtype_t dtype, float* logits, int B,
                                  int K, int V, int H, spec_stream_t stream) {
@@ -383,7 +395,8 @@ spec_status_t spec_verify_step(const void* hidden, const void* w_lmhead, spec_dt
         if (crec > 0) {
             sv::StatRec* trec = tstats;                          // M x crec
             sv::StatRec* drec = tstats + (size_t)M * crec;       // B*K x crec
-            const sv::CoopStats cs{trec, dl, dl ? B * K : 0, drec, c, fused ? ws.counters : nullptr, fused ? ns : 0};
+            const sv::CoopStats cs{trec, dl, dl ? B * K : 0, drec, c, fused ? ws.counters : nullptr,
+                                   fused ? sv::accept_zero_ints(B, ns, V) : 0};
             e = sv::launch_lmhead_coop_stats(static_cast<const uint16_t*>(hidden),
                                              static_cast<const uint16_t*>(w_lmhead), logits, M, V, H, cus, s, cs);
             if (e == hipSuccess && ng > 0)
@@ -394,7 +407,7 @@ spec_status_t spec_verify_step(const void* hidden, const void* w_lmhead, spec_dt
             if (e == hipSuccess && ns > 0) {
                 if (fused) {
                     e = sv::launch_accept_residual(logits, dl, draft_tokens, seeds, sampled_rows, ns, seq, V, c, lay,
-                                                   accepted_len, out_tokens, probs_at_draft, ws.sums, ws.counters, s);
+                                                   accepted_len, out_tokens, probs_at_draft, ws.sums, ws.counters, ws.slots, poll_limit(), s);
                 } else {
                     e = sv::launch_accept(logits, dl, draft_tokens, seeds, sampled_rows, ns, seq, V, c, true, lay,
                                           accepted_len, out_tokens, probs_at_draft, ws.info, ws.counters, s);
@@ -441,7 +454,7 @@ spec_status_t spec_verify_step(const void* hidden, const void* w_lmhead, spec_dt
     // also clears the completion counters a fused accept + residual needs)
     const int nc = sv::n_chunks(V);
     if (dl) e = sv::launch_softmax_stats(nullptr, dl, sampled_rows, ns, seq, V, c, true, ws.stats, s,
-                                         fused ? ws.counters : nullptr);
+                                         fused ? ws.counters : nullptr, sv::accept_zero_ints(B, ns, V));
     int nrec = 0;
     if (e == hipSuccess && cus == 0) e = num_cus(&cus);
     if (e == hipSuccess)
@@ -469,7 +482,7 @@ spec_status_t spec_verify_step(const void* hidden, const void* w_lmhead, spec_dt
     if (e == hipSuccess && ns > 0) {
         if (fused) {
             e = sv::launch_accept_residual(logits, dl, draft_tokens, seeds, sampled_rows, ns, seq, V, c, lay,
-                                           accepted_len, out_tokens, probs_at_draft, ws.sums, ws.counters, s);
+                                           accepted_len, out_tokens, probs_at_draft, ws.sums, ws.counters, ws.slots, poll_limit(), s);
         } else {
             e = sv::launch_accept(logits, dl, draft_tokens, seeds, sampled_rows, ns, seq, V, c, true, lay,
                                   accepted_len, out_tokens, probs_at_draft, ws.info, ws.counters, s);

@@ -25,7 +25,7 @@ hipError_t launch_lmhead_f32(const float* hidden, const float* W, float* logits,
 // per workgroup w of n_rec, the record of hidden row m over the workgroup's
 // contiguous vocabulary range at tgt[m * n_rec + w], and likewise of draft
 // row d (n_draft rows of V fp32 logits at draft) at drf[d * n_rec + w], sums
-// relative to c = log2(e) / T; workgroup 0 also clears n_zero counters.
+// relative to c = log2(e) / T; workgroup 0 also zeroes n_zero ints at zero.
 struct CoopStats {
     StatRec* tgt;
     const float* draft;
@@ -56,11 +56,11 @@ int lmhead_big_records(int M, int V, int H);
 //   jobs = (if logits) n_rows*(K+1) target slots, then (if draft_logits)
 //   n_rows*K draft slots, K = seq.K; slots past a ragged sequence's own rows
 //   are skipped.
-//   zero_counters (optional): n_rows completion counters cleared on the way,
-//   for a fused accept + residual launch that follows.
+//   zero, n_zero (optional): ints zeroed on the way (the completion counters
+//   and poll slots of a fused accept + residual launch that follows).
 hipError_t launch_softmax_stats(const float* logits, const float* draft_logits, const int32_t* rows, int n_rows,
                                 SeqRows seq, int V, float inv_t_log2e, bool need_sum, StatRec* stats,
-                                hipStream_t stream, int* zero_counters = nullptr);
+                                hipStream_t stream, int* zero = nullptr, int n_zero = 0);
 
 // Where the accept kernel finds the statistics records of a sequence's rows.
 // Target rows: tgt + (tgt_by_row ? t0 + i : j*(K+1) + i) * tgt_nc (by packed
@@ -101,18 +101,37 @@ hipError_t launch_accept_both(const float* logits, const float* draft_logits, co
                               hipStream_t stream);
 
 // Acceptance and residual draw of sampled sequences in one launch (small
-// batches); needs the counters cleared by launch_softmax_stats.  Used while
-// sequences x (2K+1) rows stay within this bound (measured: 17 vs 20 us at
-// one sequence with K = 5; 45 vs 35 us at 16 sequences with K = 15).
+// batches); needs its counters and slots zeroed by the kernel before it
+// (launch_softmax_stats or the cooperative LM head, over accept_zero_ints
+// ints from the counters).  Used while sequences x (2K+1) rows stay within
+// this bound (measured: 17 vs 20 us at one sequence with K = 5; 45 vs 35 us at
+// 16 sequences with K = 15).
 constexpr int kFusedAcceptMaxRows = 48;
 // The one-launch accept + residual splits the terminal rows into chunks of
 // kFusedPer entries per thread (1024 entries), a quarter of a statistics chunk.
 constexpr int kFusedPer = 4;
 inline int n_fused_chunks(int V) { return (V + kFusedPer * kStatThreads - 1) / (kFusedPer * kStatThreads); }
+// Launches of at most this many workgroups publish their chunk sums in
+// tagged 64-bit slots that every workgroup polls (all of them fit on the GPU
+// at once); larger ones count the sums in and select in the last workgroup.
+constexpr int kPollMaxBlocks = 256;
+constexpr unsigned long long kPollTag = 1ull << 32;   // a written slot: tag | float bits of the sum
+// Poll rounds a workgroup waits for its sequence's sums before it sums every
+// chunk itself (the default of the library; tests may lower it).
+constexpr int kDefaultPollLimit = 1 << 16;
+// Ints from the counters to zero before a launch of n_rows sequences: the
+// counters of up to B sequences (their 256-byte-aligned block), then the
+// slots that directly follow them.
+inline int accept_zero_ints(int B, int n_rows, int V) {
+    const long nc = n_fused_chunks(V);
+    const int counter_ints = (int)((((long)B * 4 + 255) / 256) * 64);
+    return (long)n_rows * nc <= kPollMaxBlocks ? counter_ints + (int)(2 * n_rows * nc) : counter_ints;
+}
 hipError_t launch_accept_residual(const float* logits, const float* draft_logits, const int32_t* draft_tokens,
                                   const uint64_t* seeds, const int32_t* rows, int n_rows, SeqRows seq, int V,
                                   float inv_t_log2e, RecLayout rec, int32_t* accepted_len, int32_t* out_tokens,
-                                  float* probs_at_draft, float* chunk_sums, int* counters, hipStream_t stream);
+                                  float* probs_at_draft, float* chunk_sums, int* counters,
+                                  unsigned long long* slots, int spin_limit, hipStream_t stream);
 
 // Greedy verification of draft trees (N+1 rows per sequence, statistics from
 // launch_softmax_stats over the dense layout with K = N).

@@ -30,9 +30,18 @@ def test_exports_every_declared_symbol(lib):
                           "spec_accept_greedy_ragged", "spec_accept_sample_ragged", "spec_tree_accept_greedy",
                           "spec_ngram_propose", "spec_ngram_workspace_bytes",
                           "spec_verify_step", "spec_verify_step_workspace_bytes", "spec_verify_step_noalloc",
-                          "spec_workspace_bytes", "spec_status_string", "spec_last_error_detail"}
+                          "spec_workspace_bytes", "spec_status_string", "spec_last_error_detail",
+                          "spec_set_poll_limit"}
     for n in names:
         assert hasattr(lib, n), n
+
+
+def test_poll_limit_setter(lib):
+    default = sv.spec_set_poll_limit(5)
+    assert default == 65536
+    assert sv.spec_set_poll_limit(0) == 5
+    assert sv.spec_set_poll_limit(-1) == 0
+    assert sv.spec_set_poll_limit(-1) == default
 
 
 def test_status_strings(lib):
