@@ -229,8 +229,8 @@ hipError_t launch_skinny(const uint16_t* hidden, const uint16_t* W, float* logit
 // and the NW partial 16 x 16 accumulators of a tile are summed in LDS in wave
 // order (fixed order: bitwise reproducible).  Loads run one tile ahead: while
 // stage st of tile t is consumed, stage st of the next tile is issued.  Each
-// workgroup takes a contiguous, balanced range of tiles, so it streams one
-// contiguous region of W.
+// workgroup takes a contiguous range of tiles (sized by the parity of its XCD,
+// below), so it streams one contiguous region of W.
 //
 // The weight loads are buffer loads, exactly kLoads per stage with no branch
 // around them: the vector-memory counter of gfx9 counts in issue order, and
@@ -251,6 +251,36 @@ hipError_t launch_skinny(const uint16_t* hidden, const uint16_t* W, float* logit
 // one 32-lane group per row reduces its row from LDS: max, first index of
 // the max, sum of 2^((z - max) c).  No per-entry checks: a NaN or +inf shows
 // in the maximum or the sum and marks the record bad.
+// Tile ranges of the cooperative kernel.  Each workgroup owns a contiguous
+// range of 16-row tiles, sized in proportion to a weight that depends on the
+// parity of its index, which is the parity of the XCD it runs on (workgroups
+// go to the XCDs round-robin).  Per-workgroup timestamps of this kernel on
+// MI355X with equal ranges put the workgroups of the even XCDs at the end of
+// their ranges ~15% sooner than those of the odd XCDs (129-135 against
+// 150-155 us at B=1, K=5, H=4096, V=128256), the same way on every box
+// measured.  The odd ones get the smaller ranges: with weights 1000 : 800 the
+// kernel took 149.4 us against 155.7 us with equal ones (920: 153.3, 830:
+// 150.9, 770: 151.0, 700: 153.1; one box, medians of 5 x 200 launches).  The
+// ranges are a fixed function of (n_tiles, grid), so results are
+// reproducible.
+#ifndef SV_COOP_WEIGHT_ODD
+#define SV_COOP_WEIGHT_ODD 800
+#endif
+constexpr long kCoopWeightEven = 1000, kCoopWeightOdd = SV_COOP_WEIGHT_ODD;
+__host__ __device__ inline long coop_weight_below(int b) {
+    return (long)((b + 1) / 2) * kCoopWeightEven + (long)(b / 2) * kCoopWeightOdd;
+}
+// first tile of workgroup b (b = grid: n_tiles)
+__host__ __device__ inline int coop_tile_begin(int b, int n_tiles, int grid) {
+    return (int)(((long)n_tiles * coop_weight_below(b)) / coop_weight_below(grid));
+}
+// the most tiles any workgroup gets: floor(a + x) - floor(a) <= ceil(x)
+__host__ __device__ inline int coop_max_tiles(int n_tiles, int grid) {
+    const long wmax = kCoopWeightEven > kCoopWeightOdd ? kCoopWeightEven : kCoopWeightOdd;
+    const long wt = coop_weight_below(grid);
+    return (int)(((long)n_tiles * wmax + wt - 1) / wt);
+}
+
 template <int RPL, int MAXST, int NW>
 struct Coop {
     static constexpr int kLanesPerRow = 64 / RPL;
@@ -266,7 +296,7 @@ struct Coop {
     // LDS with the stash: M target and n_draft draft rows, each as long as
     // the most columns a workgroup owns (whole tiles of 16) plus 16 floats,
     // which puts the two rows a wavefront reads at once 16 banks apart
-    static int stash_stride(int n_tiles, int grid) { return ((n_tiles + grid - 1) / grid) * 16 + 16; }
+    __host__ __device__ static int stash_stride(int n_tiles, int grid) { return coop_max_tiles(n_tiles, grid) * 16 + 16; }
     static size_t lds_bytes_stats(int n_tiles, int grid, int rows) {
         return lds_bytes() + (size_t)rows * stash_stride(n_tiles, grid) * sizeof(float);
     }
@@ -323,9 +353,10 @@ __global__ __launch_bounds__(NW * 64) void lmhead_coop_bf16(
                 (r < M && k < H) ? *reinterpret_cast<const u32x4*>(hidden + (size_t)r * H + k) : zero;
         }
 
-    // this workgroup's tiles: a contiguous, balanced range [t_begin, t_end)
-    const int t_begin = (int)(((long)n_tiles * blockIdx.x) / gridDim.x);
-    const int t_end = (int)(((long)n_tiles * (blockIdx.x + 1)) / gridDim.x);
+    // this workgroup's tiles: a contiguous range [t_begin, t_end), sized by
+    // the parity weights above
+    const int t_begin = coop_tile_begin(blockIdx.x, n_tiles, gridDim.x);
+    const int t_end = coop_tile_begin(blockIdx.x + 1, n_tiles, gridDim.x);
 
     // The loads of stage st of tile t: the buffer resource spans the tile's
     // rows below V (none for a tile at or past t_end), and the whole offset
@@ -380,7 +411,7 @@ __global__ __launch_bounds__(NW * 64) void lmhead_coop_bf16(
     // logits of this workgroup's tiles, [row][column - dcb] (STASH only;
     // sized by the launcher)
     float* stash = reinterpret_cast<float*>(smem + S::kLdsBase);   // [M + n_draft][stash_cols]
-    const int stash_cols = ((n_tiles + (int)gridDim.x - 1) / (int)gridDim.x) * 16 + 16;
+    const int stash_cols = S::stash_stride(n_tiles, gridDim.x);
     if constexpr (STATS) {
         // before the tiles: the target rows' columns past this workgroup's
         // tiles (-inf) and the draft rows (row `wave`'s first entries from the
