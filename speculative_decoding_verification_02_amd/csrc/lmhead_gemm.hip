@@ -791,36 +791,49 @@ struct BigPhase {
     static constexpr bool kMain = MAIN, kNext = NEXT;
 };
 
+// Work items of the direct-to-LDS kernel per XCD: the first item of XCD x of
+// n_items (x = 8: n_items).  A CU runs one workgroup at a time, so an XCD
+// (32 CUs) with n items runs ceil(n / 32) rounds.  The count of the even
+// XCDs is the larger share at weights 103 : 100 (their tiles ran 2-4%
+// faster than the odd XCDs' in per-workgroup timestamps at B=256 and B=512),
+// but no more than the rounds an equal split needs allow, so no XCD runs a
+// round more than it would with equal counts.  (Whole vocabulary tiles per
+// XCD left 675 items on two XCDs at B=256, K=8, V=152064: a 22nd round of 3
+// tiles.  Contiguous items: 4850 -> 4717 us there.  Letting the even XCDs
+// run one partial round more, so that the odd ones run fewer tiles, measured
+// no better at B=512.)
+__host__ __device__ inline long big_items_begin(int x, long n_items) {
+    const long per = (n_items + 7) / 8;                    // most items of an equal split
+    const long cap = ((per + 31) / 32) * 32;               // in the rounds that split needs
+    long even = (n_items * 103 + 4 * 203 - 1) / (4 * 203); // share at 103 : 100, rounded up
+    even = even < cap ? even : cap;
+    even = even < n_items / 4 ? even : n_items / 4;         // the four even XCDs take at most all
+    even = even > n_items / 8 ? even : n_items / 8;         // never below the equal share
+    const long rest = n_items - 4 * even;                   // for the four odd XCDs
+    const long evens_below = (x + 1) / 2, odds_below = x / 2;
+    return evens_below * even + (odds_below * rest) / 4;
+}
+
 // With STATS, the workgroup also writes the softmax statistics of each of its
 // hidden rows over its 256 vocabulary columns: stats[m * tiles_n + tn].
 template <int BK, int SLOTS, int NA, int NB, bool STATS, int NW, int HS>
 __global__ __launch_bounds__(NW * 64, 1) void lmhead_big_bf16(
     const uint16_t* __restrict__ hidden, const uint16_t* __restrict__ W, float* __restrict__ logits,
-    int M, int V, int H, int tiles_n, int tiles_m, int group_m, StatRec* __restrict__ stats, float c) {
+    int M, int V, int H, int tiles_n, int tiles_m, StatRec* __restrict__ stats, float c) {
     using G = Big<BK, SLOTS, NA, NB, NW>;
     extern __shared__ __align__(16) unsigned char smem[];
     u32x4* lds = reinterpret_cast<u32x4*>(smem);   // [slot][W rows 0..255 | hidden rows 0..BM-1][CPR chunks]
 
-    // Workgroups go to the XCDs round-robin.  XCD x owns vocabulary tiles
-    // [n_lo, n_hi) and walks them in groups of group_m hidden-row tiles:
-    // for each group, every vocabulary tile, the group's row tiles next to
-    // each other, so the workgroups running together share operand slices
-    // through the XCD's L2.
+    // Workgroups go to the XCDs round-robin.  The work items (vocabulary
+    // tile, hidden-row tile) are ordered vocabulary-major and XCD x owns the
+    // contiguous range of them that big_items_begin gives it, so the
+    // workgroups running together on an XCD share operand slices through its
+    // L2 (all row tiles of a vocabulary tile run next to each other).
     const int xcd = blockIdx.x % 8, local = blockIdx.x / 8;
-    const int n_lo = (int)((long)tiles_n * xcd / 8), nn = (int)((long)tiles_n * (xcd + 1) / 8) - n_lo;
-    if (local >= nn * tiles_m) return;
-    const int full = tiles_m / group_m;
-    int grp, rem, gm;
-    if (local < full * nn * group_m) {
-        grp = local / (nn * group_m);
-        rem = local - grp * nn * group_m;
-        gm = group_m;
-    } else {
-        grp = full;
-        rem = local - full * nn * group_m;
-        gm = tiles_m - full * group_m;
-    }
-    const int tn = n_lo + rem / gm, tm = grp * group_m + rem % gm;
+    const long i_lo = big_items_begin(xcd, (long)tiles_n * tiles_m), i_hi = big_items_begin(xcd + 1, (long)tiles_n * tiles_m);
+    if (local >= i_hi - i_lo) return;
+    const long item = i_lo + local;
+    const int tn = (int)(item / tiles_m), tm = (int)(item - (long)tn * tiles_m);
     const int v0 = tn * kBigBN, m0 = tm * G::kBM;
 
     const int tid = threadIdx.x;
@@ -1105,7 +1118,7 @@ __global__ __launch_bounds__(NW * 64, 1) void lmhead_big_bf16(
 
 template <int BK, int SLOTS, int NA, int NB, bool STATS, int NW = 4, int HS = 0>
 hipError_t launch_big_cfg(const uint16_t* hidden, const uint16_t* W, float* logits, int M, int V, int H,
-                          hipStream_t stream, StatRec* stats = nullptr, float c = 0.f, int group_m = 0) {
+                          hipStream_t stream, StatRec* stats = nullptr, float c = 0.f) {
     using G = Big<BK, SLOTS, NA, NB, NW>;
     constexpr size_t kLds = HS ? (size_t)(SLOTS * kBigBN + HS * G::kBM) * G::kCPR * 16 : G::kLds;
     static_assert(kLds <= 160 * 1024, "rings exceed the 160 KB of a CU");
@@ -1119,11 +1132,15 @@ hipError_t launch_big_cfg(const uint16_t* hidden, const uint16_t* W, float* logi
     if (e != hipSuccess) return e;
     const int tiles_n = (V + kBigBN - 1) / kBigBN;
     const int tiles_m = (M + G::kBM - 1) / G::kBM;
-    const int max_nn = (tiles_n + 7) / 8;    // most vocabulary tiles any XCD owns
-    const int grid = 8 * max_nn * tiles_m;
-    const int gm = group_m > 0 ? min(group_m, tiles_m) : tiles_m;
-    hipLaunchKernelGGL(kern, dim3(grid), dim3(G::kThreads), kLds, stream, hidden, W, logits, M, V, H, tiles_n,
-                       tiles_m, gm, stats, c);
+    long most = 0;                           // most items any XCD owns
+    for (int x = 0; x < 8; ++x) {
+        const long n = (long)tiles_n * tiles_m;
+        most = std::max(most, big_items_begin(x + 1, n) - big_items_begin(x, n));
+    }
+    const long grid = 8 * most;
+    if (grid > 0x7fffffffL) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(G::kThreads), kLds, stream, hidden, W, logits, M, V, H,
+                       tiles_n, tiles_m, stats, c);
     return hipGetLastError();
 }
 

@@ -75,8 +75,13 @@ __global__ __launch_bounds__(kStatThreads) void softmax_stats_kernel(
     // that follows
     if (blockIdx.x == 0)
         for (int i = threadIdx.x; i < n_zero; i += kStatThreads) zero[i] = 0;
+    // chunk positions rotate with the row: workgroups go to the XCDs
+    // round-robin, and with chunk = blockIdx % nc each XCD would read the
+    // same chunk positions of every row (per-workgroup timestamps put those
+    // XCDs' workgroups at 10 to 31 us for the same work)
     const int job = blockIdx.x / nc;
-    const int chunk = blockIdx.x - job * nc;
+    const int chunk = (int)(((long)(blockIdx.x - job * nc) + job) % nc);
+    const long slot = (long)job * nc + chunk;              // the record's place: (job, chunk)
     const int tgt_jobs = logits ? n_rows * (K + 1) : 0;   // no target rows: draft rows only
     const bool target = job < tgt_jobs;
     int j, i;
@@ -94,7 +99,7 @@ __global__ __launch_bounds__(kStatThreads) void softmax_stats_kernel(
     // skipped sequence, malformed row_start, or a position past this
     // sequence's drafts: the accept kernel never reads the record
     if (b < 0 || b >= seq.B || !seq.get(b, t0, kb) || (target ? i > kb : i >= kb)) {
-        if (tid == 0) stats[blockIdx.x] = StatRec{-INFINITY, 0.f, INT_MAX, 0};
+        if (tid == 0) stats[slot] = StatRec{-INFINITY, 0.f, INT_MAX, 0};
         return;
     }
     const float* row = target ? logits + ((size_t)t0 + i) * V : draft_logits + ((size_t)(t0 - b) + i) * V;
@@ -149,7 +154,7 @@ __global__ __launch_bounds__(kStatThreads) void softmax_stats_kernel(
 #pragma unroll
         for (int w = 1; w < kStatThreads / kWave; ++w) s += sm[w];
     }
-    if (tid == 0) stats[blockIdx.x] = StatRec{bm, s, bi, bbad};
+    if (tid == 0) stats[slot] = StatRec{bm, s, bi, bbad};
 }
 
 // Fold the LM-head epilogue's records (one per 256 vocabulary entries of a
