@@ -78,7 +78,8 @@ __global__ __launch_bounds__(kStatThreads) void softmax_stats_kernel(
     // chunk positions rotate with the row: workgroups go to the XCDs
     // round-robin, and with chunk = blockIdx % nc each XCD would read the
     // same chunk positions of every row (per-workgroup timestamps put those
-    // XCDs' workgroups at 10 to 31 us for the same work)
+    // XCDs' workgroups at 10 to 31 us for the same work; the pass as a whole
+    // measured the same either way, and the records are the same bits)
     const int job = blockIdx.x / nc;
     const int chunk = (int)(((long)(blockIdx.x - job * nc) + job) % nc);
     const long slot = (long)job * nc + chunk;              // the record's place: (job, chunk)
