@@ -30,13 +30,15 @@ __global__ __launch_bounds__(kAcceptThreads) void accept_kernel(
     const float* __restrict__ logits, const float* __restrict__ draft_logits, const int32_t* __restrict__ draft_tokens,
     const uint64_t* __restrict__ seeds, const int32_t* __restrict__ rows, int n_rows, SeqRows seq, int V,
     float c, RecLayout rec, int32_t* __restrict__ accepted_len, int32_t* __restrict__ out_tokens,
-    float* __restrict__ probs_at_draft, AcceptInfo* __restrict__ info, int* __restrict__ counters) {
+    float* __restrict__ probs_at_draft, AcceptInfo* __restrict__ info, int* __restrict__ counters,
+    unsigned long long* __restrict__ slots, int spq) {
     __shared__ StatRec recs[kRecBuf];
     __shared__ Merged merged[kMaxRows];
     __shared__ AcceptInfo sinfo;
     const int j = blockIdx.x;
     const int b = rows ? rows[j] : j;
     if (SAMPLED && threadIdx.x == 0) counters[j] = 0;   // the residual kernel counts its chunk blocks from zero
+    if (SAMPLED && (int)threadIdx.x < spq) slots[(size_t)j * spq + threadIdx.x] = 0ull;   // or polls these
     const AcceptInfo a = accept_sequence<SAMPLED>(logits, draft_logits, draft_tokens, seeds, j, b, seq, V, c, rec,
                                                   true, accepted_len, out_tokens, probs_at_draft, recs, merged,
                                                   &sinfo);
@@ -51,7 +53,8 @@ __global__ __launch_bounds__(kAcceptThreads) void accept_both_kernel(
     const uint64_t* __restrict__ seeds, const int32_t* __restrict__ greedy_rows, int n_greedy,
     const int32_t* __restrict__ sampled_rows, SeqRows seq, int V, float c, RecLayout rec_greedy,
     RecLayout rec_sampled, int32_t* __restrict__ accepted_len, int32_t* __restrict__ out_tokens,
-    float* __restrict__ probs_at_draft, AcceptInfo* __restrict__ info, int* __restrict__ counters) {
+    float* __restrict__ probs_at_draft, AcceptInfo* __restrict__ info, int* __restrict__ counters,
+    unsigned long long* __restrict__ slots, int spq) {
     __shared__ StatRec recs[kRecBuf];
     __shared__ Merged merged[kMaxRows];
     __shared__ AcceptInfo sinfo;
@@ -65,6 +68,7 @@ __global__ __launch_bounds__(kAcceptThreads) void accept_both_kernel(
     const int js = j - n_greedy;
     const int b = sampled_rows ? sampled_rows[js] : js;
     if (threadIdx.x == 0) counters[js] = 0;   // the residual kernel counts its chunk blocks from zero
+    if ((int)threadIdx.x < spq) slots[(size_t)js * spq + threadIdx.x] = 0ull;   // or polls these
     const AcceptInfo a = accept_sequence<true>(logits, draft_logits, draft_tokens, seeds, js, b, seq, V, c,
                                                rec_sampled, true, accepted_len, out_tokens, probs_at_draft, recs,
                                                merged, &sinfo);
@@ -192,16 +196,17 @@ hipError_t launch_accept(const float* logits, const float* draft_logits, const i
                          const uint64_t* seeds, const int32_t* rows, int n_rows, SeqRows seq, int V,
                          float inv_t_log2e, bool sampled, RecLayout rec, int32_t* accepted_len,
                          int32_t* out_tokens, float* probs_at_draft, AcceptInfo* info, int* counters,
-                         hipStream_t stream) {
+                         hipStream_t stream, unsigned long long* slots, int slots_per_seq) {
     if (n_rows == 0) return hipSuccess;
+    if (!slots || slots_per_seq > kAcceptThreads) slots_per_seq = 0;
     if (sampled)
         hipLaunchKernelGGL(accept_kernel<true>, dim3(n_rows), dim3(kAcceptThreads), 0, stream, logits, draft_logits,
                            draft_tokens, seeds, rows, n_rows, seq, V, inv_t_log2e, rec, accepted_len,
-                           out_tokens, probs_at_draft, info, counters);
+                           out_tokens, probs_at_draft, info, counters, slots, slots_per_seq);
     else
         hipLaunchKernelGGL(accept_kernel<false>, dim3(n_rows), dim3(kAcceptThreads), 0, stream, logits, draft_logits,
                            draft_tokens, seeds, rows, n_rows, seq, V, inv_t_log2e, rec, accepted_len,
-                           out_tokens, probs_at_draft, info, counters);
+                           out_tokens, probs_at_draft, info, counters, nullptr, 0);
     return hipGetLastError();
 }
 
@@ -210,11 +215,13 @@ hipError_t launch_accept_both(const float* logits, const float* draft_logits, co
                               const int32_t* sampled_rows, int n_sampled, SeqRows seq, int V, float inv_t_log2e,
                               RecLayout rec_greedy, RecLayout rec_sampled, int32_t* accepted_len,
                               int32_t* out_tokens, float* probs_at_draft, AcceptInfo* info, int* counters,
-                              hipStream_t stream) {
+                              hipStream_t stream, unsigned long long* slots, int slots_per_seq) {
     if (n_greedy + n_sampled == 0) return hipSuccess;
+    if (!slots || slots_per_seq > kAcceptThreads) slots_per_seq = 0;
     hipLaunchKernelGGL(accept_both_kernel, dim3(n_greedy + n_sampled), dim3(kAcceptThreads), 0, stream, logits,
                        draft_logits, draft_tokens, seeds, greedy_rows, n_greedy, sampled_rows, seq, V, inv_t_log2e,
-                       rec_greedy, rec_sampled, accepted_len, out_tokens, probs_at_draft, info, counters);
+                       rec_greedy, rec_sampled, accepted_len, out_tokens, probs_at_draft, info, counters, slots,
+                       slots_per_seq);
     return hipGetLastError();
 }
 

@@ -20,6 +20,8 @@
 // (possible only through rounding when q_n ~ p_n) the draw uses q_n instead.
 #include <limits.h>
 
+#include <type_traits>
+
 #include "sv_accept.h"
 
 namespace sv {
@@ -51,12 +53,11 @@ __device__ __forceinline__ float term_weight(float zt, float zd, const TermNorm&
 // + e of the chunk.  VEC (V % 4 ==
 // 0): 128-bit loads, else 32-bit ones; USE_Q: the target row only.  No load
 // sits in a branch (entries past V read an in-range address and get weight
-// 0), so all of a thread's loads are in flight together.
+// 0), so all of a thread's loads are in flight together.  Two phases, so a
+// caller can have the next chunk's loads in flight while it weighs this one.
 template <bool VEC, bool USE_Q, int PER>
-__device__ __forceinline__ void chunk_weights_impl(const float* __restrict__ zt_row, const float* __restrict__ zd_row,
-                                                   int v_begin, int V, int tid, const TermNorm& tn, float c,
-                                                   float w[PER]) {
-    float zt[PER], zd[PER];
+__device__ __forceinline__ void chunk_load(const float* __restrict__ zt_row, const float* __restrict__ zd_row,
+                                           int v_begin, int V, int tid, float zt[PER], float zd[PER]) {
 #pragma unroll
     for (int q = 0; q < PER / 4; ++q) {
         const int v = v_begin + (q * kStatThreads + tid) * 4;
@@ -77,6 +78,10 @@ __device__ __forceinline__ void chunk_weights_impl(const float* __restrict__ zt_
             }
         }
     }
+}
+template <bool USE_Q, int PER>
+__device__ __forceinline__ void chunk_weigh(const float zt[PER], const float zd[PER], int v_begin, int V, int tid,
+                                            const TermNorm& tn, float c, float w[PER]) {
 #pragma unroll
     for (int k = 0; k < PER; ++k) {
         // computed for every entry (past V from a valid duplicate), then masked
@@ -84,6 +89,14 @@ __device__ __forceinline__ void chunk_weights_impl(const float* __restrict__ zt_
         const float tw = term_weight(zt[k], USE_Q ? 0.f : zd[k], tn, c, USE_Q);
         w[k] = v < V ? tw : 0.f;
     }
+}
+template <bool VEC, bool USE_Q, int PER>
+__device__ __forceinline__ void chunk_weights_impl(const float* __restrict__ zt_row, const float* __restrict__ zd_row,
+                                                   int v_begin, int V, int tid, const TermNorm& tn, float c,
+                                                   float w[PER]) {
+    float zt[PER], zd[PER];
+    chunk_load<VEC, USE_Q, PER>(zt_row, zd_row, v_begin, V, tid, zt, zd);
+    chunk_weigh<USE_Q, PER>(zt, zd, v_begin, V, tid, tn, c, w);
 }
 
 template <int PER = kStatPerThread>
@@ -230,12 +243,13 @@ __device__ int pick_in_chunk(const float (&mine)[PER], float xr, int v_begin, in
 enum class SumSrc { Atomic, Plain, Local };
 
 // Inverse-CDF selection of the terminal token of one sequence.  With
-// writer >= 0 the token is written only if it falls in chunk `writer` (so
+// w_lo >= 0 the token is written only if it falls in chunks [w_lo, w_hi) (so
 // several workgroups may run the selection and exactly one writes).
 template <int PER = kStatPerThread>
 __device__ void select_terminal(const float* __restrict__ logits, const float* __restrict__ draft_logits,
                                 int V, int nc, float c, const AcceptInfo& a, const float* chunk_sums,
-                                int32_t* __restrict__ out_tokens, SumSrc src = SumSrc::Atomic, int writer = -1) {
+                                int32_t* __restrict__ out_tokens, SumSrc src = SumSrc::Atomic, int w_lo = -1,
+                                int w_hi = -1) {
     constexpr int CH = PER * kStatThreads;               // entries per chunk
     __shared__ float pre[kMaxChunks * kChunk / CH + 1];  // prefix over chunk sums
     __shared__ float wl[CH];                             // weights of the selected chunk, token order
@@ -284,7 +298,7 @@ __device__ void select_terminal(const float* __restrict__ logits, const float* _
     }
     __syncthreads();
     const int cs = sel[0];
-    if (writer >= 0 && cs != writer) return;   // block-uniform
+    if (w_lo >= 0 && (cs < w_lo || cs >= w_hi)) return;   // block-uniform
     const int v_begin = cs * CH;
 
     // weights of chunk cs into LDS in token order
@@ -302,6 +316,44 @@ __device__ void select_terminal(const float* __restrict__ logits, const float* _
     for (int e = 0; e < PER; ++e) mine[e] = wl[tid * PER + e];
     const int tok = pick_in_chunk<PER>(mine, x - pre[cs], v_begin, sel, wtot, redi);
     if (tid == 0) out_tokens[(size_t)a.t0 + a.n] = tok;
+}
+
+// Wave 0 reads the n (<= kPollMaxBlocks) tagged slots of a sequence until
+// every one is written, at most spin_limit + 1 rounds of one memory round
+// trip each, and leaves the sums in psum.  Returns, in every thread of the
+// workgroup, whether it saw them all.  Each slot is its own publication (the
+// sum and its tag in one atomic word), so no ordering between slots is needed.
+__device__ bool poll_sums(const unsigned long long* slots, int n, int spin_limit, float* psum) {
+    __shared__ int seen;
+    constexpr int kPer = kPollMaxBlocks / kWave;
+    const int lane = threadIdx.x & 63;
+    if (threadIdx.x < kWave) {
+        bool all = false;
+        for (int round = 0;; ++round) {
+            // every load goes out (a slot past n re-reads the last one), so a
+            // round is one memory round trip
+            unsigned long long v[kPer];
+#pragma unroll
+            for (int i = 0; i < kPer; ++i)
+                v[i] = __hip_atomic_load(const_cast<unsigned long long*>(slots) + min(lane + i * kWave, n - 1),
+                                         __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            bool miss = false;
+#pragma unroll
+            for (int i = 0; i < kPer; ++i) miss |= (v[i] >> 32) != (kPollTag >> 32);
+            if (__ballot(miss) == 0ull) {
+#pragma unroll
+                for (int i = 0; i < kPer; ++i)
+                    if (lane + i * kWave < n) psum[lane + i * kWave] = __uint_as_float((uint32_t)v[i]);
+                all = true;
+                break;
+            }
+            if (round >= spin_limit) break;
+            __builtin_amdgcn_s_sleep(1);
+        }
+        if (lane == 0) seen = all;
+    }
+    __syncthreads();
+    return seen != 0;
 }
 
 // The selection of the one-launch accept + residual for small launches, by
@@ -407,6 +459,79 @@ __global__ __launch_bounds__(kStatThreads) void residual_select_kernel(
     select_terminal(logits, draft_logits, V, nc, c, a, chunk_sums + (size_t)j * nc, out_tokens, SumSrc::Plain);
 }
 
+// The draw for moderate batches in one launch of at most kPollMaxBlocks
+// workgroups: workgroup (sequence j, group g) sums chunks [g*G, g*G + G) of
+// the terminal row (all of its loads in flight at once: with one workgroup
+// per CU, a chunk at a time streamed too slowly; each sum with the code and
+// order of residual_kernel), puts each sum in its own tagged slot (zeroed by
+// the accept kernel before), then polls all nc slots of its sequence.  Every
+// workgroup computes the prefix and the chunk the same way; the one whose
+// chunks hold it re-reads that chunk (it streamed it moments ago) and picks
+// the token, as select_terminal does.  The wait is bounded: a workgroup that
+// runs out sums every chunk itself and writes the token if it falls in its
+// chunks.
+template <int G>
+__global__ __launch_bounds__(kStatThreads) void residual_polled_kernel(
+    const float* __restrict__ logits, const float* __restrict__ draft_logits, int V, int nc, int ngroups,
+    float c, const AcceptInfo* __restrict__ info, unsigned long long* __restrict__ slots, int spin_limit,
+    int32_t* __restrict__ out_tokens) {
+    __shared__ float red[kStatThreads / kWave];
+    __shared__ float psum[kPollMaxBlocks];
+    const int j = blockIdx.x / ngroups;
+    const int grp = blockIdx.x - j * ngroups;
+    const AcceptInfo a = info[j];
+    if (a.n < 0) return;
+    const TermRows tr = term_rows(logits, draft_logits, a, V);
+    const TermNorm tn = term_norm(a);
+    const int k0 = grp * G, k1 = min(nc, k0 + G);   // k0 < nc: ngroups = ceil(nc / G)
+    unsigned long long* mine = slots + (size_t)j * nc;
+    const int tid = threadIdx.x;
+    auto run = [&](auto vec_tag, auto q_tag) {
+        constexpr bool VEC = decltype(vec_tag)::value, USE_Q = decltype(q_tag)::value;
+        float zt[G][kStatPerThread], zd[G][kStatPerThread];
+        // every load first (past the group's last chunk: that chunk again,
+        // loaded and not used)
+#pragma unroll
+        for (int g = 0; g < G; ++g)
+            chunk_load<VEC, USE_Q, kStatPerThread>(tr.zt, tr.zd, min(k0 + g, k1 - 1) * kChunk, V, tid, zt[g], zd[g]);
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+            if (k0 + g >= k1) break;   // the same in the whole workgroup
+            float w[kStatPerThread];
+            chunk_weigh<USE_Q, kStatPerThread>(zt[g], zd[g], (k0 + g) * kChunk, V, tid, tn, c, w);
+            float s = 0.f;
+#pragma unroll
+            for (int e = 0; e < kStatPerThread; ++e) s += w[e];
+            s = block_sum(s, red);
+            if (tid == 0)
+                __hip_atomic_store(mine + k0 + g, kPollTag | __float_as_uint(s), __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_AGENT);
+        }
+    };
+    const bool vec = (V & 3) == 0;
+    if (vec) {
+        if (tr.bonus) run(std::true_type{}, std::true_type{});
+        else run(std::true_type{}, std::false_type{});
+    } else {
+        if (tr.bonus) run(std::false_type{}, std::true_type{});
+        else run(std::false_type{}, std::false_type{});
+    }
+    if (poll_sums(mine, nc, spin_limit, psum))
+        select_terminal(logits, draft_logits, V, nc, c, a, psum, out_tokens, SumSrc::Plain, k0, k1);
+    else
+        select_terminal(logits, draft_logits, V, nc, c, a, nullptr, out_tokens, SumSrc::Local, k0, k1);
+}
+
+// Chunks per workgroup of the grouped polled draw for n_rows sequences over V
+// entries (one slot per chunk), or 0 when the launch would not fit it.
+int residual_poll_group(int n_rows, int V) {
+    const long nc = n_chunks(V);
+    if (n_rows <= 0 || nc > kPollMaxBlocks || (long)n_rows * nc > kPollMaxSlots) return 0;
+    for (int G = 1; G <= kResidualMaxGroup; G *= 2)
+        if ((long)n_rows * ((nc + G - 1) / G) <= kPollMaxBlocks) return G;
+    return 0;
+}
+
 // Acceptance and residual draw in one launch, for small batches where the
 // two kernels' latency dominates: one workgroup per (sampled sequence, chunk).
 // Every workgroup of a sequence takes the acceptance decision itself (a few
@@ -452,43 +577,15 @@ __global__ __launch_bounds__(kStatThreads) void accept_residual_kernel(
     s = block_sum(s, red);
     if constexpr (POLL) {
         __shared__ float psum[kPollMaxBlocks];
-        __shared__ int seen;
-        constexpr int kPer = kPollMaxBlocks / kWave;
         unsigned long long* mine = slots + (size_t)j * nc;
-        const int lane = threadIdx.x & 63;
         if (threadIdx.x == 0)
             __hip_atomic_store(mine + chunk, kPollTag | __float_as_uint(s), __ATOMIC_RELAXED,
                                __HIP_MEMORY_SCOPE_AGENT);
-        if (threadIdx.x < kWave) {
-            bool all = false;
-            for (int round = 0;; ++round) {
-                // every load goes out (a slot past nc re-reads the last one),
-                // so a round is one memory round trip
-                unsigned long long v[kPer];
-#pragma unroll
-                for (int i = 0; i < kPer; ++i)
-                    v[i] = __hip_atomic_load(mine + min(lane + i * kWave, nc - 1), __ATOMIC_RELAXED,
-                                             __HIP_MEMORY_SCOPE_AGENT);
-                bool miss = false;
-#pragma unroll
-                for (int i = 0; i < kPer; ++i) miss |= (v[i] >> 32) != (kPollTag >> 32);
-                if (__ballot(miss) == 0ull) {
-#pragma unroll
-                    for (int i = 0; i < kPer; ++i)
-                        if (lane + i * kWave < nc) psum[lane + i * kWave] = __uint_as_float((uint32_t)v[i]);
-                    all = true;
-                    break;
-                }
-                if (round >= spin_limit) break;
-                __builtin_amdgcn_s_sleep(1);
-            }
-            if (lane == 0) seen = all;
-        }
-        __syncthreads();
-        if (seen) {
+        if (poll_sums(mine, nc, spin_limit, psum)) {
             select_polled<PER>(logits, draft_logits, V, nc, c, a, chunk, w, psum, out_tokens);
         } else {
-            select_terminal<PER>(logits, draft_logits, V, nc, c, a, nullptr, out_tokens, SumSrc::Local, chunk);
+            select_terminal<PER>(logits, draft_logits, V, nc, c, a, nullptr, out_tokens, SumSrc::Local, chunk,
+                                 chunk + 1);
         }
         return;
     }
@@ -525,9 +622,17 @@ hipError_t launch_accept_residual(const float* logits, const float* draft_logits
 
 hipError_t launch_residual(const float* logits, const float* draft_logits, int n_rows, int V,
                            float inv_t_log2e, const AcceptInfo* info, float* chunk_sums, int* counters,
-                           int32_t* out_tokens, hipStream_t stream) {
+                           unsigned long long* slots, int spin_limit, int32_t* out_tokens, hipStream_t stream) {
     if (n_rows == 0) return hipSuccess;
     const int nc = n_chunks(V);
+    const int G = slots ? residual_poll_group(n_rows, V) : 0;
+    if (G > 0) {
+        const int ngroups = (nc + G - 1) / G;
+        auto kern = G == 1 ? residual_polled_kernel<1> : G == 2 ? residual_polled_kernel<2> : residual_polled_kernel<4>;
+        hipLaunchKernelGGL(kern, dim3((unsigned)(n_rows * ngroups)), dim3(kStatThreads), 0, stream, logits,
+                           draft_logits, V, nc, ngroups, inv_t_log2e, info, slots, max(spin_limit, 0), out_tokens);
+        return hipGetLastError();
+    }
     const long blocks = (long)n_rows * nc;
     if (blocks > kResidualSplitBlocks) {
         hipLaunchKernelGGL(residual_sums_kernel, dim3((unsigned)blocks), dim3(kStatThreads), 0, stream, logits,

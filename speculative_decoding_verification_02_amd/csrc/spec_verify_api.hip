@@ -34,6 +34,9 @@ std::atomic<void*> g_scratch[kMaxDevices];   // device address of `scratch`, per
 // sequence's chunk sums before it sums every chunk itself
 std::atomic<int> g_poll_limit{sv::kDefaultPollLimit};
 int poll_limit() { return g_poll_limit.load(std::memory_order_relaxed); }
+// poll slots per sequence the accept kernel zeroes for the residual draw of
+// n sequences that follows (one per chunk when that draw polls, else none)
+int residual_slots(int n, int V) { return sv::residual_poll_group(n, V) > 0 ? sv::n_chunks(V) : 0; }
 
 spec_status_t hip_fail(hipError_t e) {
     g_detail = hipGetErrorString(e);
@@ -111,7 +114,7 @@ size_t workspace_layout(int B, int K, int V, void* base, Workspace* ws) {
     // the one-launch accept + residual, whichever is more
     const size_t sums = align256((size_t)B * std::max(nc, (size_t)sv::n_fused_chunks(V)) * sizeof(float));
     const size_t counter_block = align256((size_t)B * sizeof(int));
-    const size_t counters = counter_block + align256((size_t)sv::kPollMaxBlocks * sizeof(unsigned long long));
+    const size_t counters = counter_block + align256((size_t)sv::kPollMaxSlots * sizeof(unsigned long long));
     if (ws) {
         char* p = static_cast<char*>(base);
         ws->stats = reinterpret_cast<sv::StatRec*>(p);
@@ -202,9 +205,9 @@ spec_status_t sample_impl(const float* logits, const float* draft_logits, const 
         if (e == hipSuccess)
             e = sv::launch_accept(logits, dl, draft_tokens, seeds, rows, nr, seq, V, c, true,
                                   pass_layout(ws.stats, nr, seq.K, V), accepted_len, out_tokens, probs_at_draft,
-                                  ws.info, ws.counters, s);
+                                  ws.info, ws.counters, s, ws.slots, residual_slots(nr, V));
         if (e == hipSuccess)
-            e = sv::launch_residual(logits, dl, nr, V, c, ws.info, ws.sums, ws.counters, out_tokens, s);
+            e = sv::launch_residual(logits, dl, nr, V, c, ws.info, ws.sums, ws.counters, ws.slots, poll_limit(), out_tokens, s);
     }
     return e == hipSuccess ? SPEC_OK : hip_fail(e);
 }
@@ -410,9 +413,9 @@ spec_status_t spec_verify_step(const void* hidden, const void* w_lmhead, spec_dt
                                                    accepted_len, out_tokens, probs_at_draft, ws.sums, ws.counters, ws.slots, poll_limit(), s);
                 } else {
                     e = sv::launch_accept(logits, dl, draft_tokens, seeds, sampled_rows, ns, seq, V, c, true, lay,
-                                          accepted_len, out_tokens, probs_at_draft, ws.info, ws.counters, s);
+                                          accepted_len, out_tokens, probs_at_draft, ws.info, ws.counters, s, ws.slots, residual_slots(ns, V));
                     if (e == hipSuccess)
-                        e = sv::launch_residual(logits, dl, ns, V, c, ws.info, ws.sums, ws.counters, out_tokens, s);
+                        e = sv::launch_residual(logits, dl, ns, V, c, ws.info, ws.sums, ws.counters, ws.slots, poll_limit(), out_tokens, s);
                 }
             }
             return e == hipSuccess ? SPEC_OK : hip_fail(e);
@@ -471,9 +474,9 @@ spec_status_t spec_verify_step(const void* hidden, const void* w_lmhead, spec_dt
     const sv::RecLayout lay{tgt.tgt, tgt.tgt_nc, true, ws.stats, nc, false};
     if (e == hipSuccess && ng > 0 && ns > 0 && !fused) {
         e = sv::launch_accept_both(logits, dl, draft_tokens, seeds, greedy_rows, ng, sampled_rows, ns, seq, V, c, tgt,
-                                   lay, accepted_len, out_tokens, probs_at_draft, ws.info, ws.counters, s);
+                                   lay, accepted_len, out_tokens, probs_at_draft, ws.info, ws.counters, s, ws.slots, residual_slots(ns, V));
         if (e == hipSuccess)
-            e = sv::launch_residual(logits, dl, ns, V, c, ws.info, ws.sums, ws.counters, out_tokens, s);
+            e = sv::launch_residual(logits, dl, ns, V, c, ws.info, ws.sums, ws.counters, ws.slots, poll_limit(), out_tokens, s);
         return e == hipSuccess ? SPEC_OK : hip_fail(e);
     }
     if (e == hipSuccess && ng > 0)
@@ -485,9 +488,9 @@ spec_status_t spec_verify_step(const void* hidden, const void* w_lmhead, spec_dt
                                            accepted_len, out_tokens, probs_at_draft, ws.sums, ws.counters, ws.slots, poll_limit(), s);
         } else {
             e = sv::launch_accept(logits, dl, draft_tokens, seeds, sampled_rows, ns, seq, V, c, true, lay,
-                                  accepted_len, out_tokens, probs_at_draft, ws.info, ws.counters, s);
+                                  accepted_len, out_tokens, probs_at_draft, ws.info, ws.counters, s, ws.slots, residual_slots(ns, V));
             if (e == hipSuccess)
-                e = sv::launch_residual(logits, dl, ns, V, c, ws.info, ws.sums, ws.counters, out_tokens, s);
+                e = sv::launch_residual(logits, dl, ns, V, c, ws.info, ws.sums, ws.counters, ws.slots, poll_limit(), out_tokens, s);
         }
     }
     return e == hipSuccess ? SPEC_OK : hip_fail(e);

@@ -83,12 +83,13 @@ struct RecLayout {
 constexpr int kAcceptRowsDirect = 16;
 
 // Greedy or sampled acceptance: one workgroup per selected sequence.  The
-// sampled variant also zeroes the sequence's residual counter.
+// sampled variant also zeroes the sequence's residual counter and, with
+// slots, its slots_per_seq poll slots at slots[j * slots_per_seq].
 hipError_t launch_accept(const float* logits, const float* draft_logits, const int32_t* draft_tokens,
                          const uint64_t* seeds, const int32_t* rows, int n_rows, SeqRows seq, int V,
                          float inv_t_log2e, bool sampled, RecLayout rec, int32_t* accepted_len,
                          int32_t* out_tokens, float* probs_at_draft, AcceptInfo* info, int* counters,
-                         hipStream_t stream);
+                         hipStream_t stream, unsigned long long* slots = nullptr, int slots_per_seq = 0);
 
 // Greedy and sampled acceptance in one launch: workgroups 0 .. n_greedy-1
 // take greedy_rows, the rest sampled_rows (AcceptInfo and residual counter
@@ -98,7 +99,7 @@ hipError_t launch_accept_both(const float* logits, const float* draft_logits, co
                               const int32_t* sampled_rows, int n_sampled, SeqRows seq, int V, float inv_t_log2e,
                               RecLayout rec_greedy, RecLayout rec_sampled, int32_t* accepted_len,
                               int32_t* out_tokens, float* probs_at_draft, AcceptInfo* info, int* counters,
-                              hipStream_t stream);
+                              hipStream_t stream, unsigned long long* slots = nullptr, int slots_per_seq = 0);
 
 // Acceptance and residual draw of sampled sequences in one launch (small
 // batches); needs its counters and slots zeroed by the kernel before it
@@ -140,10 +141,17 @@ hipError_t launch_tree_accept(const int32_t* parents, const int32_t* tokens, con
                               int32_t* out_nodes, hipStream_t stream);
 
 // Residual / bonus draw of the sampled sequences: per-chunk weight sums, and
-// the inverse-CDF selection of the terminal token by the last chunk block.
+// the inverse-CDF selection of the terminal token.  Launches of at most
+// kPollMaxBlocks workgroups (residual_poll_group chunks each) poll tagged
+// slots, one per (sequence, chunk), which the accept kernel zeroes first
+// (launch_accept / launch_accept_both with slots_per_seq = n_chunks(V));
+// larger ones count the chunk blocks in and select in the last one.
+constexpr int kPollMaxSlots = 2048;       // tagged slots in the workspace
+constexpr int kResidualMaxGroup = 4;      // chunks per workgroup of the polled draw at most (1, 2 or 4)
+int residual_poll_group(int n_rows, int V);
 hipError_t launch_residual(const float* logits, const float* draft_logits, int n_rows, int V,
                            float inv_t_log2e, const AcceptInfo* info, float* chunk_sums, int* counters,
-                           int32_t* out_tokens, hipStream_t stream);
+                           unsigned long long* slots, int spin_limit, int32_t* out_tokens, hipStream_t stream);
 
 // Prompt-lookup drafter: per-sequence best (match length, end position) keys
 // (B x 8 bytes of scratch), then drafts, counts and verify-row offsets.  A

@@ -11,6 +11,10 @@ wait in front of one of them:
   from the host) sums every chunk itself and writes the token if it owns the
   chosen chunk.
 
+The residual draw that follows a separate acceptance launch polls the same
+way for moderate batches (one slot per 4096-entry chunk, a group of chunks
+per workgroup) and counts its blocks in beyond that.
+
 All three evaluate the same weights with the same reductions, so their
 tokens must be identical, bit for bit.  Both end-of-draw cases occur in the
 rounds below (a
@@ -111,4 +115,35 @@ def test_step_b1_poll_give_up_agrees():
         n = int(res[0][1][0])
         assert 0 <= n <= K and 0 <= res[0][2][0, n] < V
         kinds.add("bonus" if n == K else "residual")
+    assert kinds == {"bonus", "residual"}, kinds
+
+
+def test_grouped_polled_residual_matches_counted():
+    """The residual draw of moderate batches (acceptance in its own launch):
+    at most 256 workgroups sum a group of consecutive 4096-entry chunks each
+    and poll one tagged slot per chunk; more sequences than the slots hold
+    take the counted path.  32 sequences at V = 128256 (1024 slots, four
+    chunks per workgroup) against the same 32 within 65 (counted), and
+    against a poll bound of 0; bit for bit."""
+    B, K, V, T = 65, 4, 128256, 0.8
+    zt, zd, d = _round(B, K, V, seed=4242, sigma=0.3)
+    zt, zd, d = zt.to(dev()), zd.to(dev()), d.to(dev())
+    kinds = set()
+    for rnd in range(3):
+        seeds = np.arange(B, dtype=np.uint64) * 7907 + 11 * rnd
+        rows32 = list(range(32))
+        say("grouped polled residual, round %d" % rnd)
+        polled = _with_limit(-1, lambda: gpu_accept_sample(zt, zd, d, T, seeds, rows=rows32, probs=True))
+        gave_up = _with_limit(0, lambda: gpu_accept_sample(zt, zd, d, T, seeds, rows=rows32, probs=True))
+        counted = _with_limit(-1, lambda: gpu_accept_sample(zt, zd, d, T, seeds, probs=True))
+        p_acc, p_out, p_pad = (x.cpu().numpy() for x in polled)
+        for other in (gave_up, counted):
+            o_acc, o_out, o_pad = (x.cpu().numpy() for x in other)
+            np.testing.assert_array_equal(p_acc[:32], o_acc[:32])
+            np.testing.assert_array_equal(p_out[:32], o_out[:32])
+            np.testing.assert_array_equal(p_pad[:32], o_pad[:32])
+        for b in range(32):
+            n = int(p_acc[b])
+            assert 0 <= n <= K and 0 <= p_out[b, n] < V
+            kinds.add("bonus" if n == K else "residual")
     assert kinds == {"bonus", "residual"}, kinds
