@@ -409,15 +409,17 @@ size_t spec_ngram_workspace_bytes(int B, int max_len);
  * ragged calls; 0 if the sizes are out of range). */
 size_t spec_workspace_bytes(int B, int K, int V);
 
-/* Bound on the one cross-workgroup wait in this library.  In the one-launch
- * acceptance + residual draw of small sampled batches (at most 256 workgroups,
- * all resident at once), every chunk workgroup publishes its chunk's weight
- * sum and then polls the other sums of its sequence, up to `rounds` rounds
- * (about a microsecond each), before it gives up and sums every chunk itself.
- * The result does not depend on the bound, only the time: giving up costs a
- * read of the whole terminal row per workgroup.  A negative value restores
- * the default (65536).  Process-wide; applies to launches enqueued after the
- * call.  Returns the previous bound.  Meant for tests of the give-up path. */
+/* Bound on the one kind of cross-workgroup wait in this library.  In the
+ * residual / bonus draw of sampled sequences, launches of at most 256
+ * workgroups (all resident at once: the one-launch acceptance + residual draw
+ * of small batches, and the draw of moderate batches that follows a separate
+ * acceptance launch) publish each chunk's weight sum and then poll the other
+ * sums of the sequence, up to `rounds` rounds (about a microsecond each),
+ * before a workgroup gives up and sums every chunk itself.  The result does
+ * not depend on the bound, only the time: giving up costs a read of the whole
+ * terminal row per workgroup.  A negative value restores the default
+ * (65536).  Process-wide; applies to launches enqueued after the call.
+ * Returns the previous bound.  Meant for tests of the give-up path. */
 int spec_set_poll_limit(int rounds);
 
 /* Static, human-readable name of a status code. */
