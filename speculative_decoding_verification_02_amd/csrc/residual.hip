@@ -7,11 +7,17 @@
 // speculative decoding works).  The draw is an inverse CDF:
 //     t = min{v : C_v > u' * Z},  C_v = w_0 + ... + w_v,  Z = C_{V-1}.
 //
-// One workgroup per (sequence, chunk) sums the weights of its chunk
-// (fixed-order reduction); then, for a sequence, a prefix over the chunk sums
-// finds the chunk c* holding u'Z and a workgroup scan over c*'s weights finds
-// t.  Small batches run the selection in the workgroup that finishes last
-// (one launch); large ones in a second launch, one workgroup per sequence.
+// Workgroups sum the weights of one chunk each, or of a small group of
+// chunks (fixed-order reductions); then, for a sequence, a prefix over the
+// chunk sums finds the chunk c* holding u'Z and a workgroup scan over c*'s
+// weights finds t.  Where the selection runs depends on the launch:
+//   - at most 256 workgroups (all resident at once): each publishes its sums
+//     in tagged slots and polls its sequence's slots; the workgroup that holds
+//     c* picks t (a bounded wait; a workgroup that gives up sums every chunk
+//     itself);
+//   - up to 4096 workgroups: the one that finishes last, counted in with an
+//     atomic;
+//   - beyond: a second launch, one workgroup per sequence.
 // Both phases evaluate a weight with the same function from the same inputs,
 // so a chunk's elements agree bitwise between them; only the order of the
 // within-chunk sum differs, and the selection falls back to the last (or first)
