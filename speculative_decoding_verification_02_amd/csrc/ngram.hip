@@ -73,11 +73,14 @@ __global__ __launch_bounds__(kNgThreads) void ngram_scan_kernel(const int32_t* _
     const int32_t* s = hist + s0;
     const int32_t last = s[L - 1];
 
+    // every load goes out (a position past the segment re-reads its last
+    // position, which is not scored), so all of a thread's loads are in
+    // flight together
     int32_t v[kNgPerThread];
 #pragma unroll
     for (int i = 0; i < kNgPerThread; ++i) {
         const int e = e0 + i * kNgThreads + tid;
-        v[i] = e < e1 ? s[e] : 0;
+        v[i] = s[min(e, e1 - 1)];
     }
     unsigned long long best = 0ull;
 #pragma unroll
