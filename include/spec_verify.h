@@ -48,6 +48,9 @@
  *                          (computed by the LM-head kernel itself wherever a
  *                          bf16 kernel with that option runs, which saves a
  *                          pass over the logits) and both accept rules.
+ *   spec_tree_verify_step
+ *                       -- the same for draft trees: LM head and the greedy
+ *                          tree rule in one call.
  *   spec_ngram_propose  -- the step before verification for prompt lookup:
  *                          drafts copied from the most recent earlier
  *                          occurrence of the sequence's last n tokens
@@ -286,6 +289,33 @@ spec_status_t spec_tree_accept_greedy(const float* logits, const int32_t* parent
                                       int32_t* out_nodes,
                                       void* workspace, size_t workspace_bytes,
                                       spec_stream_t stream);
+
+/*
+ * spec_tree_verify_step -- LM head and greedy tree verification in one call.
+ *
+ * Same results as spec_verify_logits (K = N) followed by
+ * spec_tree_accept_greedy: identical logits, accepted lengths, tokens and
+ * nodes (the rule needs each row's argmax only, which does not depend on the
+ * order of any sum).  Where a bf16 LM-head kernel computes statistics on the
+ * side (as in spec_verify_step: M = B*(N+1) <= 16 with H <= 8192, or M > 16
+ * with H % 64 == 0) the rows' argmaxes come from its records and the logits
+ * are not read back; otherwise the call enqueues the two calls' kernels.
+ *
+ *   hidden, w_lmhead, dtype, logits, B, V, H: as in spec_verify_logits, with
+ *                 K = N (hidden [B, N+1, H], logits [B, N+1, V])
+ *   parents, tokens, rows, n_rows, accepted_len, out_tokens, out_nodes:
+ *                 as in spec_tree_accept_greedy (0 <= N <= 63)
+ *   workspace     at least spec_verify_step_workspace_bytes(B, N, V) bytes,
+ *                 16-byte aligned; contents on entry do not matter
+ * Errors as in the two calls it replaces.
+ */
+spec_status_t spec_tree_verify_step(const void* hidden, const void* w_lmhead, spec_dtype_t dtype,
+                                    const int32_t* parents, const int32_t* tokens,
+                                    const int32_t* rows, int n_rows, int B, int N, int V, int H,
+                                    float* logits, int32_t* accepted_len, int32_t* out_tokens,
+                                    int32_t* out_nodes,
+                                    void* workspace, size_t workspace_bytes,
+                                    spec_stream_t stream);
 
 /*
  * spec_verify_step -- the whole verify step in one call.

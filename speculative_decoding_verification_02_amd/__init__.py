@@ -36,7 +36,7 @@ __all__ = [
     "SPEC_ERR_WORKSPACE", "SPEC_ERR_HIP", "SPEC_BF16", "SPEC_F32", "LIB_PATH", "HEADER_PATH",
     "load_library", "declared_symbols", "spec_verify_logits", "spec_accept_greedy",
     "spec_accept_sample", "spec_accept_greedy_ragged", "spec_accept_sample_ragged", "spec_tree_accept_greedy", "spec_ngram_propose", "spec_ngram_workspace_bytes",
-    "spec_verify_step", "spec_verify_step_workspace_bytes", "spec_verify_step_noalloc",
+    "spec_verify_step", "spec_verify_step_workspace_bytes", "spec_verify_step_noalloc", "spec_tree_verify_step",
     "spec_workspace_bytes", "spec_status_string", "spec_last_error_detail", "spec_set_poll_limit",
 ]
 
@@ -73,6 +73,9 @@ _SIGNATURES = {
                                   _c_int, _c_void_p, _c_int, _c_int, _c_int, _c_int, _c_int, _c_void_p, _c_void_p,
                                   _c_void_p, _c_void_p, _c_void_p, _c_size_t, _c_void_p]),
     "spec_verify_step_workspace_bytes": (_c_size_t, [_c_int, _c_int, _c_int]),
+    "spec_tree_verify_step": (_c_int, [_c_void_p, _c_void_p, _c_int, _c_void_p, _c_void_p, _c_void_p, _c_int, _c_int,
+                                       _c_int, _c_int, _c_int, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p,
+                                       _c_size_t, _c_void_p]),
     "spec_verify_step_noalloc": (_c_int, [_c_void_p, _c_void_p, _c_int, _c_void_p, _c_void_p, _c_float, _c_void_p,
                                           _c_void_p, _c_int, _c_void_p, _c_int, _c_int, _c_int, _c_int, _c_int,
                                           _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p]),
@@ -364,6 +367,35 @@ def spec_tree_accept_greedy(logits, parents, tokens, accepted_len, out_tokens, w
                                        _ptr(tokens) if P > 1 else None, _ptr(rows_t), n_rows, B, P - 1, V,
                                        _ptr(accepted_len), _ptr(out_tokens), _ptr(out_nodes), _ptr(workspace),
                                        workspace.numel() * workspace.element_size(), _stream(stream)))
+
+
+def spec_tree_verify_step(hidden, w_lmhead, logits, parents, tokens, accepted_len, out_tokens, workspace,
+                          out_nodes=None, rows=None, stream=None) -> None:
+    """LM head and greedy tree verification in one call: hidden [B, N+1, H],
+    w_lmhead [V, H], logits [B, N+1, V]; the rest as in
+    spec_tree_accept_greedy."""
+    B, P, H = hidden.shape
+    V = w_lmhead.shape[0]
+    if w_lmhead.dtype != hidden.dtype or w_lmhead.shape[1] != H:
+        raise ValueError("shape or dtype mismatch")
+    _dtype_code(hidden)
+    _arg(hidden, "hidden", hidden.dtype)
+    _arg(w_lmhead, "w_lmhead", hidden.dtype)
+    _arg(logits, "logits", _f32(), (B, P, V))
+    _arg(parents, "parents", _i32(), (B, P), optional=P == 1)
+    _arg(tokens, "tokens", _i32(), (B, P), optional=P == 1)
+    _arg(accepted_len, "accepted_len", _i32(), (B,))
+    _arg(out_tokens, "out_tokens", _i32(), (B, P))
+    _arg(out_nodes, "out_nodes", _i32(), (B, P), optional=True)
+    _ws(workspace)
+    rows_t, n_rows = _rows(rows)
+    lib = load_library()
+    _check("spec_tree_verify_step",
+           lib.spec_tree_verify_step(_ptr(hidden), _ptr(w_lmhead), _dtype_code(hidden),
+                                     _ptr(parents) if P > 1 else None, _ptr(tokens) if P > 1 else None,
+                                     _ptr(rows_t), n_rows, B, P - 1, V, H, _ptr(logits), _ptr(accepted_len),
+                                     _ptr(out_tokens), _ptr(out_nodes), _ptr(workspace),
+                                     workspace.numel() * workspace.element_size(), _stream(stream)))
 
 
 def spec_ngram_workspace_bytes(B: int, max_len: int) -> int:

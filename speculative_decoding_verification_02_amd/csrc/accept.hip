@@ -91,8 +91,8 @@ __global__ __launch_bounds__(kAcceptThreads) void accept_both_kernel(
 // depth below 64), each node's depth and whether its whole path is accepted.
 __global__ __launch_bounds__(kAcceptThreads) void tree_accept_kernel(
     const int32_t* __restrict__ parents, const int32_t* __restrict__ tokens, const int32_t* __restrict__ rows,
-    int n_rows, int B, int N, int V, int nc, const StatRec* __restrict__ stats, int32_t* __restrict__ accepted_len,
-    int32_t* __restrict__ out_tokens, int32_t* __restrict__ out_nodes) {
+    int n_rows, int B, int N, int V, int nc, const StatRec* __restrict__ stats, bool by_row,
+    int32_t* __restrict__ accepted_len, int32_t* __restrict__ out_tokens, int32_t* __restrict__ out_nodes) {
     __shared__ StatRec recs[kRecBuf];
     __shared__ Merged merged[kWave];
 
@@ -113,7 +113,9 @@ __global__ __launch_bounds__(kAcceptThreads) void tree_accept_kernel(
     const int rows_per_pass = max(1, min(N + 1, kRecBuf / nc));
     for (int r0 = 0; r0 <= N; r0 += rows_per_pass) {
         const int nr = min(rows_per_pass, N + 1 - r0);
-        const StatRec* src = stats + ((size_t)j * (N + 1) + r0) * nc;   // rows r0 .. r0+nr-1, contiguous
+        // rows r0 .. r0+nr-1 of the sequence, contiguous: nc records per row,
+        // rows by selection slot j (the statistics pass) or by sequence b
+        const StatRec* src = stats + ((size_t)(by_row ? b : j) * (N + 1) + r0) * nc;
         stage_records(recs, nr * nc, tid, [&](int e) { return src + e; });
         __syncthreads();
         for (int rr = wave; rr < nr; rr += kAcceptWaves) {
@@ -185,10 +187,12 @@ __global__ __launch_bounds__(kAcceptThreads) void tree_accept_kernel(
 
 hipError_t launch_tree_accept(const int32_t* parents, const int32_t* tokens, const int32_t* rows, int n_rows, int B,
                               int N, int V, const StatRec* stats, int32_t* accepted_len, int32_t* out_tokens,
-                              int32_t* out_nodes, hipStream_t stream) {
+                              int32_t* out_nodes, hipStream_t stream, int recs_per_row, bool by_row) {
+    if (recs_per_row > kRecBuf) return hipErrorInvalidValue;
     if (n_rows == 0) return hipSuccess;
     hipLaunchKernelGGL(tree_accept_kernel, dim3(n_rows), dim3(kAcceptThreads), 0, stream, parents, tokens, rows,
-                       n_rows, B, N, V, n_chunks(V), stats, accepted_len, out_tokens, out_nodes);
+                       n_rows, B, N, V, recs_per_row > 0 ? recs_per_row : n_chunks(V), stats, by_row, accepted_len,
+                       out_tokens, out_nodes);
     return hipGetLastError();
 }
 

@@ -517,6 +517,66 @@ spec_status_t spec_verify_step_noalloc(const void* hidden, const void* w_lmhead,
                             probs_at_draft, ws, kNoAllocScratchBytes, stream);
 }
 
+spec_status_t spec_tree_verify_step(const void* hidden, const void* w_lmhead, spec_dtype_t dtype,
+                                    const int32_t* parents, const int32_t* tokens, const int32_t* rows, int n_rows,
+                                    int B, int N, int V, int H, float* logits, int32_t* accepted_len,
+                                    int32_t* out_tokens, int32_t* out_nodes, void* workspace,
+                                    size_t workspace_bytes, spec_stream_t stream) {
+    if (!hidden || !w_lmhead || !logits || !accepted_len || !out_tokens) return SPEC_ERR_ARG;
+    if (dtype != SPEC_BF16 && dtype != SPEC_F32) return SPEC_ERR_DTYPE;
+    if (!sizes_ok(B, N, V) || H < 8 || (H & 7) != 0) return SPEC_ERR_ARG;
+    if (rows && (n_rows < 0 || n_rows > B)) return SPEC_ERR_ARG;
+    if (N > 0 && (!parents || !tokens)) return SPEC_ERR_ARG;
+    if (!aligned16(hidden) || !aligned16(w_lmhead) || !aligned16(logits)) return SPEC_ERR_ALIGN;
+    if (!workspace || workspace_bytes < spec_verify_step_workspace_bytes(B, N, V)) return SPEC_ERR_WORKSPACE;
+    if (!aligned16(workspace)) return SPEC_ERR_ALIGN;
+
+    const int M = B * (N + 1);
+    const int nr = rows ? n_rows : B;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    Workspace ws;
+    const size_t base = workspace_layout(B, N, V, workspace, &ws);
+    sv::StatRec* tstats = reinterpret_cast<sv::StatRec*>(static_cast<char*>(workspace) + base);
+    hipError_t e = hipSuccess;
+    // The tree rule needs each row's argmax only, and the bf16 LM-head kernels
+    // that compute statistics on the side give it without a pass over the
+    // logits: the cooperative kernel's records (one per workgroup and row),
+    // or the direct-to-LDS epilogue's (one per 256 entries), folded into
+    // 4096-entry chunk records; both by row.
+    if (dtype == SPEC_BF16 && nr > 0) {
+        int cus = 0;
+        e = num_cus(&cus);
+        if (e != hipSuccess) return hip_fail(e);
+        const int crec = sv::lmhead_coop_records(M, V, H, 0, cus);
+        if (crec > 0) {
+            const sv::CoopStats cs{tstats, nullptr, 0, nullptr, sv::kLog2e, nullptr, 0};
+            e = sv::launch_lmhead_coop_stats(static_cast<const uint16_t*>(hidden),
+                                             static_cast<const uint16_t*>(w_lmhead), logits, M, V, H, cus, s, cs);
+            if (e == hipSuccess)
+                e = sv::launch_tree_accept(parents, tokens, rows, nr, B, N, V, tstats, accepted_len, out_tokens,
+                                           out_nodes, s, crec, true);
+            return e == hipSuccess ? SPEC_OK : hip_fail(e);
+        }
+        const int big_recs = sv::lmhead_big_records(M, V, H);
+        if (big_recs > 0) {
+            int nrec = 0;
+            e = sv::launch_lmhead_bf16(static_cast<const uint16_t*>(hidden), static_cast<const uint16_t*>(w_lmhead),
+                                       logits, M, V, H, cus, s, tstats, sv::kLog2e, &nrec);
+            if (e == hipSuccess && nrec != big_recs) e = hipErrorInvalidValue;   // the kernel the shape rule named
+            if (e == hipSuccess) e = sv::launch_fold_records(tstats, nrec, M, V, sv::kLog2e, ws.stats, s);
+            if (e == hipSuccess)
+                e = sv::launch_tree_accept(parents, tokens, rows, nr, B, N, V, ws.stats, accepted_len, out_tokens,
+                                           out_nodes, s, 0, true);
+            return e == hipSuccess ? SPEC_OK : hip_fail(e);
+        }
+    }
+    // elsewhere (other hidden sizes, fp32, no rows): the separate calls' kernels
+    spec_status_t st = spec_verify_logits(hidden, w_lmhead, dtype, logits, B, N, V, H, stream);
+    if (st != SPEC_OK || nr == 0) return st;
+    return spec_tree_accept_greedy(logits, parents, tokens, rows, n_rows, B, N, V, accepted_len, out_tokens, out_nodes,
+                                   workspace, workspace_bytes, stream);
+}
+
 size_t spec_verify_step_workspace_bytes(int B, int K, int V) {
     if (!sizes_ok(B, K, V)) return 0;
     return workspace_layout(B, K, V, nullptr, nullptr) + align256(step_extra_records(B, K, V) * sizeof(sv::StatRec));

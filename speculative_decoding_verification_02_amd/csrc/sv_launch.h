@@ -134,11 +134,13 @@ hipError_t launch_accept_residual(const float* logits, const float* draft_logits
                                   float* probs_at_draft, float* chunk_sums, int* counters,
                                   unsigned long long* slots, int spin_limit, hipStream_t stream);
 
-// Greedy verification of draft trees (N+1 rows per sequence, statistics from
-// launch_softmax_stats over the dense layout with K = N).
+// Greedy verification of draft trees (N+1 rows per sequence): recs_per_row
+// records per row (0: the statistics pass's n_chunks(V)), rows by selection
+// slot (the pass over the dense layout with K = N) or, by_row, by sequence
+// (the LM head's records, folded or per workgroup).
 hipError_t launch_tree_accept(const int32_t* parents, const int32_t* tokens, const int32_t* rows, int n_rows, int B,
                               int N, int V, const StatRec* stats, int32_t* accepted_len, int32_t* out_tokens,
-                              int32_t* out_nodes, hipStream_t stream);
+                              int32_t* out_nodes, hipStream_t stream, int recs_per_row = 0, bool by_row = false);
 
 // Residual / bonus draw of the sampled sequences: per-chunk weight sums, and
 // the inverse-CDF selection of the terminal token.  Launches of at most

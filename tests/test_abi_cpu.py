@@ -30,6 +30,7 @@ def test_exports_every_declared_symbol(lib):
                           "spec_accept_greedy_ragged", "spec_accept_sample_ragged", "spec_tree_accept_greedy",
                           "spec_ngram_propose", "spec_ngram_workspace_bytes",
                           "spec_verify_step", "spec_verify_step_workspace_bytes", "spec_verify_step_noalloc",
+                          "spec_tree_verify_step",
                           "spec_workspace_bytes", "spec_status_string", "spec_last_error_detail",
                           "spec_set_poll_limit"}
     for n in names:
@@ -236,6 +237,32 @@ def test_step_validation(lib):
     assert _step(lib, ws=MIS) == sv.SPEC_ERR_ALIGN
     # greedy rows only: no seeds, draft logits or temperature needed
     assert _step(lib, ns=0, seeds=None, dl=None, T=0.0, g=A, ng=0, ws=None) == sv.SPEC_ERR_WORKSPACE
+
+
+def _tree_step(lib, hid=A, w=A, dt=sv.SPEC_BF16, par=A, tok=A, rows=None, nr=0, B=2, N=7, V=1000, H=64,
+               logits=A, acc=A, out=A, nodes=None, ws=A, wsb=None):
+    if wsb is None:
+        wsb = sv.spec_verify_step_workspace_bytes(B, N, V)
+    return lib.spec_tree_verify_step(hid, w, dt, par, tok, rows, nr, B, N, V, H, logits, acc, out, nodes, ws, wsb,
+                                     None)
+
+
+def test_tree_step_validation(lib):
+    assert _tree_step(lib, hid=None) == sv.SPEC_ERR_ARG
+    assert _tree_step(lib, logits=None) == sv.SPEC_ERR_ARG
+    assert _tree_step(lib, out=None) == sv.SPEC_ERR_ARG
+    assert _tree_step(lib, dt=7) == sv.SPEC_ERR_DTYPE
+    assert _tree_step(lib, N=64) == sv.SPEC_ERR_ARG
+    assert _tree_step(lib, H=12) == sv.SPEC_ERR_ARG
+    assert _tree_step(lib, par=None) == sv.SPEC_ERR_ARG
+    assert _tree_step(lib, tok=None) == sv.SPEC_ERR_ARG
+    assert _tree_step(lib, rows=A, nr=3) == sv.SPEC_ERR_ARG       # more than B
+    assert _tree_step(lib, w=MIS) == sv.SPEC_ERR_ALIGN
+    assert _tree_step(lib, logits=MIS) == sv.SPEC_ERR_ALIGN
+    assert _tree_step(lib, wsb=16) == sv.SPEC_ERR_WORKSPACE
+    assert _tree_step(lib, ws=MIS) == sv.SPEC_ERR_ALIGN
+    # N = 0: no parents or tokens needed (the workspace check comes after)
+    assert _tree_step(lib, N=0, par=None, tok=None, ws=None) == sv.SPEC_ERR_WORKSPACE
 
 
 def test_zero_selected_rows_is_a_no_op(lib):

@@ -7,7 +7,10 @@ a ragged last chunk, V not a multiple of 4), row subsets.  A chain is the
 linear greedy rule of spec_accept_greedy, bit for bit.  Malformed trees and
 bad rows are faults.  End to end from hidden states, decisions may differ
 only where the oracle's fp64 logits of a row on the kept path have a near
-tie; and the 8-sequence, 63-node workload at full size.
+tie; and the 8-sequence, 63-node workload at full size.  spec_tree_verify_step
+(LM head and tree rule in one call, the argmaxes from the LM head's own
+records) must give the separate calls' logits, lengths, tokens and nodes bit
+for bit on every LM-head path, faults included.
 """
 import numpy as np
 import pytest
@@ -143,3 +146,88 @@ def test_full_size_tree_workload():
     res = oracle.tree_accept_greedy(logits.double().cpu().numpy(), par, tok)
     _check_exact(res, acc, out, nodes, range(wl.B))
     say("  kept depths %s" % acc.tolist())
+
+
+def _tree_step(hid, W, par, tok, rows=None, separate=False):
+    """spec_tree_verify_step, or (separate) spec_verify_logits followed by
+    spec_tree_accept_greedy, on the same device inputs."""
+    B, P, H = hid.shape
+    V = W.shape[0]
+    logits = torch.full((B, P, V), float("nan"), dtype=torch.float32, device=dev())
+    acc = torch.full((B,), -2, dtype=torch.int32, device=dev())
+    out = torch.full((B, P), -9, dtype=torch.int32, device=dev())
+    nodes = torch.full((B, P), -9, dtype=torch.int32, device=dev())
+    rows_t = None if rows is None else torch.as_tensor(np.asarray(rows, np.int32), device=dev())
+    par_t = torch.as_tensor(par, device=dev())
+    tok_t = torch.as_tensor(np.asarray(tok), device=dev())
+    if separate:
+        sv.spec_verify_logits(hid, W, logits)
+        sv.spec_tree_accept_greedy(logits, par_t, tok_t, acc, out, workspace(B, P - 1, V), out_nodes=nodes,
+                                   rows=rows_t)
+    else:
+        ws = torch.empty(sv.spec_verify_step_workspace_bytes(B, P - 1, V), dtype=torch.uint8, device=dev())
+        sv.spec_tree_verify_step(hid, W, logits, par_t, tok_t, acc, out, ws, out_nodes=nodes, rows=rows_t)
+    torch.cuda.synchronize()
+    return logits.cpu(), acc.cpu().numpy(), out.cpu().numpy(), nodes.cpu().numpy()
+
+
+@pytest.mark.parametrize("B,N,H,V,dtype,path", [
+    (2, 7, 512, 3001, "bf16", "cooperative kernel's records (M = 16)"),
+    (1, 5, 4096, 40000, "bf16", "cooperative kernel's records, H = 4096"),
+    (3, 1, 256, 37, "bf16", "cooperative, V = 37 (workgroups with no tile)"),
+    (8, 63, 256, 4099, "bf16", "direct-to-LDS epilogue records, folded (M = 512)"),
+    (12, 31, 1024, 3001, "bf16", "direct-to-LDS, 256-row tiles in split rings (M = 384)"),
+    (5, 15, 520, 2053, "bf16", "tiled kernel (H % 64 != 0): the separate calls' kernels"),
+    (4, 7, 256, 1000, "f32", "fp32: the separate calls' kernels"),
+])
+def test_tree_step_matches_separate_calls(B, N, H, V, dtype, path):
+    wl = synth.Workload("t", B=B, K=N, H=H, V=V, dtype=dtype, w_std=0.03 if dtype == "bf16" else 0.05,
+                        temperature=1.0, draft="additive", data_seed=B + N + V)
+    W, hid = synth.weights(wl, dev()), synth.hidden_states(wl, dev())
+    par = synth.tree_parents(B, N, seed=B + N)
+    tok = synth.tree_tokens(synth.base_logits(hid, W), par, seed=V, p_random=0.1, sigma=0.05).numpy()
+    say("tree step B=%d N=%d H=%d V=%d %s: %s" % (B, N, H, V, dtype, path))
+    for rows in (None, [B - 1] + list(range(0, B - 1, 2))):
+        fused = _tree_step(hid, W, par, tok, rows=rows)
+        sep = _tree_step(hid, W, par, tok, rows=rows, separate=True)
+        assert torch.equal(fused[0], sep[0]), "the tree step changed the logits"
+        for a, b in zip(fused[1:], sep[1:]):
+            np.testing.assert_array_equal(a, b)
+        sel = range(B) if rows is None else rows
+        assert all(fused[1][b] >= 0 for b in sel)
+    say("  kept depths %s" % fused[1].tolist())
+
+
+def test_tree_step_faults():
+    """A NaN in one node row faults exactly that sequence, as in the separate
+    calls."""
+    B, N, H, V = 6, 15, 256, 3001
+    wl = synth.Workload("t", B=B, K=N, H=H, V=V, dtype="bf16", w_std=0.03, temperature=1.0, draft="additive",
+                        data_seed=5)
+    W, hid = synth.weights(wl, dev()), synth.hidden_states(wl, dev())
+    hid[2, 4, 7] = float("nan")
+    par = synth.tree_parents(B, N, seed=5)
+    tok = synth.tree_tokens(synth.base_logits(hid.nan_to_num(), W), par, seed=6).numpy()
+    say("tree step faults B=%d N=%d" % (B, N))
+    fused = _tree_step(hid, W, par, tok)
+    sep = _tree_step(hid, W, par, tok, separate=True)
+    for a, b in zip(fused[1:], sep[1:]):
+        np.testing.assert_array_equal(a, b)
+    assert fused[1][2] == -1 and (fused[2][2] == -1).all()
+    assert (np.delete(fused[1], 2) >= 0).all()
+
+
+def test_full_size_tree_step():
+    wl = synth.WORKLOADS["b8_tree63_h4096_v128256"]
+    say("full-size tree step %s" % wl.name)
+    W, hid = synth.weights(wl, dev()), synth.hidden_states(wl, dev())
+    par = synth.tree_parents(wl.B, wl.K, seed=wl.data_seed)
+    tok = synth.tree_tokens(synth.base_logits(hid, W), par, seed=wl.data_seed + 1, sigma=wl.draft_sigma[0]).numpy()
+    fused = _tree_step(hid, W, par, tok)
+    sep = _tree_step(hid, W, par, tok, separate=True)
+    assert torch.equal(fused[0], sep[0])
+    for a, b in zip(fused[1:], sep[1:]):
+        np.testing.assert_array_equal(a, b)
+    res = oracle.tree_accept_greedy(fused[0].double().numpy(), par, tok)
+    _check_exact(res, fused[1], fused[2], fused[3], range(wl.B))
+    say("  kept depths %s" % fused[1].tolist())
