@@ -4,10 +4,10 @@ One step = one pass of the whole verify path over one batch: the LM-head
 contraction of the K+1 verify positions, the softmax statistics, and the
 acceptance of every sequence (greedy or sampled, by the workload's per-row
 mode), including the residual or bonus draw.  By default the step is one
-spec_verify_step call (spec_tree_verify_step for draft trees; --path fused);
---path separate runs spec_verify_logits then spec_accept_sample /
-spec_accept_greedy / spec_tree_accept_greedy (ragged workloads always run
-separately).  Inputs
+spec_verify_step call (spec_verify_step_ragged for packed batches,
+spec_tree_verify_step for draft trees; --path fused); --path separate runs
+spec_verify_logits then the accept calls (spec_accept_sample /
+spec_accept_greedy, their ragged forms, or spec_tree_accept_greedy).  Inputs
 (weights, hidden states, draft logits, per-round draft tokens and seeds) are
 resident in HBM before the timed region; each timed step uses the next
 pre-drawn draft set and seed.
@@ -281,8 +281,10 @@ def measure(wl, args, dev, n_steps, n_warmup, cpu=False, record_rounds=0):
     stream = torch.cuda.current_stream()
 
     step_ws = None
-    if args.path == "fused" and row_start is None:
-        step_ws = torch.empty(sv.spec_verify_step_workspace_bytes(B, K, V), dtype=torch.uint8, device=dev)
+    if args.path == "fused":
+        nbytes = (sv.spec_verify_step_ragged_workspace_bytes(B, K, V) if row_start is not None
+                  else sv.spec_verify_step_workspace_bytes(B, K, V))
+        step_ws = torch.empty(nbytes, dtype=torch.uint8, device=dev)
         g_arg = None if not len(greedy_rows) else ("all" if all_greedy else greedy_rows)
         s_arg = None if not len(sampled_rows) else ("all" if all_sampled else sampled_rows)
 
@@ -291,6 +293,11 @@ def measure(wl, args, dev, n_steps, n_warmup, cpu=False, record_rounds=0):
         if step_ws is not None and tree is not None:
             sv.spec_tree_verify_step(hidden, W, logits, tree[0], tree[1][r % n_sets], acc, out, step_ws,
                                      out_nodes=tree[2], stream=stream)
+            return
+        if step_ws is not None and row_start is not None:
+            sv.spec_verify_step_ragged(hidden.view(M, H), W, logits.view(M, V), row_start, K, acc, out.view(M),
+                                       step_ws, draft_logits=zd, draft_tokens=d, temperature=T, seeds=seeds[r],
+                                       greedy_rows=g_arg, sampled_rows=s_arg, stream=stream)
             return
         if step_ws is not None:
             sv.spec_verify_step(hidden, W, logits, acc, out, step_ws, draft_logits=zd, draft_tokens=d, temperature=T,
@@ -426,7 +433,8 @@ def measure(wl, args, dev, n_steps, n_warmup, cpu=False, record_rounds=0):
         **({"verify_rows": M, "draft_counts": "K_b ~ U{0..%d}, packed" % K} if row_start is not None else {}),
         **({"tree_nodes": K, "mean_kept_depth": float(np.mean(accepted))} if tree is not None else {}),
         "verify_step_us": step_s * 1e6,
-        "path": ("spec_tree_verify_step" if tree is not None else "spec_verify_step") if step_ws is not None
+        "path": ("spec_tree_verify_step" if tree is not None else
+                 "spec_verify_step_ragged" if row_start is not None else "spec_verify_step") if step_ws is not None
                 else "separate calls",
         "step_us_median": float(np.median(step_us)),
         "step_us_p90": float(np.percentile(step_us, 90)),

@@ -48,6 +48,9 @@
  *                          (computed by the LM-head kernel itself wherever a
  *                          bf16 kernel with that option runs, which saves a
  *                          pass over the logits) and both accept rules.
+ *   spec_verify_step_ragged
+ *                       -- the same for ragged batches (packed rows, a draft
+ *                          count per sequence).
  *   spec_tree_verify_step
  *                       -- the same for draft trees: LM head and the greedy
  *                          tree rule in one call.
@@ -362,6 +365,50 @@ spec_status_t spec_verify_step(const void* hidden, const void* w_lmhead, spec_dt
 
 /* Bytes of workspace spec_verify_step needs (0 if the sizes are out of range). */
 size_t spec_verify_step_workspace_bytes(int B, int K, int V);
+
+/*
+ * spec_verify_step_ragged -- the whole verify step for a ragged batch (each
+ * sequence its own draft count K_b, rows packed; the ragged calls above
+ * define the layout and cite where the pages vary the draft count).
+ *
+ * Same results as spec_verify_logits over the R = total_rows packed hidden
+ * rows (B = R, K = 0) followed by spec_accept_greedy_ragged over greedy_rows
+ * and spec_accept_sample_ragged over sampled_rows, with the same caveat on
+ * sampled decisions within about 1e-6 of a boundary as spec_verify_step.
+ * The LM-head kernel that runs for M = R rows computes the statistics as in
+ * spec_verify_step (cooperative kernel for R <= 16, epilogue records for
+ * R > 16 with H % 64 == 0); elsewhere the call enqueues the separate calls'
+ * kernels.
+ *
+ *   hidden        device, [R, H] in dtype, 16-byte aligned (rows packed as
+ *                 the logits)
+ *   w_lmhead, dtype, V, H: as in spec_verify_logits
+ *   logits        device, [R, V] fp32, 16-byte aligned (written)
+ *   row_start, total_rows, K_max, draft_logits, draft_tokens, accepted_len,
+ *   out_tokens, probs_at_draft, temperature, seeds: as in the ragged accept
+ *                 calls
+ *   greedy_rows, n_greedy / sampled_rows, n_sampled: as in spec_verify_step
+ *   workspace     at least spec_verify_step_ragged_workspace_bytes(B, K_max,
+ *                 V) bytes, 16-byte aligned; contents on entry do not matter
+ * Errors as in the calls it replaces (host checks of row_start and
+ * total_rows as in the ragged accept calls; a sequence whose row_start
+ * entries fail the device checks gets accepted_len[b] = -1).
+ */
+spec_status_t spec_verify_step_ragged(const void* hidden, const void* w_lmhead, spec_dtype_t dtype,
+                                      const float* draft_logits, const int32_t* draft_tokens,
+                                      const int32_t* row_start, int total_rows,
+                                      float temperature, const uint64_t* seeds,
+                                      const int32_t* greedy_rows, int n_greedy,
+                                      const int32_t* sampled_rows, int n_sampled,
+                                      int B, int K_max, int V, int H,
+                                      float* logits, int32_t* accepted_len, int32_t* out_tokens,
+                                      float* probs_at_draft,
+                                      void* workspace, size_t workspace_bytes,
+                                      spec_stream_t stream);
+
+/* Bytes of workspace spec_verify_step_ragged needs for any total_rows in
+ * [B, B*(K_max+1)] (0 if the sizes are out of range). */
+size_t spec_verify_step_ragged_workspace_bytes(int B, int K_max, int V);
 
 /*
  * spec_verify_step_noalloc -- spec_verify_step for callers that cannot

@@ -23,7 +23,13 @@ in the library's HIP kernels; if the library is missing, every call raises.
     spec_verify_step_noalloc(hidden, w_lmhead, logits, accepted_len, out_tokens, draft_logits=None,
                              draft_tokens=None, temperature=1.0, seeds=None, greedy_rows=None, sampled_rows=None,
                              probs_at_draft=None)
-    spec_workspace_bytes(B, K, V), spec_ngram_workspace_bytes(B, max_len), spec_verify_step_workspace_bytes(B, K, V)
+    spec_verify_step_ragged(hidden, w_lmhead, logits, row_start, K_max, accepted_len, out_tokens, workspace,
+                            draft_logits=None, draft_tokens=None, temperature=1.0, seeds=None, greedy_rows=None,
+                            sampled_rows=None, probs_at_draft=None)
+    spec_tree_verify_step(hidden, w_lmhead, logits, parents, tokens, accepted_len, out_tokens, workspace,
+                          out_nodes=None, rows=None)
+    spec_workspace_bytes(B, K, V), spec_ngram_workspace_bytes(B, max_len), spec_verify_step_workspace_bytes(B, K, V),
+    spec_verify_step_ragged_workspace_bytes(B, K_max, V)
 """
 from __future__ import annotations
 
@@ -37,6 +43,7 @@ __all__ = [
     "load_library", "declared_symbols", "spec_verify_logits", "spec_accept_greedy",
     "spec_accept_sample", "spec_accept_greedy_ragged", "spec_accept_sample_ragged", "spec_tree_accept_greedy", "spec_ngram_propose", "spec_ngram_workspace_bytes",
     "spec_verify_step", "spec_verify_step_workspace_bytes", "spec_verify_step_noalloc", "spec_tree_verify_step",
+    "spec_verify_step_ragged", "spec_verify_step_ragged_workspace_bytes",
     "spec_workspace_bytes", "spec_status_string", "spec_last_error_detail", "spec_set_poll_limit",
 ]
 
@@ -73,6 +80,11 @@ _SIGNATURES = {
                                   _c_int, _c_void_p, _c_int, _c_int, _c_int, _c_int, _c_int, _c_void_p, _c_void_p,
                                   _c_void_p, _c_void_p, _c_void_p, _c_size_t, _c_void_p]),
     "spec_verify_step_workspace_bytes": (_c_size_t, [_c_int, _c_int, _c_int]),
+    "spec_verify_step_ragged": (_c_int, [_c_void_p, _c_void_p, _c_int, _c_void_p, _c_void_p, _c_void_p, _c_int,
+                                         _c_float, _c_void_p, _c_void_p, _c_int, _c_void_p, _c_int, _c_int, _c_int,
+                                         _c_int, _c_int, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p,
+                                         _c_size_t, _c_void_p]),
+    "spec_verify_step_ragged_workspace_bytes": (_c_size_t, [_c_int, _c_int, _c_int]),
     "spec_tree_verify_step": (_c_int, [_c_void_p, _c_void_p, _c_int, _c_void_p, _c_void_p, _c_void_p, _c_int, _c_int,
                                        _c_int, _c_int, _c_int, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p,
                                        _c_size_t, _c_void_p]),
@@ -477,6 +489,46 @@ def spec_verify_step(hidden, w_lmhead, logits, accepted_len, out_tokens, workspa
                                 float(temperature), _ptr(seeds), _ptr(g), ng, _ptr(sm), ns, B, P - 1, V, H,
                                 _ptr(logits), _ptr(accepted_len), _ptr(out_tokens), _ptr(probs_at_draft),
                                 _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream)))
+
+
+def spec_verify_step_ragged_workspace_bytes(B: int, K_max: int, V: int) -> int:
+    return int(load_library().spec_verify_step_ragged_workspace_bytes(B, K_max, V))
+
+
+def spec_verify_step_ragged(hidden, w_lmhead, logits, row_start, K_max, accepted_len, out_tokens, workspace,
+                            draft_logits=None, draft_tokens=None, temperature=1.0, seeds=None, greedy_rows=None,
+                            sampled_rows=None, probs_at_draft=None, stream=None) -> None:
+    """The whole verify step of a ragged batch: hidden [R, H] packed by
+    row_start [B+1], logits [R, V] = hidden . w_lmheadᵀ, then the two rules
+    over ``greedy_rows`` / ``sampled_rows`` as in spec_verify_step; the
+    draft and output tensors as in spec_accept_sample_ragged."""
+    R, H = hidden.shape
+    V = w_lmhead.shape[0]
+    if w_lmhead.dtype != hidden.dtype or w_lmhead.shape[1] != H:
+        raise ValueError("shape or dtype mismatch")
+    _dtype_code(hidden)
+    _arg(hidden, "hidden", hidden.dtype)
+    _arg(w_lmhead, "w_lmhead", hidden.dtype)
+    _arg(logits, "logits", _f32(), (R, V))
+    B = _arg(row_start, "row_start", _i32(), (None,)).numel() - 1
+    sampled = sampled_rows is not None and (isinstance(sampled_rows, str) or sampled_rows.numel() > 0)
+    _arg(draft_logits, "draft_logits", _f32(), (R - B, V), optional=R <= B or not sampled)
+    _arg(draft_tokens, "draft_tokens", _i32(), (R - B,), optional=R <= B)
+    _arg(seeds, "seeds", _seed_types(), (B,), optional=not sampled)
+    _arg(accepted_len, "accepted_len", _i32(), (B,))
+    _arg(out_tokens, "out_tokens", _i32(), (R,))
+    _arg(probs_at_draft, "probs_at_draft", _f32(), (R - B, 2), optional=True)
+    g, ng = _row_list(greedy_rows, B)
+    sm, ns = _row_list(sampled_rows, B)
+    _ws(workspace)
+    lib = load_library()
+    _check("spec_verify_step_ragged",
+           lib.spec_verify_step_ragged(_ptr(hidden), _ptr(w_lmhead), _dtype_code(hidden),
+                                       _ptr(draft_logits) if R > B else None, _ptr(draft_tokens) if R > B else None,
+                                       _ptr(row_start), R, float(temperature), _ptr(seeds), _ptr(g), ng, _ptr(sm), ns,
+                                       B, int(K_max), V, H, _ptr(logits), _ptr(accepted_len), _ptr(out_tokens),
+                                       _ptr(probs_at_draft), _ptr(workspace),
+                                       workspace.numel() * workspace.element_size(), _stream(stream)))
 
 
 def spec_verify_step_noalloc(hidden, w_lmhead, logits, accepted_len, out_tokens, draft_logits=None,

@@ -228,9 +228,154 @@ size_t step_extra_records(int B, int K, int V) {
     return M * (((size_t)V + 255) / 256);
 }
 
+// The same bound for a ragged batch of B sequences with at most K drafts
+// each: its total rows R lie in [B, B*(K+1)], and R <= 16 takes the
+// cooperative kernel's records for R target and R - B draft rows.
+size_t step_extra_records_ragged(int B, int K, int V) {
+    const size_t m_max = (size_t)B * (K + 1);
+    const size_t r_coop = std::min<size_t>(16, m_max);
+    const size_t coop = r_coop >= (size_t)B ? (2 * r_coop - B) * sv::kCoopMaxRecs : 0;
+    const size_t big = m_max > 16 ? m_max * (((size_t)V + 255) / 256) : 0;
+    return std::max(coop, big);
+}
+
 // A row list as the fused step takes it: (NULL, 0) none, (NULL, B) all,
 // (list, 0..B) those.
 bool rows_ok(const int32_t* rows, int n, int B) { return rows ? (n >= 0 && n <= B) : (n == 0 || n == B); }
+
+// The whole step over any batch layout: seq.total LM-head rows (hidden
+// [total, H], logits [total, V]) of which each sequence's first is its
+// target-only row, and seq.total - seq.B draft rows; arguments checked by
+// the caller, the workspace at least the size its entry point names.
+spec_status_t step_impl(const void* hidden, const void* w_lmhead, spec_dtype_t dtype, const float* draft_logits,
+                        const int32_t* draft_tokens, float temperature, const uint64_t* seeds,
+                        const int32_t* greedy_rows, int n_greedy, const int32_t* sampled_rows, int n_sampled,
+                        sv::SeqRows seq, int V, int H, float* logits, int32_t* accepted_len, int32_t* out_tokens,
+                        float* probs_at_draft, void* workspace, size_t workspace_bytes, hipStream_t s) {
+    const int B = seq.B, K = seq.K;
+    const int M = seq.total;                 // LM-head rows
+    const int n_drf = seq.total - seq.B;     // draft rows
+    Workspace ws;
+    const size_t base = workspace_layout(B, K, V, workspace, &ws);
+    sv::StatRec* tstats = reinterpret_cast<sv::StatRec*>(static_cast<char*>(workspace) + base);
+    const float c = n_sampled > 0 ? sv::kLog2e / temperature : sv::kLog2e;
+    const int ns = sampled_rows ? n_sampled : (n_sampled ? B : 0);
+    const int ng = greedy_rows ? n_greedy : (n_greedy ? B : 0);
+    const bool any = ng > 0 || ns > 0;
+    hipError_t e = hipSuccess;
+
+    // At M <= 16 the cooperative kernel computes the statistics of the
+    // target rows as it sums each tile and those of the draft rows while its
+    // first loads are in flight, one record per workgroup and row; the accept
+    // kernels merge those records straight from memory.  No pass reads the
+    // logits back and no statistics kernel runs.
+    const float* dl = (ns > 0 && n_drf > 0) ? draft_logits : nullptr;
+    const bool fused = dl && (long)ns * (2 * K + 1) <= sv::kFusedAcceptMaxRows;
+    int cus = 0;
+    if (any && dtype == SPEC_BF16) {
+        e = num_cus(&cus);
+        if (e != hipSuccess) return hip_fail(e);
+        const int crec = sv::lmhead_coop_records(M, V, H, dl ? n_drf : 0, cus);
+        if (crec > 0) {
+            sv::StatRec* trec = tstats;                          // M x crec
+            sv::StatRec* drec = tstats + (size_t)M * crec;       // n_drf x crec
+            const sv::CoopStats cs{trec, dl, dl ? n_drf : 0, drec, c, fused ? ws.counters : nullptr,
+                                   fused ? sv::accept_zero_ints(B, ns, V) : 0};
+            e = sv::launch_lmhead_coop_stats(static_cast<const uint16_t*>(hidden),
+                                             static_cast<const uint16_t*>(w_lmhead), logits, M, V, H, cus, s, cs);
+            if (e == hipSuccess && ng > 0)
+                e = sv::launch_accept(logits, nullptr, draft_tokens, nullptr, greedy_rows, ng, seq, V, sv::kLog2e,
+                                      false, sv::RecLayout{trec, crec, true, nullptr, 0, false}, accepted_len,
+                                      out_tokens, nullptr, ws.info, ws.counters, s);
+            const sv::RecLayout lay{trec, crec, true, drec, crec, true};
+            if (e == hipSuccess && ns > 0) {
+                if (fused) {
+                    e = sv::launch_accept_residual(logits, dl, draft_tokens, seeds, sampled_rows, ns, seq, V, c, lay,
+                                                   accepted_len, out_tokens, probs_at_draft, ws.sums, ws.counters, ws.slots, poll_limit(), s);
+                } else {
+                    e = sv::launch_accept(logits, dl, draft_tokens, seeds, sampled_rows, ns, seq, V, c, true, lay,
+                                          accepted_len, out_tokens, probs_at_draft, ws.info, ws.counters, s, ws.slots, residual_slots(ns, V));
+                    if (e == hipSuccess)
+                        e = sv::launch_residual(logits, dl, ns, V, c, ws.info, ws.sums, ws.counters, ws.slots, poll_limit(), out_tokens, s);
+                }
+            }
+            return e == hipSuccess ? SPEC_OK : hip_fail(e);
+        }
+    }
+
+    // The statistics epilogue pays where the direct-to-LDS kernel runs: it
+    // removes the pass that reads the logits back, and with the loop's order
+    // pinned it costs the kernel ~2%.  Its records (one per 256 vocabulary
+    // entries) are merged by the accept kernels straight from memory when a
+    // sequence has at most kAcceptRowsDirect rows, else folded into the
+    // statistics pass's chunk records first.  Greedy and sampled rows are
+    // accepted in one launch.  Elsewhere (the skinny and tiled kernels, fp32)
+    // the step runs the separate calls' kernels.
+    const int big_recs = dtype == SPEC_BF16 ? sv::lmhead_big_records(M, V, H) : 0;
+    const bool epilogue = any && big_recs > 0;
+    if (!epilogue) {
+        if (dtype == SPEC_BF16) {
+            e = num_cus(&cus);
+            if (e == hipSuccess)
+                e = sv::launch_lmhead_bf16(static_cast<const uint16_t*>(hidden),
+                                           static_cast<const uint16_t*>(w_lmhead), logits, M, V, H, cus, s);
+        } else {
+            e = sv::launch_lmhead_f32(static_cast<const float*>(hidden), static_cast<const float*>(w_lmhead), logits,
+                                      M, V, H, s);
+        }
+        if (e != hipSuccess) return hip_fail(e);
+        spec_status_t st = SPEC_OK;
+        if (ng > 0)
+            st = greedy_impl(logits, draft_tokens, greedy_rows, n_greedy, seq, V, accepted_len, out_tokens,
+                             workspace, workspace_bytes, s);
+        if (st == SPEC_OK && ns > 0)
+            st = sample_impl(logits, draft_logits, draft_tokens, temperature, seeds, sampled_rows, n_sampled, seq, V,
+                             accepted_len, out_tokens, probs_at_draft, workspace, workspace_bytes, s);
+        return st;
+    }
+
+    // draft-row statistics first: they do not depend on the LM head (the pass
+    // also clears the completion counters a fused accept + residual needs)
+    const int nc = sv::n_chunks(V);
+    if (dl) e = sv::launch_softmax_stats(nullptr, dl, sampled_rows, ns, seq, V, c, true, ws.stats, s,
+                                         fused ? ws.counters : nullptr, sv::accept_zero_ints(B, ns, V));
+    int nrec = 0;
+    if (e == hipSuccess && cus == 0) e = num_cus(&cus);
+    if (e == hipSuccess)
+        e = sv::launch_lmhead_bf16(static_cast<const uint16_t*>(hidden), static_cast<const uint16_t*>(w_lmhead), logits,
+                                   M, V, H, cus, s, tstats, c, &nrec);
+    if (e == hipSuccess && nrec != big_recs) e = hipErrorInvalidValue;   // the kernel the shape rule named
+    // target chunk records after the draft slots: B*K + M rows fit the
+    // statistics area, which is sized for B*(K+1) + B*K rows (M <= B*(K+1))
+    const bool direct = (ns > 0 ? 2 * K + 1 : K + 1) <= sv::kAcceptRowsDirect;
+    sv::StatRec* trec = ws.stats + (size_t)B * K * nc;
+    if (e == hipSuccess && !direct) e = sv::launch_fold_records(tstats, nrec, M, V, c, trec, s);
+    const sv::RecLayout tgt = direct ? sv::RecLayout{tstats, nrec, true, nullptr, 0, false}
+                                     : sv::RecLayout{trec, nc, true, nullptr, 0, false};
+    const sv::RecLayout lay{tgt.tgt, tgt.tgt_nc, true, ws.stats, nc, false};
+    if (e == hipSuccess && ng > 0 && ns > 0 && !fused) {
+        e = sv::launch_accept_both(logits, dl, draft_tokens, seeds, greedy_rows, ng, sampled_rows, ns, seq, V, c, tgt,
+                                   lay, accepted_len, out_tokens, probs_at_draft, ws.info, ws.counters, s, ws.slots, residual_slots(ns, V));
+        if (e == hipSuccess)
+            e = sv::launch_residual(logits, dl, ns, V, c, ws.info, ws.sums, ws.counters, ws.slots, poll_limit(), out_tokens, s);
+        return e == hipSuccess ? SPEC_OK : hip_fail(e);
+    }
+    if (e == hipSuccess && ng > 0)
+        e = sv::launch_accept(logits, nullptr, draft_tokens, nullptr, greedy_rows, ng, seq, V, sv::kLog2e, false, tgt,
+                              accepted_len, out_tokens, nullptr, ws.info, ws.counters, s);
+    if (e == hipSuccess && ns > 0) {
+        if (fused) {
+            e = sv::launch_accept_residual(logits, dl, draft_tokens, seeds, sampled_rows, ns, seq, V, c, lay,
+                                           accepted_len, out_tokens, probs_at_draft, ws.sums, ws.counters, ws.slots, poll_limit(), s);
+        } else {
+            e = sv::launch_accept(logits, dl, draft_tokens, seeds, sampled_rows, ns, seq, V, c, true, lay,
+                                  accepted_len, out_tokens, probs_at_draft, ws.info, ws.counters, s, ws.slots, residual_slots(ns, V));
+            if (e == hipSuccess)
+                e = sv::launch_residual(logits, dl, ns, V, c, ws.info, ws.sums, ws.counters, ws.slots, poll_limit(), out_tokens, s);
+        }
+    }
+    return e == hipSuccess ? SPEC_OK : hip_fail(e);
+}
 
 }  // namespace
 
@@ -371,129 +516,40 @@ spec_status_t spec_verify_step(const void* hidden, const void* w_lmhead, spec_dt
     if (!aligned16(hidden) || !aligned16(w_lmhead) || !aligned16(logits)) return SPEC_ERR_ALIGN;
     if (!workspace || workspace_bytes < spec_verify_step_workspace_bytes(B, K, V)) return SPEC_ERR_WORKSPACE;
     if (!aligned16(workspace)) return SPEC_ERR_ALIGN;
+    return step_impl(hidden, w_lmhead, dtype, draft_logits, draft_tokens, temperature, seeds, greedy_rows, n_greedy,
+                     sampled_rows, n_sampled, dense_rows(B, K), V, H, logits, accepted_len, out_tokens, probs_at_draft,
+                     workspace, workspace_bytes, static_cast<hipStream_t>(stream));
+}
 
-    const int M = B * (K + 1);
-    Workspace ws;
-    const size_t base = workspace_layout(B, K, V, workspace, &ws);
-    sv::StatRec* tstats = reinterpret_cast<sv::StatRec*>(static_cast<char*>(workspace) + base);
-    const sv::SeqRows seq = dense_rows(B, K);
-    const float c = n_sampled > 0 ? sv::kLog2e / temperature : sv::kLog2e;
-    const int ns = sampled_rows ? n_sampled : (n_sampled ? B : 0);
-    const int ng = greedy_rows ? n_greedy : (n_greedy ? B : 0);
-    hipStream_t s = static_cast<hipStream_t>(stream);
-    hipError_t e = hipSuccess;
-
-    // At M <= 16 the cooperative kernel computes the statistics of the
-    // target rows as it sums each tile and those of the draft rows while its
-    // first loads are in flight, one record per workgroup and row; the accept
-    // kernels merge those records straight from memory.  No pass reads the
-    // logits back and no statistics kernel runs.
-    const float* dl = (ns > 0 && K > 0) ? draft_logits : nullptr;
-    const bool fused = dl && (long)ns * (2 * K + 1) <= sv::kFusedAcceptMaxRows;
-    int cus = 0;
-    if (any && dtype == SPEC_BF16) {
-        e = num_cus(&cus);
-        if (e != hipSuccess) return hip_fail(e);
-        const int crec = sv::lmhead_coop_records(M, V, H, dl ? B * K : 0, cus);
-        if (crec > 0) {
-            sv::StatRec* trec = tstats;                          // M x crec
-            sv::StatRec* drec = tstats + (size_t)M * crec;       // B*K x crec
-            const sv::CoopStats cs{trec, dl, dl ? B * K : 0, drec, c, fused ? ws.counters : nullptr,
-                                   fused ? sv::accept_zero_ints(B, ns, V) : 0};
-            e = sv::launch_lmhead_coop_stats(static_cast<const uint16_t*>(hidden),
-                                             static_cast<const uint16_t*>(w_lmhead), logits, M, V, H, cus, s, cs);
-            if (e == hipSuccess && ng > 0)
-                e = sv::launch_accept(logits, nullptr, draft_tokens, nullptr, greedy_rows, ng, seq, V, sv::kLog2e,
-                                      false, sv::RecLayout{trec, crec, true, nullptr, 0, false}, accepted_len,
-                                      out_tokens, nullptr, ws.info, ws.counters, s);
-            const sv::RecLayout lay{trec, crec, true, drec, crec, true};
-            if (e == hipSuccess && ns > 0) {
-                if (fused) {
-                    e = sv::launch_accept_residual(logits, dl, draft_tokens, seeds, sampled_rows, ns, seq, V, c, lay,
-                                                   accepted_len, out_tokens, probs_at_draft, ws.sums, ws.counters, ws.slots, poll_limit(), s);
-                } else {
-                    e = sv::launch_accept(logits, dl, draft_tokens, seeds, sampled_rows, ns, seq, V, c, true, lay,
-                                          accepted_len, out_tokens, probs_at_draft, ws.info, ws.counters, s, ws.slots, residual_slots(ns, V));
-                    if (e == hipSuccess)
-                        e = sv::launch_residual(logits, dl, ns, V, c, ws.info, ws.sums, ws.counters, ws.slots, poll_limit(), out_tokens, s);
-                }
-            }
-            return e == hipSuccess ? SPEC_OK : hip_fail(e);
-        }
+spec_status_t spec_verify_step_ragged(const void* hidden, const void* w_lmhead, spec_dtype_t dtype,
+                                      const float* draft_logits, const int32_t* draft_tokens,
+                                      const int32_t* row_start, int total_rows, float temperature,
+                                      const uint64_t* seeds, const int32_t* greedy_rows, int n_greedy,
+                                      const int32_t* sampled_rows, int n_sampled, int B, int K_max, int V, int H,
+                                      float* logits, int32_t* accepted_len, int32_t* out_tokens,
+                                      float* probs_at_draft, void* workspace, size_t workspace_bytes,
+                                      spec_stream_t stream) {
+    if (!hidden || !w_lmhead || !logits || !accepted_len || !out_tokens) return SPEC_ERR_ARG;
+    if (dtype != SPEC_BF16 && dtype != SPEC_F32) return SPEC_ERR_DTYPE;
+    if (!sizes_ok(B, K_max, V) || H < 8 || (H & 7) != 0) return SPEC_ERR_ARG;
+    spec_status_t st = check_ragged(row_start, total_rows, B, K_max);
+    if (st != SPEC_OK) return st;
+    if (!rows_ok(greedy_rows, n_greedy, B) || !rows_ok(sampled_rows, n_sampled, B)) return SPEC_ERR_ARG;
+    const bool any = n_greedy > 0 || n_sampled > 0;
+    const bool has_drafts = total_rows > B;
+    if (any && has_drafts && !draft_tokens) return SPEC_ERR_ARG;
+    if (n_sampled > 0) {
+        if (!seeds || (has_drafts && !draft_logits)) return SPEC_ERR_ARG;
+        if (!(temperature > 0.f) || !isfinite(temperature)) return SPEC_ERR_ARG;
+        if (has_drafts && !aligned16(draft_logits)) return SPEC_ERR_ALIGN;
     }
-
-    // The statistics epilogue pays where the direct-to-LDS kernel runs: it
-    // removes the pass that reads the logits back, and with the loop's order
-    // pinned it costs the kernel ~2%.  Its records (one per 256 vocabulary
-    // entries) are merged by the accept kernels straight from memory when a
-    // sequence has at most kAcceptRowsDirect rows, else folded into the
-    // statistics pass's chunk records first.  Greedy and sampled rows are
-    // accepted in one launch.  Elsewhere (the skinny and tiled kernels, fp32)
-    // the step runs the separate calls' kernels.
-    const int big_recs = dtype == SPEC_BF16 ? sv::lmhead_big_records(M, V, H) : 0;
-    const bool epilogue = any && big_recs > 0;
-    if (!epilogue) {
-        if (dtype == SPEC_BF16) {
-            e = num_cus(&cus);
-            if (e == hipSuccess)
-                e = sv::launch_lmhead_bf16(static_cast<const uint16_t*>(hidden),
-                                           static_cast<const uint16_t*>(w_lmhead), logits, M, V, H, cus, s);
-        } else {
-            e = sv::launch_lmhead_f32(static_cast<const float*>(hidden), static_cast<const float*>(w_lmhead), logits,
-                                      M, V, H, s);
-        }
-        if (e != hipSuccess) return hip_fail(e);
-        spec_status_t st = SPEC_OK;
-        if (ng > 0)
-            st = greedy_impl(logits, draft_tokens, greedy_rows, n_greedy, seq, V, accepted_len, out_tokens,
-                             workspace, workspace_bytes, s);
-        if (st == SPEC_OK && ns > 0)
-            st = sample_impl(logits, draft_logits, draft_tokens, temperature, seeds, sampled_rows, n_sampled, seq, V,
-                             accepted_len, out_tokens, probs_at_draft, workspace, workspace_bytes, s);
-        return st;
-    }
-
-    // draft-row statistics first: they do not depend on the LM head (the pass
-    // also clears the completion counters a fused accept + residual needs)
-    const int nc = sv::n_chunks(V);
-    if (dl) e = sv::launch_softmax_stats(nullptr, dl, sampled_rows, ns, seq, V, c, true, ws.stats, s,
-                                         fused ? ws.counters : nullptr, sv::accept_zero_ints(B, ns, V));
-    int nrec = 0;
-    if (e == hipSuccess && cus == 0) e = num_cus(&cus);
-    if (e == hipSuccess)
-        e = sv::launch_lmhead_bf16(static_cast<const uint16_t*>(hidden), static_cast<const uint16_t*>(w_lmhead), logits,
-                                   M, V, H, cus, s, tstats, c, &nrec);
-    if (e == hipSuccess && nrec != big_recs) e = hipErrorInvalidValue;   // the kernel the shape rule named
-    // target chunk records after the draft slots: B*K + M rows fit the
-    // statistics area, which is sized for B*(K+1) + B*K rows
-    const bool direct = (ns > 0 ? 2 * K + 1 : K + 1) <= sv::kAcceptRowsDirect;
-    sv::StatRec* trec = ws.stats + (size_t)B * K * nc;
-    if (e == hipSuccess && !direct) e = sv::launch_fold_records(tstats, nrec, M, V, c, trec, s);
-    const sv::RecLayout tgt = direct ? sv::RecLayout{tstats, nrec, true, nullptr, 0, false}
-                                     : sv::RecLayout{trec, nc, true, nullptr, 0, false};
-    const sv::RecLayout lay{tgt.tgt, tgt.tgt_nc, true, ws.stats, nc, false};
-    if (e == hipSuccess && ng > 0 && ns > 0 && !fused) {
-        e = sv::launch_accept_both(logits, dl, draft_tokens, seeds, greedy_rows, ng, sampled_rows, ns, seq, V, c, tgt,
-                                   lay, accepted_len, out_tokens, probs_at_draft, ws.info, ws.counters, s, ws.slots, residual_slots(ns, V));
-        if (e == hipSuccess)
-            e = sv::launch_residual(logits, dl, ns, V, c, ws.info, ws.sums, ws.counters, ws.slots, poll_limit(), out_tokens, s);
-        return e == hipSuccess ? SPEC_OK : hip_fail(e);
-    }
-    if (e == hipSuccess && ng > 0)
-        e = sv::launch_accept(logits, nullptr, draft_tokens, nullptr, greedy_rows, ng, seq, V, sv::kLog2e, false, tgt,
-                              accepted_len, out_tokens, nullptr, ws.info, ws.counters, s);
-    if (e == hipSuccess && ns > 0) {
-        if (fused) {
-            e = sv::launch_accept_residual(logits, dl, draft_tokens, seeds, sampled_rows, ns, seq, V, c, lay,
-                                           accepted_len, out_tokens, probs_at_draft, ws.sums, ws.counters, ws.slots, poll_limit(), s);
-        } else {
-            e = sv::launch_accept(logits, dl, draft_tokens, seeds, sampled_rows, ns, seq, V, c, true, lay,
-                                  accepted_len, out_tokens, probs_at_draft, ws.info, ws.counters, s, ws.slots, residual_slots(ns, V));
-            if (e == hipSuccess)
-                e = sv::launch_residual(logits, dl, ns, V, c, ws.info, ws.sums, ws.counters, ws.slots, poll_limit(), out_tokens, s);
-        }
-    }
-    return e == hipSuccess ? SPEC_OK : hip_fail(e);
+    if (!aligned16(hidden) || !aligned16(w_lmhead) || !aligned16(logits)) return SPEC_ERR_ALIGN;
+    if (!workspace || workspace_bytes < spec_verify_step_ragged_workspace_bytes(B, K_max, V)) return SPEC_ERR_WORKSPACE;
+    if (!aligned16(workspace)) return SPEC_ERR_ALIGN;
+    return step_impl(hidden, w_lmhead, dtype, draft_logits, draft_tokens, temperature, seeds, greedy_rows, n_greedy,
+                     sampled_rows, n_sampled, sv::SeqRows{row_start, B, K_max, total_rows}, V, H, logits,
+                     accepted_len, out_tokens, probs_at_draft, workspace, workspace_bytes,
+                     static_cast<hipStream_t>(stream));
 }
 
 spec_status_t spec_verify_step_noalloc(const void* hidden, const void* w_lmhead, spec_dtype_t dtype,
@@ -580,6 +636,12 @@ spec_status_t spec_tree_verify_step(const void* hidden, const void* w_lmhead, sp
 size_t spec_verify_step_workspace_bytes(int B, int K, int V) {
     if (!sizes_ok(B, K, V)) return 0;
     return workspace_layout(B, K, V, nullptr, nullptr) + align256(step_extra_records(B, K, V) * sizeof(sv::StatRec));
+}
+
+size_t spec_verify_step_ragged_workspace_bytes(int B, int K_max, int V) {
+    if (!sizes_ok(B, K_max, V)) return 0;
+    return workspace_layout(B, K_max, V, nullptr, nullptr) +
+           align256(step_extra_records_ragged(B, K_max, V) * sizeof(sv::StatRec));
 }
 
 size_t spec_workspace_bytes(int B, int K, int V) {

@@ -30,7 +30,8 @@ def test_exports_every_declared_symbol(lib):
                           "spec_accept_greedy_ragged", "spec_accept_sample_ragged", "spec_tree_accept_greedy",
                           "spec_ngram_propose", "spec_ngram_workspace_bytes",
                           "spec_verify_step", "spec_verify_step_workspace_bytes", "spec_verify_step_noalloc",
-                          "spec_tree_verify_step",
+                          "spec_tree_verify_step", "spec_verify_step_ragged",
+                          "spec_verify_step_ragged_workspace_bytes",
                           "spec_workspace_bytes", "spec_status_string", "spec_last_error_detail",
                           "spec_set_poll_limit"}
     for n in names:
@@ -237,6 +238,61 @@ def test_step_validation(lib):
     assert _step(lib, ws=MIS) == sv.SPEC_ERR_ALIGN
     # greedy rows only: no seeds, draft logits or temperature needed
     assert _step(lib, ns=0, seeds=None, dl=None, T=0.0, g=A, ng=0, ws=None) == sv.SPEC_ERR_WORKSPACE
+
+
+def _step_ragged(lib, hid=A, w=A, dt=0, dl=A, dtok=A, rs=A, total=5, T=1.0, seeds=A, g=None, ng=0, sm=None, ns=2,
+                 B=2, K=3, V=100, H=64, logits=A, acc=A, out=A, ws=A, wsb=None):
+    if wsb is None:
+        wsb = sv.spec_verify_step_ragged_workspace_bytes(B, K, V) or (1 << 20)
+    return lib.spec_verify_step_ragged(hid, w, dt, dl, dtok, rs, total, T, seeds, g, ng, sm, ns, B, K, V, H, logits,
+                                       acc, out, None, ws, wsb, None)
+
+
+def test_ragged_step_workspace_bytes(lib):
+    """Any R in [B, B*(K_max+1)]: R <= 16 takes the cooperative kernel's
+    records (at most 1024 per row) for R target and R - B draft rows, R > 16
+    one record per 256 vocabulary entries of each target row."""
+    base = sv.spec_workspace_bytes
+    rec = 16                                                 # bytes per record
+    # B = 1, K_max = 5: R <= 6, so 2*6 - 1 = 11 rows of cooperative records,
+    # as in the dense step
+    assert sv.spec_verify_step_ragged_workspace_bytes(1, 5, 128256) == sv.spec_verify_step_workspace_bytes(1, 5, 128256)
+    # B = 4, K_max = 7: R up to 32, but R = 16 (cooperative) needs 28 rows of
+    # 1024 records, more than 32 rows of 501
+    assert sv.spec_verify_step_ragged_workspace_bytes(4, 7, 128256) == base(4, 7, 128256) + 28 * 1024 * rec
+    # B = 20: R >= 20 > 16, never cooperative
+    assert sv.spec_verify_step_ragged_workspace_bytes(20, 3, 128256) == \
+        base(20, 3, 128256) + (80 * 501 * rec + 255) // 256 * 256
+    assert sv.spec_verify_step_ragged_workspace_bytes(1, 64, 100) == 0
+    assert sv.spec_verify_step_ragged_workspace_bytes(0, 3, 100) == 0
+
+
+def test_ragged_step_validation(lib):
+    assert _step_ragged(lib, hid=None) == sv.SPEC_ERR_ARG
+    assert _step_ragged(lib, logits=None) == sv.SPEC_ERR_ARG
+    assert _step_ragged(lib, dt=3) == sv.SPEC_ERR_DTYPE
+    assert _step_ragged(lib, K=64) == sv.SPEC_ERR_ARG
+    assert _step_ragged(lib, H=12) == sv.SPEC_ERR_ARG
+    assert _step_ragged(lib, rs=None) == sv.SPEC_ERR_ARG
+    assert _step_ragged(lib, rs=P(0x10002)) == sv.SPEC_ERR_ALIGN
+    assert _step_ragged(lib, total=1) == sv.SPEC_ERR_ARG           # fewer rows than sequences
+    assert _step_ragged(lib, total=9) == sv.SPEC_ERR_ARG           # more than B*(K_max+1)
+    assert _step_ragged(lib, ns=1) == sv.SPEC_ERR_ARG              # NULL list: 0 or B only
+    assert _step_ragged(lib, sm=A, ns=3) == sv.SPEC_ERR_ARG
+    assert _step_ragged(lib, dtok=None) == sv.SPEC_ERR_ARG         # R > B: there are drafts
+    assert _step_ragged(lib, dl=None) == sv.SPEC_ERR_ARG
+    assert _step_ragged(lib, seeds=None) == sv.SPEC_ERR_ARG
+    assert _step_ragged(lib, T=-1.0) == sv.SPEC_ERR_ARG
+    assert _step_ragged(lib, dl=MIS) == sv.SPEC_ERR_ALIGN
+    assert _step_ragged(lib, hid=MIS) == sv.SPEC_ERR_ALIGN
+    assert _step_ragged(lib, logits=MIS) == sv.SPEC_ERR_ALIGN
+    assert _step_ragged(lib, wsb=16) == sv.SPEC_ERR_WORKSPACE
+    # the dense step's size is not enough where R <= 16 can be cooperative
+    assert _step_ragged(lib, B=4, K=7, total=16, ns=4,
+                        wsb=sv.spec_verify_step_workspace_bytes(4, 7, 100)) == sv.SPEC_ERR_WORKSPACE
+    assert _step_ragged(lib, ws=MIS) == sv.SPEC_ERR_ALIGN
+    # no drafts at all (R == B): neither draft logits nor tokens needed
+    assert _step_ragged(lib, total=2, dl=None, dtok=None, ws=None) == sv.SPEC_ERR_WORKSPACE
 
 
 def _tree_step(lib, hid=A, w=A, dt=sv.SPEC_BF16, par=A, tok=A, rows=None, nr=0, B=2, N=7, V=1000, H=64,

@@ -235,3 +235,150 @@ def test_full_size_packed_workload():
     c = _compare("greedy", rg, acc, out, rs, greedy_rows, exact=True)
     c.merge(_compare("sample", rsmp, acc, out, rs, sampled_rows))
     say("  " + str(c))
+
+
+# ------------------------------------------------ the one-call ragged step --
+
+def _step_inputs(B, K_max, H, V, dtype, seed, counts=None, T=0.9):
+    wl = synth.Workload("t", B=B, K=K_max, H=H, V=V, dtype=dtype, w_std=0.03 if dtype == "bf16" else 0.05,
+                        temperature=T, draft="additive", draft_sigma=(0.5, 0.5), data_seed=seed)
+    inp = synth.round_inputs(wl, 0, device=dev())
+    counts = synth.draft_counts(B, K_max, seed) if counts is None else np.asarray(counts, np.int32)
+    rs = synth.row_start(counts)
+    hp = synth.pack_rows(inp["hidden"], counts).contiguous()
+    zdp = synth.pack_rows(inp["draft_logits"], counts, True).contiguous()
+    dp = synth.pack_rows(inp["drafts"], counts, True).contiguous()
+    return wl, inp, rs, hp, zdp, dp
+
+
+def _ragged_step(hp, W, rs, K_max, zdp, dp, T, seeds, greedy_rows, sampled_rows):
+    R, V = hp.shape[0], W.shape[0]
+    B = len(rs) - 1
+    logits = torch.full((R, V), float("nan"), dtype=torch.float32, device=dev())
+    acc = torch.full((B,), -2, dtype=torch.int32, device=dev())
+    out = torch.full((R,), -9, dtype=torch.int32, device=dev())
+    pad = torch.full((R - B, 2), float("nan"), dtype=torch.float32, device=dev())
+    ws = torch.empty(sv.spec_verify_step_ragged_workspace_bytes(B, K_max, V), dtype=torch.uint8, device=dev())
+
+    def rl(r):
+        if r is None or isinstance(r, str):
+            return r
+        return torch.as_tensor(np.asarray(r, np.int32), device=dev())
+    sv.spec_verify_step_ragged(hp, W, logits, torch.as_tensor(rs, device=dev()), K_max, acc, out, ws,
+                               draft_logits=zdp if R > B else None, draft_tokens=dp if R > B else None,
+                               temperature=T, seeds=seeds_tensor(seeds), greedy_rows=rl(greedy_rows),
+                               sampled_rows=rl(sampled_rows), probs_at_draft=pad)
+    torch.cuda.synchronize()
+    return logits, acc.cpu().numpy(), out.cpu().numpy(), pad.cpu().numpy()
+
+
+def _check_step(wl, inp, rs, hp, zdp, dp, greedy_rows, sampled_rows):
+    """Logits bit-identical to spec_verify_logits on the packed rows; greedy
+    decisions identical to spec_accept_greedy_ragged and exact against the
+    oracle; sampled decisions of the step and of spec_accept_sample_ragged
+    against the oracle, probabilities within 1e-5."""
+    B, K, V, T = wl.B, wl.K, wl.V, wl.temperature
+    R = hp.shape[0]
+    logits, acc, out, pad = _ragged_step(hp, inp["W"], rs, K, zdp, dp, T, inp["seeds"], greedy_rows, sampled_rows)
+    ref = gpu_logits(hp.view(R, 1, wl.H), inp["W"]).view(R, V)
+    assert torch.equal(logits, ref), "the ragged step changed the logits"
+    z = ref.double().cpu().numpy()
+    g_rows = np.arange(B) if isinstance(greedy_rows, str) else np.asarray(greedy_rows if greedy_rows is not None
+                                                                          else [], np.int64)
+    s_rows = np.arange(B) if isinstance(sampled_rows, str) else np.asarray(sampled_rows if sampled_rows is not None
+                                                                           else [], np.int64)
+    c = ParityCounts()
+    if len(g_rows):
+        acc_g, out_g = _run_greedy(rs, ref.cpu(), dp.cpu(), K, g_rows)
+        np.testing.assert_array_equal(acc[g_rows], acc_g[g_rows])
+        for b in g_rows:
+            np.testing.assert_array_equal(out[rs[b]:rs[b + 1]], out_g[rs[b]:rs[b + 1]])
+        res = oracle.accept_greedy_ragged(z, dp.cpu().numpy(), rs, K, g_rows)
+        c.merge(_compare("greedy", res, acc, out, rs, g_rows, exact=True))
+    if len(s_rows):
+        res = oracle.accept_sample_ragged(z, zdp.double().cpu().numpy(), dp.cpu().numpy(), rs, K, T, inp["seeds"],
+                                          s_rows)
+        c.merge(_compare("sample", res, acc, out, rs, s_rows))
+        acc_s, out_s, _ = _run_sample(rs, ref.cpu(), zdp.cpu(), dp.cpu(), K, T, inp["seeds"], s_rows)
+        c.merge(_compare("sample", res, acc_s, out_s, rs, s_rows))
+        for b in s_rows:
+            d0, d1 = int(rs[b]) - b, int(rs[b + 1]) - 1 - b
+            np.testing.assert_allclose(pad[d0:d1], res.probs_at_draft[d0:d1], atol=1e-5, rtol=0)
+    say("  " + str(c))
+
+
+@pytest.mark.parametrize("B,K_max,H,V,dtype,counts,path", [
+    (3, 4, 512, 3001, "bf16", [4, 0, 2], "cooperative records, one-launch accept + residual (R = 9)"),
+    (6, 4, 256, 2053, "bf16", [1, 0, 2, 1, 0, 1], "cooperative records, separate residual launch (R = 11)"),
+    (2, 5, 4096, 40000, "bf16", [5, 3], "cooperative records, H = 4096 (R = 10)"),
+    (4, 7, 256, 5003, "bf16", [0, 7, 3, 2], "cooperative at R = 16 where B*(K_max+1) = 32"),
+    (8, 5, 256, 4099, "bf16", None, "direct-to-LDS epilogue records merged from memory"),
+    (6, 15, 256, 5003, "bf16", None, "direct-to-LDS epilogue records folded to chunks (K_max = 15)"),
+    (20, 3, 128, 1031, "bf16", [0] * 20, "direct-to-LDS, no draft rows at all (R = B)"),
+    (5, 7, 520, 2053, "bf16", None, "tiled kernel (H % 64 != 0): the separate calls' kernels"),
+    (4, 3, 256, 1000, "f32", None, "fp32: the separate calls' kernels"),
+])
+def test_ragged_step_paths(B, K_max, H, V, dtype, counts, path):
+    wl, inp, rs, hp, zdp, dp = _step_inputs(B, K_max, H, V, dtype, seed=B * 7 + K_max + V, counts=counts)
+    say("ragged step B=%d K_max=%d H=%d V=%d %s R=%d: %s" % (B, K_max, H, V, dtype, hp.shape[0], path))
+    half = B // 2
+    _check_step(wl, inp, rs, hp, zdp, dp, list(range(half)), list(range(half, B)))
+    _check_step(wl, inp, rs, hp, zdp, dp, None, "all")
+    _check_step(wl, inp, rs, hp, zdp, dp, "all", None)
+
+
+@pytest.mark.parametrize("B,K", [(2, 5), (8, 4)])
+def test_ragged_step_uniform_counts_match_dense_step(B, K):
+    """Every K_b = K: the same kernels and record layouts as spec_verify_step
+    on the dense batch, so every output matches bit for bit."""
+    wl, inp, rs, hp, zdp, dp = _step_inputs(B, K, 256, 3001, "bf16", seed=50 + B, counts=[K] * B)
+    say("ragged step, uniform counts B=%d K=%d: against the dense step" % (B, K))
+    P, V = K + 1, wl.V
+    sm = list(range(1, B, 2))
+    gr = list(range(0, B, 2))
+    logits, acc, out, pad = _ragged_step(hp, inp["W"], rs, K, zdp, dp, wl.temperature, inp["seeds"], gr, sm)
+    d_logits = torch.empty((B, P, V), dtype=torch.float32, device=dev())
+    d_acc = torch.full((B,), -2, dtype=torch.int32, device=dev())
+    d_out = torch.full((B, P), -9, dtype=torch.int32, device=dev())
+    d_pad = torch.full((B, K, 2), float("nan"), dtype=torch.float32, device=dev())
+    ws = torch.empty(sv.spec_verify_step_workspace_bytes(B, K, V), dtype=torch.uint8, device=dev())
+    sv.spec_verify_step(inp["hidden"], inp["W"], d_logits, d_acc, d_out, ws, draft_logits=inp["draft_logits"],
+                        draft_tokens=inp["drafts"], temperature=wl.temperature, seeds=seeds_tensor(inp["seeds"]),
+                        greedy_rows=torch.as_tensor(np.asarray(gr, np.int32), device=dev()),
+                        sampled_rows=torch.as_tensor(np.asarray(sm, np.int32), device=dev()), probs_at_draft=d_pad)
+    torch.cuda.synchronize()
+    assert torch.equal(logits, d_logits.view(B * P, V))
+    np.testing.assert_array_equal(acc, d_acc.cpu().numpy())
+    np.testing.assert_array_equal(out, d_out.cpu().numpy().reshape(-1))
+    p_r, p_d = pad.reshape(B, K, 2)[sm], d_pad.cpu().numpy()[sm]
+    np.testing.assert_array_equal(p_r, p_d)
+
+
+def test_ragged_step_malformed_offsets():
+    B, K_max, H, V = 5, 3, 256, 2000
+    wl, inp, rs, hp, zdp, dp = _step_inputs(B, K_max, H, V, "bf16", seed=5, counts=[1, 2, 0, 3, 1])
+    bad = rs.copy()
+    bad[2] = bad[3] + 1          # sequence 1: K_1 = 4 > K_max; sequence 2: K_2 = -2
+    say("ragged step, malformed offsets %s -> %s" % (rs.tolist(), bad.tolist()))
+    for gr, sm in (([0, 1, 2], [3, 4]), (None, "all")):
+        _, acc, out, _ = _ragged_step(hp, inp["W"], bad, K_max, zdp, dp, wl.temperature, inp["seeds"], gr, sm)
+        assert acc[1] == -1 and acc[2] == -1, acc
+        np.testing.assert_array_equal(out[rs[1]:rs[3]], -9)      # rows of sequences 1 and 2 never written
+        R = hp.shape[0]
+        ref = gpu_logits(hp.view(R, 1, H), inp["W"]).view(R, V)
+        res = oracle.accept_sample_ragged(ref.double().cpu().numpy(), zdp.double().cpu().numpy(), dp.cpu().numpy(),
+                                          bad, K_max, wl.temperature, inp["seeds"], [3, 4])
+        _compare("sample", res, acc, out, rs, [3, 4])
+
+
+def test_full_size_ragged_step():
+    wl = synth.WORKLOADS["b64_k0to7_h4096_v128256"]
+    counts = synth.draft_counts(wl.B, wl.K, wl.data_seed)
+    rs = synth.row_start(counts)
+    say("full-size packed workload %s through the one-call step, R=%d" % (wl.name, int(rs[-1])))
+    inp = synth.round_inputs(wl, 0, device=dev())
+    hp = synth.pack_rows(inp["hidden"], counts).contiguous()
+    zdp = synth.pack_rows(inp["draft_logits"], counts, True).contiguous()
+    dp = synth.pack_rows(inp["drafts"], counts, True).contiguous()
+    sm = inp["sampled"]
+    _check_step(wl, inp, rs, hp, zdp, dp, np.nonzero(~sm)[0], np.nonzero(sm)[0])
