@@ -26,9 +26,9 @@ namespace sv {
 // caches; small ones keep them cached for the accept kernels' reads of the
 // terminal rows that follow.  VEC (V % 4 == 0): four 128-bit loads, else
 // sixteen 32-bit loads.  No load sits in a branch: entries past V read an
-// in-range address and become -inf.  (With a vector/scalar branch per load
-// the compiler waited for the first loads before issuing the last one, which
-// halved the bytes in flight.)
+// in-range address (with a vector/scalar branch per load the compiler waited
+// for the first loads before issuing the last one, which halved the bytes in
+// flight); mask_tail then sets them to -inf, in the last chunk of a row only.
 template <bool STREAM, bool VEC>
 __device__ __forceinline__ void load_chunk(const float* __restrict__ row, int v_begin, int V, int tid,
                                            float x[kStatPerThread]) {
@@ -43,18 +43,23 @@ __device__ __forceinline__ void load_chunk(const float* __restrict__ row, int v_
                 f = __builtin_nontemporal_load(p);
             else
                 f = *p;
-            const bool in = v < V;   // V % 4 == 0: all four entries or none
-            x[4 * q + 0] = in ? f.x : -INFINITY;
-            x[4 * q + 1] = in ? f.y : -INFINITY;
-            x[4 * q + 2] = in ? f.z : -INFINITY;
-            x[4 * q + 3] = in ? f.w : -INFINITY;
+            x[4 * q + 0] = f.x;
+            x[4 * q + 1] = f.y;
+            x[4 * q + 2] = f.z;
+            x[4 * q + 3] = f.w;
         } else {
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const float f = row[min(v + e, V - 1)];
-                x[4 * q + e] = v + e < V ? f : -INFINITY;
-            }
+            for (int e = 0; e < 4; ++e) x[4 * q + e] = row[min(v + e, V - 1)];
         }
+    }
+}
+
+__device__ __forceinline__ void mask_tail(int v_begin, int V, int tid, float x[kStatPerThread]) {
+#pragma unroll
+    for (int q = 0; q < kStatPerThread / 4; ++q) {
+        const int v = v_begin + (q * kStatThreads + tid) * 4;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) x[4 * q + e] = v + e < V ? x[4 * q + e] : -INFINITY;
     }
 }
 
@@ -69,6 +74,7 @@ __global__ __launch_bounds__(kStatThreads) void softmax_stats_kernel(
     __shared__ float sm[kStatThreads / kWave];
     __shared__ int si[kStatThreads / kWave];
     __shared__ int sb[kStatThreads / kWave];
+    __shared__ float ss[kStatThreads / kWave];
 
     const int K = seq.K;
     // completion counters and poll slots of a fused accept + residual launch
@@ -108,54 +114,71 @@ __global__ __launch_bounds__(kStatThreads) void softmax_stats_kernel(
     const int v_begin = chunk * kChunk;
     float x[kStatPerThread];
     load_chunk<STREAM, VEC>(row, v_begin, V, tid, x);
+    if (v_begin + kChunk > V) mask_tail(v_begin, V, tid, x);   // the same for the whole workgroup
 
-    float m = -INFINITY;
-    int mi = INT_MAX;
-    int bad = 0;
+    // The pass is bound by its arithmetic per element, not by the loads, so
+    // each element costs a compare for the data check, a compare-select for
+    // the maximum and one fma, exp and add for the sum; the index of the
+    // maximum is searched for only by the threads that hold it.
+    //   bad: some entry is NaN or +inf (the row is unusable);
+    //   tm:  the thread's maximum (NaN never compares greater).
+    bool bad = false;
+    float tm = -INFINITY;
 #pragma unroll
     for (int k = 0; k < kStatPerThread; ++k) {
-        float z = x[k];
-        if (z != z || z == INFINITY) {  // NaN or +inf: the row is unusable
-            bad = 1;
-            z = -INFINITY;
-            x[k] = -INFINITY;
-        }
-        if (z > m) {  // ascending index within a thread: strict > keeps the first
-            m = z;
-            mi = chunk_index(v_begin, tid, k);
-        }
+        bad = bad || !(x[k] < INFINITY);
+        tm = fmaxf(tm, x[k]);
     }
-    wave_argmax(m, mi);
     const int lane = tid & 63, wave = tid >> 6;
+    const float wm = wave_max(tm);
     const unsigned long long anybad = __ballot(bad);
     if (lane == 0) {
-        sm[wave] = m;
-        si[wave] = mi;
+        sm[wave] = wm;
         sb[wave] = anybad != 0ull;
     }
     __syncthreads();
     float bm = sm[0];
-    int bi = si[0];
     int bbad = sb[0];
 #pragma unroll
     for (int w = 1; w < kStatThreads / kWave; ++w) {
-        argmax_combine(bm, bi, sm[w], si[w]);
+        bm = max_cs(bm, sm[w]);
         bbad |= sb[w];
     }
+    if (bbad) {   // canonical record of an unusable chunk: only its flag is read
+        if (tid == 0) stats[slot] = StatRec{-INFINITY, 0.f, INT_MAX, 1};
+        return;
+    }
 
+    // lowest index attaining the maximum: a thread's indices ascend with k
+    int mi = INT_MAX;
+    if (tm == bm && bm != -INFINITY) {
+#pragma unroll
+        for (int k = kStatPerThread - 1; k >= 0; --k)
+            if (x[k] == bm) mi = chunk_index(v_begin, tid, k);
+    }
     float s = 0.f;
     if (NEED_SUM && bm != -INFINITY) {
+        const float mc = bm * c;
 #pragma unroll
-        for (int k = 0; k < kStatPerThread; ++k) s += exp2f((x[k] - bm) * c);
+        for (int k = 0; k < kStatPerThread; ++k) s += __builtin_amdgcn_exp2f(fmaf(x[k], c, -mc));
         s = wave_sum(s);
-        __syncthreads();  // everyone has read sm before it is reused
-        if (lane == 0) sm[wave] = s;
-        __syncthreads();
-        s = sm[0];
-#pragma unroll
-        for (int w = 1; w < kStatThreads / kWave; ++w) s += sm[w];
     }
-    if (tid == 0) stats[slot] = StatRec{bm, s, bi, bbad};
+    mi = wave_min(mi);
+    if (lane == 0) {
+        si[wave] = mi;
+        ss[wave] = s;
+    }
+    __syncthreads();
+    if (tid == 0) {
+        int bi = si[0];
+        float bs = ss[0];
+#pragma unroll
+        for (int w = 1; w < kStatThreads / kWave; ++w) {
+            bi = min(bi, si[w]);
+            bs += ss[w];
+        }
+        stats[slot] = StatRec{bm, bs, bi, 0};
+    }
 }
 
 // Fold the LM-head epilogue's records (one per 256 vocabulary entries of a

@@ -130,6 +130,28 @@ __device__ __forceinline__ float wave_sum(float x) {
     return x;
 }
 
+// Maximum of values that are never NaN (compare-select: no canonicalising
+// of the operands) and minimum of ints, over the wavefront.
+__device__ __forceinline__ float max_cs(float a, float b) { return b > a ? b : a; }
+__device__ __forceinline__ float wave_max(float x) {
+    x = max_cs(x, as_f(dpp_xor1(as_i(x))));
+    x = max_cs(x, as_f(dpp_xor2(as_i(x))));
+    x = max_cs(x, as_f(dpp_half_mirror(as_i(x))));
+    x = max_cs(x, as_f(dpp_mirror(as_i(x))));
+    x = max_cs(x, __shfl_xor(x, 16, kWave));
+    x = max_cs(x, __shfl_xor(x, 32, kWave));
+    return x;
+}
+__device__ __forceinline__ int wave_min(int x) {
+    x = min(x, dpp_xor1(x));
+    x = min(x, dpp_xor2(x));
+    x = min(x, dpp_half_mirror(x));
+    x = min(x, dpp_mirror(x));
+    x = min(x, __shfl_xor(x, 16, kWave));
+    x = min(x, __shfl_xor(x, 32, kWave));
+    return x;
+}
+
 __device__ __forceinline__ void wave_argmax(float& m, int& i) {
     row16_argmax(m, i);
 #pragma unroll
