@@ -40,7 +40,10 @@ constexpr long kResidualSplitBlocks = 4096;
 
 // w_v for the terminal row: q_n(v) - p_n(v) clipped at 0, or q_n(v) itself,
 // each probability as one exp2 with its normaliser folded into the exponent:
-// q = 2^((z - M) c - log2 S).
+// q = 2^((z - M) c - log2 S).  The exp2 is the hardware instruction alone:
+// a probability below 2^-126 becomes 0 (exp2f would rescale to keep it as a
+// denormal, at five more instructions per exp2, and the draws are
+// bandwidth-bound only without them).
 struct TermNorm {
     float mt, lst, md, lsd;   // maxima and log2 of the sums of the terminal rows
 };
@@ -48,9 +51,9 @@ __device__ __forceinline__ TermNorm term_norm(const AcceptInfo& a) {
     return TermNorm{a.mt, log2f(a.st), a.md, a.sd > 0.f ? log2f(a.sd) : 0.f};
 }
 __device__ __forceinline__ float term_weight(float zt, float zd, const TermNorm& t, float c, bool use_q) {
-    const float q = exp2f(fmaf(zt - t.mt, c, -t.lst));
+    const float q = __builtin_amdgcn_exp2f(fmaf(zt - t.mt, c, -t.lst));
     if (use_q) return q;
-    const float p = exp2f(fmaf(zd - t.md, c, -t.lsd));
+    const float p = __builtin_amdgcn_exp2f(fmaf(zd - t.md, c, -t.lsd));
     return fmaxf(q - p, 0.f);
 }
 
@@ -89,11 +92,15 @@ template <bool USE_Q, int PER>
 __device__ __forceinline__ void chunk_weigh(const float zt[PER], const float zd[PER], int v_begin, int V, int tid,
                                             const TermNorm& tn, float c, float w[PER]) {
 #pragma unroll
-    for (int k = 0; k < PER; ++k) {
-        // computed for every entry (past V from a valid duplicate), then masked
-        const int v = v_begin + ((k >> 2) * kStatThreads + tid) * 4 + (k & 3);
-        const float tw = term_weight(zt[k], USE_Q ? 0.f : zd[k], tn, c, USE_Q);
-        w[k] = v < V ? tw : 0.f;
+    for (int k = 0; k < PER; ++k) w[k] = term_weight(zt[k], USE_Q ? 0.f : zd[k], tn, c, USE_Q);
+    // entries past V were weighed from a valid duplicate: zero them, in the
+    // last chunk of a row only (the test is the same for the whole workgroup)
+    if (v_begin + PER * kStatThreads > V) {
+#pragma unroll
+        for (int k = 0; k < PER; ++k) {
+            const int v = v_begin + ((k >> 2) * kStatThreads + tid) * 4 + (k & 3);
+            w[k] = v < V ? w[k] : 0.f;
+        }
     }
 }
 template <bool VEC, bool USE_Q, int PER>
