@@ -64,7 +64,20 @@ __device__ __forceinline__ float term_weight(float zt, float zd, const TermNorm&
 // sits in a branch (entries past V read an in-range address and get weight
 // 0), so all of a thread's loads are in flight together.  Two phases, so a
 // caller can have the next chunk's loads in flight while it weighs this one.
-template <bool VEC, bool USE_Q, int PER>
+template <bool NT>
+__device__ __forceinline__ float4 load4(const float* p) {
+    if constexpr (NT) {
+        typedef float f4v __attribute__((ext_vector_type(4)));
+        const f4v f = __builtin_nontemporal_load(reinterpret_cast<const f4v*>(p));
+        return float4{f.x, f.y, f.z, f.w};
+    } else {
+        return *reinterpret_cast<const float4*>(p);
+    }
+}
+
+// NT: stream the rows past the caches (the split draw of large batches,
+// whose terminal rows were not read recently).
+template <bool VEC, bool USE_Q, int PER, bool NT = false>
 __device__ __forceinline__ void chunk_load(const float* __restrict__ zt_row, const float* __restrict__ zd_row,
                                            int v_begin, int V, int tid, float zt[PER], float zd[PER]) {
 #pragma unroll
@@ -72,10 +85,10 @@ __device__ __forceinline__ void chunk_load(const float* __restrict__ zt_row, con
         const int v = v_begin + (q * kStatThreads + tid) * 4;
         if constexpr (VEC) {
             const int vc = min(v, V - 4);
-            const float4 f = *reinterpret_cast<const float4*>(zt_row + vc);
+            const float4 f = load4<NT>(zt_row + vc);
             zt[4 * q] = f.x; zt[4 * q + 1] = f.y; zt[4 * q + 2] = f.z; zt[4 * q + 3] = f.w;
             if constexpr (!USE_Q) {
-                const float4 g = *reinterpret_cast<const float4*>(zd_row + vc);
+                const float4 g = load4<NT>(zd_row + vc);
                 zd[4 * q] = g.x; zd[4 * q + 1] = g.y; zd[4 * q + 2] = g.z; zd[4 * q + 3] = g.w;
             }
         } else {
@@ -103,26 +116,26 @@ __device__ __forceinline__ void chunk_weigh(const float zt[PER], const float zd[
         }
     }
 }
-template <bool VEC, bool USE_Q, int PER>
+template <bool VEC, bool USE_Q, int PER, bool NT>
 __device__ __forceinline__ void chunk_weights_impl(const float* __restrict__ zt_row, const float* __restrict__ zd_row,
                                                    int v_begin, int V, int tid, const TermNorm& tn, float c,
                                                    float w[PER]) {
     float zt[PER], zd[PER];
-    chunk_load<VEC, USE_Q, PER>(zt_row, zd_row, v_begin, V, tid, zt, zd);
+    chunk_load<VEC, USE_Q, PER, NT>(zt_row, zd_row, v_begin, V, tid, zt, zd);
     chunk_weigh<USE_Q, PER>(zt, zd, v_begin, V, tid, tn, c, w);
 }
 
-template <int PER = kStatPerThread>
+template <int PER = kStatPerThread, bool NT = false>
 __device__ __forceinline__ void chunk_weights(const float* __restrict__ zt_row, const float* __restrict__ zd_row,
                                               int v_begin, int V, bool vec, int tid, const AcceptInfo& a, float c,
                                               bool use_q, float w[PER]) {
     const TermNorm tn = term_norm(a);
     if (vec) {
-        if (use_q) chunk_weights_impl<true, true, PER>(zt_row, zd_row, v_begin, V, tid, tn, c, w);
-        else chunk_weights_impl<true, false, PER>(zt_row, zd_row, v_begin, V, tid, tn, c, w);
+        if (use_q) chunk_weights_impl<true, true, PER, NT>(zt_row, zd_row, v_begin, V, tid, tn, c, w);
+        else chunk_weights_impl<true, false, PER, NT>(zt_row, zd_row, v_begin, V, tid, tn, c, w);
     } else {
-        if (use_q) chunk_weights_impl<false, true, PER>(zt_row, zd_row, v_begin, V, tid, tn, c, w);
-        else chunk_weights_impl<false, false, PER>(zt_row, zd_row, v_begin, V, tid, tn, c, w);
+        if (use_q) chunk_weights_impl<false, true, PER, NT>(zt_row, zd_row, v_begin, V, tid, tn, c, w);
+        else chunk_weights_impl<false, false, PER, NT>(zt_row, zd_row, v_begin, V, tid, tn, c, w);
     }
 }
 
@@ -455,7 +468,8 @@ __global__ __launch_bounds__(kStatThreads) void residual_sums_kernel(
     if (a.n < 0) return;
     const TermRows tr = term_rows(logits, draft_logits, a, V);
     float w[kStatPerThread];
-    chunk_weights(tr.zt, tr.zd, chunk * kChunk, V, (V & 3) == 0, threadIdx.x, a, c, tr.bonus, w);
+    chunk_weights<kStatPerThread, true>(tr.zt, tr.zd, chunk * kChunk, V, (V & 3) == 0, threadIdx.x, a, c, tr.bonus,
+                                        w);
     float s = 0.f;
 #pragma unroll
     for (int k = 0; k < kStatPerThread; ++k) s += w[k];
