@@ -1065,40 +1065,52 @@ __global__ __launch_bounds__(NW * 64, 1) void lmhead_big_bf16(
         // then the kWN waves side by side along the vocabulary, in order,
         // through the LDS ring (free once every wave is past its last slice);
         // the logits follow, staged above these records.
-        // No per-entry checks: fmaxf skips NaN and a NaN or +inf shows in the
-        // maximum or the sum, which marks the row bad; entries past V are
-        // masked only in the last vocabulary tile.
+        // No per-entry checks: NaN never wins the maximum, and a NaN or +inf
+        // shows in the maximum or the sum, which marks the row bad; entries
+        // past V are masked only in the last vocabulary tile.
         __syncthreads();
         StatRec* part = reinterpret_cast<StatRec*>(smem);   // [kWN][BM]
-        const bool full = v0 + wn + 32 * NA <= V;
+        // This loop runs after the main loop with the matrix cores idle, so
+        // its vector instructions count: per entry a compare and two selects
+        // for the maximum and its index (NaN never compares greater), then
+        // fma, exp and add for the sum.  The mask past V is a separate copy of
+        // the loop, taken by the last vocabulary tile only.
+        const auto fold_rows = [&](auto masked) {
 #pragma unroll
-        for (int b = 0; b < NB; ++b) {
-            float mx = -INFINITY;
-            int mi = INT_MAX;
+            for (int b = 0; b < NB; ++b) {
+                float mx = -INFINITY;
+                int mi = INT_MAX;
 #pragma unroll
-            for (int a = 0; a < NA; ++a)
+                for (int a = 0; a < NA; ++a)
 #pragma unroll
-                for (int i = 0; i < 16; ++i) {
-                    const int v = v0 + wn + a * 32 + 8 * (i / 4) + 4 * h + (i % 4);
-                    const float z = (full || v < V) ? acc[a][b][i] : -INFINITY;
-                    mi = z > mx ? v : mi;
-                    mx = fmaxf(mx, z);
-                }
-            argmax_combine(mx, mi, __shfl_xor(mx, 32, kWave), __shfl_xor(mi, 32, kWave));
-            const float mc = (mx == -INFINITY ? 0.f : mx) * c;
-            float sum = 0.f;
+                    for (int i = 0; i < 16; ++i) {
+                        const int v = v0 + wn + a * 32 + 8 * (i / 4) + 4 * h + (i % 4);
+                        const float z = (!masked || v < V) ? acc[a][b][i] : -INFINITY;
+                        if (z > mx) {   // ascending index within a lane: strict > keeps the first
+                            mx = z;
+                            mi = v;
+                        }
+                    }
+                argmax_combine(mx, mi, __shfl_xor(mx, 32, kWave), __shfl_xor(mi, 32, kWave));
+                const float mc = (mx == -INFINITY ? 0.f : mx) * c;
+                float sum = 0.f;
 #pragma unroll
-            for (int a = 0; a < NA; ++a)
+                for (int a = 0; a < NA; ++a)
 #pragma unroll
-                for (int i = 0; i < 16; ++i) {
-                    const int v = v0 + wn + a * 32 + 8 * (i / 4) + 4 * h + (i % 4);
-                    const float z = (full || v < V) ? acc[a][b][i] : -INFINITY;
-                    sum += __builtin_amdgcn_exp2f(fmaf(z, c, -mc));
-                }
-            sum += __shfl_xor(sum, 32, kWave);
-            const int bad = mx == INFINITY || sum != sum;
-            if (h == 0) part[(wave % G::kWN) * G::kBM + wm + b * 32 + r] = StatRec{mx, sum, mi, bad};
-        }
+                    for (int i = 0; i < 16; ++i) {
+                        const int v = v0 + wn + a * 32 + 8 * (i / 4) + 4 * h + (i % 4);
+                        const float z = (!masked || v < V) ? acc[a][b][i] : -INFINITY;
+                        sum += __builtin_amdgcn_exp2f(fmaf(z, c, -mc));
+                    }
+                sum += __shfl_xor(sum, 32, kWave);
+                const int bad = mx == INFINITY || sum != sum;
+                if (h == 0) part[(wave % G::kWN) * G::kBM + wm + b * 32 + r] = StatRec{mx, sum, mi, bad};
+            }
+        };
+        if (v0 + wn + 32 * NA <= V)
+            fold_rows(std::false_type{});
+        else
+            fold_rows(std::true_type{});
         __syncthreads();
         for (int row = threadIdx.x; row < G::kBM; row += G::kThreads) {
             if (m0 + row >= M) continue;
