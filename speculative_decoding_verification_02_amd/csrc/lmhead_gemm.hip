@@ -303,27 +303,6 @@ struct Coop {
     static bool fits(int M, int H) { return M <= 16 && H <= NW * kSlice; }
 };
 
-// Records of the entries z[0..n) at vocabulary indices v0 + j*step: max,
-// sum of 2^((z - max) c), first index attaining the max, bad flag.  The
-// sum runs over every entry (with the max taken as 0 when there is none),
-// so a NaN anywhere makes it NaN.
-template <int N>
-__device__ __forceinline__ void coop_fold(StatRec& a, const float (&z)[N], int v0, int step, float c) {
-    float bm = -INFINITY;
-    int bi = INT_MAX;
-#pragma unroll
-    for (int j = 0; j < N; ++j)
-        if (z[j] > bm) {   // indices ascend with j: strict > keeps the first
-            bm = z[j];
-            bi = v0 + j * step;
-        }
-    const float mc = (bm == -INFINITY ? 0.f : bm) * c;
-    float bs = 0.f;
-#pragma unroll
-    for (int j = 0; j < N; ++j) bs += exp2f(fmaf(z[j], c, -mc));
-    stat_fold(a, bm, bs, bi, (bs != bs) | (bm == INFINITY), c);
-}
-
 template <int RPL, int MAXST, int NW, bool STATS, bool STASH, int PIPE>
 __global__ __launch_bounds__(NW * 64) void lmhead_coop_bf16(
     const uint16_t* __restrict__ hidden, const uint16_t* __restrict__ W, float* __restrict__ logits,
