@@ -509,10 +509,10 @@ __global__ __launch_bounds__(NW * 64) void lmhead_coop_bf16(
                         bm = z[k];
                         bi = dcb + c0 + 128 * (k / 4) + 4 * l32 + (k % 4);
                     }
-                const float mc = (bm == -INFINITY ? 0.f : bm) * cs.c;
+                const float mz = bm == -INFINITY ? 0.f : bm;   // (z - max) c: exact at the maximum
                 float bs = 0.f;
 #pragma unroll
-                for (int k = 0; k < 16; ++k) bs += __builtin_amdgcn_exp2f(fmaf(z[k], cs.c, -mc));
+                for (int k = 0; k < 16; ++k) bs += __builtin_amdgcn_exp2f((z[k] - mz) * cs.c);
                 stat_fold(a, bm, bs, bi, (bs != bs) | (bm == INFINITY), cs.c);
             }
             // the 32 lanes of the group: DPP within each 16-lane row, then
@@ -1052,7 +1052,7 @@ __global__ __launch_bounds__(NW * 64, 1) void lmhead_big_bf16(
         // This loop runs after the main loop with the matrix cores idle, so
         // its vector instructions count: per entry a compare and two selects
         // for the maximum and its index (NaN never compares greater), then
-        // fma, exp and add for the sum.  The mask past V is a separate copy of
+        // subtract, multiply, exp and add for the sum.  The mask past V is a separate copy of
         // the loop, taken by the last vocabulary tile only.
         const auto fold_rows = [&](auto masked) {
 #pragma unroll
@@ -1071,7 +1071,9 @@ __global__ __launch_bounds__(NW * 64, 1) void lmhead_big_bf16(
                         }
                     }
                 argmax_combine(mx, mi, __shfl_xor(mx, 32, kWave), __shfl_xor(mi, 32, kWave));
-                const float mc = (mx == -INFINITY ? 0.f : mx) * c;
+                // (z - max) c, not z c - max c: the second rounds max c, an
+                // absolute error in every exponent that grows as T shrinks
+                const float mz = mx == -INFINITY ? 0.f : mx;
                 float sum = 0.f;
 #pragma unroll
                 for (int a = 0; a < NA; ++a)
@@ -1079,7 +1081,7 @@ __global__ __launch_bounds__(NW * 64, 1) void lmhead_big_bf16(
                     for (int i = 0; i < 16; ++i) {
                         const int v = v0 + wn + a * 32 + 8 * (i / 4) + 4 * h + (i % 4);
                         const float z = (!masked || v < V) ? acc[a][b][i] : -INFINITY;
-                        sum += __builtin_amdgcn_exp2f(fmaf(z, c, -mc));
+                        sum += __builtin_amdgcn_exp2f((z - mz) * c);
                     }
                 sum += __shfl_xor(sum, 32, kWave);
                 const int bad = mx == INFINITY || sum != sum;

@@ -116,10 +116,13 @@ __global__ __launch_bounds__(kStatThreads) void softmax_stats_kernel(
     load_chunk<STREAM, VEC>(row, v_begin, V, tid, x);
     if (v_begin + kChunk > V) mask_tail(v_begin, V, tid, x);   // the same for the whole workgroup
 
-    // The pass is bound by its arithmetic per element, not by the loads, so
-    // each element costs a compare for the data check, a compare-select for
-    // the maximum and one fma, exp and add for the sum; the index of the
-    // maximum is searched for only by the threads that hold it.
+    // The pass was bound by its arithmetic per element, not by the loads, so
+    // each element costs a compare for the data check, half a max3 for the
+    // maximum and a subtract, multiply, exp and add for the sum; the index of
+    // the maximum is searched for only by the threads that hold it.  The
+    // exponent is (z - max) c, exact at the maximum: z c - max c would round
+    // max c, an error in every term that grows as T shrinks (1e-5 in the
+    // probabilities at T = 0.05).
     //   bad: some entry is NaN or +inf (the row is unusable);
     //   tm:  the thread's maximum (NaN never compares greater).
     bool bad = false;
@@ -158,9 +161,8 @@ __global__ __launch_bounds__(kStatThreads) void softmax_stats_kernel(
     }
     float s = 0.f;
     if (NEED_SUM && bm != -INFINITY) {
-        const float mc = bm * c;
 #pragma unroll
-        for (int k = 0; k < kStatPerThread; ++k) s += __builtin_amdgcn_exp2f(fmaf(x[k], c, -mc));
+        for (int k = 0; k < kStatPerThread; ++k) s += __builtin_amdgcn_exp2f((x[k] - bm) * c);
         s = wave_sum(s);
     }
     mi = wave_min(mi);

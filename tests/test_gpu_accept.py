@@ -220,3 +220,29 @@ def test_largest_vocabulary():
     res = oracle.accept_sample(zt.double().numpy(), zd.double().numpy(), d.numpy(), T, seeds)
     c.merge(compare_sample(res, acc.cpu().numpy(), out.cpu().numpy(), range(B)))
     say("  " + str(c))
+
+
+@pytest.mark.parametrize("T", [0.05, 0.25, 4.0])
+def test_sample_extreme_temperatures(T):
+    """Very sharp and very flat distributions at full vocabulary.  At T = 0.05
+    (logits of spread 2, so z/T spreads over ~40) almost every term of the
+    softmax sums and residual weights underflows: the kernels flush
+    probabilities below 2^-126 to zero, which moves a sum by less than its
+    own rounding.  At T = 4 every one of the 128256 terms counts.  All
+    sequences (statistics pass, counted residual), eight of them (polled
+    residual) and one (acceptance and draw in one launch), each against the
+    oracle by the margin rule, probabilities within PROB_ATOL."""
+    B, K, V = 64, 4, 128256
+    zt, zd = _logits(B, K, V, seed=int(T * 1000) + 7, scale=2.0, sigma=0.6)
+    d = _sampled_drafts(zd, T, seed=int(T * 100) + 3)
+    seeds = np.arange(B, dtype=np.uint64) * np.uint64(7919) + np.uint64(int(T * 100))
+    res = oracle.accept_sample(zt.numpy(), zd.numpy(), d.numpy(), T, seeds)
+    zt_d, zd_d, d_d = zt.to(dev()), zd.to(dev()), d.to(dev())
+    for rows in (None, np.arange(8, dtype=np.int32) * 7, np.array([5], np.int32)):
+        sel = range(B) if rows is None else rows
+        say("sampled parity at T=%g, B=%d K=%d V=%d, %d sequences" % (T, B, K, V, len(sel)))
+        acc, out, pad = gpu_accept_sample(zt_d, zd_d, d_d, T, seeds, rows=rows, probs=True)
+        acc, out, pad = acc.cpu().numpy(), out.cpu().numpy(), pad.cpu().numpy()
+        c = compare_sample(res, acc, out, sel)
+        say("  " + str(c) + " accepted=%s" % np.bincount(acc[list(sel)], minlength=K + 1).tolist())
+        np.testing.assert_allclose(pad[list(sel)], res.probs_at_draft[list(sel)], rtol=0, atol=PROB_ATOL)

@@ -166,3 +166,16 @@ def test_step_full_size(name):
     say("fused step, full-size workload %s" % name)
     sm = synth.sampled_mask(wl)
     _check(wl, np.nonzero(~sm)[0], np.nonzero(sm)[0])
+
+
+@pytest.mark.parametrize("B,K,H,V,path", [(1, 5, 512, 128256, "cooperative LM head statistics"),
+                                          (8, 4, 256, 128256, "direct-to-LDS epilogue statistics")])
+@pytest.mark.parametrize("T", [0.05, 4.0])
+def test_step_extreme_temperatures(B, K, H, V, path, T):
+    """The one-call step at a very sharp and a very flat temperature, half
+    the sequences greedy: the statistics the LM-head kernels compute on the
+    side (most terms underflow at T = 0.05) against the oracle."""
+    wl = _wl(B, K, H, V, T=T, seed=int(T * 100) + B)
+    say("fused step at T=%g, B=%d K=%d H=%d V=%d: %s" % (T, B, K, H, V, path))
+    half = B // 2
+    _check(wl, list(range(half)), list(range(half, B)))
