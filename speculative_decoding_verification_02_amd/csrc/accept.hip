@@ -118,9 +118,15 @@ __global__ __launch_bounds__(kAcceptThreads) void tree_accept_kernel(
         const StatRec* src = stats + ((size_t)(by_row ? b : j) * (N + 1) + r0) * nc;
         stage_records(recs, nr * nc, tid, [&](int e) { return src + e; });
         __syncthreads();
-        for (int rr = wave; rr < nr; rr += kAcceptWaves) {
-            const Merged x = wave_merge(recs + rr * nc, nc, 0.f, false, lane);
-            if (lane == 0) merged[r0 + rr] = x;
+        // one row per 16-lane DPP row: four rows per wavefront at a time
+        // (the argmax does not depend on the order records are combined in)
+        const int gl = lane & 15;
+        for (int base = wave * 4; base < nr; base += kAcceptWaves * 4) {
+            const int rr = base + (lane >> 4);
+            if (rr < nr) {
+                const Merged x = row16_merge(recs + rr * nc, nc, 0.f, false, gl);
+                if (gl == 0) merged[r0 + rr] = x;
+            }
         }
         __syncthreads();
     }
