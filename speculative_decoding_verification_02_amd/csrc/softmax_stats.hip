@@ -185,12 +185,14 @@ __global__ __launch_bounds__(kStatThreads) void softmax_stats_kernel(
 
 // Fold the LM-head epilogue's records (one per 256 vocabulary entries of a
 // row, in vocabulary order) into the chunk records the statistics pass
-// writes (one per kChunk entries): 16 lanes per chunk, lane t holding record
-// 16k + t, folded by a butterfly over the 16 lanes.  Both partners of a
-// butterfly step compute the same combination (the sum is commutative), so
-// every lane of a group ends with the same record; bad records contribute
-// only their flag, as in the epilogue's own fold.
+// writes (one per kChunk entries): 16 lanes per chunk, one DPP row, lane t
+// holding record 16k + t, combined by the DPP row all-reduce (xor 1, xor 2,
+// half-row mirror, row mirror).  Both partners of a step compute the same
+// combination (the sum is commutative), so every lane of the row ends with
+// the same record; bad records contribute only their flag, as in the
+// epilogue's own fold.
 constexpr int kRecsPerChunk = kChunk / 256;
+static_assert(kRecsPerChunk == 16, "one DPP row per chunk");
 
 __device__ __forceinline__ StatRec rec_combine(StatRec a, StatRec b, float c) {
     StatRec r;
@@ -201,16 +203,21 @@ __device__ __forceinline__ StatRec rec_combine(StatRec a, StatRec b, float c) {
         r.m = a.m; r.s = a.s; r.idx = a.idx;
     } else {
         r.m = fmaxf(a.m, b.m);
-        r.s = a.s * exp2f((a.m - r.m) * c) + b.s * exp2f((b.m - r.m) * c);
+        r.s = a.s * __builtin_amdgcn_exp2f((a.m - r.m) * c) + b.s * __builtin_amdgcn_exp2f((b.m - r.m) * c);
         r.idx = (a.m > b.m || (a.m == b.m && a.idx < b.idx)) ? a.idx : b.idx;
     }
     return r;
 }
 
+template <int (*MOVE)(int)>
+__device__ __forceinline__ StatRec rec_move(const StatRec& a) {
+    return StatRec{as_f(MOVE(as_i(a.m))), as_f(MOVE(as_i(a.s))), MOVE(a.idx), MOVE(a.bad)};
+}
+
 __global__ __launch_bounds__(kStatThreads) void fold_records_kernel(const StatRec* __restrict__ in, int recs, long items,
                                                                     int nc, float c, StatRec* __restrict__ out) {
     const long g = (long)blockIdx.x * (kStatThreads / kRecsPerChunk) + threadIdx.x / kRecsPerChunk;   // (row, chunk)
-    if (g >= items) return;   // whole 16-lane groups leave together
+    if (g >= items) return;   // whole 16-lane groups (DPP rows) leave together
     const int t = threadIdx.x % kRecsPerChunk;
     const long row = g / nc;
     const int chunk = (int)(g - row * nc);
@@ -220,15 +227,10 @@ __global__ __launch_bounds__(kStatThreads) void fold_records_kernel(const StatRe
         const StatRec x = in[row * recs + k];
         a = StatRec{x.bad ? -INFINITY : x.m, x.bad ? 0.f : x.s, x.idx, x.bad};
     }
-#pragma unroll
-    for (int o = kRecsPerChunk / 2; o > 0; o >>= 1) {
-        StatRec b;
-        b.m = __shfl_xor(a.m, o, kWave);
-        b.s = __shfl_xor(a.s, o, kWave);
-        b.idx = __shfl_xor(a.idx, o, kWave);
-        b.bad = __shfl_xor(a.bad, o, kWave);
-        a = rec_combine(a, b, c);
-    }
+    a = rec_combine(a, rec_move<dpp_xor1>(a), c);
+    a = rec_combine(a, rec_move<dpp_xor2>(a), c);
+    a = rec_combine(a, rec_move<dpp_half_mirror>(a), c);
+    a = rec_combine(a, rec_move<dpp_mirror>(a), c);
     if (t == 0) out[g] = a;
 }
 
